@@ -1,0 +1,180 @@
+"""Per-layer slot table as a step-by-step LRU simulator (oracle side, plain ints).
+
+What the pages fix:
+
+* each layer owns a fixed number of GPU slots holding copies of experts; the
+  routing yields two tables, expert -> GPU slot (-1 when not cached) and
+  expert -> CPU id (-1 when cached) ("How it works", llama.cpp + MoE expert
+  cache, step 2);
+* replacement is least-recently-used, independently per layer; the experts of
+  the current batch are planned together, those already needed by the batch
+  are protected from eviction and duplicate ids load once; when one step needs
+  more experts than there are slots, the routed computation runs in stages whose
+  partial results are summed (longhaul.md, "Longhaul MoE loading");
+* a slot leaves the table before its copy starts and is published after it
+  ("Keeping the cache fresh", llama.cpp + MoE expert cache).
+
+Readings taken where the pages are silent:
+
+* start: slot s holds expert s (s < S), last_use = 0, clock = 0;
+* per call: U = sorted unique selected ids; pre_view = the table at call start;
+  a selection is a hit when pre_view[e] >= 0 (counted per selection);
+* each stage: clock += 1; the stage's resident experts are protected
+  (last_use = clock); pending misses are taken in ascending id; the victim is the
+  lowest-index empty slot, else the slot with the smallest (last_use, index)
+  among last_use < clock; evict, insert, last_use = clock, log
+  (call, stage, slot, old expert, new expert); no victim -> the stage ends;
+* stream mode: every miss is filled; stage views map the experts of that stage
+  to their slot and every other expert to -1; the host table is all -1;
+* host mode: one stage; fills capped by max_fills (-1 = no cap), in ascending
+  id; the views are the full tables at call start (cached -> slot,
+  uncached -> -1 / uncached -> own id, cached -> -1); fills are visible from the
+  same layer's next call on.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Tuple
+
+STREAM = "stream"
+HOST = "host"
+
+
+@dataclass
+class PlanResult:
+    call: int
+    unique: List[int]
+    hits: int
+    misses: int
+    stage_views: List[List[int]]          # one slot view per stage
+    host_view: List[int]
+    evictions: List[Tuple[int, int, int, int, int]] = field(default_factory=list)
+    fills: int = 0
+    stage_experts: List[List[int]] = field(default_factory=list)
+
+
+class LayerSlots:
+    """LRU slot state of one layer."""
+
+    def __init__(self, n_experts: int, slots: int):
+        if not 1 <= slots <= n_experts:
+            raise ValueError("slots must be in [1, n_experts]")
+        self.E = n_experts
+        self.S = slots
+        self.expert_in = list(range(slots))
+        self.slot_of = [-1] * n_experts
+        for s in range(slots):
+            self.slot_of[s] = s
+        self.last_use = [0] * slots
+        self.clock = 0
+        self.calls = 0
+        self.log: List[Tuple[int, int, int, int, int]] = []
+        self.stats = dict(calls=0, selections=0, hits=0, misses=0, unique=0, fills=0,
+                          evictions=0, host_selections=0, stages=0)
+
+    # -- victim choice -------------------------------------------------------
+    def victim(self):
+        for s in range(self.S):
+            if self.expert_in[s] == -1:
+                return s
+        best = None
+        for s in range(self.S):
+            if self.last_use[s] < self.clock:
+                if best is None or self.last_use[s] < self.last_use[best]:
+                    best = s
+        return best
+
+    def _insert(self, call, stage, slot, e, log):
+        old = self.expert_in[slot]
+        if old >= 0:
+            self.slot_of[old] = -1
+            self.stats["evictions"] += 1
+        self.expert_in[slot] = e
+        self.slot_of[e] = slot
+        self.last_use[slot] = self.clock
+        rec = (call, stage, slot, old, e)
+        self.log.append(rec)
+        log.append(rec)
+        self.stats["fills"] += 1
+
+    # -- one call ------------------------------------------------------------
+    def plan(self, idx, mode: str = STREAM, max_fills: int = -1) -> PlanResult:
+        idx = [int(e) for e in idx]
+        for e in idx:
+            if not 0 <= e < self.E:
+                raise ValueError("expert id out of range")
+        call = self.calls
+        self.calls += 1
+        uniq = sorted(set(idx))
+        pre_view = list(self.slot_of)
+        hits = sum(1 for e in idx if pre_view[e] >= 0)
+        misses = len(idx) - hits
+        hit_experts = [e for e in uniq if pre_view[e] >= 0]
+        pending = [e for e in uniq if pre_view[e] < 0]
+        log: List[Tuple[int, int, int, int, int]] = []
+        views: List[List[int]] = []
+        stage_experts: List[List[int]] = []
+
+        if mode == STREAM:
+            stage = 0
+            while stage == 0 or pending:
+                self.clock += 1
+                members = []
+                if stage == 0:
+                    for e in hit_experts:
+                        self.last_use[self.slot_of[e]] = self.clock
+                        members.append(e)
+                placed = 0
+                for e in pending:
+                    v = self.victim()
+                    if v is None:
+                        break
+                    self._insert(call, stage, v, e, log)
+                    members.append(e)
+                    placed += 1
+                pending = pending[placed:]
+                view = [-1] * self.E
+                for e in members:
+                    view[e] = self.slot_of[e]
+                views.append(view)
+                stage_experts.append(sorted(members))
+                stage += 1
+            host_view = [-1] * self.E
+        elif mode == HOST:
+            self.clock += 1
+            for e in hit_experts:
+                self.last_use[self.slot_of[e]] = self.clock
+            placed = 0
+            for e in pending:
+                if max_fills >= 0 and placed >= max_fills:
+                    break
+                v = self.victim()
+                if v is None:
+                    break
+                self._insert(call, 0, v, e, log)
+                placed += 1
+            views.append(pre_view)
+            stage_experts.append(hit_experts)
+            host_view = [e if pre_view[e] < 0 else -1 for e in range(self.E)]
+            self.stats["host_selections"] += misses
+        else:
+            raise ValueError("mode must be 'stream' or 'host'")
+
+        st = self.stats
+        st["calls"] += 1
+        st["selections"] += len(idx)
+        st["hits"] += hits
+        st["misses"] += misses
+        st["unique"] += len(uniq)
+        st["stages"] += len(views)
+        return PlanResult(call=call, unique=uniq, hits=hits, misses=misses, stage_views=views,
+                          host_view=host_view, evictions=log, fills=len(log),
+                          stage_experts=stage_experts)
+
+    def check_invariants(self):
+        for s, e in enumerate(self.expert_in):
+            if e >= 0:
+                assert self.slot_of[e] == s
+        for e, s in enumerate(self.slot_of):
+            if s >= 0:
+                assert self.expert_in[s] == e

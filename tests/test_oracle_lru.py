@@ -1,0 +1,149 @@
+"""Pins of the LRU slot simulator (oracle/lru.py): hand-worked traces, the
+textbook LRU list for k = 1, S = E, a full-scan victim check and invariants."""
+import os
+import random
+from collections import OrderedDict
+
+import pytest
+
+from oracle.lru import HOST, STREAM, LayerSlots
+
+G = os.path.join(os.path.dirname(__file__), "golden", "lru_traces.txt")
+
+
+def _parse_traces():
+    traces = {}
+    for line in open(G):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        parts = [p.strip() for p in line.split("|")]
+        name = parts[0]
+        tr = traces.setdefault(name, {"calls": [], "views": [], "stages": None})
+        if parts[1].startswith("E="):
+            kv = dict(p.split("=") for p in parts[1].split())
+            tr.update(E=int(kv["E"]), S=int(kv["S"]), mode=kv["mode"], fills=int(kv["fills"]))
+        elif parts[1].startswith("call"):
+            idx = [int(v) for v in parts[2].split()[1:]]
+            hits = int(parts[3].split()[1])
+            ev_txt = parts[4][len("evict"):].strip()
+            evs = [] if ev_txt == "-" else [tuple(int(v) for v in t.strip("()").split(","))
+                                            for t in ev_txt.split()]
+            tr["calls"].append((idx, hits, evs))
+        elif parts[1] == "views":
+            sv = [int(v) for v in parts[2].split()[1:]]
+            hv = [int(v) for v in parts[3].split()[1:]]
+            tr["views"].append((sv, hv))
+        elif parts[1] == "stages":
+            tr["stages"] = [[int(e) for e in s.split(":")[1].split(",")] for s in parts[2].split()]
+        elif parts[1] == "final":
+            tr["final"] = [int(v) for v in parts[2].split()[1:]]
+    return traces
+
+
+TRACES = _parse_traces()
+
+
+@pytest.mark.parametrize("name", sorted(TRACES))
+def test_golden_trace(name):
+    tr = TRACES[name]
+    sim = LayerSlots(tr["E"], tr["S"])
+    for c, (idx, hits, evs) in enumerate(tr["calls"]):
+        res = sim.plan(idx, tr["mode"], tr["fills"])
+        assert res.hits == hits
+        assert res.evictions == evs
+        if tr["views"]:
+            sv, hv = tr["views"][c]
+            assert res.stage_views[0] == sv
+            assert res.host_view == hv
+        if tr["stages"] is not None:
+            assert res.stage_experts == tr["stages"]
+        sim.check_invariants()
+    assert sim.expert_in == tr["final"]
+
+
+def test_k1_host_mode_is_textbook_lru():
+    rnd = random.Random(5)
+    for e_count, s_count in ((5, 2), (8, 3), (16, 7), (4, 4)):
+        sim = LayerSlots(e_count, s_count)
+        lru = OrderedDict((e, None) for e in range(s_count))  # first = least recent
+        for _ in range(400):
+            e = rnd.randrange(e_count) if rnd.random() < 0.6 else rnd.randrange(min(3, e_count))
+            res = sim.plan([e], HOST)
+            if e in lru:
+                assert res.hits == 1 and res.evictions == []
+                lru.move_to_end(e)
+            else:
+                old, _ = lru.popitem(last=False)
+                lru[e] = None
+                assert res.hits == 0
+                assert [(r[3], r[4]) for r in res.evictions] == [(old, e)]
+            assert set(sim.expert_in) == set(lru)
+
+
+@pytest.mark.parametrize("mode", [STREAM, HOST])
+def test_slots_equal_experts_all_hits(mode):
+    rnd = random.Random(6)
+    sim = LayerSlots(16, 16)
+    for _ in range(100):
+        idx = rnd.sample(range(16), 4) + rnd.sample(range(16), 4)
+        res = sim.plan(idx, mode)
+        assert res.misses == 0 and res.hits == 8 and res.evictions == []
+    assert sim.stats["evictions"] == 0
+
+
+def _full_scan_victim(sim):
+    empty = [s for s in range(sim.S) if sim.expert_in[s] == -1]
+    if empty:
+        return empty[0]
+    cands = sorted((sim.last_use[s], s) for s in range(sim.S) if sim.last_use[s] < sim.clock)
+    return cands[0][1] if cands else None
+
+
+@pytest.mark.parametrize("mode", [STREAM, HOST])
+def test_invariants_random(mode):
+    rnd = random.Random(7)
+    for e_count, s_count, k, t in ((8, 4, 2, 1), (32, 5, 4, 3), (64, 8, 8, 4), (20, 2, 3, 6)):
+        sim = LayerSlots(e_count, s_count)
+        orig_victim = sim.victim
+        sim.victim = lambda: (lambda v: (v, _assert_eq(v, _full_scan_victim(sim)))[0])(orig_victim())
+        for _ in range(200):
+            idx = []
+            for _t in range(t):
+                idx += rnd.sample(range(e_count), k)
+            before_use = list(sim.last_use)
+            res = sim.plan(idx, mode, max_fills=rnd.choice([-1, -1, 0, 1, 2]) if mode == HOST else -1)
+            sim.check_invariants()
+            assert res.hits + res.misses == len(idx)
+            uniq = sorted(set(idx))
+            if mode == STREAM:
+                # every unique expert is computed in exactly one stage
+                flat = [e for st in res.stage_experts for e in st]
+                assert sorted(flat) == uniq
+                for v, members in zip(res.stage_views, res.stage_experts):
+                    assert sorted(e for e in range(e_count) if v[e] >= 0) == members
+                # within a stage, no stage member's slot is evicted in that stage
+                for (call, stage, slot, old, new) in res.evictions:
+                    assert old not in res.stage_experts[stage]
+            else:
+                hits = [e for e in uniq if res.stage_views[0][e] >= 0]
+                evicted = [r[3] for r in res.evictions]
+                assert not set(hits) & set(evicted)
+                for e in range(e_count):
+                    assert (res.stage_views[0][e] >= 0) != (res.host_view[e] >= 0)
+            del before_use
+
+
+def _assert_eq(a, b):
+    assert a == b
+    return True
+
+
+def test_stream_stage_count_closed_form():
+    # cold selection of all E experts with S slots: ceil((E - S) / S) fill stages
+    # after the stage of the S initial hits.
+    for e_count, s_count in ((8, 2), (9, 2), (256, 64), (12, 5)):
+        sim = LayerSlots(e_count, s_count)
+        res = sim.plan(list(range(e_count)), STREAM)
+        assert len(res.stage_views) == 1 + -(-(e_count - s_count) // s_count)
+        assert res.hits == s_count and res.fills == e_count - s_count
