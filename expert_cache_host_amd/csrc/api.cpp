@@ -1,0 +1,829 @@
+// C ABI of libmoecache (declared in include/moe_cache.h).
+//
+// Per layer: a page-locked host arena holding every expert in the slot layout,
+// a device arena of (slots + n_shared) records, an LRU planner and the record
+// of its last call.  One side stream carries slot fills; the caller's stream
+// carries the compute.  The copy protocol follows "Keeping the cache fresh"
+// (llama.cpp + MoE expert cache): a slot leaves the table before its copy and
+// is published after it, so no kernel ever reads a half-copied expert.  Here
+// the publication points are fixed (stream mode: before the stage that needs
+// the slot; host mode: the same layer's next call), which makes every table a
+// deterministic function of the routing history.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <cstdio>
+#include <cstring>
+#include <memory>
+#include <new>
+#include <stdexcept>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/moe_cache.h"
+#include "host_expert.hpp"
+#include "kernels.hpp"
+#include "layout.hpp"
+#include "planner.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const std::string &msg) {
+  g_err = msg;
+  return st;
+}
+
+struct HipError : std::runtime_error {
+  using std::runtime_error::runtime_error;
+};
+
+#define HIPCHK(expr)                                                                      \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess)                                                                 \
+      throw HipError(std::string(#expr) + ": " + hipGetErrorString(e_));                  \
+  } while (0)
+
+double now_s() {
+  return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch())
+      .count();
+}
+
+int default_threads() {
+  unsigned n = std::thread::hardware_concurrency();
+  return n > 1 ? (int)n - 1 : 1;
+}
+
+struct PinnedBuf {
+  void *p = nullptr;
+  size_t bytes = 0;
+  void ensure(size_t n) {
+    if (n <= bytes) return;
+    if (p) (void)hipHostFree(p);
+    p = nullptr;
+    bytes = 0;
+    HIPCHK(hipHostMalloc(&p, n, hipHostMallocDefault));
+    bytes = n;
+  }
+  ~PinnedBuf() {
+    if (p) (void)hipHostFree(p);
+  }
+};
+
+struct DevBuf {
+  void *p = nullptr;
+  size_t bytes = 0;
+  void ensure(size_t n) {
+    if (n <= bytes) return;
+    if (p) (void)hipFree(p);
+    p = nullptr;
+    bytes = 0;
+    HIPCHK(hipMalloc(&p, n));
+    bytes = n;
+  }
+  ~DevBuf() {
+    if (p) (void)hipFree(p);
+  }
+};
+
+// Pairs of timing events, summed on demand.
+struct TimingLog {
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+  std::vector<hipEvent_t> free_list;
+  double total = 0.0;
+  hipEvent_t get() {
+    if (!free_list.empty()) {
+      hipEvent_t e = free_list.back();
+      free_list.pop_back();
+      return e;
+    }
+    hipEvent_t e;
+    HIPCHK(hipEventCreate(&e));
+    return e;
+  }
+  void collect() {
+    for (auto &pr : pending) {
+      HIPCHK(hipEventSynchronize(pr.second));
+      float ms = 0.f;
+      HIPCHK(hipEventElapsedTime(&ms, pr.first, pr.second));
+      total += ms * 1e-3;
+      free_list.push_back(pr.first);
+      free_list.push_back(pr.second);
+    }
+    pending.clear();
+  }
+  ~TimingLog() {
+    for (auto &pr : pending) {
+      (void)hipEventDestroy(pr.first);
+      (void)hipEventDestroy(pr.second);
+    }
+    for (auto e : free_list) (void)hipEventDestroy(e);
+  }
+};
+
+}  // namespace
+
+struct LayerState {
+  std::unique_ptr<moe::SlotPlanner> planner;
+  uint8_t *d_slots = nullptr;     // (S + n_shared) records
+  hipEvent_t fill_ev = nullptr;   // last fills of this layer (side stream)
+  hipEvent_t compute_ev = nullptr;  // last kernels that read this layer's slots
+  bool fill_pending = false;
+  bool compute_recorded = false;
+  moe::CallPlan plan;             // last call
+  int32_t last_T = 0;
+  std::vector<int32_t> last_idx;
+  std::vector<float> last_w;
+  std::vector<float> dbg_host;    // keep_debug: host partial
+  DevBuf dbg_gpu;                 // keep_debug: GPU partial
+  moe_stats st{};
+  TimingLog t_gpu, t_h2d;
+};
+
+struct moe_cache {
+  int32_t L = 0, E = 0, S = 0, d = 0, f = 0;
+  moe_cache_opts o{};
+  moe::RecordLayout lay;
+  int device = 0;
+  uint8_t *h_arena = nullptr;   // L * (E + n_shared) records, page-locked
+  std::vector<LayerState> layers;
+  hipStream_t side = nullptr;
+  hipEvent_t ev_idx = nullptr, ev_ready = nullptr;
+  bool poisoned = false;
+  bool timing = false;
+  // device workspace
+  int32_t cap_T = 0;
+  DevBuf z, idx, w, pair_gpu, meta, bucket_pair, h, y;
+  // pinned host staging
+  PinnedBuf h_idx, h_w, h_x, partial[2];
+  hipEvent_t partial_ev[2] = {nullptr, nullptr};
+  bool partial_used[2] = {false, false};
+  int partial_cur = 0;
+  std::vector<float> h_scratch;
+  std::unique_ptr<moe::ThreadPool> pool;
+
+  size_t rec() const { return (size_t)lay.bytes; }
+  int32_t n_total() const { return E + o.n_shared; }
+  const uint8_t *host_record(int32_t l, int32_t e) const {
+    return h_arena + ((size_t)l * n_total() + e) * rec();
+  }
+  uint8_t *dev_slot(int32_t l, int32_t s) const { return layers[l].d_slots + (size_t)s * rec(); }
+
+  ~moe_cache() {
+    (void)hipSetDevice(device);
+    if (side) (void)hipStreamSynchronize(side);
+    (void)hipDeviceSynchronize();
+    for (auto &ly : layers) {
+      if (ly.d_slots) (void)hipFree(ly.d_slots);
+      if (ly.fill_ev) (void)hipEventDestroy(ly.fill_ev);
+      if (ly.compute_ev) (void)hipEventDestroy(ly.compute_ev);
+    }
+    layers.clear();
+    if (h_arena) (void)hipHostFree(h_arena);
+    if (ev_idx) (void)hipEventDestroy(ev_idx);
+    if (ev_ready) (void)hipEventDestroy(ev_ready);
+    for (auto &e : partial_ev)
+      if (e) (void)hipEventDestroy(e);
+    if (side) (void)hipStreamDestroy(side);
+  }
+
+  void ensure_ws(int32_t T) {
+    if (T <= cap_T) return;
+    HIPCHK(hipDeviceSynchronize());
+    const size_t k = (size_t)o.top_k;
+    const size_t P = (size_t)T * k + (size_t)T * o.n_shared;
+    z.ensure((size_t)T * E * 4);
+    idx.ensure((size_t)T * k * 4);
+    w.ensure((size_t)T * k * 4);
+    pair_gpu.ensure((size_t)T * k * 4);
+    meta.ensure((size_t)moe::kMetaInts * 4);
+    bucket_pair.ensure(P * 4);
+    h.ensure(P * (size_t)f * 4);
+    y.ensure(P * (size_t)d * 4);
+    h_idx.ensure((size_t)T * k * 4);
+    h_w.ensure((size_t)T * k * 4);
+    if (o.miss_mode == MOE_MISS_HOST) {
+      h_x.ensure((size_t)T * d * 4);
+      for (auto &pb : partial) pb.ensure((size_t)T * d * 4);
+    }
+    cap_T = T;
+  }
+};
+
+namespace {
+
+moe::SlotView make_view(const std::vector<int32_t> &table) {
+  moe::SlotView v;
+  for (int i = 0; i < moe::kMaxExperts; ++i) v.slot[i] = -1;
+  for (size_t e = 0; e < table.size(); ++e) v.slot[e] = (int16_t)table[e];
+  return v;
+}
+
+void record_compute(moe_cache *c, LayerState &ly, hipStream_t st) {
+  HIPCHK(hipEventRecord(ly.compute_ev, st));
+  ly.compute_recorded = true;
+}
+
+// Copies the fills of one stage on the side stream after every earlier reader of
+// the victim slots (work enqueued so far on `st`, and the layer's last kernels).
+void enqueue_fills(moe_cache *c, int32_t layer, const std::vector<moe::Fill> &fills,
+                   hipStream_t st) {
+  LayerState &ly = c->layers[layer];
+  HIPCHK(hipEventRecord(c->ev_ready, st));
+  HIPCHK(hipStreamWaitEvent(c->side, c->ev_ready, 0));
+  if (ly.compute_recorded) HIPCHK(hipStreamWaitEvent(c->side, ly.compute_ev, 0));
+  hipEvent_t t0 = nullptr, t1 = nullptr;
+  if (c->timing) {
+    t0 = ly.t_h2d.get();
+    t1 = ly.t_h2d.get();
+    HIPCHK(hipEventRecord(t0, c->side));
+  }
+  for (const moe::Fill &fl : fills) {
+    HIPCHK(hipMemcpyAsync(c->dev_slot(layer, fl.slot), c->host_record(layer, fl.expert), c->rec(),
+                          hipMemcpyHostToDevice, c->side));
+  }
+  if (c->timing) {
+    HIPCHK(hipEventRecord(t1, c->side));
+    ly.t_h2d.pending.emplace_back(t0, t1);
+  }
+  HIPCHK(hipEventRecord(ly.fill_ev, c->side));
+  ly.st.fills += fills.size();
+  ly.st.fill_bytes += fills.size() * (uint64_t)c->rec();
+}
+
+// K3 + K4 + K5 for one stage whose expert -> slot table is `view`.
+void run_stage(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &view, bool with_shared,
+               int n_buckets, const float *x, hipStream_t st) {
+  const int32_t k = c->o.top_k;
+  const int shared_slot = with_shared ? c->S : -1;
+  const int n_ids = c->S + c->o.n_shared;
+  HIPCHK(moe::launch_remap((const int32_t *)c->idx.p, T, k, view, shared_slot, n_ids,
+                           (int32_t *)c->meta.p, (int32_t *)c->bucket_pair.p,
+                           (int32_t *)c->pair_gpu.p, st));
+  if (n_buckets <= 0) return;
+  const moe::RecordLayout &L = c->lay;
+  moe::GemvArgs a{};
+  a.slots = c->layers[layer].d_slots;
+  a.rec_bytes = L.bytes;
+  a.T = T;
+  a.k = k;
+  a.meta = (const int32_t *)c->meta.p;
+  a.bucket_pair = (const int32_t *)c->bucket_pair.p;
+  // gate/up + SwiGLU: rows f, K = d, input = x by token
+  a.off_q0 = L.off_gq;
+  a.off_s0 = L.off_gs;
+  a.off_q1 = L.off_uq;
+  a.off_s1 = L.off_us;
+  a.rows = c->f;
+  a.nb = (int)L.nb_gu;
+  a.in = x;
+  a.in_by_pair = 0;
+  a.out = (float *)c->h.p;
+  const int max_tok = T;
+  moe::GemvShape sh1 = moe::choose_gemv(a.rows, a.nb, n_buckets, max_tok);
+  HIPCHK(moe::launch_gemv(a, sh1, true, n_buckets, st));
+  // down: rows d, K = f, input = h by pair
+  moe::GemvArgs b = a;
+  b.off_q0 = L.off_dq;
+  b.off_s0 = L.off_ds;
+  b.rows = c->d;
+  b.nb = (int)L.nb_dn;
+  b.in = (const float *)c->h.p;
+  b.in_by_pair = 1;
+  b.out = (float *)c->y.p;
+  moe::GemvShape sh2 = moe::choose_gemv(b.rows, b.nb, n_buckets, max_tok);
+  HIPCHK(moe::launch_gemv(b, sh2, false, n_buckets, st));
+}
+
+moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
+                        const float *router_w, const float *router_bias, float *out,
+                        hipStream_t st) {
+  LayerState &ly = c->layers[layer];
+  const int32_t k = c->o.top_k, E = c->E, d = c->d;
+  const bool host_mode = c->o.miss_mode == MOE_MISS_HOST;
+  c->ensure_ws(T);
+  hipEvent_t g0 = nullptr, g1 = nullptr;
+  if (c->timing) {
+    g0 = ly.t_gpu.get();
+    g1 = ly.t_gpu.get();
+    HIPCHK(hipEventRecord(g0, st));
+  }
+  // publication of the previous call's fills (host mode)
+  if (ly.fill_pending) {
+    HIPCHK(hipStreamWaitEvent(st, ly.fill_ev, 0));
+    ly.fill_pending = false;
+  }
+  if (host_mode)
+    HIPCHK(hipMemcpyAsync(c->h_x.p, x, (size_t)T * d * 4, hipMemcpyDeviceToHost, st));
+  HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)c->z.p, st));
+  HIPCHK(moe::launch_topk((const float *)c->z.p, T, E, k, c->o.norm_topk, (int32_t *)c->idx.p,
+                          (float *)c->w.p, (int32_t *)c->pair_gpu.p, st));
+  HIPCHK(hipMemcpyAsync(c->h_idx.p, c->idx.p, (size_t)T * k * 4, hipMemcpyDeviceToHost, st));
+  HIPCHK(hipMemcpyAsync(c->h_w.p, c->w.p, (size_t)T * k * 4, hipMemcpyDeviceToHost, st));
+  HIPCHK(hipEventRecord(c->ev_idx, st));
+
+  float *dbg_gpu = nullptr;
+  if (c->o.keep_debug) {
+    ly.dbg_gpu.ensure((size_t)T * d * 4);
+    dbg_gpu = (float *)ly.dbg_gpu.p;
+  }
+  bool combined = false;
+
+  if (!host_mode) {
+    HIPCHK(hipEventSynchronize(c->ev_idx));
+    const double tp = now_s();
+    ly.planner->plan((const int32_t *)c->h_idx.p, T * k, 0, -1, ly.plan);
+    ly.st.plan_s += now_s() - tp;
+    std::vector<int32_t> table(E);
+    for (size_t s = 0; s < ly.plan.stages.size(); ++s) {
+      const moe::PlanStage &stg = ly.plan.stages[s];
+      if (!stg.fills.empty()) {
+        enqueue_fills(c, layer, stg.fills, st);
+        HIPCHK(hipStreamWaitEvent(st, ly.fill_ev, 0));
+      }
+      ly.planner->stage_view(ly.plan, (int32_t)s, table.data(), nullptr);
+      const bool sh = s == 0 && c->o.n_shared > 0;
+      const int nb = (int)stg.members.size() + (sh ? 1 : 0);
+      run_stage(c, layer, T, make_view(table), sh, nb, x, st);
+      record_compute(c, ly, st);
+    }
+    if (c->o.keep_debug) ly.dbg_host.assign((size_t)T * d, 0.0f);
+  } else {
+    // GPU part on the table published at call start; no host wait before it
+    const std::vector<int32_t> &pre = ly.planner->slot_of();
+    const int nb_bound = std::min(T * k, c->S) + (c->o.n_shared > 0 ? 1 : 0);
+    run_stage(c, layer, T, make_view(pre), c->o.n_shared > 0, nb_bound, x, st);
+    record_compute(c, ly, st);
+    HIPCHK(hipEventSynchronize(c->ev_idx));
+    const double tp = now_s();
+    ly.planner->plan((const int32_t *)c->h_idx.p, T * k, 1, c->o.max_fills_per_call, ly.plan);
+    ly.st.plan_s += now_s() - tp;
+    const moe::PlanStage &stg = ly.plan.stages[0];
+    if (!stg.fills.empty()) {
+      enqueue_fills(c, layer, stg.fills, st);
+      ly.fill_pending = true;
+    }
+    if (!ly.plan.host_experts.empty()) {
+      const double th = now_s();
+      const int b = c->partial_cur;
+      c->partial_cur ^= 1;
+      if (c->partial_used[b]) HIPCHK(hipEventSynchronize(c->partial_ev[b]));
+      // host jobs: one per missed expert, its tokens ascending
+      std::vector<moe::HostExpertJob> jobs(ly.plan.host_experts.size());
+      std::vector<int32_t> job_of(E, -1);
+      for (size_t i = 0; i < jobs.size(); ++i) {
+        const int32_t e = ly.plan.host_experts[i];
+        job_of[e] = (int32_t)i;
+        jobs[i].record = c->host_record(layer, e);
+      }
+      const int32_t *hidx = (const int32_t *)c->h_idx.p;
+      std::vector<int32_t> rank_job((size_t)T * k, -1);
+      for (int32_t t = 0; t < T; ++t)
+        for (int32_t j = 0; j < k; ++j) {
+          const int32_t jb = job_of[hidx[t * k + j]];
+          rank_job[(size_t)t * k + j] = jb;
+          if (jb >= 0) jobs[jb].tokens.push_back(t);
+        }
+      moe::host_moe_partial(*c->pool, c->lay, jobs, rank_job.data(), (const float *)c->h_w.p, T, k,
+                            (const float *)c->h_x.p, (float *)c->partial[b].p, c->h_scratch);
+      const float *host_part = (const float *)c->partial[b].p;
+      if (c->o.keep_debug)
+        ly.dbg_host.assign(host_part, host_part + (size_t)T * d);
+      ly.st.host_s += now_s() - th;
+      ly.st.host_selections += ly.plan.misses;
+      HIPCHK(moe::launch_combine((const float *)c->y.p, (const float *)c->w.p,
+                                 (const int32_t *)c->pair_gpu.p, T, k, d, c->o.n_shared, host_part,
+                                 out, dbg_gpu, st));
+      HIPCHK(hipEventRecord(c->partial_ev[b], st));
+      c->partial_used[b] = true;
+      combined = true;
+    } else if (c->o.keep_debug) {
+      ly.dbg_host.assign((size_t)T * d, 0.0f);
+    }
+  }
+  if (!combined)
+    HIPCHK(moe::launch_combine((const float *)c->y.p, (const float *)c->w.p,
+                               (const int32_t *)c->pair_gpu.p, T, k, d, c->o.n_shared, nullptr, out,
+                               dbg_gpu, st));
+  if (c->timing) {
+    HIPCHK(hipEventRecord(g1, st));
+    ly.t_gpu.pending.emplace_back(g0, g1);
+  }
+  // record of the call
+  ly.last_T = T;
+  ly.last_idx.assign((const int32_t *)c->h_idx.p, (const int32_t *)c->h_idx.p + (size_t)T * k);
+  ly.last_w.assign((const float *)c->h_w.p, (const float *)c->h_w.p + (size_t)T * k);
+  moe_stats &s = ly.st;
+  s.calls++;
+  s.tokens += T;
+  s.selections += (uint64_t)T * k;
+  s.hits += ly.plan.hits;
+  s.misses += ly.plan.misses;
+  s.unique += ly.plan.unique;
+  s.evictions += ly.plan.evictions;
+  s.stages += ly.plan.stages.size();
+  return MOE_OK;
+}
+
+template <class F>
+moe_status guarded(moe_cache *c, F &&f) {
+  if (c && c->poisoned) return fail(MOE_ESTATE, "cache poisoned by an earlier HIP failure");
+  try {
+    if (c) HIPCHK(hipSetDevice(c->device));
+    return f();
+  } catch (const HipError &e) {
+    if (c) c->poisoned = true;
+    return fail(MOE_EHIP, e.what());
+  } catch (const std::bad_alloc &) {
+    return fail(MOE_ENOMEM, "host allocation failed");
+  } catch (const std::exception &e) {
+    return fail(MOE_EINVAL, e.what());
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+void moe_cache_default_opts(moe_cache_opts *o) {
+  if (!o) return;
+  std::memset(o, 0, sizeof(*o));
+  o->top_k = 8;
+  o->miss_mode = MOE_MISS_STREAM;
+  o->n_shared = 0;
+  o->norm_topk = 1;
+  o->host_threads = 0;
+  o->max_fills_per_call = -1;
+  o->keep_debug = 0;
+}
+
+const char *moe_last_error(void) { return g_err.c_str(); }
+
+int64_t moe_slot_bytes(int32_t d_model, int32_t d_ff) {
+  if (d_model <= 0 || d_ff <= 0 || d_model % 64 || d_ff % 32) return 0;
+  return moe::RecordLayout::make(d_model, d_ff).bytes;
+}
+
+moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, int32_t d_model,
+                            int32_t d_ff, const void *host_q4_weights, const moe_cache_opts *opts,
+                            moe_cache **out) {
+  g_err.clear();
+  if (!out) return fail(MOE_EINVAL, "out is NULL");
+  *out = nullptr;
+  moe_cache_opts o;
+  moe_cache_default_opts(&o);
+  if (opts) o = *opts;
+  if (layers < 1) return fail(MOE_EINVAL, "layers must be >= 1");
+  if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_EINVAL, "n_experts must be in [1, 512]");
+  if (slots < 1 || slots > n_experts) return fail(MOE_EINVAL, "slots must be in [1, n_experts]");
+  if (d_model <= 0 || d_model % 64) return fail(MOE_EINVAL, "d_model must be a positive multiple of 64");
+  if (d_ff <= 0 || d_ff % 32) return fail(MOE_EINVAL, "d_ff must be a positive multiple of 32");
+  if (!host_q4_weights) return fail(MOE_EINVAL, "host_q4_weights is NULL");
+  if (o.top_k < 1 || o.top_k > n_experts || o.top_k > MOE_MAX_TOPK)
+    return fail(MOE_EINVAL, "top_k must be in [1, min(n_experts, 64)]");
+  if (o.miss_mode != MOE_MISS_STREAM && o.miss_mode != MOE_MISS_HOST)
+    return fail(MOE_EINVAL, "miss_mode must be MOE_MISS_STREAM or MOE_MISS_HOST");
+  if (o.n_shared < 0 || o.n_shared > 1) return fail(MOE_EINVAL, "n_shared must be 0 or 1");
+  if (o.norm_topk != 0 && o.norm_topk != 1) return fail(MOE_EINVAL, "norm_topk must be 0 or 1");
+  if (o.max_fills_per_call < -1) return fail(MOE_EINVAL, "max_fills_per_call must be >= -1");
+  if (o.keep_debug != 0 && o.keep_debug != 1) return fail(MOE_EINVAL, "keep_debug must be 0 or 1");
+  if (o.timing != 0 && o.timing != 1) return fail(MOE_EINVAL, "timing must be 0 or 1");
+  for (int i = 0; i < 8; ++i)
+    if (o.reserved[i] != 0) return fail(MOE_EINVAL, "reserved fields must be 0");
+
+  std::unique_ptr<moe_cache> c;
+  try {
+    c.reset(new moe_cache());
+  } catch (const std::bad_alloc &) {
+    return fail(MOE_ENOMEM, "host allocation failed");
+  }
+  c->L = layers;
+  c->E = n_experts;
+  c->S = slots;
+  c->d = d_model;
+  c->f = d_ff;
+  c->o = o;
+  c->timing = o.timing != 0;
+  c->lay = moe::RecordLayout::make(d_model, d_ff);
+  moe_status rc = guarded(nullptr, [&]() -> moe_status {
+    HIPCHK(hipGetDevice(&c->device));
+    const size_t ntot = (size_t)n_experts + o.n_shared;
+    const size_t arena = (size_t)layers * ntot * c->rec();
+    hipError_t he = hipHostMalloc((void **)&c->h_arena, arena, hipHostMallocDefault);
+    if (he != hipSuccess) {
+      c->h_arena = nullptr;
+      (void)hipGetLastError();
+      return fail(MOE_ENOMEM, "page-locked host arena allocation failed");
+    }
+    const int nthr = o.host_threads > 0 ? o.host_threads : default_threads();
+    c->pool.reset(new moe::ThreadPool(nthr));
+    {
+      const uint8_t *src = (const uint8_t *)host_q4_weights;
+      const size_t total = (size_t)layers * ntot;
+      const size_t ib = (size_t)c->lay.interchange_bytes;
+      std::atomic<size_t> next{0};
+      moe::RecordLayout lay = c->lay;
+      uint8_t *dst = c->h_arena;
+      const size_t rb = c->rec();
+      c->pool->run([&](int) {
+        for (;;) {
+          const size_t i = next.fetch_add(1);
+          if (i >= total) break;
+          moe::repack_expert(src + i * ib, lay, dst + i * rb);
+        }
+      });
+    }
+    HIPCHK(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking));
+    HIPCHK(hipEventCreateWithFlags(&c->ev_idx, hipEventDisableTiming));
+    HIPCHK(hipEventCreateWithFlags(&c->ev_ready, hipEventDisableTiming));
+    for (auto &e : c->partial_ev) HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    c->layers.resize(layers);
+    for (int32_t l = 0; l < layers; ++l) {
+      LayerState &ly = c->layers[l];
+      ly.planner.reset(new moe::SlotPlanner(n_experts, slots));
+      const size_t nslots = (size_t)slots + o.n_shared;
+      he = hipMalloc((void **)&ly.d_slots, nslots * c->rec());
+      if (he != hipSuccess) {
+        ly.d_slots = nullptr;
+        (void)hipGetLastError();
+        return fail(MOE_ENOMEM, "device slot arena allocation failed");
+      }
+      HIPCHK(hipEventCreateWithFlags(&ly.fill_ev, hipEventDisableTiming));
+      HIPCHK(hipEventCreateWithFlags(&ly.compute_ev, hipEventDisableTiming));
+      // preload: slot s <- expert s; shared slot S <- expert E
+      for (int32_t s = 0; s < slots; ++s)
+        HIPCHK(hipMemcpyAsync(c->dev_slot(l, s), c->host_record(l, s), c->rec(),
+                              hipMemcpyHostToDevice, c->side));
+      for (int32_t s = 0; s < o.n_shared; ++s)
+        HIPCHK(hipMemcpyAsync(c->dev_slot(l, slots + s), c->host_record(l, n_experts + s), c->rec(),
+                              hipMemcpyHostToDevice, c->side));
+    }
+    HIPCHK(hipStreamSynchronize(c->side));
+    return MOE_OK;
+  });
+  if (rc != MOE_OK) return rc;
+  *out = c.release();
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(moe_cache *c, int32_t layer, const float *x, int32_t n_tokens,
+                             const float *router_w, const float *router_bias, float *out,
+                             void *stream) {
+  g_err.clear();
+  if (!c) return fail(MOE_EINVAL, "cache is NULL");
+  if (layer < 0 || layer >= c->L) return fail(MOE_EINVAL, "layer out of range");
+  if (n_tokens < 1) return fail(MOE_EINVAL, "n_tokens must be >= 1");
+  if (n_tokens > (1 << 20)) return fail(MOE_EINVAL, "n_tokens too large");
+  if (!x || !router_w || !out) return fail(MOE_EINVAL, "x, router_w and out must be non-NULL");
+  return guarded(c, [&]() {
+    return forward_impl(c, layer, x, n_tokens, router_w, router_bias, out, (hipStream_t)stream);
+  });
+}
+
+moe_status moe_cache_stats(moe_cache *c, int32_t layer, moe_stats *out) {
+  g_err.clear();
+  if (!c || !out) return fail(MOE_EINVAL, "NULL argument");
+  if (layer < -1 || layer >= c->L) return fail(MOE_EINVAL, "layer out of range");
+  return guarded(c, [&]() {
+    std::memset(out, 0, sizeof(*out));
+    for (int32_t l = 0; l < c->L; ++l) {
+      if (layer >= 0 && l != layer) continue;
+      LayerState &ly = c->layers[l];
+      ly.t_gpu.collect();
+      ly.t_h2d.collect();
+      ly.st.gpu_s = ly.t_gpu.total;
+      ly.st.h2d_s = ly.t_h2d.total;
+      const moe_stats &s = ly.st;
+      out->calls += s.calls;
+      out->tokens += s.tokens;
+      out->selections += s.selections;
+      out->hits += s.hits;
+      out->misses += s.misses;
+      out->unique += s.unique;
+      out->fills += s.fills;
+      out->fill_bytes += s.fill_bytes;
+      out->evictions += s.evictions;
+      out->host_selections += s.host_selections;
+      out->stages += s.stages;
+      out->plan_s += s.plan_s;
+      out->h2d_s += s.h2d_s;
+      out->host_s += s.host_s;
+      out->gpu_s += s.gpu_s;
+    }
+    return MOE_OK;
+  });
+}
+
+moe_status moe_cache_reset_stats(moe_cache *c) {
+  g_err.clear();
+  if (!c) return fail(MOE_EINVAL, "cache is NULL");
+  return guarded(c, [&]() {
+    for (auto &ly : c->layers) {
+      ly.t_gpu.collect();
+      ly.t_h2d.collect();
+      ly.t_gpu.total = 0;
+      ly.t_h2d.total = 0;
+      std::memset(&ly.st, 0, sizeof(ly.st));
+    }
+    return MOE_OK;
+  });
+}
+
+moe_status moe_cache_sync(moe_cache *c) {
+  g_err.clear();
+  if (!c) return fail(MOE_EINVAL, "cache is NULL");
+  return guarded(c, [&]() {
+    HIPCHK(hipStreamSynchronize(c->side));
+    return MOE_OK;
+  });
+}
+
+void moe_cache_destroy(moe_cache *c) { delete c; }
+
+moe_status moe_debug_last_call(moe_cache *c, int32_t layer, int32_t *n_stages, int32_t *n_tokens) {
+  g_err.clear();
+  if (!c) return fail(MOE_EINVAL, "cache is NULL");
+  if (layer < 0 || layer >= c->L) return fail(MOE_EINVAL, "layer out of range");
+  const LayerState &ly = c->layers[layer];
+  if (n_stages) *n_stages = ly.last_T ? (int32_t)ly.plan.stages.size() : 0;
+  if (n_tokens) *n_tokens = ly.last_T;
+  return MOE_OK;
+}
+
+moe_status moe_debug_routing(moe_cache *c, int32_t layer, int32_t *idx, float *w) {
+  g_err.clear();
+  if (!c) return fail(MOE_EINVAL, "cache is NULL");
+  if (layer < 0 || layer >= c->L) return fail(MOE_EINVAL, "layer out of range");
+  const LayerState &ly = c->layers[layer];
+  if (idx) std::copy(ly.last_idx.begin(), ly.last_idx.end(), idx);
+  if (w) std::copy(ly.last_w.begin(), ly.last_w.end(), w);
+  return MOE_OK;
+}
+
+moe_status moe_debug_views(moe_cache *c, int32_t layer, int32_t stage, int32_t *slot_view,
+                           int32_t *host_view) {
+  g_err.clear();
+  if (!c) return fail(MOE_EINVAL, "cache is NULL");
+  if (layer < 0 || layer >= c->L) return fail(MOE_EINVAL, "layer out of range");
+  const LayerState &ly = c->layers[layer];
+  if (!ly.last_T) return fail(MOE_EINVAL, "layer has no call yet");
+  if (stage < 0 || stage >= (int32_t)ly.plan.stages.size()) return fail(MOE_EINVAL, "stage out of range");
+  ly.planner->stage_view(ly.plan, stage, slot_view, host_view);
+  return MOE_OK;
+}
+
+moe_status moe_debug_slots(moe_cache *c, int32_t layer, int32_t *expert_in, uint64_t *last_use) {
+  g_err.clear();
+  if (!c) return fail(MOE_EINVAL, "cache is NULL");
+  if (layer < 0 || layer >= c->L) return fail(MOE_EINVAL, "layer out of range");
+  const auto &p = *c->layers[layer].planner;
+  if (expert_in) std::copy(p.expert_in().begin(), p.expert_in().end(), expert_in);
+  if (last_use) std::copy(p.last_use().begin(), p.last_use().end(), last_use);
+  return MOE_OK;
+}
+
+static void copy_log(const std::vector<moe::EvictRecord> &log, moe_evict_rec *buf, size_t cap,
+                     size_t *n) {
+  const size_t m = std::min(cap, log.size());
+  for (size_t i = 0; i < m; ++i) {
+    buf[i].call = log[i].call;
+    buf[i].stage = log[i].stage;
+    buf[i].slot = log[i].slot;
+    buf[i].evicted_expert = log[i].evicted;
+    buf[i].inserted_expert = log[i].inserted;
+  }
+  if (n) *n = log.size();
+}
+
+moe_status moe_debug_evictions(moe_cache *c, int32_t layer, moe_evict_rec *buf, size_t cap,
+                               size_t *n) {
+  g_err.clear();
+  if (!c) return fail(MOE_EINVAL, "cache is NULL");
+  if (layer < 0 || layer >= c->L) return fail(MOE_EINVAL, "layer out of range");
+  if (cap && !buf) return fail(MOE_EINVAL, "buf is NULL");
+  copy_log(c->layers[layer].planner->log(), buf, cap, n);
+  return MOE_OK;
+}
+
+moe_status moe_debug_partials(moe_cache *c, int32_t layer, float *gpu_part, float *host_part) {
+  g_err.clear();
+  if (!c) return fail(MOE_EINVAL, "cache is NULL");
+  if (layer < 0 || layer >= c->L) return fail(MOE_EINVAL, "layer out of range");
+  if (!c->o.keep_debug) return fail(MOE_EINVAL, "create the cache with keep_debug = 1");
+  LayerState &ly = c->layers[layer];
+  if (!ly.last_T) return fail(MOE_EINVAL, "layer has no call yet");
+  return guarded(c, [&]() {
+    const size_t n = (size_t)ly.last_T * c->d;
+    if (gpu_part) {
+      HIPCHK(hipDeviceSynchronize());
+      HIPCHK(hipMemcpy(gpu_part, ly.dbg_gpu.p, n * 4, hipMemcpyDeviceToHost));
+    }
+    if (host_part) std::copy(ly.dbg_host.begin(), ly.dbg_host.begin() + n, host_part);
+    return MOE_OK;
+  });
+}
+
+// ---------------------------------------------------------------- planner only
+
+struct moe_planner {
+  std::unique_ptr<moe::SlotPlanner> p;
+  int32_t mode = 0, max_fills = -1;
+  moe::CallPlan last;
+  bool has_call = false;
+};
+
+moe_status moe_planner_create(int32_t n_experts, int32_t slots, int32_t miss_mode,
+                              int32_t max_fills_per_call, moe_planner **out) {
+  g_err.clear();
+  if (!out) return fail(MOE_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS) return fail(MOE_EINVAL, "n_experts out of range");
+  if (slots < 1 || slots > n_experts) return fail(MOE_EINVAL, "slots must be in [1, n_experts]");
+  if (miss_mode != MOE_MISS_STREAM && miss_mode != MOE_MISS_HOST)
+    return fail(MOE_EINVAL, "bad miss_mode");
+  if (max_fills_per_call < -1) return fail(MOE_EINVAL, "max_fills_per_call must be >= -1");
+  try {
+    auto *p = new moe_planner();
+    p->p.reset(new moe::SlotPlanner(n_experts, slots));
+    p->mode = miss_mode;
+    p->max_fills = max_fills_per_call;
+    *out = p;
+  } catch (const std::bad_alloc &) {
+    return fail(MOE_ENOMEM, "host allocation failed");
+  }
+  return MOE_OK;
+}
+
+moe_status moe_planner_plan(moe_planner *p, const int32_t *idx, int32_t n_sel, int32_t *n_stages,
+                            int32_t *hits, int32_t *misses) {
+  g_err.clear();
+  if (!p || (!idx && n_sel > 0)) return fail(MOE_EINVAL, "NULL argument");
+  if (n_sel < 1) return fail(MOE_EINVAL, "n_sel must be >= 1");
+  for (int32_t i = 0; i < n_sel; ++i)
+    if (idx[i] < 0 || idx[i] >= p->p->n_experts()) return fail(MOE_EINVAL, "expert id out of range");
+  try {
+    p->p->plan(idx, n_sel, p->mode, p->max_fills, p->last);
+  } catch (const std::bad_alloc &) {
+    return fail(MOE_ENOMEM, "host allocation failed");
+  }
+  p->has_call = true;
+  if (n_stages) *n_stages = (int32_t)p->last.stages.size();
+  if (hits) *hits = p->last.hits;
+  if (misses) *misses = p->last.misses;
+  return MOE_OK;
+}
+
+moe_status moe_planner_views(moe_planner *p, int32_t stage, int32_t *slot_view, int32_t *host_view) {
+  g_err.clear();
+  if (!p) return fail(MOE_EINVAL, "planner is NULL");
+  if (!p->has_call) return fail(MOE_EINVAL, "no call planned yet");
+  if (stage < 0 || stage >= (int32_t)p->last.stages.size()) return fail(MOE_EINVAL, "stage out of range");
+  p->p->stage_view(p->last, stage, slot_view, host_view);
+  return MOE_OK;
+}
+
+moe_status moe_planner_slots(moe_planner *p, int32_t *expert_in, uint64_t *last_use) {
+  g_err.clear();
+  if (!p) return fail(MOE_EINVAL, "planner is NULL");
+  if (expert_in) std::copy(p->p->expert_in().begin(), p->p->expert_in().end(), expert_in);
+  if (last_use) std::copy(p->p->last_use().begin(), p->p->last_use().end(), last_use);
+  return MOE_OK;
+}
+
+moe_status moe_planner_evictions(moe_planner *p, moe_evict_rec *buf, size_t cap, size_t *n) {
+  g_err.clear();
+  if (!p) return fail(MOE_EINVAL, "planner is NULL");
+  if (cap && !buf) return fail(MOE_EINVAL, "buf is NULL");
+  copy_log(p->p->log(), buf, cap, n);
+  return MOE_OK;
+}
+
+void moe_planner_destroy(moe_planner *p) { delete p; }
+
+moe_status moe_host_expert_forward(const void *expert_q4, int32_t d_model, int32_t d_ff,
+                                   const float *x, int32_t n_tokens, float *y, int32_t threads) {
+  g_err.clear();
+  if (!expert_q4 || !x || !y) return fail(MOE_EINVAL, "NULL argument");
+  if (d_model <= 0 || d_model % 64 || d_ff <= 0 || d_ff % 32) return fail(MOE_EINVAL, "bad shape");
+  if (n_tokens < 1) return fail(MOE_EINVAL, "n_tokens must be >= 1");
+  try {
+    const moe::RecordLayout L = moe::RecordLayout::make(d_model, d_ff);
+    std::vector<uint8_t> rec((size_t)L.bytes);
+    moe::repack_expert((const uint8_t *)expert_q4, L, rec.data());
+    moe::ThreadPool pool(threads > 0 ? threads : default_threads());
+    moe::host_expert_forward(pool, L, rec.data(), x, n_tokens, y);
+  } catch (const std::bad_alloc &) {
+    return fail(MOE_ENOMEM, "host allocation failed");
+  } catch (const std::exception &e) {
+    return fail(MOE_EINVAL, e.what());
+  }
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+#include "planner.hpp"
+
+#include <algorithm>
+
+namespace moe {
+
+SlotPlanner::SlotPlanner(int32_t n_experts, int32_t slots)
+    : E_(n_experts), S_(slots), expert_in_(slots), slot_of_(n_experts, -1), last_use_(slots, 0),
+      seen_(n_experts, 0) {
+  for (int32_t s = 0; s < slots; ++s) {
+    expert_in_[s] = s;
+    slot_of_[s] = s;
+  }
+}
+
+int32_t SlotPlanner::victim() const {
+  for (int32_t s = 0; s < S_; ++s)
+    if (expert_in_[s] < 0) return s;
+  int32_t best = -1;
+  for (int32_t s = 0; s < S_; ++s) {
+    if (last_use_[s] >= clock_) continue;
+    if (best < 0 || last_use_[s] < last_use_[best]) best = s;
+  }
+  return best;
+}
+
+void SlotPlanner::insert(int64_t call, int32_t stage, int32_t slot, int32_t e, CallPlan &out) {
+  const int32_t old = expert_in_[slot];
+  if (old >= 0) {
+    slot_of_[old] = -1;
+    out.evictions++;
+  }
+  expert_in_[slot] = e;
+  slot_of_[e] = slot;
+  last_use_[slot] = clock_;
+  log_.push_back(EvictRecord{call, stage, slot, old, e});
+  out.fills++;
+}
+
+void SlotPlanner::plan(const int32_t *idx, int32_t n_sel, int32_t mode, int32_t max_fills,
+                       CallPlan &out) {
+  out = CallPlan();
+  out.call = calls_++;
+  out.mode = mode;
+  out.pre_view = slot_of_;
+  // distinct ids in ascending order; hits counted per selection
+  std::vector<int32_t> uniq;
+  uniq.reserve(n_sel);
+  for (int32_t i = 0; i < n_sel; ++i) {
+    const int32_t e = idx[i];
+    if (slot_of_[e] >= 0) out.hits++;
+    if (!seen_[e]) {
+      seen_[e] = 1;
+      uniq.push_back(e);
+    }
+  }
+  for (int32_t e : uniq) seen_[e] = 0;
+  std::sort(uniq.begin(), uniq.end());
+  out.misses = n_sel - out.hits;
+  out.unique = (int32_t)uniq.size();
+
+  std::vector<int32_t> hit_experts, pending;
+  for (int32_t e : uniq) (slot_of_[e] >= 0 ? hit_experts : pending).push_back(e);
+
+  if (mode == 0) {
+    size_t next = 0;
+    int32_t stage = 0;
+    while (stage == 0 || next < pending.size()) {
+      clock_++;
+      PlanStage st;
+      if (stage == 0) {
+        for (int32_t e : hit_experts) {
+          last_use_[slot_of_[e]] = clock_;
+          st.members.push_back(e);
+        }
+      }
+      while (next < pending.size()) {
+        const int32_t v = victim();
+        if (v < 0) break;
+        const int32_t e = pending[next++];
+        insert(out.call, stage, v, e, out);
+        st.members.push_back(e);
+        st.fills.push_back(Fill{e, v});
+      }
+      std::sort(st.members.begin(), st.members.end());
+      out.stages.push_back(std::move(st));
+      stage++;
+    }
+  } else {
+    clock_++;
+    PlanStage st;
+    for (int32_t e : hit_experts) {
+      last_use_[slot_of_[e]] = clock_;
+      st.members.push_back(e);
+    }
+    int32_t placed = 0;
+    for (int32_t e : pending) {
+      if (max_fills >= 0 && placed >= max_fills) break;
+      const int32_t v = victim();
+      if (v < 0) break;
+      insert(out.call, 0, v, e, out);
+      st.fills.push_back(Fill{e, v});
+      placed++;
+    }
+    out.stages.push_back(std::move(st));
+    out.host_experts = pending;
+  }
+}
+
+void SlotPlanner::stage_view(const CallPlan &p, int32_t s, int32_t *slot_view,
+                             int32_t *host_view) const {
+  if (p.mode == 0) {
+    if (slot_view) {
+      std::fill(slot_view, slot_view + E_, -1);
+      // members of stage s keep the slot they were given; later stages may
+      // reuse slots, so rebuild from the stage's own record
+      const PlanStage &st = p.stages[s];
+      for (int32_t e : st.members) slot_view[e] = -1;
+      for (const Fill &f : st.fills) slot_view[f.expert] = f.slot;
+      if (s == 0)
+        for (int32_t e : st.members)
+          if (p.pre_view[e] >= 0) slot_view[e] = p.pre_view[e];
+    }
+    if (host_view) std::fill(host_view, host_view + E_, -1);
+  } else {
+    for (int32_t e = 0; e < E_; ++e) {
+      if (slot_view) slot_view[e] = p.pre_view[e];
+      if (host_view) host_view[e] = p.pre_view[e] < 0 ? e : -1;
+    }
+  }
+}
+
+}  // namespace moe

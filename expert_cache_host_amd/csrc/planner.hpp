@@ -1,0 +1,80 @@
+// Per-layer LRU slot planner (host only, no HIP calls).
+//
+// Rules (longhaul.md, "Longhaul MoE loading": fixed budget, least-recently-used
+// replacement per layer, the batch's experts protected, duplicate ids loaded
+// once, staged execution when one step needs more experts than slots;
+// "How it works", llama.cpp + MoE expert cache, step 2: expert -> slot table
+// with -1 when not cached and expert -> CPU id table with -1 when cached):
+//
+//   start: slot s holds expert s, last_use 0, clock 0.
+//   per call: U = sorted distinct ids; a selection hits when its expert is
+//   cached at call start.
+//   per stage: clock += 1; resident experts of the stage get last_use = clock;
+//   pending misses in ascending id take the lowest-index empty slot, else the
+//   slot with the smallest (last_use, index) among last_use < clock; no such
+//   slot ends the stage.
+//   stream mode: every miss is filled, over as many stages as needed; a stage's
+//   slot table maps that stage's experts only; the host table is all -1.
+//   host mode: one stage; at most max_fills fills (-1 = no cap) in ascending id;
+//   the tables are the full tables at call start.
+#pragma once
+#include <cstdint>
+#include <vector>
+
+namespace moe {
+
+struct EvictRecord {
+  int64_t call;
+  int32_t stage, slot, evicted, inserted;
+};
+
+struct Fill {
+  int32_t expert, slot;
+};
+
+struct PlanStage {
+  std::vector<int32_t> members;  // experts computed in this stage, ascending
+  std::vector<Fill> fills;       // copies that must land before the stage runs
+};
+
+struct CallPlan {
+  int64_t call = -1;
+  int32_t hits = 0, misses = 0, unique = 0, fills = 0, evictions = 0;
+  std::vector<PlanStage> stages;
+  std::vector<int32_t> host_experts;  // host mode: experts computed on host cores
+  std::vector<int32_t> pre_view;      // table at call start [E]
+  int32_t mode = 0;
+};
+
+class SlotPlanner {
+ public:
+  SlotPlanner(int32_t n_experts, int32_t slots);
+
+  // Plans one call; `scratch` marks are internal.  mode: 0 stream, 1 host.
+  void plan(const int32_t *idx, int32_t n_sel, int32_t mode, int32_t max_fills, CallPlan &out);
+
+  // Slot table of stage s of `p` (stream: that stage's members; host: pre_view).
+  void stage_view(const CallPlan &p, int32_t s, int32_t *slot_view, int32_t *host_view) const;
+
+  int32_t n_experts() const { return E_; }
+  int32_t slots() const { return S_; }
+  const std::vector<int32_t> &expert_in() const { return expert_in_; }
+  const std::vector<int32_t> &slot_of() const { return slot_of_; }
+  const std::vector<uint64_t> &last_use() const { return last_use_; }
+  const std::vector<EvictRecord> &log() const { return log_; }
+  uint64_t clock() const { return clock_; }
+
+ private:
+  int32_t victim() const;
+  void insert(int64_t call, int32_t stage, int32_t slot, int32_t e, CallPlan &out);
+
+  int32_t E_, S_;
+  std::vector<int32_t> expert_in_, slot_of_;
+  std::vector<uint64_t> last_use_;
+  std::vector<uint8_t> seen_;
+  uint64_t clock_ = 0;
+  int64_t calls_ = 0;
+  std::vector<EvictRecord> log_;
+};
+
+}  // namespace moe

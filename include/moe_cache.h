@@ -1,0 +1,254 @@
+/*
+ * moe_cache.h -- C ABI of libmoecache: a routed Mixture-of-Experts FFN layer
+ * served from a per-layer GPU cache of hot experts, for one AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method (pages: "llama.cpp + MoE expert cache", section "How it works";
+ * "longhaul.md", section "Longhaul MoE loading"):
+ *   - every expert of every layer stays in host RAM in 4-bit blocks (32 weights
+ *     plus a binary16 scale in 18 bytes);
+ *   - each layer owns a fixed number of GPU slots holding copies of experts,
+ *     replaced least-recently-used, independently per layer; the experts the
+ *     current batch already needs are protected from eviction and duplicate ids
+ *     load once;
+ *   - routing gives two tables, expert -> GPU slot (-1 when not cached) and
+ *     expert -> host id (-1 when cached); cached experts are computed on the GPU,
+ *     misses either on host cores in parallel (MOE_MISS_HOST) or streamed into
+ *     slots first (MOE_MISS_STREAM); every selected expert is computed exactly
+ *     once and the partial results are summed;
+ *   - when a step selects more experts than there are slots, the routed work
+ *     runs in stages whose partial results are summed.
+ *
+ * Conventions for every call below:
+ *   - A function returns MOE_OK (0) or a negative moe_status.  On failure
+ *     moe_last_error() returns a message (thread-local, valid until the next
+ *     call on the same thread).  No C++ exception crosses this interface.
+ *   - MOE_EINVAL: an argument is invalid; nothing was changed.
+ *   - MOE_ENOMEM: an allocation failed; nothing leaks.
+ *   - MOE_EHIP: a HIP runtime call failed; the cache is poisoned and every later
+ *     call on it returns MOE_ESTATE (destroy still works).
+ *   - "device pointer" means memory the current HIP device can read/write
+ *     (hipMalloc, or a torch CUDA tensor's data_ptr()); "host pointer" means
+ *     ordinary process memory.
+ *   - One cache is driven by one host thread at a time; calls are not
+ *     re-entrant.  Calls for different layers may interleave in any order.
+ */
+#ifndef MOE_CACHE_H
+#define MOE_CACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+#define MOE_OK 0
+#define MOE_EINVAL (-1)
+#define MOE_ENOMEM (-2)
+#define MOE_EHIP (-3)
+#define MOE_ESTATE (-4)
+
+/* Miss handling ("How it works" step 3 computes misses on the CPU; longhaul.md
+ * populates missing slots and continues with cache-local ids). */
+#define MOE_MISS_STREAM 0
+#define MOE_MISS_HOST 1
+
+/* Limits of this build. */
+#define MOE_MAX_EXPERTS 512 /* routed experts per layer */
+#define MOE_MAX_TOPK 64
+
+typedef struct moe_cache moe_cache; /* opaque, owned by the library */
+
+typedef struct moe_cache_opts {
+  int32_t top_k;              /* k experts per token, 1..min(n_experts, 64)     default 8 */
+  int32_t miss_mode;          /* MOE_MISS_STREAM or MOE_MISS_HOST               default STREAM */
+  int32_t n_shared;           /* 0 or 1 always-resident shared experts/layer    default 0 */
+  int32_t norm_topk;          /* 1: renormalise the k softmax weights           default 1 */
+  int32_t host_threads;       /* host-miss workers, 0 = cores - 1               default 0 */
+  int32_t max_fills_per_call; /* host mode: fills per call, -1 = every miss     default -1 */
+  int32_t keep_debug;         /* 1: keep per-layer GPU/host partials            default 0 */
+  int32_t timing;             /* 1: time fills and compute with HIP events       default 0 */
+  int32_t reserved[8];        /* must be 0 */
+} moe_cache_opts;
+
+/* Counters since create or the last moe_cache_reset_stats.  A "selection" is one
+ * (token, rank) pick of the router; hits and misses count selections, as the
+ * pages' hit rates do ("of the picks"). */
+typedef struct moe_stats {
+  uint64_t calls;           /* moe_layer_forward calls */
+  uint64_t tokens;          /* tokens over all calls */
+  uint64_t selections;      /* tokens * top_k */
+  uint64_t hits;            /* selections whose expert was cached at call start */
+  uint64_t misses;          /* selections - hits */
+  uint64_t unique;          /* distinct experts per call, summed */
+  uint64_t fills;           /* experts copied host -> slot */
+  uint64_t fill_bytes;      /* bytes of those copies */
+  uint64_t evictions;       /* fills that replaced a cached expert */
+  uint64_t host_selections; /* selections computed on host cores (host mode) */
+  uint64_t stages;          /* stages over all calls (1 per call unless staged) */
+  double plan_s;            /* host time in the slot planner */
+  double h2d_s;             /* device time of slot fills (opts.timing only) */
+  double host_s;            /* host time computing missed experts */
+  double gpu_s;             /* device time of the call's GPU work (opts.timing only) */
+} moe_stats;
+
+/* One slot replacement: in call `call` (per layer, from 0), stage `stage`, slot
+ * `slot` changed from `evicted_expert` (-1 = was empty) to `inserted_expert`. */
+typedef struct moe_evict_rec {
+  int64_t call;
+  int32_t stage;
+  int32_t slot;
+  int32_t evicted_expert;
+  int32_t inserted_expert;
+} moe_evict_rec;
+
+/* Fills *o with the defaults listed in moe_cache_opts. */
+void moe_cache_default_opts(moe_cache_opts *o);
+
+/*
+ * moe_cache_create -- build a cache for `layers` MoE layers.
+ *
+ * host_q4_weights (host pointer, read during this call only): every expert of
+ * every layer in the interchange layout -- for layer l, for expert e in
+ * [0, n_experts + n_shared): gate rows [d_ff][d_model], up rows [d_ff][d_model],
+ * down rows [d_model][d_ff]; each row quantised along its reduction dimension
+ * in 18-byte blocks (bytes 0-1: binary16 scale d, little-endian; byte 2+j:
+ * element j in the low nibble, element j+16 in the high nibble; w = d*(q-8)),
+ * blocks in K order, no padding.  The 18/32 bytes per weight are the Q4_0 size
+ * of "Multi-GPU LLM Calculator" (Memory placement).  Shared experts follow the
+ * routed ones of their layer.
+ *
+ * The library copies the weights into its own page-locked host arena (repacked
+ * per expert so that one slot fill is one contiguous copy), allocates
+ * (slots + n_shared) device slots per layer, uploads the shared experts, and
+ * preloads slot s with expert s (s < slots) so that slots == n_experts gives
+ * hits from the first call.  Uses the current HIP device.
+ *
+ * Requirements: layers >= 1; 1 <= n_experts <= MOE_MAX_EXPERTS;
+ * 1 <= slots <= n_experts; d_model % 64 == 0; d_ff % 32 == 0; opts may be NULL.
+ * On success *out receives the cache.
+ */
+moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, int32_t d_model,
+                            int32_t d_ff, const void *host_q4_weights, const moe_cache_opts *opts,
+                            moe_cache **out);
+
+/*
+ * moe_layer_forward -- out = the MoE layer `layer` applied to x.
+ *
+ *   x           device pointer, float32 [n_tokens][d_model], row-major
+ *   router_w    device pointer, float32 [n_experts][d_model], row-major
+ *   router_bias device pointer, float32 [n_experts], or NULL (no bias)
+ *   out         device pointer, float32 [n_tokens][d_model]; overwritten
+ *   stream      the caller's hipStream_t (NULL = the default stream)
+ *
+ * Router logits z = x . router_w^T + bias are formed in float32 in one fixed
+ * order (64 lane partials over i = l, l+64, ..., product and sum rounded
+ * separately, then a halving tree, then the bias); the k largest are selected,
+ * ties to the lower expert id, ordered by decreasing z; gating weights are the
+ * softmax over all n_experts logits, renormalised over the k when norm_topk.
+ * Each selected expert computes y = D (silu(G x) * (U x)); shared experts add
+ * with weight 1; out[t] = sum_j w[t,j] y_{idx[t,j]} + shared.
+ *
+ * MOE_MISS_STREAM: the call waits for the routing (a device->host copy of the
+ * ids), plans, copies missed experts into slots on a side stream and computes
+ * every selected expert on the GPU, in stages when more experts are selected
+ * than slots exist.  MOE_MISS_HOST: GPU work on cached experts is enqueued
+ * before the routing reaches the host; host threads then compute the misses,
+ * the misses' slot fills are queued on the side stream and become visible at
+ * the same layer's next call, and the GPU adds the host partial; the call
+ * returns when the host partial has been handed to `stream`.
+ *
+ * x, router_w, router_bias and out must stay valid until `stream` has passed
+ * this call's work.  Requirements: 0 <= layer < layers; 1 <= n_tokens; the
+ * pointers non-NULL except router_bias and stream.
+ */
+moe_status moe_layer_forward(moe_cache *c, int32_t layer, const float *x, int32_t n_tokens,
+                             const float *router_w, const float *router_bias, float *out,
+                             void *stream);
+
+/* Counters of one layer (layer >= 0) or summed over layers (layer == -1).
+ * Synchronises the library's own streams to read device timings. */
+moe_status moe_cache_stats(moe_cache *c, int32_t layer, moe_stats *out);
+
+/* Zeroes every counter and timing (slot contents and eviction logs stay). */
+moe_status moe_cache_reset_stats(moe_cache *c);
+
+/* Waits for the library's side-stream work (slot fills) to finish. */
+moe_status moe_cache_sync(moe_cache *c);
+
+/* Frees everything the cache owns; waits for its streams first.  NULL is a no-op. */
+void moe_cache_destroy(moe_cache *c);
+
+/* Message of the last failure on this thread ("" if none). */
+const char *moe_last_error(void);
+
+/* Bytes of one expert in the library's slot layout (>= 3*d*f*18/32, rounded up
+ * to 4096); 0 for invalid shapes. */
+int64_t moe_slot_bytes(int32_t d_model, int32_t d_ff);
+
+/* ---- inspection of the LAST call of a layer (host pointers, caller-owned) ---- */
+
+/* Number of stages and tokens of the last call of `layer` (0 before any call). */
+moe_status moe_debug_last_call(moe_cache *c, int32_t layer, int32_t *n_stages,
+                               int32_t *n_tokens);
+
+/* idx [n_tokens*top_k] int32 and w [n_tokens*top_k] float32 of the last call
+ * (either may be NULL).  Synchronises the compute work of that call. */
+moe_status moe_debug_routing(moe_cache *c, int32_t layer, int32_t *idx, float *w);
+
+/* The two lookup tables of stage `stage` of the last call, [n_experts] each:
+ * slot_view[e] = slot computing e in that stage or -1; host_view[e] = e when
+ * e is computed on host cores, else -1 (all -1 in stream mode). */
+moe_status moe_debug_views(moe_cache *c, int32_t layer, int32_t stage, int32_t *slot_view,
+                           int32_t *host_view);
+
+/* Current slot state: expert_in[slots] (-1 = empty) and last_use[slots]. */
+moe_status moe_debug_slots(moe_cache *c, int32_t layer, int32_t *expert_in, uint64_t *last_use);
+
+/* The layer's whole replacement log since create; copies min(cap, total)
+ * records into buf (may be NULL when cap == 0) and stores the total in *n. */
+moe_status moe_debug_evictions(moe_cache *c, int32_t layer, moe_evict_rec *buf, size_t cap,
+                               size_t *n);
+
+/* Requires opts.keep_debug.  gpu_part [n_tokens*d_model]: the GPU's sum (routed
+ * experts on slots + shared); host_part: the host cores' weighted sum (zeros in
+ * stream mode).  out == gpu_part + host_part element by element. */
+moe_status moe_debug_partials(moe_cache *c, int32_t layer, float *gpu_part, float *host_part);
+
+/* ---- host-only pieces, callable without a GPU ---- */
+
+typedef struct moe_planner moe_planner; /* the per-layer LRU slot planner alone */
+
+/* A planner with the same rules and initial state as one layer of a cache
+ * (slot s holds expert s).  miss_mode as in moe_cache_opts. */
+moe_status moe_planner_create(int32_t n_experts, int32_t slots, int32_t miss_mode,
+                              int32_t max_fills_per_call, moe_planner **out);
+
+/* Plans one call on the router ids idx[n_sel] (n_sel = tokens * top_k).  After
+ * it, *n_stages, *hits and *misses describe the call. */
+moe_status moe_planner_plan(moe_planner *p, const int32_t *idx, int32_t n_sel, int32_t *n_stages,
+                            int32_t *hits, int32_t *misses);
+
+/* Tables of one stage of the last planned call, as moe_debug_views. */
+moe_status moe_planner_views(moe_planner *p, int32_t stage, int32_t *slot_view,
+                             int32_t *host_view);
+
+/* Slot state and full replacement log, as moe_debug_slots / moe_debug_evictions. */
+moe_status moe_planner_slots(moe_planner *p, int32_t *expert_in, uint64_t *last_use);
+moe_status moe_planner_evictions(moe_planner *p, moe_evict_rec *buf, size_t cap, size_t *n);
+
+void moe_planner_destroy(moe_planner *p);
+
+/* One expert on host cores, as host mode computes a miss: y[t] = D (silu(G x_t)
+ * * (U x_t)) for t < n_tokens.  expert_q4: host pointer to ONE expert in the
+ * interchange layout; x, y: host float32 [n_tokens][d_model]; threads <= 0
+ * means cores - 1. */
+moe_status moe_host_expert_forward(const void *expert_q4, int32_t d_model, int32_t d_ff,
+                                   const float *x, int32_t n_tokens, float *y, int32_t threads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_CACHE_H */

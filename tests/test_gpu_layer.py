@@ -1,0 +1,136 @@
+"""GPU parity of the whole layer through the C ABI, call by call, against the
+oracle: bit-exact top-k ids, slot tables, slot state and replacement log;
+outputs within 2e-3 of the oracle's RMS."""
+import numpy as np
+import pytest
+
+import synth
+from layer_check import Runner, check_close, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import expert_cache_host_amd as m
+    m.load_library()
+
+
+@pytest.mark.parametrize("mode", ["stream", "host"])
+@pytest.mark.parametrize("slots", [1, 2, 4, 8])
+def test_tiny_all_calls(mode, slots):
+    wl = synth.WORKLOADS["tiny"]
+    log(f"tiny mode={mode} slots={slots}")
+    r = Runner(wl, [0], slots=slots, mode=mode)
+    x = synth.gen_hidden(wl, 0)
+    for t in range(x.shape[0]):
+        r.call(0, x[t])
+    r.check_log()
+    st = r.cache.stats()
+    assert st["calls"] == 64 and st["selections"] == 128
+    assert st["hits"] + st["misses"] == 128
+    if slots == 8:
+        assert st["hits"] == 128 and st["evictions"] == 0
+    r.close()
+
+
+def test_tiny_host_partials_sum():
+    wl = synth.WORKLOADS["tiny"]
+    log("tiny host partials")
+    r = Runner(wl, [0], slots=2, mode="host", keep_debug=True)
+    x = synth.gen_hidden(wl, 0)
+    saw_host = False
+    for t in range(24):
+        out, res = r.call(0, x[t])
+        g, h = r.cache.partials(0)
+        np.testing.assert_array_equal(g + h, out)
+        if res.misses:
+            saw_host = True
+            assert np.any(h != 0)
+        else:
+            assert np.all(h == 0)
+    assert saw_host
+    r.close()
+
+
+@pytest.mark.parametrize("T", [2, 3, 4, 5, 17])
+@pytest.mark.parametrize("mode", ["stream", "host"])
+def test_multi_token_ragged(T, mode):
+    wl = synth.Workload("rag", 11, 1, 256, 512, 16, 4, 6, n_shared=1, router_sigma=0.1,
+                        zipf_s=0.5, rho=None, tokens=T * 6, batch=T)
+    log(f"ragged T={T} mode={mode}")
+    r = Runner(wl, [0], mode=mode)
+    x = synth.gen_hidden(wl, 0)
+    for c in range(x.shape[0]):
+        r.call(0, x[c])
+    r.check_log()
+    r.close()
+
+
+def test_staged_small_prefill():
+    # 64 tokens x top-8 of 64 experts through 8 slots: several stages per call
+    wl = synth.Workload("stg", 12, 1, 128, 256, 64, 8, 8, n_shared=1, router_sigma=0.14,
+                        rho=None, tokens=192, batch=64)
+    log("staged small prefill")
+    r = Runner(wl, [0], mode="stream")
+    x = synth.gen_hidden(wl, 0)
+    for c in range(x.shape[0]):
+        _, res = r.call(0, x[c])
+        assert len(res.stage_views) > 1
+    r.check_log()
+    r.close()
+
+
+def test_gemma_shape_two_layers():
+    wl = synth.WORKLOADS["gemma"]
+    log("gemma shape, 2 layers x 6 calls")
+    r = Runner(wl, [0, 17])
+    xs = [synth.gen_hidden(wl, l, 6) for l in (0, 17)]
+    for t in range(6):
+        for li in range(2):
+            r.call(li, xs[li][t])
+    r.check_log()
+    r.close()
+
+
+@pytest.mark.parametrize("b", [2, 4])
+def test_qwen_shape_batches(b):
+    wl = synth.qwen_batch(b)
+    log(f"qwen shape b={b}")
+    r = Runner(wl, [5])
+    x = synth.gen_hidden(wl, 5, 6)
+    for t in range(6):
+        r.call(0, x[t])
+    r.check_log()
+    r.close()
+
+
+def test_large_host_mode_sampled():
+    wl = synth.WORKLOADS["large"]
+    log("large shape, host mode, 1 layer x 4 calls, sampled columns")
+    r = Runner(wl, [3], mode="host", keep_debug=True)
+    x = synth.gen_hidden(wl, 3, 4)
+    cols = np.random.default_rng(0).choice(wl.d_model, 96, replace=False)
+    for t in range(4):
+        out, _ = r.call(0, x[t], col_sample=cols)
+        g, h = r.cache.partials(0)
+        np.testing.assert_array_equal(g + h, out)
+    r.check_log()
+    r.close()
+
+
+def test_prefill_ubatch_sampled():
+    wl = synth.WORKLOADS["prefill"]
+    log("prefill shape, 1 layer x 1 ubatch of 512, sampled tokens and columns")
+    r = Runner(wl, [2])
+    x = synth.gen_hidden(wl, 2, 1)[0]
+    rng = np.random.default_rng(1)
+    toks = np.sort(rng.choice(512, 6, replace=False))
+    cols = rng.choice(wl.d_model, 64, replace=False)
+    _, res = r.call(0, x, tok_sample=toks, col_sample=cols)
+    assert len(res.stage_views) >= 4
+    r.check_log()
+    r.close()

@@ -1,0 +1,67 @@
+"""The library's LRU planner (C++, via the C ABI, no GPU) against the oracle's
+step-by-step simulator: views, hits, slot state and the replacement log must
+agree bit for bit."""
+import random
+
+import numpy as np
+import pytest
+
+import expert_cache_host_amd as m
+from oracle.lru import LayerSlots
+
+
+def _compare(e_count, s_count, mode, max_fills, calls, seed):
+    rnd = random.Random(seed)
+    lib_p = m.Planner(e_count, s_count, mode, max_fills)
+    sim = LayerSlots(e_count, s_count)
+    for _ in range(calls):
+        t, k = rnd.choice([(1, 1), (1, 2), (1, 8), (2, 4), (4, 8), (3, 3)])
+        k = min(k, e_count)
+        hot = max(1, e_count // 4)
+        idx = []
+        for _t in range(t):
+            pool = list(range(e_count))
+            if rnd.random() < 0.7:
+                pool = list(range(hot)) + rnd.sample(range(e_count), min(e_count, k))
+                pool = sorted(set(pool))
+            idx += rnd.sample(pool, k) if len(pool) >= k else rnd.sample(range(e_count), k)
+        ns, hits, misses = lib_p.plan(idx)
+        res = sim.plan(idx, mode, max_fills)
+        assert (ns, hits, misses) == (len(res.stage_views), res.hits, res.misses)
+        for s in range(ns):
+            sv, hv = lib_p.views(s)
+            assert sv.tolist() == res.stage_views[s]
+            if mode == "host":
+                assert hv.tolist() == res.host_view
+            else:
+                assert hv.tolist() == [-1] * e_count
+        ein, lu = lib_p.slot_state()
+        assert ein.tolist() == sim.expert_in
+        assert lu.tolist() == sim.last_use
+    assert lib_p.evictions() == sim.log
+
+
+@pytest.mark.parametrize("mode", ["stream", "host"])
+@pytest.mark.parametrize("e_count,s_count", [(8, 4), (8, 1), (16, 16), (128, 32), (256, 64), (20, 3)])
+def test_planner_matches_oracle(mode, e_count, s_count):
+    _compare(e_count, s_count, mode, -1, 150, seed=e_count * 31 + s_count)
+
+
+@pytest.mark.parametrize("max_fills", [0, 1, 2])
+def test_planner_budget_matches_oracle(max_fills):
+    _compare(32, 6, "host", max_fills, 200, seed=max_fills)
+
+
+def test_planner_staging_prefill_like():
+    # 512 tokens x top-8 of 256 experts through 64 slots: many stages
+    rng = np.random.default_rng(0)
+    lib_p = m.Planner(256, 64, "stream")
+    sim = LayerSlots(256, 64)
+    for _ in range(3):
+        idx = np.stack([rng.choice(256, 8, replace=False) for _ in range(512)]).ravel()
+        ns, hits, misses = lib_p.plan(idx)
+        res = sim.plan(idx.tolist(), "stream")
+        assert ns == len(res.stage_views) >= 4
+        for s in range(ns):
+            assert lib_p.views(s)[0].tolist() == res.stage_views[s]
+    assert lib_p.evictions() == sim.log
