@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-MoE layer served from per-layer GPU expert slots.
+
+    python bench.py [--steps K] [--warmup W] [--workload gemma|qwen|qwen_b2|qwen_b4|large|prefill|tiny]
+
+One step = one batch (decode: one token per stream; prefill: one ubatch) through
+every layer of the workload, layer after layer, through the C ABI.  The default
+workload is the Gemma-4-26B-A4B-like decode (30 layers, d_model 2816, d_ff 704,
+128 experts, top-8, 32 slots per layer, batch 1, misses streamed into slots).
+
+Prints one JSON line.  `value` = MoE-layer tokens/s (tokens x layers / wall
+time) over exactly K timed steps, inputs resident in HBM and expert weights in
+the library's page-locked host arena before the timed region starts.  A second
+pass of K steps (not timed end to end) brackets every kernel launch with HIP
+events inside the library, for the per-kernel roofline.  The oracle is timed on
+a bounded sample of the same workload as the CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def pick_workload(name):
+    import synth
+    if name.startswith("qwen_b"):
+        return synth.qwen_batch(int(name[len("qwen_b"):]))
+    return synth.WORKLOADS[name]
+
+
+def describe(wl):
+    kind = "prefill ubatch" if wl.rho is None else f"decode b={wl.batch}"
+    miss = wl.miss_mode + " misses"
+    sh = f" + {wl.n_shared} shared" if wl.n_shared else ""
+    return (f"{wl.name}: {wl.layers} layers, d_model {wl.d_model}, d_ff {wl.d_ff}, "
+            f"{wl.n_experts} experts{sh}, top-{wl.top_k}, {wl.slots} slots/layer, {kind} "
+            f"({wl.batch} tokens/call), {miss}")
+
+
+def cpu_baseline(wl, weights, routers, hidden, budget_s=12.0, max_calls=64):
+    """The oracle, as it stands, on the first calls of layer 0 until ~budget_s."""
+    from oracle.layer import moe_layer
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    lb = weights[:wl.layer_bytes]
+    w_r, b = routers[0]
+    n = 0
+    t0 = time.perf_counter()
+    while n < max_calls and n < hidden[0].shape[0]:
+        moe_layer(hidden[0][n], w_r, b, lb, wl.d_model, wl.d_ff, wl.n_experts, wl.top_k,
+                  n_shared=wl.n_shared)
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": n * wl.batch / dt, "unit": "layer-tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {n} calls of layer 0 ({n * wl.batch} tokens), fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="gemma")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-pass", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import expert_cache_host_amd as m
+    import synth
+
+    wl = pick_workload(args.workload)
+    per_layer = wl.calls_per_layer
+    if wl.rho is None:
+        steps = args.steps if args.steps is not None else 6
+        warmup = args.warmup if args.warmup is not None else 1
+    else:
+        steps = args.steps if args.steps is not None else 224
+        warmup = args.warmup if args.warmup is not None else 16
+    kernel_steps = 0 if args.no_kernel_pass else min(steps, max(1, per_layer - warmup - steps))
+    need = warmup + steps + kernel_steps
+    if need > per_layer:
+        raise SystemExit(f"{wl.name} has {per_layer} calls per layer; warmup+steps(+kernel pass) "
+                         f"= {need}")
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.perf_counter()
+    weights = synth.gen_all_weights(wl)
+    log(f"[bench] generated {wl.total_bytes / 1e9:.2f} GB of Q4 experts in "
+        f"{time.perf_counter() - t0:.1f} s")
+    routers = [synth.gen_router(wl, l) for l in range(wl.layers)]
+    hidden = [synth.gen_hidden(wl, l, need) for l in range(wl.layers)]
+    t0 = time.perf_counter()
+    cache = m.MoECache(wl.layers, wl.n_experts, wl.slots, wl.d_model, wl.d_ff, weights,
+                       top_k=wl.top_k, miss_mode=wl.miss_mode, n_shared=wl.n_shared)
+    log(f"[bench] cache created (pinned arena + slot preload) in {time.perf_counter() - t0:.1f} s")
+    w_d = [torch.from_numpy(w).to(dev) for w, _ in routers]
+    b_d = [torch.from_numpy(b).to(dev) if b is not None else None for _, b in routers]
+    x_d = [torch.from_numpy(h).to(dev) for h in hidden]          # [calls, batch, d] per layer
+    out = torch.empty((wl.batch, wl.d_model), dtype=torch.float32, device=dev)
+
+    def run(step0, n):
+        for s in range(step0, step0 + n):
+            for l in range(wl.layers):
+                cache.forward(l, x_d[l][s], w_d[l], b_d[l], out=out)
+
+    run(0, warmup)
+    torch.cuda.synchronize()
+    cache.reset_stats()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(warmup, steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = cache.stats()
+    log(f"[bench] timed {steps} steps in {wall:.3f} s")
+
+    layer_tokens = steps * wl.batch * wl.layers
+    value = layer_tokens / wall
+    sel = max(1, st["selections"])
+    extra = {
+        "stack_tokens_per_s": steps * wl.batch / wall,
+        "hit_rate": st["hits"] / sel,
+        "fills_per_call": st["fills"] / max(1, st["calls"]),
+        "fill_GB": st["fill_bytes"] / 1e9,
+        "stages_per_call": st["stages"] / max(1, st["calls"]),
+        "plan_us_per_call": 1e6 * st["plan_s"] / max(1, st["calls"]),
+        "host_ms_per_call": 1e3 * st["host_s"] / max(1, st["calls"]),
+    }
+
+    roofline = None
+    kernels = {}
+    if kernel_steps:
+        cache.reset_stats()
+        cache.set_timing(True)
+        run(warmup + steps, kernel_steps)
+        torch.cuda.synchronize()
+        cache.sync()
+        ks = cache.kernel_stats()
+        st2 = cache.stats()
+        cache.set_timing(False)
+        for name, (n, sec, by) in ks.items():
+            if n:
+                kernels[name] = {"launches": n, "avg_us": 1e6 * sec / n,
+                                 "GB_per_s": by / sec / 1e9 if sec > 0 else None,
+                                 "bytes_per_launch": by / n}
+        if st2["h2d_s"] > 0:
+            extra["fill_H2D_GB_per_s"] = st2["fill_bytes"] / st2["h2d_s"] / 1e9
+        dom = max((k for k in kernels if k in ("gateup", "down")),
+                  key=lambda k: ks[k][1], default=None)
+        if dom:
+            n, sec, by = ks[dom]
+            ach = by / sec / 1e9
+            roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                        "avg_launch_us": 1e6 * sec / n, "bytes_per_launch": by / n}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, weights, routers, hidden)
+
+    line = {
+        "metric": "MoE-layer tokens/s (decode b=1)" if wl.rho is not None else
+                  "MoE-layer tokens/s (prefill ub=512)",
+        "value": value,
+        "unit": "layer-tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": 1e3 * wall / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Q4_0 experts ~N(0,0.02), AR(1) hidden states, Zipf router bias)",
+        "config": {"workload": describe(wl), "layers": wl.layers, "tokens_per_call": wl.batch,
+                   "steps_are": "one batch through every layer"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+        "kernels": kernels,
+    }
+    cache.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

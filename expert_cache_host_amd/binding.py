@@ -69,6 +69,9 @@ def load_library():
         "moe_layer_forward": (I32, [P, I32, P, I32, P, P, P, P]),
         "moe_cache_stats": (I32, [P, I32, ctypes.POINTER(Stats)]),
         "moe_cache_reset_stats": (I32, [P]),
+        "moe_cache_set_timing": (I32, [P, I32]),
+        "moe_cache_kernel_stats": (I32, [P, I32, ctypes.POINTER(ctypes.c_int64),
+                                         ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
         "moe_cache_sync": (I32, [P]),
         "moe_cache_destroy": (None, [P]),
         "moe_last_error": (ctypes.c_char_p, []),
@@ -174,6 +177,21 @@ class MoECache:
         st = Stats()
         _check(load_library().moe_cache_stats(self._h, layer, ctypes.byref(st)))
         return {n: getattr(st, n) for n, _ in Stats._fields_}
+
+    KERNELS = ("router", "topk", "remap", "gateup", "down", "combine")
+
+    def set_timing(self, on: bool):
+        _check(load_library().moe_cache_set_timing(self._h, 1 if on else 0))
+
+    def kernel_stats(self) -> dict:
+        """{kernel: (launches, device seconds, algorithmic bytes)} while timing was on."""
+        out = {}
+        for i, name in enumerate(self.KERNELS):
+            n, sec, by = ctypes.c_int64(), ctypes.c_double(), ctypes.c_double()
+            _check(load_library().moe_cache_kernel_stats(self._h, i, ctypes.byref(n), ctypes.byref(sec),
+                                                         ctypes.byref(by)))
+            out[name] = (n.value, sec.value, by.value)
+        return out
 
     def reset_stats(self):
         _check(load_library().moe_cache_reset_stats(self._h))

@@ -145,8 +145,15 @@ struct LayerState {
   TimingLog t_gpu, t_h2d;
 };
 
+struct KernelTiming {
+  TimingLog log;
+  int64_t launches = 0;
+  double bytes = 0.0;
+};
+
 struct moe_cache {
   int32_t L = 0, E = 0, S = 0, d = 0, f = 0;
+  KernelTiming kt[MOE_K_COUNT];
   moe_cache_opts o{};
   moe::RecordLayout lay;
   int device = 0;
@@ -224,6 +231,28 @@ moe::SlotView make_view(const std::vector<int32_t> &table) {
   return v;
 }
 
+// Event pair around one kernel launch (timing on only).
+struct KTime {
+  moe_cache *c;
+  int kid;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  KTime(moe_cache *c_, int kid_, hipStream_t st_) : c(c_), kid(kid_), st(st_) {
+    if (c->timing) {
+      a = c->kt[kid].log.get();
+      HIPCHK(hipEventRecord(a, st));
+    }
+  }
+  void end(double bytes) {
+    if (!c->timing) return;
+    hipEvent_t b = c->kt[kid].log.get();
+    HIPCHK(hipEventRecord(b, st));
+    c->kt[kid].log.pending.emplace_back(a, b);
+    c->kt[kid].launches++;
+    c->kt[kid].bytes += bytes;
+  }
+};
+
 void record_compute(moe_cache *c, LayerState &ly, hipStream_t st) {
   HIPCHK(hipEventRecord(ly.compute_ev, st));
   ly.compute_recorded = true;
@@ -257,14 +286,19 @@ void enqueue_fills(moe_cache *c, int32_t layer, const std::vector<moe::Fill> &fi
 }
 
 // K3 + K4 + K5 for one stage whose expert -> slot table is `view`.
+// work_experts: experts the Q4 kernels actually read (for the byte counters).
 void run_stage(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &view, bool with_shared,
-               int n_buckets, const float *x, hipStream_t st) {
+               int n_buckets, double work_experts, const float *x, hipStream_t st) {
   const int32_t k = c->o.top_k;
   const int shared_slot = with_shared ? c->S : -1;
   const int n_ids = c->S + c->o.n_shared;
-  HIPCHK(moe::launch_remap((const int32_t *)c->idx.p, T, k, view, shared_slot, n_ids,
-                           (int32_t *)c->meta.p, (int32_t *)c->bucket_pair.p,
-                           (int32_t *)c->pair_gpu.p, st));
+  {
+    KTime kt(c, MOE_K_REMAP, st);
+    HIPCHK(moe::launch_remap((const int32_t *)c->idx.p, T, k, view, shared_slot, n_ids,
+                             (int32_t *)c->meta.p, (int32_t *)c->bucket_pair.p,
+                             (int32_t *)c->pair_gpu.p, st));
+    kt.end((double)T * k * 8);
+  }
   if (n_buckets <= 0) return;
   const moe::RecordLayout &L = c->lay;
   moe::GemvArgs a{};
@@ -286,7 +320,11 @@ void run_stage(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &view
   a.out = (float *)c->h.p;
   const int max_tok = T;
   moe::GemvShape sh1 = moe::choose_gemv(a.rows, a.nb, n_buckets, max_tok);
-  HIPCHK(moe::launch_gemv(a, sh1, true, n_buckets, st));
+  {
+    KTime kt(c, MOE_K_GATEUP, st);
+    HIPCHK(moe::launch_gemv(a, sh1, true, n_buckets, st));
+    kt.end(work_experts * 2.0 * (double)c->f * (double)L.nb_gu * 18.0);
+  }
   // down: rows d, K = f, input = h by pair
   moe::GemvArgs b = a;
   b.off_q0 = L.off_dq;
@@ -297,7 +335,11 @@ void run_stage(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &view
   b.in_by_pair = 1;
   b.out = (float *)c->y.p;
   moe::GemvShape sh2 = moe::choose_gemv(b.rows, b.nb, n_buckets, max_tok);
-  HIPCHK(moe::launch_gemv(b, sh2, false, n_buckets, st));
+  {
+    KTime kt(c, MOE_K_DOWN, st);
+    HIPCHK(moe::launch_gemv(b, sh2, false, n_buckets, st));
+    kt.end(work_experts * (double)c->d * (double)L.nb_dn * 18.0);
+  }
 }
 
 moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
@@ -320,9 +362,17 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   }
   if (host_mode)
     HIPCHK(hipMemcpyAsync(c->h_x.p, x, (size_t)T * d * 4, hipMemcpyDeviceToHost, st));
-  HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)c->z.p, st));
-  HIPCHK(moe::launch_topk((const float *)c->z.p, T, E, k, c->o.norm_topk, (int32_t *)c->idx.p,
-                          (float *)c->w.p, (int32_t *)c->pair_gpu.p, st));
+  {
+    KTime kt(c, MOE_K_ROUTER, st);
+    HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)c->z.p, st));
+    kt.end(4.0 * ((double)E * d + (double)T * d + (double)T * E + (router_bias ? E : 0)));
+  }
+  {
+    KTime kt(c, MOE_K_TOPK, st);
+    HIPCHK(moe::launch_topk((const float *)c->z.p, T, E, k, c->o.norm_topk, (int32_t *)c->idx.p,
+                            (float *)c->w.p, (int32_t *)c->pair_gpu.p, st));
+    kt.end(4.0 * ((double)T * E + 3.0 * T * k));
+  }
   HIPCHK(hipMemcpyAsync(c->h_idx.p, c->idx.p, (size_t)T * k * 4, hipMemcpyDeviceToHost, st));
   HIPCHK(hipMemcpyAsync(c->h_w.p, c->w.p, (size_t)T * k * 4, hipMemcpyDeviceToHost, st));
   HIPCHK(hipEventRecord(c->ev_idx, st));
@@ -349,7 +399,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
       ly.planner->stage_view(ly.plan, (int32_t)s, table.data(), nullptr);
       const bool sh = s == 0 && c->o.n_shared > 0;
       const int nb = (int)stg.members.size() + (sh ? 1 : 0);
-      run_stage(c, layer, T, make_view(table), sh, nb, x, st);
+      run_stage(c, layer, T, make_view(table), sh, nb, (double)nb, x, st);
       record_compute(c, ly, st);
     }
     if (c->o.keep_debug) ly.dbg_host.assign((size_t)T * d, 0.0f);
@@ -357,12 +407,19 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
     // GPU part on the table published at call start; no host wait before it
     const std::vector<int32_t> &pre = ly.planner->slot_of();
     const int nb_bound = std::min(T * k, c->S) + (c->o.n_shared > 0 ? 1 : 0);
-    run_stage(c, layer, T, make_view(pre), c->o.n_shared > 0, nb_bound, x, st);
+    // bytes are booked once the plan tells how many selected experts were cached
+    run_stage(c, layer, T, make_view(pre), c->o.n_shared > 0, nb_bound, 0.0, x, st);
     record_compute(c, ly, st);
     HIPCHK(hipEventSynchronize(c->ev_idx));
     const double tp = now_s();
     ly.planner->plan((const int32_t *)c->h_idx.p, T * k, 1, c->o.max_fills_per_call, ly.plan);
     ly.st.plan_s += now_s() - tp;
+    if (c->timing) {
+      const double n_gpu = (double)(ly.plan.unique - (int32_t)ly.plan.host_experts.size()) +
+                           (double)c->o.n_shared;
+      c->kt[MOE_K_GATEUP].bytes += n_gpu * 2.0 * (double)c->f * (double)c->lay.nb_gu * 18.0;
+      c->kt[MOE_K_DOWN].bytes += n_gpu * (double)c->d * (double)c->lay.nb_dn * 18.0;
+    }
     const moe::PlanStage &stg = ly.plan.stages[0];
     if (!stg.fills.empty()) {
       enqueue_fills(c, layer, stg.fills, st);
@@ -396,9 +453,13 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
         ly.dbg_host.assign(host_part, host_part + (size_t)T * d);
       ly.st.host_s += now_s() - th;
       ly.st.host_selections += ly.plan.misses;
-      HIPCHK(moe::launch_combine((const float *)c->y.p, (const float *)c->w.p,
-                                 (const int32_t *)c->pair_gpu.p, T, k, d, c->o.n_shared, host_part,
-                                 out, dbg_gpu, st));
+      {
+        KTime kt(c, MOE_K_COMBINE, st);
+        HIPCHK(moe::launch_combine((const float *)c->y.p, (const float *)c->w.p,
+                                   (const int32_t *)c->pair_gpu.p, T, k, d, c->o.n_shared,
+                                   host_part, out, dbg_gpu, st));
+        kt.end(4.0 * (double)T * d * (k + c->o.n_shared + 2));
+      }
       HIPCHK(hipEventRecord(c->partial_ev[b], st));
       c->partial_used[b] = true;
       combined = true;
@@ -406,10 +467,13 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
       ly.dbg_host.assign((size_t)T * d, 0.0f);
     }
   }
-  if (!combined)
+  if (!combined) {
+    KTime kt(c, MOE_K_COMBINE, st);
     HIPCHK(moe::launch_combine((const float *)c->y.p, (const float *)c->w.p,
                                (const int32_t *)c->pair_gpu.p, T, k, d, c->o.n_shared, nullptr, out,
                                dbg_gpu, st));
+    kt.end(4.0 * (double)T * d * (k + c->o.n_shared + 1));
+  }
   if (c->timing) {
     HIPCHK(hipEventRecord(g1, st));
     ly.t_gpu.pending.emplace_back(g0, g1);
@@ -620,10 +684,39 @@ moe_status moe_cache_stats(moe_cache *c, int32_t layer, moe_stats *out) {
   });
 }
 
+moe_status moe_cache_set_timing(moe_cache *c, int32_t on) {
+  g_err.clear();
+  if (!c) return fail(MOE_EINVAL, "cache is NULL");
+  if (on != 0 && on != 1) return fail(MOE_EINVAL, "on must be 0 or 1");
+  c->timing = on != 0;
+  return MOE_OK;
+}
+
+moe_status moe_cache_kernel_stats(moe_cache *c, int32_t kernel, int64_t *launches, double *seconds,
+                                  double *bytes) {
+  g_err.clear();
+  if (!c) return fail(MOE_EINVAL, "cache is NULL");
+  if (kernel < 0 || kernel >= MOE_K_COUNT) return fail(MOE_EINVAL, "kernel id out of range");
+  return guarded(c, [&]() {
+    KernelTiming &k = c->kt[kernel];
+    k.log.collect();
+    if (launches) *launches = k.launches;
+    if (seconds) *seconds = k.log.total;
+    if (bytes) *bytes = k.bytes;
+    return MOE_OK;
+  });
+}
+
 moe_status moe_cache_reset_stats(moe_cache *c) {
   g_err.clear();
   if (!c) return fail(MOE_EINVAL, "cache is NULL");
   return guarded(c, [&]() {
+    for (auto &k : c->kt) {
+      k.log.collect();
+      k.log.total = 0.0;
+      k.launches = 0;
+      k.bytes = 0.0;
+    }
     for (auto &ly : c->layers) {
       ly.t_gpu.collect();
       ly.t_h2d.collect();

@@ -172,6 +172,26 @@ moe_status moe_layer_forward(moe_cache *c, int32_t layer, const float *x, int32_
  * Synchronises the library's own streams to read device timings. */
 moe_status moe_cache_stats(moe_cache *c, int32_t layer, moe_stats *out);
 
+/* Turns the event timing of opts.timing on (1) or off (0) from now on. */
+moe_status moe_cache_set_timing(moe_cache *c, int32_t on);
+
+/* Kernels timed one launch at a time when timing is on. */
+#define MOE_K_ROUTER 0  /* router logits */
+#define MOE_K_TOPK 1    /* top-k + softmax gating weights */
+#define MOE_K_REMAP 2   /* expert -> slot remap and bucketing */
+#define MOE_K_GATEUP 3  /* Q4 gate/up projections + SwiGLU */
+#define MOE_K_DOWN 4    /* Q4 down projection */
+#define MOE_K_COMBINE 5 /* weighted combine */
+#define MOE_K_COUNT 6
+
+/* Launches, summed device seconds (HIP events on the launching stream, read
+ * when this is called) and summed algorithmic bytes of kernel `kernel` since the
+ * last reset.  Algorithmic bytes: router = W_r + x + logits; Q4 kernels = the
+ * 18/32-byte-per-weight bytes of every expert matrix the launch reads; combine =
+ * expert outputs read + layer output written. */
+moe_status moe_cache_kernel_stats(moe_cache *c, int32_t kernel, int64_t *launches, double *seconds,
+                                  double *bytes);
+
 /* Zeroes every counter and timing (slot contents and eviction logs stay). */
 moe_status moe_cache_reset_stats(moe_cache *c);
 
