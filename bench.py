@@ -173,6 +173,8 @@ def main():
                                  "bytes_per_launch": by / n}
         if st2["h2d_s"] > 0:
             extra["fill_H2D_GB_per_s"] = st2["fill_bytes"] / st2["h2d_s"] / 1e9
+        if ks["fill"][0]:
+            extra["fill_kernel_H2D_GB_per_s"] = ks["fill"][2] / ks["fill"][1] / 1e9
         dom = max((k for k in kernels if k in ("gateup", "down")),
                   key=lambda k: ks[k][1], default=None)
         if dom:

@@ -131,7 +131,8 @@ struct TimingLog {
 struct LayerState {
   std::unique_ptr<moe::SlotPlanner> planner;
   uint8_t *d_slots = nullptr;     // (S + n_shared) records
-  hipEvent_t fill_ev = nullptr;   // last fills of this layer (side stream)
+  hipEvent_t fill_ev[2] = {nullptr, nullptr};  // last fills of this layer (side streams)
+  bool fill_used[2] = {false, false};
   hipEvent_t compute_ev = nullptr;  // last kernels that read this layer's slots
   bool fill_pending = false;
   bool compute_recorded = false;
@@ -159,13 +160,13 @@ struct moe_cache {
   int device = 0;
   uint8_t *h_arena = nullptr;   // L * (E + n_shared) records, page-locked
   std::vector<LayerState> layers;
-  hipStream_t side = nullptr;
+  hipStream_t side[2] = {nullptr, nullptr};  // slot fills alternate over two copy streams
   hipEvent_t ev_idx = nullptr, ev_ready = nullptr;
   bool poisoned = false;
   bool timing = false;
   // device workspace
   int32_t cap_T = 0;
-  DevBuf z, idx, w, pair_gpu, meta, bucket_pair, h, y;
+  DevBuf z, idx, w, meta, bucket_pair, h, y, xp, xsw, xscale;
   // pinned host staging
   PinnedBuf h_idx, h_w, h_x, partial[2];
   hipEvent_t partial_ev[2] = {nullptr, nullptr};
@@ -183,11 +184,13 @@ struct moe_cache {
 
   ~moe_cache() {
     (void)hipSetDevice(device);
-    if (side) (void)hipStreamSynchronize(side);
+    for (auto sd : side)
+      if (sd) (void)hipStreamSynchronize(sd);
     (void)hipDeviceSynchronize();
     for (auto &ly : layers) {
       if (ly.d_slots) (void)hipFree(ly.d_slots);
-      if (ly.fill_ev) (void)hipEventDestroy(ly.fill_ev);
+      for (auto &e : ly.fill_ev)
+        if (e) (void)hipEventDestroy(e);
       if (ly.compute_ev) (void)hipEventDestroy(ly.compute_ev);
     }
     layers.clear();
@@ -196,7 +199,8 @@ struct moe_cache {
     if (ev_ready) (void)hipEventDestroy(ev_ready);
     for (auto &e : partial_ev)
       if (e) (void)hipEventDestroy(e);
-    if (side) (void)hipStreamDestroy(side);
+    for (auto sd : side)
+      if (sd) (void)hipStreamDestroy(sd);
   }
 
   void ensure_ws(int32_t T) {
@@ -207,11 +211,13 @@ struct moe_cache {
     z.ensure((size_t)T * E * 4);
     idx.ensure((size_t)T * k * 4);
     w.ensure((size_t)T * k * 4);
-    pair_gpu.ensure((size_t)T * k * 4);
     meta.ensure((size_t)moe::kMetaInts * 4);
     bucket_pair.ensure(P * 4);
     h.ensure(P * (size_t)f * 4);
     y.ensure(P * (size_t)d * 4);
+    xp.ensure((size_t)T * d * 4);
+    xsw.ensure((size_t)T * (d / 8) * 4);
+    xscale.ensure((size_t)T * 4);
     h_idx.ensure((size_t)T * k * 4);
     h_w.ensure((size_t)T * k * 4);
     if (o.miss_mode == MOE_MISS_HOST) {
@@ -258,57 +264,81 @@ void record_compute(moe_cache *c, LayerState &ly, hipStream_t st) {
   ly.compute_recorded = true;
 }
 
-// Copies the fills of one stage on the side stream after every earlier reader of
-// the victim slots (work enqueued so far on `st`, and the layer's last kernels).
+// Copies the fills of one stage on the two side streams after every earlier
+// reader of the victim slots (work enqueued so far on `st`, and the layer's last
+// kernels), and records the layer's fill events.
 void enqueue_fills(moe_cache *c, int32_t layer, const std::vector<moe::Fill> &fills,
                    hipStream_t st) {
   LayerState &ly = c->layers[layer];
   HIPCHK(hipEventRecord(c->ev_ready, st));
-  HIPCHK(hipStreamWaitEvent(c->side, c->ev_ready, 0));
-  if (ly.compute_recorded) HIPCHK(hipStreamWaitEvent(c->side, ly.compute_ev, 0));
+  const int n_sd = fills.size() > 1 ? 2 : 1;
   hipEvent_t t0 = nullptr, t1 = nullptr;
+  for (int i = 0; i < n_sd; ++i) {
+    HIPCHK(hipStreamWaitEvent(c->side[i], c->ev_ready, 0));
+    if (ly.compute_recorded) HIPCHK(hipStreamWaitEvent(c->side[i], ly.compute_ev, 0));
+  }
   if (c->timing) {
     t0 = ly.t_h2d.get();
     t1 = ly.t_h2d.get();
-    HIPCHK(hipEventRecord(t0, c->side));
+    HIPCHK(hipEventRecord(t0, c->side[0]));
+    if (n_sd > 1) HIPCHK(hipStreamWaitEvent(c->side[1], t0, 0));
   }
-  for (const moe::Fill &fl : fills) {
+  for (size_t i = 0; i < fills.size(); ++i) {
+    const moe::Fill &fl = fills[i];
     HIPCHK(hipMemcpyAsync(c->dev_slot(layer, fl.slot), c->host_record(layer, fl.expert), c->rec(),
-                          hipMemcpyHostToDevice, c->side));
+                          hipMemcpyHostToDevice, c->side[i % n_sd]));
+  }
+  for (int i = 0; i < 2; ++i) {
+    ly.fill_used[i] = i < n_sd;
+    if (i < n_sd) HIPCHK(hipEventRecord(ly.fill_ev[i], c->side[i]));
   }
   if (c->timing) {
-    HIPCHK(hipEventRecord(t1, c->side));
+    if (n_sd > 1) HIPCHK(hipStreamWaitEvent(c->side[0], ly.fill_ev[1], 0));
+    HIPCHK(hipEventRecord(t1, c->side[0]));
     ly.t_h2d.pending.emplace_back(t0, t1);
   }
-  HIPCHK(hipEventRecord(ly.fill_ev, c->side));
   ly.st.fills += fills.size();
   ly.st.fill_bytes += fills.size() * (uint64_t)c->rec();
 }
 
-// K3 + K4 + K5 for one stage whose expert -> slot table is `view`.
-// work_experts: experts the Q4 kernels actually read (for the byte counters).
-void run_stage(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &view, bool with_shared,
-               int n_buckets, double work_experts, const float *x, hipStream_t st) {
+void wait_fills(moe_cache *c, LayerState &ly, hipStream_t st) {
+  for (int i = 0; i < 2; ++i)
+    if (ly.fill_used[i]) HIPCHK(hipStreamWaitEvent(st, ly.fill_ev[i], 0));
+}
+
+// Gate/up + SwiGLU and down for the pairs whose expert `view` maps to a slot
+// (plus the shared expert's pairs when with_shared), into h and y.  The decode
+// path (few tokens) lets each workgroup find its bucket; larger batches bucket
+// once with the remap kernel.  work_experts: experts read (byte counters).
+void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &view,
+                 bool with_shared, int n_buckets, double work_experts, const float *x,
+                 hipStream_t st, const moe::BucketTable *tab = nullptr) {
+  if (n_buckets <= 0) return;
   const int32_t k = c->o.top_k;
   const int shared_slot = with_shared ? c->S : -1;
-  const int n_ids = c->S + c->o.n_shared;
-  {
-    KTime kt(c, MOE_K_REMAP, st);
-    HIPCHK(moe::launch_remap((const int32_t *)c->idx.p, T, k, view, shared_slot, n_ids,
-                             (int32_t *)c->meta.p, (int32_t *)c->bucket_pair.p,
-                             (int32_t *)c->pair_gpu.p, st));
-    kt.end((double)T * k * 8);
-  }
-  if (n_buckets <= 0) return;
+  const int P = T * k + (with_shared ? T : 0);
+  const bool decode = T <= moe::kDecodeMaxTokens && P <= moe::kDecodeMaxPairs;
   const moe::RecordLayout &L = c->lay;
   moe::GemvArgs a{};
+  if (!decode && !tab) {
+    KTime kt(c, MOE_K_REMAP, st);
+    HIPCHK(moe::launch_remap((const int32_t *)c->idx.p, T, k, view, shared_slot,
+                             c->S + c->o.n_shared, (int32_t *)c->meta.p,
+                             (int32_t *)c->bucket_pair.p, st));
+    kt.end((double)P * 8);
+    a.meta = (const int32_t *)c->meta.p;
+    a.bucket_pair = (const int32_t *)c->bucket_pair.p;
+  }
   a.slots = c->layers[layer].d_slots;
+  a.xp = (const uint32_t *)c->xp.p;
+  a.xsw = (const float *)c->xsw.p;
+  a.xscale = (const float *)c->xscale.p;
   a.rec_bytes = L.bytes;
   a.T = T;
   a.k = k;
-  a.meta = (const int32_t *)c->meta.p;
-  a.bucket_pair = (const int32_t *)c->bucket_pair.p;
-  // gate/up + SwiGLU: rows f, K = d, input = x by token
+  a.idx = (const int32_t *)c->idx.p;
+  a.shared_slot = shared_slot;
+  // gate/up + SwiGLU: rows f, K = d, input = prepared x by token
   a.off_q0 = L.off_gq;
   a.off_s0 = L.off_gs;
   a.off_q1 = L.off_uq;
@@ -319,10 +349,10 @@ void run_stage(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &view
   a.in_by_pair = 0;
   a.out = (float *)c->h.p;
   const int max_tok = T;
-  moe::GemvShape sh1 = moe::choose_gemv(a.rows, a.nb, n_buckets, max_tok);
+  moe::GemvShape sh1 = moe::choose_gemv(true, a.rows, a.nb, n_buckets, max_tok);
   {
     KTime kt(c, MOE_K_GATEUP, st);
-    HIPCHK(moe::launch_gemv(a, sh1, true, n_buckets, st));
+    HIPCHK(moe::launch_gemv(a, view, tab, sh1, true, n_buckets, st));
     kt.end(work_experts * 2.0 * (double)c->f * (double)L.nb_gu * 18.0);
   }
   // down: rows d, K = f, input = h by pair
@@ -334,10 +364,10 @@ void run_stage(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &view
   b.in = (const float *)c->h.p;
   b.in_by_pair = 1;
   b.out = (float *)c->y.p;
-  moe::GemvShape sh2 = moe::choose_gemv(b.rows, b.nb, n_buckets, max_tok);
+  moe::GemvShape sh2 = moe::choose_gemv(false, b.rows, b.nb, n_buckets, max_tok);
   {
     KTime kt(c, MOE_K_DOWN, st);
-    HIPCHK(moe::launch_gemv(b, sh2, false, n_buckets, st));
+    HIPCHK(moe::launch_gemv(b, view, tab, sh2, false, n_buckets, st));
     kt.end(work_experts * (double)c->d * (double)L.nb_dn * 18.0);
   }
 }
@@ -348,6 +378,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   LayerState &ly = c->layers[layer];
   const int32_t k = c->o.top_k, E = c->E, d = c->d;
   const bool host_mode = c->o.miss_mode == MOE_MISS_HOST;
+  const int ns = c->o.n_shared;
   c->ensure_ws(T);
   hipEvent_t g0 = nullptr, g1 = nullptr;
   if (c->timing) {
@@ -357,69 +388,106 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   }
   // publication of the previous call's fills (host mode)
   if (ly.fill_pending) {
-    HIPCHK(hipStreamWaitEvent(st, ly.fill_ev, 0));
+    wait_fills(c, ly, st);
     ly.fill_pending = false;
   }
   if (host_mode)
     HIPCHK(hipMemcpyAsync(c->h_x.p, x, (size_t)T * d * 4, hipMemcpyDeviceToHost, st));
   {
     KTime kt(c, MOE_K_ROUTER, st);
-    HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)c->z.p, st));
-    kt.end(4.0 * ((double)E * d + (double)T * d + (double)T * E + (router_bias ? E : 0)));
+    HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)c->z.p,
+                              (uint32_t *)c->xp.p, (float *)c->xsw.p, (float *)c->xscale.p, st));
+    kt.end(4.0 * ((double)E * d + (double)T * d * 2 + (double)T * E + (router_bias ? E : 0)));
   }
   {
     KTime kt(c, MOE_K_TOPK, st);
     HIPCHK(moe::launch_topk((const float *)c->z.p, T, E, k, c->o.norm_topk, (int32_t *)c->idx.p,
-                            (float *)c->w.p, (int32_t *)c->pair_gpu.p, st));
-    kt.end(4.0 * ((double)T * E + 3.0 * T * k));
+                            (float *)c->w.p, (int32_t *)c->h_idx.p, (float *)c->h_w.p, st));
+    kt.end(4.0 * ((double)T * E + 4.0 * T * k));
   }
-  HIPCHK(hipMemcpyAsync(c->h_idx.p, c->idx.p, (size_t)T * k * 4, hipMemcpyDeviceToHost, st));
-  HIPCHK(hipMemcpyAsync(c->h_w.p, c->w.p, (size_t)T * k * 4, hipMemcpyDeviceToHost, st));
   HIPCHK(hipEventRecord(c->ev_idx, st));
+
+  // Cached experts (and the shared one) on the table published at call start,
+  // enqueued before the host reads the routing.
+  const moe::SlotView pre = make_view(ly.planner->slot_of());
+  const int nb_hits = std::min(T * k, c->S) + (ns > 0 ? 1 : 0);
+  run_experts(c, layer, T, pre, ns > 0, nb_hits, 0.0, x, st);
+  record_compute(c, ly, st);
 
   float *dbg_gpu = nullptr;
   if (c->o.keep_debug) {
     ly.dbg_gpu.ensure((size_t)T * d * 4);
     dbg_gpu = (float *)ly.dbg_gpu.p;
   }
+  HIPCHK(hipEventSynchronize(c->ev_idx));
+  const double tp = now_s();
+  ly.planner->plan((const int32_t *)c->h_idx.p, T * k, host_mode ? 1 : 0,
+                   host_mode ? c->o.max_fills_per_call : -1, ly.plan);
+  ly.st.plan_s += now_s() - tp;
+  if (c->timing) {
+    const double n_hit = (double)(ly.plan.stages[0].members.size() -
+                                  (host_mode ? 0 : ly.plan.stages[0].fills.size())) + ns;
+    c->kt[MOE_K_GATEUP].bytes += n_hit * 2.0 * (double)c->f * (double)c->lay.nb_gu * 18.0;
+    c->kt[MOE_K_DOWN].bytes += n_hit * (double)c->d * (double)c->lay.nb_dn * 18.0;
+  }
   bool combined = false;
-
-  if (!host_mode) {
-    HIPCHK(hipEventSynchronize(c->ev_idx));
-    const double tp = now_s();
-    ly.planner->plan((const int32_t *)c->h_idx.p, T * k, 0, -1, ly.plan);
-    ly.st.plan_s += now_s() - tp;
-    std::vector<int32_t> table(E);
+  const bool decode_pairs = T <= moe::kDecodeMaxTokens && T * k <= moe::kDecodeMaxPairs;
+  if (!host_mode && decode_pairs) {
+    // every miss is pulled from the pinned arena into its slot by a copy
+    // kernel on the compute stream, then computed there from host-built buckets
+    const int32_t *hidx = (const int32_t *)c->h_idx.p;
     for (size_t s = 0; s < ly.plan.stages.size(); ++s) {
       const moe::PlanStage &stg = ly.plan.stages[s];
-      if (!stg.fills.empty()) {
-        enqueue_fills(c, layer, stg.fills, st);
-        HIPCHK(hipStreamWaitEvent(st, ly.fill_ev, 0));
+      for (size_t f0 = 0; f0 < stg.fills.size(); f0 += moe::kTabMax) {
+        moe::BucketTable tab;
+        moe::PullList pl;
+        tab.n = 0;
+        for (size_t f = f0; f < stg.fills.size() && tab.n < moe::kTabMax; ++f) {
+          const moe::Fill &fl = stg.fills[f];
+          const int b = tab.n++;
+          pl.src[b] = c->host_record(layer, fl.expert);
+          pl.dst[b] = c->dev_slot(layer, fl.slot);
+          tab.src[b] = c->dev_slot(layer, fl.slot);
+          tab.dst[b] = nullptr;
+          int cnt = 0;
+          for (int32_t p = 0; p < T * k; ++p)
+            if (hidx[p] == fl.expert) tab.pairs[b][cnt++] = (uint8_t)p;
+          tab.cnt[b] = (uint8_t)cnt;
+          for (int i = cnt; i < moe::kDecodeMaxTokens; ++i) tab.pairs[b][i] = tab.pairs[b][0];
+        }
+        pl.n = tab.n;
+        pl.per_expert = 64;
+        pl.bytes16 = (long long)c->rec() / 16;
+        // victims may still be read by earlier kernels of this layer on another stream
+        if (ly.compute_recorded) HIPCHK(hipStreamWaitEvent(st, ly.compute_ev, 0));
+        {
+          KTime kt(c, MOE_K_FILL, st);
+          HIPCHK(moe::launch_pull(pl, st));
+          kt.end((double)pl.n * (double)c->rec());
+        }
+        run_experts(c, layer, T, pre, false, tab.n, (double)tab.n, x, st, &tab);
+        record_compute(c, ly, st);
       }
-      ly.planner->stage_view(ly.plan, (int32_t)s, table.data(), nullptr);
-      const bool sh = s == 0 && c->o.n_shared > 0;
-      const int nb = (int)stg.members.size() + (sh ? 1 : 0);
-      run_stage(c, layer, T, make_view(table), sh, nb, (double)nb, x, st);
+      ly.st.fills += stg.fills.size();
+      ly.st.fill_bytes += stg.fills.size() * (uint64_t)c->rec();
+    }
+    if (c->o.keep_debug) ly.dbg_host.assign((size_t)T * d, 0.0f);
+  } else if (!host_mode) {
+    // every miss is streamed into a slot, stage by stage, then computed there
+    std::vector<int32_t> table(E, -1);
+    for (size_t s = 0; s < ly.plan.stages.size(); ++s) {
+      const moe::PlanStage &stg = ly.plan.stages[s];
+      if (stg.fills.empty()) continue;
+      enqueue_fills(c, layer, stg.fills, st);
+      wait_fills(c, ly, st);
+      std::fill(table.begin(), table.end(), -1);
+      for (const moe::Fill &fl : stg.fills) table[fl.expert] = fl.slot;
+      const int nb = (int)stg.fills.size();
+      run_experts(c, layer, T, make_view(table), false, nb, (double)nb, x, st);
       record_compute(c, ly, st);
     }
     if (c->o.keep_debug) ly.dbg_host.assign((size_t)T * d, 0.0f);
   } else {
-    // GPU part on the table published at call start; no host wait before it
-    const std::vector<int32_t> &pre = ly.planner->slot_of();
-    const int nb_bound = std::min(T * k, c->S) + (c->o.n_shared > 0 ? 1 : 0);
-    // bytes are booked once the plan tells how many selected experts were cached
-    run_stage(c, layer, T, make_view(pre), c->o.n_shared > 0, nb_bound, 0.0, x, st);
-    record_compute(c, ly, st);
-    HIPCHK(hipEventSynchronize(c->ev_idx));
-    const double tp = now_s();
-    ly.planner->plan((const int32_t *)c->h_idx.p, T * k, 1, c->o.max_fills_per_call, ly.plan);
-    ly.st.plan_s += now_s() - tp;
-    if (c->timing) {
-      const double n_gpu = (double)(ly.plan.unique - (int32_t)ly.plan.host_experts.size()) +
-                           (double)c->o.n_shared;
-      c->kt[MOE_K_GATEUP].bytes += n_gpu * 2.0 * (double)c->f * (double)c->lay.nb_gu * 18.0;
-      c->kt[MOE_K_DOWN].bytes += n_gpu * (double)c->d * (double)c->lay.nb_dn * 18.0;
-    }
     const moe::PlanStage &stg = ly.plan.stages[0];
     if (!stg.fills.empty()) {
       enqueue_fills(c, layer, stg.fills, st);
@@ -449,16 +517,15 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
       moe::host_moe_partial(*c->pool, c->lay, jobs, rank_job.data(), (const float *)c->h_w.p, T, k,
                             (const float *)c->h_x.p, (float *)c->partial[b].p, c->h_scratch);
       const float *host_part = (const float *)c->partial[b].p;
-      if (c->o.keep_debug)
-        ly.dbg_host.assign(host_part, host_part + (size_t)T * d);
+      if (c->o.keep_debug) ly.dbg_host.assign(host_part, host_part + (size_t)T * d);
       ly.st.host_s += now_s() - th;
       ly.st.host_selections += ly.plan.misses;
       {
         KTime kt(c, MOE_K_COMBINE, st);
         HIPCHK(moe::launch_combine((const float *)c->y.p, (const float *)c->w.p,
-                                   (const int32_t *)c->pair_gpu.p, T, k, d, c->o.n_shared,
-                                   host_part, out, dbg_gpu, st));
-        kt.end(4.0 * (double)T * d * (k + c->o.n_shared + 2));
+                                   (const int32_t *)c->idx.p, pre, 0, T, k, d, ns, host_part, out,
+                                   dbg_gpu, st));
+        kt.end(4.0 * (double)T * d * (k + ns + 2));
       }
       HIPCHK(hipEventRecord(c->partial_ev[b], st));
       c->partial_used[b] = true;
@@ -470,9 +537,9 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   if (!combined) {
     KTime kt(c, MOE_K_COMBINE, st);
     HIPCHK(moe::launch_combine((const float *)c->y.p, (const float *)c->w.p,
-                               (const int32_t *)c->pair_gpu.p, T, k, d, c->o.n_shared, nullptr, out,
-                               dbg_gpu, st));
-    kt.end(4.0 * (double)T * d * (k + c->o.n_shared + 1));
+                               (const int32_t *)c->idx.p, pre, host_mode ? 0 : 1, T, k, d, ns,
+                               nullptr, out, dbg_gpu, st));
+    kt.end(4.0 * (double)T * d * (k + ns + 1));
   }
   if (c->timing) {
     HIPCHK(hipEventRecord(g1, st));
@@ -603,7 +670,7 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
         }
       });
     }
-    HIPCHK(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking));
+    for (auto &sd : c->side) HIPCHK(hipStreamCreateWithFlags(&sd, hipStreamNonBlocking));
     HIPCHK(hipEventCreateWithFlags(&c->ev_idx, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&c->ev_ready, hipEventDisableTiming));
     for (auto &e : c->partial_ev) HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
@@ -618,17 +685,17 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
         (void)hipGetLastError();
         return fail(MOE_ENOMEM, "device slot arena allocation failed");
       }
-      HIPCHK(hipEventCreateWithFlags(&ly.fill_ev, hipEventDisableTiming));
+      for (auto &e : ly.fill_ev) HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
       HIPCHK(hipEventCreateWithFlags(&ly.compute_ev, hipEventDisableTiming));
       // preload: slot s <- expert s; shared slot S <- expert E
       for (int32_t s = 0; s < slots; ++s)
         HIPCHK(hipMemcpyAsync(c->dev_slot(l, s), c->host_record(l, s), c->rec(),
-                              hipMemcpyHostToDevice, c->side));
+                              hipMemcpyHostToDevice, c->side[s & 1]));
       for (int32_t s = 0; s < o.n_shared; ++s)
         HIPCHK(hipMemcpyAsync(c->dev_slot(l, slots + s), c->host_record(l, n_experts + s), c->rec(),
-                              hipMemcpyHostToDevice, c->side));
+                              hipMemcpyHostToDevice, c->side[0]));
     }
-    HIPCHK(hipStreamSynchronize(c->side));
+    for (auto sd : c->side) HIPCHK(hipStreamSynchronize(sd));
     return MOE_OK;
   });
   if (rc != MOE_OK) return rc;
@@ -732,7 +799,7 @@ moe_status moe_cache_sync(moe_cache *c) {
   g_err.clear();
   if (!c) return fail(MOE_EINVAL, "cache is NULL");
   return guarded(c, [&]() {
-    HIPCHK(hipStreamSynchronize(c->side));
+    for (auto sd : c->side) HIPCHK(hipStreamSynchronize(sd));
     return MOE_OK;
   });
 }

@@ -13,33 +13,105 @@
 
 namespace moe {
 
+// ============================================================== small helpers
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+template <int CTRL>
+__device__ __forceinline__ int mov_dpp(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+
+// (value, id) order for top-k: larger value first, then lower id; id == sent
+// marks "no candidate".
+__device__ __forceinline__ void take_better(float &bv, int &be, float ov, int oe, int sent) {
+  if (oe != sent && (be == sent || ov > bv || (ov == bv && oe < be))) {
+    bv = ov;
+    be = oe;
+  }
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float &bv, int &be, int sent) {
+  const float ov = __builtin_bit_cast(float, mov_dpp<CTRL>(__builtin_bit_cast(int, bv)));
+  const int oe = mov_dpp<CTRL>(be);
+  take_better(bv, be, ov, oe, sent);
+}
+
+// Best (value, id) over the wave, uniform in every lane: DPP within rows of 16
+// lanes (xor 1, xor 2, half-row mirror, row mirror), then the four row results.
+__device__ __forceinline__ void wave_argmax(float &bv, int &be, int sent) {
+  argmax_step<0xB1>(bv, be, sent);   // quad_perm [1,0,3,2]
+  argmax_step<0x4E>(bv, be, sent);   // quad_perm [2,3,0,1]
+  argmax_step<0x141>(bv, be, sent);  // row_half_mirror
+  argmax_step<0x140>(bv, be, sent);  // row_mirror
+  float rv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 0));
+  int re = __builtin_amdgcn_readlane(be, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float ov =
+        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 16 * r));
+    const int oe = __builtin_amdgcn_readlane(be, 16 * r);
+    take_better(rv, re, ov, oe, sent);
+  }
+  bv = rv;
+  be = re;
+}
+
 // ============================================================== router logits
 // One wave per (expert, tile of TT tokens).  Lane l accumulates i = l, l+64, ...
 // with the product and the sum rounded separately (no contraction), then a
 // halving tree off = 32..1, then the bias: the fixed order that makes every
-// top-k decision reproducible bit for bit on the host.
-template <int TT>
+// top-k decision reproducible bit for bit on the host.  Loads are issued CH at
+// a time ahead of the ordered adds.  The waves also prepare the activations of
+// the gate/up kernel (see kernels.hpp).
+template <int TT, int CH>
 __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x, int T, int d,
                                                      const float *__restrict__ W,
                                                      const float *__restrict__ bias, int E,
-                                                     float *__restrict__ z) {
+                                                     float *__restrict__ z,
+                                                     uint32_t *__restrict__ xp,
+                                                     float *__restrict__ xsw,
+                                                     float *__restrict__ xscale) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int t0 = blockIdx.y * TT;
   if (e >= E) return;
-  const float *w = W + (long long)e * d;
-  float p[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) p[tt] = 0.0f;
+  const float *w = W + (long long)e * d + lane;
   const int nt = min(TT, T - t0);
-  for (int i = lane; i < d; i += 64) {
-    const float wv = w[i];
+  const float *xr[TT];
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      if (tt < nt) {
-        const float prod = x[(long long)(t0 + tt) * d + i] * wv;
-        p[tt] = p[tt] + prod;
+  for (int tt = 0; tt < TT; ++tt) xr[tt] = x + (long long)(t0 + min(tt, nt - 1)) * d + lane;
+  float p[TT], mx[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    p[tt] = 0.0f;
+    mx[tt] = 0.0f;
+  }
+  const int M = d / 64;
+  for (int m0 = 0; m0 < M; m0 += CH) {
+    float wv[CH], xv[TT][CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int m = min(m0 + j, M - 1);
+      wv[j] = w[64 * m];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) xv[tt][j] = xr[tt][64 * m];
+    }
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      if (m0 + j < M) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          const float prod = xv[tt][j] * wv[j];
+          p[tt] = p[tt] + prod;
+          mx[tt] = fmaxf(mx[tt], fabsf(xv[tt][j]));
+        }
       }
     }
   }
@@ -57,18 +129,64 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
       if (tt < nt) z[(long long)(t0 + tt) * E + e] = bias ? p[tt] + bias[e] : p[tt];
     }
   }
+  if (xp == nullptr) return;
+  const int words = d / 8;
+  const int gid = e * 64 + lane, stride = E * 64;
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    if (tt >= nt) break;
+    float m = mx[tt];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    int ex2 = 0;
+    if (m > 0.0f && m <= 3.0e38f) {
+      int fe;
+      (void)frexpf(m, &fe);  // m = f * 2^fe, f in [0.5, 1)
+      ex2 = max(0, fe - 14);
+    }
+    const float sc = ldexpf(1.0f, -ex2);
+    const int t = t0 + tt;
+    if (gid == 0) xscale[t] = ldexpf(1.0f, ex2);
+    const float *xt = x + (long long)t * d;
+    for (int j = gid; j < words; j += stride) {
+      const int b = j >> 2, wq = j & 3;
+      const float4 a = *reinterpret_cast<const float4 *>(xt + b * 32 + 4 * wq);
+      const float4 c = *reinterpret_cast<const float4 *>(xt + b * 32 + 16 + 4 * wq);
+      const float e0 = a.x * sc, e1 = a.y * sc, e2 = a.z * sc, e3 = a.w * sc;
+      const float f0 = c.x * sc, f1 = c.y * sc, f2 = c.z * sc, f3 = c.w * sc;
+      const float he0 = (float)(_Float16)e0, he1 = (float)(_Float16)e1;
+      const float he2 = (float)(_Float16)e2, he3 = (float)(_Float16)e3;
+      const float hf0 = (float)(_Float16)f0, hf1 = (float)(_Float16)f1;
+      const float hf2 = (float)(_Float16)f2, hf3 = (float)(_Float16)f3;
+      uint4 hi, lo;
+      hi.x = pack_h2(he0, he2);
+      hi.y = pack_h2(hf0, hf2);
+      hi.z = pack_h2(he1, he3);
+      hi.w = pack_h2(hf1, hf3);
+      lo.x = pack_h2(e0 - he0, e2 - he2);
+      lo.y = pack_h2(f0 - hf0, f2 - hf2);
+      lo.z = pack_h2(e1 - he1, e3 - he3);
+      lo.w = pack_h2(f1 - hf1, f3 - hf3);
+      uint4 *dst = reinterpret_cast<uint4 *>(xp + ((long long)t * words + j) * 8);
+      dst[0] = hi;
+      dst[1] = lo;
+      xsw[(long long)t * words + j] = ((e0 + e1) + (e2 + e3)) + ((f0 + f1) + (f2 + f3));
+    }
+  }
 }
 
 hipError_t launch_router(const float *x, int T, int d, const float *W, const float *bias, int E,
-                         float *z, hipStream_t s) {
+                         float *z, uint32_t *xp, float *xsw, float *xscale, hipStream_t s) {
   const int gx = (E + 3) / 4;
   if (T <= 1) {
-    hipLaunchKernelGGL(router_kernel<1>, dim3(gx, T), dim3(256), 0, s, x, T, d, W, bias, E, z);
+    hipLaunchKernelGGL((router_kernel<1, 32>), dim3(gx, T), dim3(256), 0, s, x, T, d, W, bias, E,
+                       z, xp, xsw, xscale);
   } else if (T <= 4) {
-    hipLaunchKernelGGL(router_kernel<4>, dim3(gx, 1), dim3(256), 0, s, x, T, d, W, bias, E, z);
+    hipLaunchKernelGGL((router_kernel<4, 16>), dim3(gx, 1), dim3(256), 0, s, x, T, d, W, bias, E,
+                       z, xp, xsw, xscale);
   } else {
-    hipLaunchKernelGGL(router_kernel<8>, dim3(gx, (T + 7) / 8), dim3(256), 0, s, x, T, d, W, bias,
-                       E, z);
+    hipLaunchKernelGGL((router_kernel<8, 8>), dim3(gx, (T + 7) / 8), dim3(256), 0, s, x, T, d, W,
+                       bias, E, z, xp, xsw, xscale);
   }
   return hipGetLastError();
 }
@@ -77,12 +195,10 @@ hipError_t launch_router(const float *x, int T, int d, const float *W, const flo
 // One wave per token; E <= 512, so each lane owns up to 8 logits.
 __global__ __launch_bounds__(64) void topk_kernel(const float *__restrict__ z, int T, int E, int k,
                                                   int norm_topk, int32_t *__restrict__ idx,
-                                                  float *__restrict__ w,
-                                                  int32_t *__restrict__ pair_gpu) {
+                                                  float *__restrict__ w, int32_t *h_idx,
+                                                  float *h_w) {
   const int t = blockIdx.x;
   const int lane = threadIdx.x;
-  __shared__ int sel_e[64];
-  __shared__ float sel_v[64];
   float v[8];
   bool ok[8];
 #pragma unroll
@@ -91,6 +207,8 @@ __global__ __launch_bounds__(64) void topk_kernel(const float *__restrict__ z, i
     ok[c] = e < E;
     v[c] = ok[c] ? z[(long long)t * E + e] : 0.0f;
   }
+  int my_e = 0;
+  float my_v = 0.0f;
   for (int j = 0; j < k; ++j) {
     float bv = 0.0f;
     int be = E;  // sentinel: nothing yet
@@ -101,27 +219,19 @@ __global__ __launch_bounds__(64) void topk_kernel(const float *__restrict__ z, i
         be = lane + 64 * c;
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      if (oe != E && (be == E || ov > bv || (ov == bv && oe < be))) {
-        bv = ov;
-        be = oe;
-      }
-    }
+    wave_argmax(bv, be, E);
 #pragma unroll
     for (int c = 0; c < 8; ++c)
       if (lane + 64 * c == be) ok[c] = false;
-    if (lane == 0) {
-      sel_e[j] = be;
-      sel_v[j] = bv;
+    if (lane == j) {
+      my_e = be;
+      my_v = bv;
     }
   }
-  __syncthreads();
-  const float zmax = sel_v[0];
+  const float zmax =
+      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
   float ex = 0.0f;
-  if (lane < k) ex = expf(sel_v[lane] - zmax);
+  if (lane < k) ex = expf(my_v - zmax);
   float denom;
   if (norm_topk) {
     denom = ex;
@@ -134,16 +244,19 @@ __global__ __launch_bounds__(64) void topk_kernel(const float *__restrict__ z, i
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) denom += __shfl_xor(denom, off, 64);
   if (lane < k) {
-    idx[(long long)t * k + lane] = sel_e[lane];
-    w[(long long)t * k + lane] = ex / denom;
-    pair_gpu[(long long)t * k + lane] = 0;
+    const long long o = (long long)t * k + lane;
+    const float wv = ex / denom;
+    idx[o] = my_e;
+    w[o] = wv;
+    h_idx[o] = my_e;
+    h_w[o] = wv;
   }
 }
 
 hipError_t launch_topk(const float *z, int T, int E, int k, int norm_topk, int32_t *idx, float *w,
-                       int32_t *pair_gpu, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(64), 0, s, z, T, E, k, norm_topk, idx, w,
-                     pair_gpu);
+                       int32_t *h_idx, float *h_w, hipStream_t s) {
+  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(64), 0, s, z, T, E, k, norm_topk, idx, w, h_idx,
+                     h_w);
   return hipGetLastError();
 }
 
@@ -153,8 +266,7 @@ hipError_t launch_topk(const float *z, int T, int E, int k, int norm_topk, int32
 __global__ __launch_bounds__(256) void remap_kernel(const int32_t *__restrict__ idx, int T, int k,
                                                     SlotView view, int shared_slot, int n_ids,
                                                     int32_t *__restrict__ meta,
-                                                    int32_t *__restrict__ bucket_pair,
-                                                    int32_t *__restrict__ pair_gpu) {
+                                                    int32_t *__restrict__ bucket_pair) {
   __shared__ int cnt[kMetaB];
   __shared__ int base[kMetaB];
   __shared__ int run[kMetaB];
@@ -220,7 +332,6 @@ __global__ __launch_bounds__(256) void remap_kernel(const int32_t *__restrict__ 
       int rank = 0;
       for (int i = 0; i < tid; ++i) rank += (sl[i] == s) ? 1 : 0;
       bucket_pair[base[s] + run[s] + rank] = p;
-      if (p < P_routed) pair_gpu[p] = 1;
     }
     __syncthreads();
     if (s >= 0) atomicAdd(&run[s], 1);
@@ -229,25 +340,155 @@ __global__ __launch_bounds__(256) void remap_kernel(const int32_t *__restrict__ 
 }
 
 hipError_t launch_remap(const int32_t *idx, int T, int k, const SlotView &view, int shared_slot,
-                        int n_slot_ids, int32_t *meta, int32_t *bucket_pair, int32_t *pair_gpu,
-                        hipStream_t s) {
+                        int n_slot_ids, int32_t *meta, int32_t *bucket_pair, hipStream_t s) {
   hipLaunchKernelGGL(remap_kernel, dim3(1), dim3(256), 0, s, idx, T, k, view, shared_slot,
-                     n_slot_ids, meta, bucket_pair, pair_gpu);
+                     n_slot_ids, meta, bucket_pair);
   return hipGetLastError();
+}
+
+// ============================================================== bucket lookup
+// The (slot, pairs) of bucket b.  With remap metadata it is a table read; on the
+// decode path each wave derives it from the router ids: lane p takes pair p's
+// slot, a pair opens a bucket when no lower pair has its slot, bucket b is the
+// b-th opener, and its pairs are the lanes with the same slot, ascending.
+template <int TT>
+struct Bucket {
+  int slot, off, cnt;
+  int pairs[TT];  // decode path: the bucket's pairs (cnt <= TT)
+  const uint8_t *src;
+  uint8_t *dst;
+};
+
+// Modes of a launch: buckets from remap metadata, derived on the device
+// (decode), or given by the host in a BucketTable.
+enum { BK_META = 0, BK_DEVICE = 1, BK_TABLE = 2 };
+
+template <int TT, int MODE>
+__device__ __forceinline__ bool find_bucket(const GemvArgs &a, const SlotView &view,
+                                            const BucketTable &tab, int b, int *sl,
+                                            Bucket<TT> &bk) {
+  bk.dst = nullptr;
+  if constexpr (MODE == BK_TABLE) {
+    if (b >= tab.n) return false;
+    bk.src = tab.src[b];
+    bk.dst = tab.dst[b];
+    bk.cnt = tab.cnt[b];
+    bk.off = 0;
+    bk.slot = 0;
+#pragma unroll
+    for (int i = 0; i < TT; ++i) bk.pairs[i] = tab.pairs[b][i < kDecodeMaxTokens ? i : 0];
+    return true;
+  }
+  if constexpr (MODE == BK_META) {
+    if (b >= a.meta[0]) return false;
+    bk.slot = a.meta[2 + b];
+    bk.off = a.meta[2 + kMetaB + b];
+    bk.cnt = a.meta[2 + 2 * kMetaB + b];
+    bk.src = a.slots + (long long)bk.slot * a.rec_bytes;
+    return true;
+  }
+  const int lane = threadIdx.x & 63;
+  const int Pr = a.T * a.k;
+  const int P = Pr + (a.shared_slot >= 0 ? a.T : 0);
+  int s = -1;
+  if (lane < P) s = lane < Pr ? (int)view.slot[a.idx[lane]] : a.shared_slot;
+  sl[lane] = s;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0);
+  bool first = s >= 0;
+  for (int q = 0; q < lane; ++q)
+    if (sl[q] == s) first = false;
+  uint64_t openers = __ballot(first);
+  if (__popcll(openers) <= b) return false;
+  for (int i = 0; i < b; ++i) openers &= openers - 1;
+  const int L = __ffsll((unsigned long long)openers) - 1;
+  bk.slot = __builtin_amdgcn_readlane(s, L);
+  bk.src = a.slots + (long long)bk.slot * a.rec_bytes;
+  uint64_t same = __ballot(s == bk.slot);
+  bk.cnt = __popcll(same);
+  bk.off = 0;
+  int last = 0;
+#pragma unroll
+  for (int i = 0; i < TT; ++i) {
+    if (same) {
+      last = __ffsll((unsigned long long)same) - 1;
+      same &= same - 1;
+    }
+    bk.pairs[i] = last;
+  }
+  return true;
+}
+
+template <int TT, int MODE>
+__device__ __forceinline__ int bucket_pair_at(const GemvArgs &a, const Bucket<TT> &bk, int i) {
+  if constexpr (MODE == BK_META) return a.bucket_pair[bk.off + i];
+  return bk.pairs[i < TT ? i : TT - 1];
+}
+
+template <int V>
+__device__ __forceinline__ void store_words(uint32_t *p, const uint32_t (&q)[V]) {
+  if constexpr (V == 4) {
+    *reinterpret_cast<uint4 *>(p) = make_uint4(q[0], q[1], q[2], q[3]);
+  } else {
+    *reinterpret_cast<uint2 *>(p) = make_uint2(q[0], q[1]);
+  }
 }
 
 // ============================================================== Q4 grouped GEMV
 // Workgroup = 4 waves, one slot bucket (blockIdx.y) and a tile of rows
 // (blockIdx.x).  In a wave, G lanes share a row and RG = 64/G rows run side by
-// side; each lane walks the row's units u = lane%G, +G, ... where a unit is V
-// consecutive 32-bit nibble words (V = 4: a whole block, V = 2: half a block);
-// R rows per lane reuse the unit's activations from registers.  The -8 offset
-// is folded in as d * (sum q x - 8 sum x).  Partial sums meet across the G
-// lanes with xor shuffles.
-__device__ __forceinline__ float word_dot(uint32_t q, const float4 &xl, const float4 &xh) {
-  const uint32_t lo = q & 0x0F0F0F0Fu;
-  const uint32_t hi = (q >> 4) & 0x0F0F0F0Fu;
-  float acc = (float)(lo & 0xFFu) * xl.x;
+// side; a lane walks its row's units (V consecutive 32-bit nibble words: V = 4 a
+// whole block, V = 2 half a block) and R rows per lane reuse the unit's
+// activations from registers.  The -8 offset of the weights is folded in per
+// unit; partial sums meet across the G lanes with xor shuffles.
+//
+// gate/up (GLU): the K dimension is split over the 4 waves of the workgroup,
+// whose partials meet in LDS in a fixed order.  A nibble word q holds the
+// elements (0,2),(16,18),(1,3),(17,19) of its 4-element group as the low/high
+// nibbles of bytes (0,2) and (1,3); OR-ing each nibble pair into 0x6400 gives two
+// binary16 values 1024 + q, so one v_dot2 against the prepared hi and lo
+// activation pairs accumulates (1024 + q) x in fp32, and 1032 * sum(x) per unit
+// brings it back to (q - 8) x.
+//
+// down: whole K per wave; nibbles become floats with v_cvt_f32_ubyte0..3.
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
+
+// sum over one word of (1024 + q) * x, x given as hi and lo binary16 pairs
+__device__ __forceinline__ float word_dot_h(uint32_t q, const uint4 &xh, const uint4 &xl,
+                                            float acc) {
+  const uint32_t m = 0x000F000Fu, mag = 0x64006400u;
+  const uint32_t a = and_or(q, m, mag);
+  const uint32_t b = and_or(q >> 4, m, mag);
+  const uint32_t c = and_or(q >> 8, m, mag);
+  const uint32_t d = and_or(q >> 12, m, mag);
+  acc = __builtin_amdgcn_fdot2(as_h2(a), as_h2(xh.x), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(b), as_h2(xh.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(c), as_h2(xh.z), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(d), as_h2(xh.w), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(a), as_h2(xl.x), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(b), as_h2(xl.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(c), as_h2(xl.z), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(d), as_h2(xl.w), acc, false);
+  return acc;
+}
+
+// sum over one word of q * x in fp32 (x: elements 0..3 and 16..19 of the group)
+__device__ __forceinline__ float word_dot_f(uint32_t q, const float4 &xl, const float4 &xh,
+                                            float acc) {
+  uint32_t lo = q & 0x0F0F0F0Fu;
+  uint32_t hi = (q >> 4) & 0x0F0F0F0Fu;
+  // hide the known-zero high nibbles so each byte converts with one v_cvt_f32_ubyteN
+  asm volatile("" : "+v"(lo), "+v"(hi));
+  acc += (float)(lo & 0xFFu) * xl.x;
   acc += (float)((lo >> 8) & 0xFFu) * xl.y;
   acc += (float)((lo >> 16) & 0xFFu) * xl.z;
   acc += (float)(lo >> 24) * xl.w;
@@ -275,46 +516,189 @@ __device__ __forceinline__ void load_words(const uint32_t *p, uint32_t (&q)[V]) 
 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + expf(-v)); }
 
-template <int G, int V, int TT, int R, bool GLU>
-__global__ __launch_bounds__(256) void q4_gemv_kernel(GemvArgs a) {
+__device__ __forceinline__ int pair_row(const GemvArgs &a, int p) {
+  return p < a.T * a.k ? p / a.k : p - a.T * a.k;
+}
+
+template <int G, int V, int TT, int R, int MODE>
+__global__ __launch_bounds__(256) void q4_gateup_kernel(GemvArgs a, SlotView view,
+                                                        BucketTable tab) {
+  constexpr int RG = 64 / G;
+  constexpr int KS = 4;
+  __shared__ float red[KS][R * RG][TT][2];
+  __shared__ int sl[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  Bucket<TT> bk;
+  if (!find_bucket<TT, MODE>(a, view, tab, blockIdx.y, sl[wave], bk)) return;
+  const uint8_t *rec = bk.src;
+  uint8_t *wr = bk.dst;
+  const int grp = lane / G, gl = lane % G;
+  const int row0 = blockIdx.x * (R * RG) + grp;
+  const int row_words = a.nb * 4;
+  const int units = row_words / V;
+  const int words_x = a.nb * 4;  // words per activation row
+  // rows past the end read the last row and are never written
+  const uint32_t *qg[R];
+  const uint32_t *qu[R];
+  const __half *sg[R];
+  const __half *su[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const long long r = min(row0 + i * RG, a.rows - 1);
+    qg[i] = reinterpret_cast<const uint32_t *>(rec + a.off_q0) + r * row_words;
+    qu[i] = reinterpret_cast<const uint32_t *>(rec + a.off_q1) + r * row_words;
+    sg[i] = reinterpret_cast<const __half *>(rec + a.off_s0) + r * a.nb;
+    su[i] = reinterpret_cast<const __half *>(rec + a.off_s1) + r * a.nb;
+  }
+
+  for (int tg = 0; tg < bk.cnt; tg += TT) {
+    const int nt = min(TT, bk.cnt - tg);
+    int prs[TT], tok[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      prs[tt] = bucket_pair_at<TT, MODE>(a, bk, tg + min(tt, nt - 1));
+      tok[tt] = pair_row(a, prs[tt]);
+    }
+    float ag[R][TT], au[R][TT];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        ag[i][tt] = 0.0f;
+        au[i][tt] = 0.0f;
+      }
+    for (int u = gl + G * wave; u < units; u += G * KS) {
+      const int w0 = u * V;
+      const int blk = w0 >> 2;
+      uint4 xh[TT][V], xl[TT][V];
+      float xs[TT];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const uint4 *xq =
+            reinterpret_cast<const uint4 *>(a.xp + ((long long)tok[tt] * words_x + w0) * 8);
+        const float *xw = a.xsw + (long long)tok[tt] * words_x + w0;
+        xs[tt] = 0.0f;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          xh[tt][v] = xq[2 * v];
+          xl[tt][v] = xq[2 * v + 1];
+          xs[tt] += xw[v];
+        }
+      }
+      uint32_t q0[R][V], q1[R][V];
+      float s0[R], s1[R];
+      __half hs0[R], hs1[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        load_words<V>(qg[i] + w0, q0[i]);
+        load_words<V>(qu[i] + w0, q1[i]);
+        hs0[i] = sg[i][blk];
+        hs1[i] = su[i][blk];
+        s0[i] = __half2float(hs0[i]);
+        s1[i] = __half2float(hs1[i]);
+      }
+      if (MODE == BK_TABLE && wr != nullptr && tg == 0) {
+        // stream the expert into its slot: same offsets as the reads
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          store_words<V>(reinterpret_cast<uint32_t *>(wr + ((const uint8_t *)(qg[i] + w0) - rec)),
+                         q0[i]);
+          store_words<V>(reinterpret_cast<uint32_t *>(wr + ((const uint8_t *)(qu[i] + w0) - rec)),
+                         q1[i]);
+          *reinterpret_cast<__half *>(wr + ((const uint8_t *)(sg[i] + blk) - rec)) = hs0[i];
+          *reinterpret_cast<__half *>(wr + ((const uint8_t *)(su[i] + blk) - rec)) = hs1[i];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          float d0 = -1032.0f * xs[tt], d1 = -1032.0f * xs[tt];
+#pragma unroll
+          for (int v = 0; v < V; ++v) {
+            d0 = word_dot_h(q0[i][v], xh[tt][v], xl[tt][v], d0);
+            d1 = word_dot_h(q1[i][v], xh[tt][v], xl[tt][v], d1);
+          }
+          ag[i][tt] += s0[i] * d0;
+          au[i][tt] += s1[i] * d1;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+#pragma unroll
+        for (int o = G / 2; o >= 1; o >>= 1) {
+          ag[i][tt] += __shfl_xor(ag[i][tt], o, 64);
+          au[i][tt] += __shfl_xor(au[i][tt], o, 64);
+        }
+      }
+    if (gl == 0) {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          red[wave][i * RG + grp][tt][0] = ag[i][tt];
+          red[wave][i * RG + grp][tt][1] = au[i][tt];
+        }
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < R * RG * TT; o += 256) {
+      const int rr = o / TT, tt = o % TT;
+      const int r = blockIdx.x * (R * RG) + rr;
+      if (r < a.rows && tt < nt) {
+        const float sc = a.xscale[tok[tt]];
+        const float g = (((red[0][rr][tt][0] + red[1][rr][tt][0]) + red[2][rr][tt][0]) +
+                         red[3][rr][tt][0]) * sc;
+        const float uu = (((red[0][rr][tt][1] + red[1][rr][tt][1]) + red[2][rr][tt][1]) +
+                          red[3][rr][tt][1]) * sc;
+        a.out[(long long)prs[tt] * a.rows + r] = silu_f(g) * uu;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int G, int V, int TT, int R, int MODE>
+__global__ __launch_bounds__(256) void q4_down_kernel(GemvArgs a, SlotView view, BucketTable tab) {
   constexpr int RG = 64 / G;
   constexpr int ROWS_WAVE = R * RG;
+  __shared__ int sl[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int bucket = blockIdx.y;
-  if (bucket >= a.meta[0]) return;
-  const int slot = a.meta[2 + bucket];
-  const int off = a.meta[2 + kMetaB + bucket];
-  const int cnt = a.meta[2 + 2 * kMetaB + bucket];
-  const uint8_t *rec = a.slots + (long long)slot * a.rec_bytes;
+  Bucket<TT> bk;
+  if (!find_bucket<TT, MODE>(a, view, tab, blockIdx.y, sl[wave], bk)) return;
+  const uint8_t *rec = bk.src;
+  uint8_t *wr = bk.dst;
   const int grp = lane / G, gl = lane % G;
   const int row0 = (blockIdx.x * 4 + wave) * ROWS_WAVE + grp;
   const int row_words = a.nb * 4;
   const int units = row_words / V;
   const int K = a.nb * 32;
-  const uint32_t *q0b = reinterpret_cast<const uint32_t *>(rec + a.off_q0);
-  const __half *s0b = reinterpret_cast<const __half *>(rec + a.off_s0);
-  const uint32_t *q1b = reinterpret_cast<const uint32_t *>(rec + a.off_q1);
-  const __half *s1b = reinterpret_cast<const __half *>(rec + a.off_s1);
+  const uint32_t *qr[R];
+  const __half *sr[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const long long r = min(row0 + i * RG, a.rows - 1);
+    qr[i] = reinterpret_cast<const uint32_t *>(rec + a.off_q0) + r * row_words;
+    sr[i] = reinterpret_cast<const __half *>(rec + a.off_s0) + r * a.nb;
+  }
 
-  for (int tg = 0; tg < cnt; tg += TT) {
-    const int nt = min(TT, cnt - tg);
+  for (int tg = 0; tg < bk.cnt; tg += TT) {
+    const int nt = min(TT, bk.cnt - tg);
     const float *xin[TT];
     int prs[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-      const int p = a.bucket_pair[off + tg + min(tt, nt - 1)];
+      const int p = bucket_pair_at<TT, MODE>(a, bk, tg + min(tt, nt - 1));
       prs[tt] = p;
-      const int r = a.in_by_pair ? p : (p < a.T * a.k ? p / a.k : p - a.T * a.k);
-      xin[tt] = a.in + (long long)r * K;
+      xin[tt] = a.in + (long long)(a.in_by_pair ? p : pair_row(a, p)) * K;
     }
-    float acc0[R][TT], acc1[R][TT];
+    float acc[R][TT];
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        acc0[i][tt] = 0.0f;
-        acc1[i][tt] = 0.0f;
-      }
+      for (int tt = 0; tt < TT; ++tt) acc[i][tt] = 0.0f;
     for (int u = gl; u < units; u += G) {
       const int w0 = u * V;
       const int blk = w0 >> 2;
@@ -326,39 +710,38 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvArgs a) {
 #pragma unroll
         for (int v = 0; v < V; ++v) {
           const int wb = (w0 + v) & 3;
-          const float *xp = xin[tt] + blk * 32 + 4 * wb;
-          xl[tt][v] = *reinterpret_cast<const float4 *>(xp);
-          xh[tt][v] = *reinterpret_cast<const float4 *>(xp + 16);
-          xs[tt] += (xl[tt][v].x + xl[tt][v].y) + (xl[tt][v].z + xl[tt][v].w) +
-                    (xh[tt][v].x + xh[tt][v].y) + (xh[tt][v].z + xh[tt][v].w);
+          const float *xq = xin[tt] + blk * 32 + 4 * wb;
+          xl[tt][v] = *reinterpret_cast<const float4 *>(xq);
+          xh[tt][v] = *reinterpret_cast<const float4 *>(xq + 16);
+          xs[tt] += ((xl[tt][v].x + xl[tt][v].y) + (xl[tt][v].z + xl[tt][v].w)) +
+                    ((xh[tt][v].x + xh[tt][v].y) + (xh[tt][v].z + xh[tt][v].w));
+        }
+      }
+      uint32_t q0[R][V];
+      float sc0[R];
+      __half hs[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        load_words<V>(qr[i] + w0, q0[i]);
+        hs[i] = sr[i][blk];
+        sc0[i] = __half2float(hs[i]);
+      }
+      if (MODE == BK_TABLE && wr != nullptr && tg == 0) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          store_words<V>(reinterpret_cast<uint32_t *>(wr + ((const uint8_t *)(qr[i] + w0) - rec)),
+                         q0[i]);
+          *reinterpret_cast<__half *>(wr + ((const uint8_t *)(sr[i] + blk) - rec)) = hs[i];
         }
       }
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const int r = row0 + i * RG;
-        if (r < a.rows) {
-          uint32_t q0[V];
-          load_words<V>(q0b + (long long)r * row_words + w0, q0);
-          const float sc0 = __half2float(s0b[(long long)r * a.nb + blk]);
-          uint32_t q1[V];
-          float sc1 = 0.0f;
-          if constexpr (GLU) {
-            load_words<V>(q1b + (long long)r * row_words + w0, q1);
-            sc1 = __half2float(s1b[(long long)r * a.nb + blk]);
-          }
 #pragma unroll
-          for (int tt = 0; tt < TT; ++tt) {
-            float d0 = 0.0f;
+        for (int tt = 0; tt < TT; ++tt) {
+          float d0 = -8.0f * xs[tt];
 #pragma unroll
-            for (int v = 0; v < V; ++v) d0 += word_dot(q0[v], xl[tt][v], xh[tt][v]);
-            acc0[i][tt] += sc0 * (d0 - 8.0f * xs[tt]);
-            if constexpr (GLU) {
-              float d1 = 0.0f;
-#pragma unroll
-              for (int v = 0; v < V; ++v) d1 += word_dot(q1[v], xl[tt][v], xh[tt][v]);
-              acc1[i][tt] += sc1 * (d1 - 8.0f * xs[tt]);
-            }
-          }
+          for (int v = 0; v < V; ++v) d0 = word_dot_f(q0[i][v], xl[tt][v], xh[tt][v], d0);
+          acc[i][tt] += sc0[i] * d0;
         }
       }
     }
@@ -367,10 +750,7 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvArgs a) {
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
 #pragma unroll
-        for (int o = G / 2; o >= 1; o >>= 1) {
-          acc0[i][tt] += __shfl_xor(acc0[i][tt], o, 64);
-          if constexpr (GLU) acc1[i][tt] += __shfl_xor(acc1[i][tt], o, 64);
-        }
+        for (int o = G / 2; o >= 1; o >>= 1) acc[i][tt] += __shfl_xor(acc[i][tt], o, 64);
       }
     if (gl == 0) {
 #pragma unroll
@@ -378,19 +758,16 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvArgs a) {
         const int r = row0 + i * RG;
         if (r < a.rows) {
 #pragma unroll
-          for (int tt = 0; tt < TT; ++tt) {
-            if (tt < nt) {
-              const float val = GLU ? silu_f(acc0[i][tt]) * acc1[i][tt] : acc0[i][tt];
-              a.out[(long long)prs[tt] * a.rows + r] = val;
-            }
-          }
+          for (int tt = 0; tt < TT; ++tt)
+            if (tt < nt) a.out[(long long)prs[tt] * a.rows + r] = acc[i][tt];
         }
       }
     }
   }
 }
 
-GemvShape choose_gemv(int rows, int nb, int n_buckets, int max_tokens) {
+GemvShape choose_gemv(bool glu, int rows, int nb, int n_buckets, int max_tokens) {
+  const int KS = glu ? 4 : 1;
   GemvShape best{64, 4, 1, 1};
   double best_eff = -1.0;
   const int gs[3] = {64, 32, 16};
@@ -399,8 +776,9 @@ GemvShape choose_gemv(int rows, int nb, int n_buckets, int max_tokens) {
     for (int gi = 0; gi < 3; ++gi) {
       const int V = vs[vi], G = gs[gi];
       const int units = nb * 4 / V;
-      const int ni = (units + G - 1) / G;
-      const double eff = (double)units / (double)(G * ni) + 1e-3 * V + 1e-5 * G;
+      const int span = G * KS;
+      const int ni = (units + span - 1) / span;
+      const double eff = (double)units / (double)(span * ni) + 1e-3 * V + 1e-5 * G;
       if (eff > best_eff) {
         best_eff = eff;
         best.G = G;
@@ -409,12 +787,14 @@ GemvShape choose_gemv(int rows, int nb, int n_buckets, int max_tokens) {
     }
   best.TT = max_tokens <= 1 ? 1 : (max_tokens <= 2 ? 2 : 4);
   const int RG = 64 / best.G;
+  const int rows_wg_per_r = glu ? RG : 4 * RG;
   best.R = 1;
   const int rs[2] = {4, 2};
   for (int ri = 0; ri < 2; ++ri) {
     const int R = rs[ri];
-    const long long waves = (long long)n_buckets * ((rows + R * RG - 1) / (R * RG));
-    if (waves >= 4096) {
+    const long long waves =
+        4LL * n_buckets * ((rows + R * rows_wg_per_r - 1) / (R * rows_wg_per_r));
+    if (waves >= 2048) {
       best.R = R;
       break;
     }
@@ -422,57 +802,111 @@ GemvShape choose_gemv(int rows, int nb, int n_buckets, int max_tokens) {
   return best;
 }
 
-template <int G, int V, int TT, int R, bool GLU>
-static hipError_t launch_one(const GemvArgs &a, int n_buckets, hipStream_t s) {
-  constexpr int rows_blk = 4 * R * (64 / G);
-  const dim3 grid((a.rows + rows_blk - 1) / rows_blk, n_buckets);
-  hipLaunchKernelGGL((q4_gemv_kernel<G, V, TT, R, GLU>), grid, dim3(256), 0, s, a);
+struct LaunchCtx {
+  const GemvArgs *a;
+  const SlotView *view;
+  const BucketTable *tab;
+  bool glu;
+  int nbk;
+  hipStream_t s;
+};
+
+template <int G, int V, int TT, int R, int MODE>
+static hipError_t launch_one(const LaunchCtx &c) {
+  constexpr int RG = 64 / G;
+  const GemvArgs &a = *c.a;
+  if (c.glu) {
+    const dim3 grid((a.rows + R * RG - 1) / (R * RG), c.nbk);
+    hipLaunchKernelGGL((q4_gateup_kernel<G, V, TT, R, MODE>), grid, dim3(256), 0, c.s, a, *c.view,
+                       *c.tab);
+  } else {
+    constexpr int rows_blk = 4 * R * RG;
+    const dim3 grid((a.rows + rows_blk - 1) / rows_blk, c.nbk);
+    hipLaunchKernelGGL((q4_down_kernel<G, V, TT, R, MODE>), grid, dim3(256), 0, c.s, a, *c.view,
+                       *c.tab);
+  }
   return hipGetLastError();
 }
 
-template <int G, int V, int TT, bool GLU>
-static hipError_t launch_r(const GemvArgs &a, int R, int nbk, hipStream_t s) {
+template <int G, int V, int TT, int R>
+static hipError_t launch_m(const LaunchCtx &c) {
+  if (c.tab->n >= 0) return launch_one<G, V, TT, R, BK_TABLE>(c);
+  if (c.a->meta != nullptr) return launch_one<G, V, TT, R, BK_META>(c);
+  return launch_one<G, V, TT, R, BK_DEVICE>(c);
+}
+
+template <int G, int V, int TT>
+static hipError_t launch_r(const LaunchCtx &c, int R) {
   switch (R) {
-    case 4: return launch_one<G, V, TT, 4, GLU>(a, nbk, s);
-    case 2: return launch_one<G, V, TT, 2, GLU>(a, nbk, s);
-    default: return launch_one<G, V, TT, 1, GLU>(a, nbk, s);
+    case 4: return launch_m<G, V, TT, 4>(c);
+    case 2: return launch_m<G, V, TT, 2>(c);
+    default: return launch_m<G, V, TT, 1>(c);
   }
 }
 
-template <int G, int V, bool GLU>
-static hipError_t launch_t(const GemvArgs &a, const GemvShape &sh, int nbk, hipStream_t s) {
+template <int G, int V>
+static hipError_t launch_t(const LaunchCtx &c, const GemvShape &sh) {
   switch (sh.TT) {
-    case 1: return launch_r<G, V, 1, GLU>(a, sh.R, nbk, s);
-    case 2: return launch_r<G, V, 2, GLU>(a, sh.R, nbk, s);
-    default: return launch_r<G, V, 4, GLU>(a, sh.R, nbk, s);
+    case 1: return launch_r<G, V, 1>(c, sh.R);
+    case 2: return launch_r<G, V, 2>(c, sh.R);
+    default: return launch_r<G, V, 4>(c, sh.R);
   }
 }
 
-template <int G, bool GLU>
-static hipError_t launch_v(const GemvArgs &a, const GemvShape &sh, int nbk, hipStream_t s) {
-  return sh.V == 4 ? launch_t<G, 4, GLU>(a, sh, nbk, s) : launch_t<G, 2, GLU>(a, sh, nbk, s);
+template <int G>
+static hipError_t launch_v(const LaunchCtx &c, const GemvShape &sh) {
+  return sh.V == 4 ? launch_t<G, 4>(c, sh) : launch_t<G, 2>(c, sh);
 }
 
-template <bool GLU>
-static hipError_t launch_g(const GemvArgs &a, const GemvShape &sh, int nbk, hipStream_t s) {
-  switch (sh.G) {
-    case 64: return launch_v<64, GLU>(a, sh, nbk, s);
-    case 32: return launch_v<32, GLU>(a, sh, nbk, s);
-    default: return launch_v<16, GLU>(a, sh, nbk, s);
-  }
-}
-
-hipError_t launch_gemv(const GemvArgs &a, const GemvShape &sh, bool glu, int n_buckets,
-                       hipStream_t s) {
+hipError_t launch_gemv(const GemvArgs &a, const SlotView &view, const BucketTable *tab,
+                       const GemvShape &sh, bool glu, int n_buckets, hipStream_t s) {
   if (n_buckets <= 0) return hipSuccess;
-  return glu ? launch_g<true>(a, sh, n_buckets, s) : launch_g<false>(a, sh, n_buckets, s);
+  BucketTable none;
+  none.n = -1;
+  const LaunchCtx c{&a, &view, tab ? tab : &none, glu, n_buckets, s};
+  switch (sh.G) {
+    case 64: return launch_v<64>(c, sh);
+    case 32: return launch_v<32>(c, sh);
+    default: return launch_v<16>(c, sh);
+  }
+}
+
+// ============================================================== slot fills
+__global__ __launch_bounds__(256) void pull_kernel(PullList l) {
+  const int e = blockIdx.x / l.per_expert, part = blockIdx.x % l.per_expert;
+  if (e >= l.n) return;
+  const long long per = (l.bytes16 + l.per_expert - 1) / l.per_expert;
+  const long long b = part * per, end = min(b + per, l.bytes16);
+  const uint4 *__restrict__ src = reinterpret_cast<const uint4 *>(l.src[e]);
+  uint4 *__restrict__ dst = reinterpret_cast<uint4 *>(l.dst[e]);
+  constexpr int U = 8;
+  for (long long i = b + threadIdx.x; i < end; i += 256 * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long long j = i + (long long)u * 256;
+      if (j < end) v[u] = src[j];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long long j = i + (long long)u * 256;
+      if (j < end) dst[j] = v[u];
+    }
+  }
+}
+
+hipError_t launch_pull(const PullList &l, hipStream_t s) {
+  if (l.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(pull_kernel, dim3(l.n * l.per_expert), dim3(256), 0, s, l);
+  return hipGetLastError();
 }
 
 // ============================================================== combine
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y,
                                                       const float *__restrict__ w,
-                                                      const int32_t *__restrict__ pair_gpu, int T,
-                                                      int k, int d, int n_shared,
+                                                      const int32_t *__restrict__ idx,
+                                                      SlotView view, int all_gpu, int T, int k,
+                                                      int d, int n_shared,
                                                       const float *__restrict__ host_part,
                                                       float *__restrict__ out,
                                                       float *__restrict__ dbg_gpu) {
@@ -482,7 +916,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j < k; ++j) {
     const long long p = (long long)t * k + j;
-    if (pair_gpu[p]) {
+    if (all_gpu || view.slot[idx[p]] >= 0) {
       const float wv = w[p];
       const float4 yv = *reinterpret_cast<const float4 *>(y + p * d + i);
       acc.x += wv * yv.x;
@@ -509,12 +943,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   *reinterpret_cast<float4 *>(out + (long long)t * d + i) = acc;
 }
 
-hipError_t launch_combine(const float *y, const float *w, const int32_t *pair_gpu, int T, int k,
-                          int d, int n_shared, const float *host_part, float *out,
-                          float *dbg_gpu, hipStream_t s) {
+hipError_t launch_combine(const float *y, const float *w, const int32_t *idx,
+                          const SlotView &view, int all_gpu, int T, int k, int d, int n_shared,
+                          const float *host_part, float *out, float *dbg_gpu, hipStream_t s) {
   const dim3 grid((d / 4 + 255) / 256, T);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, y, w, pair_gpu, T, k, d, n_shared,
-                     host_part, out, dbg_gpu);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, y, w, idx, view, all_gpu, T, k, d,
+                     n_shared, host_part, out, dbg_gpu);
   return hipGetLastError();
 }
 
