@@ -448,7 +448,6 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
           pl.src[b] = c->host_record(layer, fl.expert);
           pl.dst[b] = c->dev_slot(layer, fl.slot);
           tab.src[b] = c->dev_slot(layer, fl.slot);
-          tab.dst[b] = nullptr;
           int cnt = 0;
           for (int32_t p = 0; p < T * k; ++p)
             if (hidx[p] == fl.expert) tab.pairs[b][cnt++] = (uint8_t)p;

@@ -356,7 +356,6 @@ struct Bucket {
   int slot, off, cnt;
   int pairs[TT];  // decode path: the bucket's pairs (cnt <= TT)
   const uint8_t *src;
-  uint8_t *dst;
 };
 
 // Modes of a launch: buckets from remap metadata, derived on the device
@@ -367,11 +366,9 @@ template <int TT, int MODE>
 __device__ __forceinline__ bool find_bucket(const GemvArgs &a, const SlotView &view,
                                             const BucketTable &tab, int b, int *sl,
                                             Bucket<TT> &bk) {
-  bk.dst = nullptr;
   if constexpr (MODE == BK_TABLE) {
     if (b >= tab.n) return false;
     bk.src = tab.src[b];
-    bk.dst = tab.dst[b];
     bk.cnt = tab.cnt[b];
     bk.off = 0;
     bk.slot = 0;
@@ -425,14 +422,7 @@ __device__ __forceinline__ int bucket_pair_at(const GemvArgs &a, const Bucket<TT
   return bk.pairs[i < TT ? i : TT - 1];
 }
 
-template <int V>
-__device__ __forceinline__ void store_words(uint32_t *p, const uint32_t (&q)[V]) {
-  if constexpr (V == 4) {
-    *reinterpret_cast<uint4 *>(p) = make_uint4(q[0], q[1], q[2], q[3]);
-  } else {
-    *reinterpret_cast<uint2 *>(p) = make_uint2(q[0], q[1]);
-  }
-}
+
 
 // ============================================================== Q4 grouped GEMV
 // Workgroup = 4 waves, one slot bucket (blockIdx.y) and a tile of rows
@@ -521,8 +511,8 @@ __device__ __forceinline__ int pair_row(const GemvArgs &a, int p) {
 }
 
 template <int G, int V, int TT, int R, int MODE>
-__global__ __launch_bounds__(256) void q4_gateup_kernel(GemvArgs a, SlotView view,
-                                                        BucketTable tab) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void q4_gateup_kernel(GemvArgs a, SlotView view, BucketTable tab) {
   constexpr int RG = 64 / G;
   constexpr int KS = 4;
   __shared__ float red[KS][R * RG][TT][2];
@@ -531,7 +521,6 @@ __global__ __launch_bounds__(256) void q4_gateup_kernel(GemvArgs a, SlotView vie
   Bucket<TT> bk;
   if (!find_bucket<TT, MODE>(a, view, tab, blockIdx.y, sl[wave], bk)) return;
   const uint8_t *rec = bk.src;
-  uint8_t *wr = bk.dst;
   const int grp = lane / G, gl = lane % G;
   const int row0 = blockIdx.x * (R * RG) + grp;
   const int row_words = a.nb * 4;
@@ -587,27 +576,12 @@ __global__ __launch_bounds__(256) void q4_gateup_kernel(GemvArgs a, SlotView vie
       }
       uint32_t q0[R][V], q1[R][V];
       float s0[R], s1[R];
-      __half hs0[R], hs1[R];
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         load_words<V>(qg[i] + w0, q0[i]);
         load_words<V>(qu[i] + w0, q1[i]);
-        hs0[i] = sg[i][blk];
-        hs1[i] = su[i][blk];
-        s0[i] = __half2float(hs0[i]);
-        s1[i] = __half2float(hs1[i]);
-      }
-      if (MODE == BK_TABLE && wr != nullptr && tg == 0) {
-        // stream the expert into its slot: same offsets as the reads
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-          store_words<V>(reinterpret_cast<uint32_t *>(wr + ((const uint8_t *)(qg[i] + w0) - rec)),
-                         q0[i]);
-          store_words<V>(reinterpret_cast<uint32_t *>(wr + ((const uint8_t *)(qu[i] + w0) - rec)),
-                         q1[i]);
-          *reinterpret_cast<__half *>(wr + ((const uint8_t *)(sg[i] + blk) - rec)) = hs0[i];
-          *reinterpret_cast<__half *>(wr + ((const uint8_t *)(su[i] + blk) - rec)) = hs1[i];
-        }
+        s0[i] = __half2float(sg[i][blk]);
+        s1[i] = __half2float(su[i][blk]);
       }
 #pragma unroll
       for (int i = 0; i < R; ++i) {
@@ -660,18 +634,21 @@ __global__ __launch_bounds__(256) void q4_gateup_kernel(GemvArgs a, SlotView vie
   }
 }
 
-template <int G, int V, int TT, int R, int MODE>
-__global__ __launch_bounds__(256) void q4_down_kernel(GemvArgs a, SlotView view, BucketTable tab) {
+template <int G, int V, int TT, int R, int MODE, int KS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void q4_down_kernel(GemvArgs a, SlotView view, BucketTable tab) {
   constexpr int RG = 64 / G;
   constexpr int ROWS_WAVE = R * RG;
+  constexpr int NRG = 4 / KS;  // row groups per workgroup; KS waves share a row group's K
   __shared__ int sl[4][64];
+  __shared__ float red[KS > 1 ? 4 : 1][ROWS_WAVE][TT];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kslice = wave % KS, rgrp = wave / KS;
   Bucket<TT> bk;
   if (!find_bucket<TT, MODE>(a, view, tab, blockIdx.y, sl[wave], bk)) return;
   const uint8_t *rec = bk.src;
-  uint8_t *wr = bk.dst;
   const int grp = lane / G, gl = lane % G;
-  const int row0 = (blockIdx.x * 4 + wave) * ROWS_WAVE + grp;
+  const int row0 = (blockIdx.x * NRG + rgrp) * ROWS_WAVE + grp;
   const int row_words = a.nb * 4;
   const int units = row_words / V;
   const int K = a.nb * 32;
@@ -699,7 +676,7 @@ __global__ __launch_bounds__(256) void q4_down_kernel(GemvArgs a, SlotView view,
     for (int i = 0; i < R; ++i)
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) acc[i][tt] = 0.0f;
-    for (int u = gl; u < units; u += G) {
+    for (int u = gl + G * kslice; u < units; u += G * KS) {
       const int w0 = u * V;
       const int blk = w0 >> 2;
       float4 xl[TT][V], xh[TT][V];
@@ -719,20 +696,10 @@ __global__ __launch_bounds__(256) void q4_down_kernel(GemvArgs a, SlotView view,
       }
       uint32_t q0[R][V];
       float sc0[R];
-      __half hs[R];
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         load_words<V>(qr[i] + w0, q0[i]);
-        hs[i] = sr[i][blk];
-        sc0[i] = __half2float(hs[i]);
-      }
-      if (MODE == BK_TABLE && wr != nullptr && tg == 0) {
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-          store_words<V>(reinterpret_cast<uint32_t *>(wr + ((const uint8_t *)(qr[i] + w0) - rec)),
-                         q0[i]);
-          *reinterpret_cast<__half *>(wr + ((const uint8_t *)(sr[i] + blk) - rec)) = hs[i];
-        }
+        sc0[i] = __half2float(sr[i][blk]);
       }
 #pragma unroll
       for (int i = 0; i < R; ++i) {
@@ -752,54 +719,73 @@ __global__ __launch_bounds__(256) void q4_down_kernel(GemvArgs a, SlotView view,
 #pragma unroll
         for (int o = G / 2; o >= 1; o >>= 1) acc[i][tt] += __shfl_xor(acc[i][tt], o, 64);
       }
-    if (gl == 0) {
+    if constexpr (KS == 1) {
+      if (gl == 0) {
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const int r = row0 + i * RG;
-        if (r < a.rows) {
+        for (int i = 0; i < R; ++i) {
+          const int r = row0 + i * RG;
+          if (r < a.rows) {
 #pragma unroll
-          for (int tt = 0; tt < TT; ++tt)
-            if (tt < nt) a.out[(long long)prs[tt] * a.rows + r] = acc[i][tt];
+            for (int tt = 0; tt < TT; ++tt)
+              if (tt < nt) a.out[(long long)prs[tt] * a.rows + r] = acc[i][tt];
+          }
         }
       }
+    } else {
+      // the KS waves of a row group meet in LDS, summed in wave order
+      if (gl == 0) {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) red[wave][i * RG + grp][tt] = acc[i][tt];
+      }
+      __syncthreads();
+      for (int o = threadIdx.x; o < NRG * ROWS_WAVE * TT; o += 256) {
+        const int g = o / (ROWS_WAVE * TT), rr = (o / TT) % ROWS_WAVE, tt = o % TT;
+        const int r = (blockIdx.x * NRG + g) * ROWS_WAVE + rr;
+        if (r < a.rows && tt < nt) {
+          float v = 0.0f;
+#pragma unroll
+          for (int q = 0; q < KS; ++q) v += red[g * KS + q][rr][tt];
+          a.out[(long long)prs[tt] * a.rows + r] = v;
+        }
+      }
+      __syncthreads();
     }
   }
 }
 
+// Shapes measured on MI355X (cold Infinity Cache) over the decode shapes
+// d x f = 6144 x 2048, 2816 x 704, 2048 x 768 with 8 experts: half-block units
+// (V = 2) always beat whole blocks; gate/up runs best with 32 lanes per row and
+// 4 rows per lane; down with 16 lanes per row and 4 rows per lane, its K split
+// over the workgroup's waves only when the grid is small.  Fewer rows per lane
+// when the grid would otherwise leave the chip idle.
 GemvShape choose_gemv(bool glu, int rows, int nb, int n_buckets, int max_tokens) {
-  const int KS = glu ? 4 : 1;
-  GemvShape best{64, 4, 1, 1};
-  double best_eff = -1.0;
-  const int gs[3] = {64, 32, 16};
-  const int vs[2] = {4, 2};
-  for (int vi = 0; vi < 2; ++vi)
-    for (int gi = 0; gi < 3; ++gi) {
-      const int V = vs[vi], G = gs[gi];
-      const int units = nb * 4 / V;
-      const int span = G * KS;
-      const int ni = (units + span - 1) / span;
-      const double eff = (double)units / (double)(span * ni) + 1e-3 * V + 1e-5 * G;
-      if (eff > best_eff) {
-        best_eff = eff;
-        best.G = G;
-        best.V = V;
-      }
-    }
-  best.TT = max_tokens <= 1 ? 1 : (max_tokens <= 2 ? 2 : 4);
-  const int RG = 64 / best.G;
-  const int rows_wg_per_r = glu ? RG : 4 * RG;
-  best.R = 1;
+  GemvShape sh{16, 2, 1, 1, 1};
+  const int units = nb * 2;  // half-block units per row
+  if (glu) {
+    sh.KS = 4;
+    sh.G = units >= 128 ? 32 : 16;
+  } else {
+    sh.KS = (long long)rows * n_buckets <= 16384 ? 4 : 1;
+    sh.G = 16;
+  }
+  sh.TT = max_tokens <= 1 ? 1 : (max_tokens <= 2 ? 2 : 4);
+  const int RG = 64 / sh.G;
+  const int rows_wg_per_r = (4 / sh.KS) * RG;
+  sh.R = 1;
   const int rs[2] = {4, 2};
   for (int ri = 0; ri < 2; ++ri) {
     const int R = rs[ri];
     const long long waves =
         4LL * n_buckets * ((rows + R * rows_wg_per_r - 1) / (R * rows_wg_per_r));
-    if (waves >= 2048) {
-      best.R = R;
+    if (waves >= 512) {
+      sh.R = R;
       break;
     }
   }
-  return best;
+  return sh;
 }
 
 struct LaunchCtx {
@@ -809,6 +795,7 @@ struct LaunchCtx {
   bool glu;
   int nbk;
   hipStream_t s;
+  int ks;
 };
 
 template <int G, int V, int TT, int R, int MODE>
@@ -819,11 +806,16 @@ static hipError_t launch_one(const LaunchCtx &c) {
     const dim3 grid((a.rows + R * RG - 1) / (R * RG), c.nbk);
     hipLaunchKernelGGL((q4_gateup_kernel<G, V, TT, R, MODE>), grid, dim3(256), 0, c.s, a, *c.view,
                        *c.tab);
+  } else if (c.ks == 4) {
+    constexpr int rows_blk = R * RG;
+    const dim3 grid((a.rows + rows_blk - 1) / rows_blk, c.nbk);
+    hipLaunchKernelGGL((q4_down_kernel<G, V, TT, R, MODE, 4>), grid, dim3(256), 0, c.s, a,
+                       *c.view, *c.tab);
   } else {
     constexpr int rows_blk = 4 * R * RG;
     const dim3 grid((a.rows + rows_blk - 1) / rows_blk, c.nbk);
-    hipLaunchKernelGGL((q4_down_kernel<G, V, TT, R, MODE>), grid, dim3(256), 0, c.s, a, *c.view,
-                       *c.tab);
+    hipLaunchKernelGGL((q4_down_kernel<G, V, TT, R, MODE, 1>), grid, dim3(256), 0, c.s, a,
+                       *c.view, *c.tab);
   }
   return hipGetLastError();
 }
@@ -863,7 +855,7 @@ hipError_t launch_gemv(const GemvArgs &a, const SlotView &view, const BucketTabl
   if (n_buckets <= 0) return hipSuccess;
   BucketTable none;
   none.n = -1;
-  const LaunchCtx c{&a, &view, tab ? tab : &none, glu, n_buckets, s};
+  const LaunchCtx c{&a, &view, tab ? tab : &none, glu, n_buckets, s, sh.KS};
   switch (sh.G) {
     case 64: return launch_v<64>(c, sh);
     case 32: return launch_v<32>(c, sh);

@@ -64,15 +64,11 @@ struct GemvArgs {
 constexpr int kDecodeMaxPairs = 64;
 constexpr int kDecodeMaxTokens = 4;
 
-// Buckets built on the host (stream mode, decode path): bucket b reads its
-// expert record at src[b] -- a device slot, or the expert's record in the
-// page-locked host arena -- and, when dst[b] is set, writes every byte it reads
-// into that slot, so a miss is streamed into its slot by the same pass that
-// computes it.
+// Buckets built on the host (stream mode, decode path, after the slot fills):
+// bucket b reads the expert record at src[b] (a device slot).
 constexpr int kTabMax = 32;
 struct BucketTable {
   const uint8_t *src[kTabMax];
-  uint8_t *dst[kTabMax];
   int n;                                  // buckets, or -1 for "no table"
   uint8_t cnt[kTabMax];                   // pairs per bucket (<= kDecodeMaxTokens)
   uint8_t pairs[kTabMax][kDecodeMaxTokens];  // pair ids (< kDecodeMaxPairs)
@@ -80,6 +76,7 @@ struct BucketTable {
 
 struct GemvShape {
   int G, V, TT, R;
+  int KS;  // waves of a workgroup that split one row group's K (down: 1 or 4; gate/up: 4)
 };
 
 // Chooses lanes per row G, words per unit V, token tile TT and rows per lane R
