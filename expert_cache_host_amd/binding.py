@@ -178,7 +178,7 @@ class MoECache:
         _check(load_library().moe_cache_stats(self._h, layer, ctypes.byref(st)))
         return {n: getattr(st, n) for n, _ in Stats._fields_}
 
-    KERNELS = ("router", "topk", "remap", "gateup", "down", "combine", "fill")
+    KERNELS = ("router", "topk", "remap", "gateup", "down", "combine", "fill", "prep")
 
     def set_timing(self, on: bool):
         _check(load_library().moe_cache_set_timing(self._h, 1 if on else 0))

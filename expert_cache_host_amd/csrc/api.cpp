@@ -166,7 +166,7 @@ struct moe_cache {
   bool timing = false;
   // device workspace
   int32_t cap_T = 0;
-  DevBuf z, idx, w, meta, bucket_pair, h, y, xp, xsw, xscale;
+  DevBuf z, idx, w, meta, bucket_pair, h, y, xp, xsw, xscale, hp, hsw, hscale;
   // pinned host staging
   PinnedBuf h_idx, h_w, h_x, partial[2];
   hipEvent_t partial_ev[2] = {nullptr, nullptr};
@@ -218,6 +218,11 @@ struct moe_cache {
     xp.ensure((size_t)T * d * 4);
     xsw.ensure((size_t)T * (d / 8) * 4);
     xscale.ensure((size_t)T * 4);
+    if (T > moe::kDecodeMaxTokens) {
+      hp.ensure(P * (size_t)f * 4);
+      hsw.ensure(P * (size_t)(f / 8) * 4);
+      hscale.ensure(P * 4);
+    }
     h_idx.ensure((size_t)T * k * 4);
     h_w.ensure((size_t)T * k * 4);
     if (o.miss_mode == MOE_MISS_HOST) {
@@ -348,6 +353,37 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
   a.in = x;
   a.in_by_pair = 0;
   a.out = (float *)c->h.p;
+  if (!decode && !tab) {
+    // matrix-core grouped GEMM: gate/up + SwiGLU, h -> binary16 pairs, down
+    {
+      KTime kt(c, MOE_K_GATEUP, st);
+      HIPCHK(moe::launch_mfma(a, true, n_buckets, st));
+      kt.end(work_experts * 2.0 * (double)c->f * (double)L.nb_gu * 18.0);
+    }
+    const int P_all = T * k + T * c->o.n_shared;
+    {
+      KTime kt(c, MOE_K_PREP, st);
+      HIPCHK(moe::launch_prep_pairs((const float *)c->h.p, P_all, c->f, (uint32_t *)c->hp.p,
+                                    (float *)c->hsw.p, (float *)c->hscale.p, st));
+      kt.end((double)P_all * c->f * 8.0);
+    }
+    moe::GemvArgs b = a;
+    b.off_q0 = L.off_dq;
+    b.off_s0 = L.off_ds;
+    b.rows = c->d;
+    b.nb = (int)L.nb_dn;
+    b.xp = (const uint32_t *)c->hp.p;
+    b.xsw = (const float *)c->hsw.p;
+    b.xscale = (const float *)c->hscale.p;
+    b.in_by_pair = 1;
+    b.out = (float *)c->y.p;
+    {
+      KTime kt(c, MOE_K_DOWN, st);
+      HIPCHK(moe::launch_mfma(b, false, n_buckets, st));
+      kt.end(work_experts * (double)c->d * (double)L.nb_dn * 18.0);
+    }
+    return;
+  }
   const int max_tok = T;
   moe::GemvShape sh1 = moe::choose_gemv(true, a.rows, a.nb, n_buckets, max_tok);
   {

@@ -863,6 +863,279 @@ hipError_t launch_gemv(const GemvArgs &a, const SlotView &view, const BucketTabl
   }
 }
 
+// ============================================================== prefill MFMA GEMM
+// Per workgroup: 4 waves x 2 row blocks of 16 = 128 weight rows of one bucket's
+// expert, and its tokens in passes of up to NT x 16.  The K dimension runs in
+// chunks of KC blocks through two LDS buffers: while the waves multiply chunk c,
+// the chunk c+1 loads (raw nibble words, block scales, the tokens' hi/lo
+// activation pairs and block sums) are in flight and land in the other buffer.
+// A lane turns its nibble word into binary16 (1024 + q) as it builds the MFMA A
+// operand; each 32-weight block is one pair of v_mfma_f32_16x16x32_f16 (x hi,
+// x lo), and d * (C - 1032 * sum x) is folded into the accumulators in fp32.
+// Operand lanes: A lane l = row l%16 and the 8 K values of word l/16 of the
+// block (elements g, g+2, g+16, g+18, g+1, g+3, g+17, g+19 with g = 4*(l/16));
+// B lane l = token l%16 and the same 8 K values; C lane l = rows 4*(l/16)+i,
+// token l%16.
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int K6_RB = 2;                  // 16-row blocks per wave
+constexpr int K6_ROWS = 4 * 16 * K6_RB;   // rows per workgroup
+constexpr int K6_KC = 4;                  // blocks per K chunk
+constexpr int K6_NT = 2;                  // 16-token tiles per pass
+constexpr int K6_AW = K6_KC * 4 + 1;      // words per LDS row (one pad against bank conflicts)
+
+__device__ __forceinline__ uint4 decode_word_h(uint32_t q) {
+  const uint32_t m = 0x000F000Fu, mag = 0x64006400u;
+  uint4 r;
+  r.x = and_or(q, m, mag);
+  r.y = and_or(q >> 4, m, mag);
+  r.z = and_or(q >> 8, m, mag);
+  r.w = and_or(q >> 12, m, mag);
+  return r;
+}
+
+template <int NM>
+struct K6Buf {
+  uint32_t A[NM][K6_ROWS][K6_AW];
+  float S[NM][K6_ROWS][K6_KC];
+  uint4 B[K6_NT * 16][K6_KC * 4][2];
+  float X[K6_NT * 16][K6_KC];
+};
+
+template <int NM>
+struct K6Regs {
+  uint4 w[NM][2];
+  float sc[NM][2];
+  uint4 b[2][2];
+  float4 xs;
+};
+
+template <bool GLU>
+__global__ __launch_bounds__(256) void q4_mfma_kernel(GemvArgs a) {
+  constexpr int NM = GLU ? 2 : 1;
+  __shared__ K6Buf<NM> buf[2];
+  __shared__ int lTok[K6_NT * 16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bucket = blockIdx.y;
+  if (bucket >= a.meta[0]) return;
+  const int slot = a.meta[2 + bucket];
+  const int off = a.meta[2 + kMetaB + bucket];
+  const int cnt = a.meta[2 + 2 * kMetaB + bucket];
+  const uint8_t *rec = a.slots + (long long)slot * a.rec_bytes;
+  const int row_base = blockIdx.x * K6_ROWS;
+  const int words = a.nb * 4;
+  const uint32_t *qb[NM];
+  const __half *sb[NM];
+  qb[0] = reinterpret_cast<const uint32_t *>(rec + a.off_q0);
+  sb[0] = reinterpret_cast<const __half *>(rec + a.off_s0);
+  if constexpr (GLU) {
+    qb[NM - 1] = reinterpret_cast<const uint32_t *>(rec + a.off_q1);
+    sb[NM - 1] = reinterpret_cast<const __half *>(rec + a.off_s1);
+  }
+  const int m = lane & 15, kg = lane >> 4;
+  const int n_chunks = (a.nb + K6_KC - 1) / K6_KC;
+
+  for (int g0 = 0; g0 < cnt; g0 += K6_NT * 16) {
+    const int ntok = min(K6_NT * 16, cnt - g0);
+    const int n_tiles = (ntok + 15) >> 4;
+    if (tid < K6_NT * 16) {
+      const int p = a.bucket_pair[off + g0 + min(tid, ntok - 1)];
+      lTok[tid] = a.in_by_pair ? p : pair_row(a, p);
+    }
+    __syncthreads();
+    // staging roles: items (row, block) = 128 x KC per matrix, 2 per thread;
+    // (token, word) = 32 x 4*KC, 2 per thread; (token, block) = 32 x KC, 1 per thread
+    auto load_chunk = [&](int c, K6Regs<NM> &r) {
+      const int kc = c * K6_KC;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int it = tid + 256 * j;
+        const int row = it >> 2, blk = min(kc + (it & 3), a.nb - 1);
+        const long long gr = min(row_base + row, a.rows - 1);
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+          r.w[q][j] = *reinterpret_cast<const uint4 *>(qb[q] + gr * words + blk * 4);
+          r.sc[q][j] = __half2float(sb[q][gr * a.nb + blk]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int it = tid + 256 * j;
+        const int t = it >> 4, w = it & 15;
+        const int wq = min(kc * 4 + w, words - 1);
+        const uint4 *src =
+            reinterpret_cast<const uint4 *>(a.xp + ((long long)lTok[t] * words + wq) * 8);
+        r.b[j][0] = src[0];
+        r.b[j][1] = src[1];
+      }
+      {
+        const int t = (tid >> 2) & 31, b = tid & 3;
+        const int blk = min(kc + b, a.nb - 1);
+        r.xs = *reinterpret_cast<const float4 *>(a.xsw + (long long)lTok[t] * words + blk * 4);
+      }
+    };
+    auto store_chunk = [&](K6Buf<NM> &B, const K6Regs<NM> &r) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int it = tid + 256 * j;
+        const int row = it >> 2, b = it & 3;
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+          B.A[q][row][b * 4 + 0] = r.w[q][j].x;
+          B.A[q][row][b * 4 + 1] = r.w[q][j].y;
+          B.A[q][row][b * 4 + 2] = r.w[q][j].z;
+          B.A[q][row][b * 4 + 3] = r.w[q][j].w;
+          B.S[q][row][b] = r.sc[q][j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int it = tid + 256 * j;
+        B.B[it >> 4][it & 15][0] = r.b[j][0];
+        B.B[it >> 4][it & 15][1] = r.b[j][1];
+      }
+      if (tid < 128) B.X[tid >> 2][tid & 3] = (r.xs.x + r.xs.y) + (r.xs.z + r.xs.w);
+    };
+
+    floatx4 acc[NM][K6_RB][K6_NT];
+#pragma unroll
+    for (int q = 0; q < NM; ++q)
+#pragma unroll
+      for (int rb = 0; rb < K6_RB; ++rb)
+#pragma unroll
+        for (int t = 0; t < K6_NT; ++t) acc[q][rb][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    K6Regs<NM> regs;
+    load_chunk(0, regs);
+    store_chunk(buf[0], regs);
+    __syncthreads();
+    for (int c = 0; c < n_chunks; ++c) {
+      if (c + 1 < n_chunks) load_chunk(c + 1, regs);
+      const K6Buf<NM> &B = buf[c & 1];
+      const int kb_n = min(K6_KC, a.nb - c * K6_KC);
+      for (int kb = 0; kb < kb_n; ++kb) {
+        half8_t Bh[K6_NT], Bl[K6_NT];
+        float o1032[K6_NT];
+#pragma unroll
+        for (int t = 0; t < K6_NT; ++t) {
+          Bh[t] = __builtin_bit_cast(half8_t, B.B[t * 16 + m][kb * 4 + kg][0]);
+          Bl[t] = __builtin_bit_cast(half8_t, B.B[t * 16 + m][kb * 4 + kg][1]);
+          o1032[t] = 1032.0f * B.X[t * 16 + m][kb];
+        }
+#pragma unroll
+        for (int rb = 0; rb < K6_RB; ++rb) {
+          const int rw = wave * (16 * K6_RB) + rb * 16;
+#pragma unroll
+          for (int q = 0; q < NM; ++q) {
+            const half8_t A = __builtin_bit_cast(half8_t, decode_word_h(B.A[q][rw + m][kb * 4 + kg]));
+            float sc[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[i] = B.S[q][rw + kg * 4 + i][kb];
+#pragma unroll
+            for (int t = 0; t < K6_NT; ++t) {
+              if (t < n_tiles) {
+                floatx4 cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh[t], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl[t], cc, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[q][rb][t][i] += sc[i] * (cc[i] - o1032[t]);
+              }
+            }
+          }
+        }
+      }
+      if (c + 1 < n_chunks) store_chunk(buf[(c + 1) & 1], regs);
+      __syncthreads();
+    }
+    // C lane layout: rows rw + kg*4 + i, token column m of each tile
+#pragma unroll
+    for (int t = 0; t < K6_NT; ++t) {
+      const int col = t * 16 + m;
+      if (t < n_tiles && col < ntok) {
+        const int p = a.bucket_pair[off + g0 + col];
+        const float sc = a.xscale[lTok[col]];
+#pragma unroll
+        for (int rb = 0; rb < K6_RB; ++rb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = row_base + wave * (16 * K6_RB) + rb * 16 + kg * 4 + i;
+            if (r < a.rows) {
+              const float v = GLU ? silu_f(acc[0][rb][t][i] * sc) * (acc[NM - 1][rb][t][i] * sc)
+                                  : acc[0][rb][t][i] * sc;
+              a.out[(long long)p * a.rows + r] = v;
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_mfma(const GemvArgs &a, bool glu, int n_buckets, hipStream_t s) {
+  if (n_buckets <= 0) return hipSuccess;
+  const dim3 grid((a.rows + K6_ROWS - 1) / K6_ROWS, n_buckets);
+  if (glu)
+    hipLaunchKernelGGL(q4_mfma_kernel<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(q4_mfma_kernel<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// One wave per row: scale, binary16 hi/lo pairs in the decoder's order, word sums.
+__global__ __launch_bounds__(64) void prep_pairs_kernel(const float *__restrict__ in, int rows, int K,
+                                                        uint32_t *__restrict__ xp,
+                                                        float *__restrict__ xsw,
+                                                        float *__restrict__ xscale) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  if (r >= rows) return;
+  const float *xt = in + (long long)r * K;
+  float m = 0.0f;
+  for (int i = lane; i < K; i += 64) m = fmaxf(m, fabsf(xt[i]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  int ex2 = 0;
+  if (m > 0.0f && m <= 3.0e38f) {
+    int fe;
+    (void)frexpf(m, &fe);
+    ex2 = max(0, fe - 14);
+  }
+  const float sc = ldexpf(1.0f, -ex2);
+  if (lane == 0) xscale[r] = ldexpf(1.0f, ex2);
+  const int words = K / 8;
+  for (int j = lane; j < words; j += 64) {
+    const int b = j >> 2, wq = j & 3;
+    const float4 av = *reinterpret_cast<const float4 *>(xt + b * 32 + 4 * wq);
+    const float4 cv = *reinterpret_cast<const float4 *>(xt + b * 32 + 16 + 4 * wq);
+    const float e0 = av.x * sc, e1 = av.y * sc, e2 = av.z * sc, e3 = av.w * sc;
+    const float f0 = cv.x * sc, f1 = cv.y * sc, f2 = cv.z * sc, f3 = cv.w * sc;
+    const float he0 = (float)(_Float16)e0, he1 = (float)(_Float16)e1;
+    const float he2 = (float)(_Float16)e2, he3 = (float)(_Float16)e3;
+    const float hf0 = (float)(_Float16)f0, hf1 = (float)(_Float16)f1;
+    const float hf2 = (float)(_Float16)f2, hf3 = (float)(_Float16)f3;
+    uint4 hi, lo;
+    hi.x = pack_h2(he0, he2);
+    hi.y = pack_h2(hf0, hf2);
+    hi.z = pack_h2(he1, he3);
+    hi.w = pack_h2(hf1, hf3);
+    lo.x = pack_h2(e0 - he0, e2 - he2);
+    lo.y = pack_h2(f0 - hf0, f2 - hf2);
+    lo.z = pack_h2(e1 - he1, e3 - he3);
+    lo.w = pack_h2(f1 - hf1, f3 - hf3);
+    uint4 *dst = reinterpret_cast<uint4 *>(xp + ((long long)r * words + j) * 8);
+    dst[0] = hi;
+    dst[1] = lo;
+    xsw[(long long)r * words + j] = ((e0 + e1) + (e2 + e3)) + ((f0 + f1) + (f2 + f3));
+  }
+}
+
+hipError_t launch_prep_pairs(const float *in, int rows, int K, uint32_t *xp, float *xsw,
+                             float *xscale, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(prep_pairs_kernel, dim3(rows), dim3(64), 0, s, in, rows, K, xp, xsw, xscale);
+  return hipGetLastError();
+}
+
 // ============================================================== slot fills
 __global__ __launch_bounds__(256) void pull_kernel(PullList l) {
   const int e = blockIdx.x / l.per_expert, part = blockIdx.x % l.per_expert;

@@ -93,6 +93,21 @@ GemvShape choose_gemv(bool glu, int rows, int nb, int n_buckets, int max_tokens)
 hipError_t launch_gemv(const GemvArgs &a, const SlotView &view, const BucketTable *tab,
                        const GemvShape &sh, bool glu, int n_buckets, hipStream_t s);
 
+// Prefill grouped GEMM on the matrix cores (batches beyond the decode path).
+// Buckets from launch_remap; per workgroup 64 weight rows of one bucket's expert
+// and up to 64 of its tokens at a time.  Weights are decoded chunk by chunk into
+// LDS as binary16 (1024 + q), activations come as binary16 hi/lo pairs in the
+// same K order (xp / xsw / xscale as prepared for the gate/up GEMV, indexed by
+// token for gate/up and by pair for down), each 32-weight block is one pair of
+// v_mfma_f32_16x16x32_f16 (hi, lo) and its scale and the 1032 * sum(x) offset are
+// applied per block in fp32.  glu: out[p][r] = silu(g) * u; else out = M in.
+hipError_t launch_mfma(const GemvArgs &a, bool glu, int n_buckets, hipStream_t s);
+
+// Binary16 hi/lo pairs, word sums and power-of-two scale of `rows` float rows of
+// length K (the preparation the router does for x), for the down GEMM's input h.
+hipError_t launch_prep_pairs(const float *in, int rows, int K, uint32_t *xp, float *xsw,
+                             float *xscale, hipStream_t s);
+
 // Copies n expert records (bytes16 x 16 bytes each) from the page-locked host
 // arena into device slots; `per_expert` workgroups each read one contiguous
 // chunk with wide loads (PCIe reads stay long and in flight).

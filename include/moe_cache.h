@@ -183,14 +183,17 @@ moe_status moe_cache_set_timing(moe_cache *c, int32_t on);
 #define MOE_K_DOWN 4    /* Q4 down projection */
 #define MOE_K_COMBINE 5 /* weighted combine */
 #define MOE_K_FILL 6    /* slot fills pulled from the page-locked arena by a kernel */
-#define MOE_K_COUNT 7
+#define MOE_K_PREP 7    /* binary16 hi/lo preparation of h for the prefill down GEMM */
+#define MOE_K_COUNT 8
 
 /* Launches, summed device seconds (HIP events on the launching stream, read
  * when this is called) and summed algorithmic bytes of kernel `kernel` since the
  * last reset.  Algorithmic bytes: router = W_r + x + logits; Q4 kernels = the
  * 18/32-byte-per-weight bytes of every expert matrix the launch reads; fill =
- * the slot records copied host -> device; combine = expert outputs read + layer
- * output written. */
+ * the slot records copied host -> device; prep = h read + pairs written;
+ * combine = expert outputs read + layer output written.  On batches beyond the
+ * decode path (more than 4 tokens) MOE_K_GATEUP / MOE_K_DOWN time the matrix-core
+ * grouped GEMM. */
 moe_status moe_cache_kernel_stats(moe_cache *c, int32_t kernel, int64_t *launches, double *seconds,
                                   double *bytes);
 
