@@ -10,10 +10,20 @@ workload is the Gemma-4-26B-A4B-like decode (30 layers, d_model 2816, d_ff 704,
 
 Prints one JSON line.  `value` = MoE-layer tokens/s (tokens x layers / wall
 time) over exactly K timed steps, inputs resident in HBM and expert weights in
-the library's page-locked host arena before the timed region starts.  A second
-pass of K steps (not timed end to end) brackets every kernel launch with HIP
-events inside the library, for the per-kernel roofline.  The oracle is timed on
-a bounded sample of the same workload as the CPU baseline.
+the library's page-locked host arena before the timed region starts.  Then the
+same number of further steps runs with the library bracketing every kernel
+launch with HIP events on the stream it launches on (recording them inside the
+timed region would cost ~30% of the throughput, since the host enqueues on the
+critical path).  `roofline` is the decode expert GEMV (gate/up + SwiGLU and
+down launches of a call taken together: expert bytes read / their device time)
+against HBM, or for prefill the grouped GEMM against the fp16 matrix-core peak;
+`roofline_fill` is the slot-fill kernel against PCIe Gen5 x16, which under pure
+LRU holds the most device time (`dominant_kernel_by_device_time`).  `traffic` comes from the
+rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in profiles/pmc_traffic.json
+and is null when the kernel source changed since.  The oracle is timed on a
+bounded sample of the same workload as the CPU baseline.
+
+    python bench.py --copy-calibration   # plain 256 MiB device copies, for PMC scaling
 """
 from __future__ import annotations
 
@@ -30,8 +40,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0
-MFMA_BF16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+PCIE_PEAK_GBS = 64.0             # PCIe Gen5 x16, one direction
+MFMA_F16_PEAK_TFLOPS = 2500.0    # dense fp16 / bf16 matrix cores
+KERNEL_SRC = os.path.join(ROOT, "expert_cache_host_amd", "csrc", "kernels.hip")
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+# the library's kernel ids -> kernel names in rocprofv3 output
+KERNEL_SYMBOL = {"gateup": "q4_gateup_kernel", "down": "q4_down_kernel", "fill": "pull_kernel",
+                 "router": "router_kernel", "topk": "topk_kernel", "combine": "combine_kernel"}
 
 
 def log(msg):
@@ -52,6 +68,38 @@ def describe(wl):
     return (f"{wl.name}: {wl.layers} layers, d_model {wl.d_model}, d_ff {wl.d_ff}, "
             f"{wl.n_experts} experts{sh}, top-{wl.top_k}, {wl.slots} slots/layer, {kind} "
             f"({wl.batch} tokens/call), {miss}")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def pmc_traffic(workload: str, kernel: str, launches: int, bytes_per_launch: float):
+    """Calibrated FETCH+WRITE bytes per launch for `kernel`, or None."""
+    try:
+        data = json.load(open(PMC_FILE))
+    except (OSError, ValueError):
+        return None
+    if data.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    ent = data.get("workloads", {}).get(workload, {}).get(kernel)
+    if not ent:
+        return None
+    return (ent["fetch_KiB"] * data["fetch_scale"] + ent["write_KiB"] * data["write_scale"]) * 1024.0
+
+
+def copy_calibration():
+    """Plain device-to-device copies of known size (rocprofv3 --pmc scaling)."""
+    import torch
+    n = 256 << 20
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}))
 
 
 def cpu_baseline(wl, weights, routers, hidden, budget_s=12.0, max_calls=64):
@@ -85,8 +133,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="gemma")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-kernel-pass", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="time the steps without per-kernel events (no roofline)")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -103,11 +156,10 @@ def main():
     else:
         steps = args.steps if args.steps is not None else 224
         warmup = args.warmup if args.warmup is not None else 16
-    kernel_steps = 0 if args.no_kernel_pass else min(steps, max(1, per_layer - warmup - steps))
-    need = warmup + steps + kernel_steps
+    ev_steps = 0 if args.no_kernel_events else min(steps, per_layer - warmup - steps)
+    need = warmup + steps + ev_steps
     if need > per_layer:
-        raise SystemExit(f"{wl.name} has {per_layer} calls per layer; warmup+steps(+kernel pass) "
-                         f"= {need}")
+        raise SystemExit(f"{wl.name} has {per_layer} calls per layer; warmup+steps = {need}")
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -139,8 +191,20 @@ def main():
     run(warmup, steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    cache.sync()
     st = cache.stats()
     log(f"[bench] timed {steps} steps in {wall:.3f} s")
+    ks = {k: (0, 0.0, 0.0) for k in cache.KERNELS}
+    if ev_steps > 0:
+        cache.reset_stats()
+        cache.set_timing(True)
+        run(warmup + steps, ev_steps)
+        torch.cuda.synchronize()
+        cache.set_timing(False)
+        cache.sync()
+        ks = cache.kernel_stats()
+        st2 = cache.stats()
+        log(f"[bench] kernel-event pass of {ev_steps} steps done")
 
     layer_tokens = steps * wl.batch * wl.layers
     value = layer_tokens / wall
@@ -154,35 +218,69 @@ def main():
         "plan_us_per_call": 1e6 * st["plan_s"] / max(1, st["calls"]),
         "host_ms_per_call": 1e3 * st["host_s"] / max(1, st["calls"]),
     }
+    if ev_steps > 0 and st2["h2d_s"] > 0:
+        extra["fill_copy_engine_GB_per_s"] = st2["fill_bytes"] / st2["h2d_s"] / 1e9
+    if ks["fill"][0]:
+        extra["fill_kernel_GB_per_s"] = ks["fill"][2] / ks["fill"][1] / 1e9
 
-    roofline = None
     kernels = {}
-    if kernel_steps:
-        cache.reset_stats()
-        cache.set_timing(True)
-        run(warmup + steps, kernel_steps)
-        torch.cuda.synchronize()
-        cache.sync()
-        ks = cache.kernel_stats()
-        st2 = cache.stats()
-        cache.set_timing(False)
-        for name, (n, sec, by) in ks.items():
-            if n:
-                kernels[name] = {"launches": n, "avg_us": 1e6 * sec / n,
-                                 "GB_per_s": by / sec / 1e9 if sec > 0 else None,
-                                 "bytes_per_launch": by / n}
-        if st2["h2d_s"] > 0:
-            extra["fill_H2D_GB_per_s"] = st2["fill_bytes"] / st2["h2d_s"] / 1e9
-        if ks["fill"][0]:
-            extra["fill_kernel_H2D_GB_per_s"] = ks["fill"][2] / ks["fill"][1] / 1e9
-        dom = max((k for k in kernels if k in ("gateup", "down")),
-                  key=lambda k: ks[k][1], default=None)
-        if dom:
-            n, sec, by = ks[dom]
+    for name, (n, sec, by) in ks.items():
+        if n:
+            kernels[name] = {"launches": n, "avg_us": 1e6 * sec / n,
+                             "GB_per_s": by / sec / 1e9 if sec > 0 else None,
+                             "bytes_per_launch": by / n, "device_s": sec}
+
+    def roof_pair(a, b):
+        """Two kernels launched back to back per call, taken as one: algorithmic bytes / time."""
+        na, sa, ba = ks[a]
+        nb_, sb, bb = ks[b]
+        if not na or sa + sb <= 0:
+            return None
+        ach = (ba + bb) / (sa + sb) / 1e9
+        tr = [pmc_traffic(wl.name, k, 0, 0) for k in (a, b)]
+        traffic = None if None in tr else (tr[0] * na + tr[1] * nb_) / na
+        return {"bound": "hbm", "kernel": f"{KERNEL_SYMBOL[a]} + {KERNEL_SYMBOL[b]}",
+                "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                "traffic": traffic, "avg_launch_us": 1e6 * (sa + sb) / na, "launches": na,
+                "algorithmic_bytes_per_launch": (ba + bb) / na,
+                "per_kernel": {a: roof(a, "hbm", HBM_PEAK_GBS, "GB/s"),
+                               b: roof(b, "hbm", HBM_PEAK_GBS, "GB/s")}}
+
+    def roof(name, bound, peak, unit):
+        n, sec, by = ks[name]
+        if not n or sec <= 0:
+            return None
+        if unit == "TFLOP/s":
+            ach = by / sec / 1e12
+        else:
             ach = by / sec / 1e9
-            roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
-                        "avg_launch_us": 1e6 * sec / n, "bytes_per_launch": by / n}
+        tr = pmc_traffic(wl.name, name, n, by / n)
+        return {"bound": bound, "kernel": KERNEL_SYMBOL.get(name, name), "achieved": ach,
+                "peak": peak, "unit": unit, "frac": ach / peak,
+                "traffic": tr, "avg_launch_us": 1e6 * sec / n, "launches": n,
+                "algorithmic_bytes_per_launch": by / n}
+
+    roofline = roofline_fill = roofline_mfma = None
+    dominant = None
+    if kernels:
+        dominant = KERNEL_SYMBOL.get(max(kernels, key=lambda k: kernels[k]["device_s"]))
+        if wl.batch <= 4:
+            # decode: the expert GEMV (gate/up + SwiGLU, then down) on the bytes it reads
+            roofline = roof_pair("gateup", "down")
+        roofline_fill = roof("fill", "pcie", PCIE_PEAK_GBS, "GB/s")
+        if wl.batch > 4 and ks["gateup"][0]:
+            # algorithmic flops of the grouped GEMM: 2 * tokens * rows * K per expert
+            n, sec, by = ks["gateup"]
+            n2, sec2, by2 = ks["down"]
+            flops = 2.0 * wl.batch * (wl.top_k + wl.n_shared) * 3 * wl.d_model * wl.d_ff * ev_steps * wl.layers
+            t_mm = sec + sec2
+            roofline_mfma = {"bound": "mfma", "kernel": "q4_mfma_kernel", "achieved": flops / t_mm / 1e12,
+                             "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": flops / t_mm / 1e12 / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                             "avg_launch_us": 1e6 * t_mm / max(1, n + n2), "launches": n + n2,
+                             "hbm_GB_per_s": (by + by2) / t_mm / 1e9,
+                             "hbm_frac": (by + by2) / t_mm / 1e9 / HBM_PEAK_GBS}
+            roofline = roofline_mfma
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -203,8 +301,11 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded Q4_0 experts ~N(0,0.02), AR(1) hidden states, Zipf router bias)",
         "config": {"workload": describe(wl), "layers": wl.layers, "tokens_per_call": wl.batch,
-                   "steps_are": "one batch through every layer"},
+                   "steps_are": "one batch through every layer",
+                   "kernel_timing": f"HIP events per launch over {ev_steps} further steps"},
         "roofline": roofline,
+        "dominant_kernel_by_device_time": dominant,
+        "roofline_fill": roofline_fill,
         "cpu_baseline": cpu,
         "extra": extra,
         "kernels": kernels,
