@@ -147,3 +147,52 @@ def test_stream_stage_count_closed_form():
         res = sim.plan(list(range(e_count)), STREAM)
         assert len(res.stage_views) == 1 + -(-(e_count - s_count) // s_count)
         assert res.hits == s_count and res.fills == e_count - s_count
+
+
+class _MRU(LayerSlots):
+    def victim(self):  # planted mistake: most recently used
+        for s in range(self.S):
+            if self.expert_in[s] == -1:
+                return s
+        c = [s for s in range(self.S) if self.last_use[s] < self.clock]
+        return max(c, key=lambda s: (self.last_use[s], s)) if c else None
+
+
+class _NoProtect(LayerSlots):
+    def victim(self):  # planted mistake: protected slots may be evicted
+        for s in range(self.S):
+            if self.expert_in[s] == -1:
+                return s
+        return min(range(self.S), key=lambda s: (self.last_use[s], s))
+
+
+class _HighTie(LayerSlots):
+    def victim(self):  # planted mistake: ties on last_use go to the higher slot
+        for s in range(self.S):
+            if self.expert_in[s] == -1:
+                return s
+        c = [s for s in range(self.S) if self.last_use[s] < self.clock]
+        return max(c, key=lambda s: (-self.last_use[s], s)) if c else None
+
+
+def _trace_passes(cls, tr):
+    sim = cls(tr["E"], tr["S"])
+    try:
+        for c, (idx, hits, evs) in enumerate(tr["calls"]):
+            res = sim.plan(idx, tr["mode"], tr["fills"])
+            if res.hits != hits or res.evictions != evs:
+                return False
+            if tr["views"] and (res.stage_views[0], res.host_view) != tr["views"][c]:
+                return False
+            if tr["stages"] is not None and res.stage_experts != tr["stages"]:
+                return False
+    except Exception:
+        return False
+    return sim.expert_in == tr["final"]
+
+
+@pytest.mark.parametrize("cls", [_MRU, _NoProtect, _HighTie])
+def test_planted_victim_mistakes_fail_the_traces(cls):
+    """Each plausible slip in the victim rule contradicts at least one hand-worked trace."""
+    assert all(_trace_passes(LayerSlots, tr) for tr in TRACES.values())
+    assert not all(_trace_passes(cls, tr) for tr in TRACES.values())
