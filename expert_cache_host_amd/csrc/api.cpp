@@ -166,7 +166,8 @@ struct moe_cache {
   bool timing = false;
   // device workspace
   int32_t cap_T = 0;
-  DevBuf z, idx, w, meta, bucket_pair, h, y, xp, xsw, xscale, hp, hsw, hscale;
+  DevBuf z, idx, w, meta, bucket_pair, h, y, xp, xsw, xscale, hp, hsw, hscale, xq, xs;
+  DevBuf buckets, pair_slot;  // decode: bucket list and pair -> slot of the hits
   // pinned host staging
   PinnedBuf h_idx, h_w, h_x, partial[2];
   hipEvent_t partial_ev[2] = {nullptr, nullptr};
@@ -176,6 +177,13 @@ struct moe_cache {
   std::unique_ptr<moe::ThreadPool> pool;
 
   size_t rec() const { return (size_t)lay.bytes; }
+  // T tokens per call take the decode GEMV (workgroups find their own buckets)
+  bool decode_ok(int32_t T) const {
+    constexpr size_t kLdsBudget = 60 * 1024;  // dynamic LDS per workgroup
+    return T <= moe::kDecodeMaxTokens && T * (o.top_k + o.n_shared) <= moe::kDecodeMaxPairs &&
+           moe::gemv_lds_bytes(true, (int)lay.nb_gu, T) <= kLdsBudget &&
+           moe::gemv_lds_bytes(false, (int)lay.nb_dn, T) <= kLdsBudget;
+  }
   int32_t n_total() const { return E + o.n_shared; }
   const uint8_t *host_record(int32_t l, int32_t e) const {
     return h_arena + ((size_t)l * n_total() + e) * rec();
@@ -218,6 +226,10 @@ struct moe_cache {
     xp.ensure((size_t)T * d * 4);
     xsw.ensure((size_t)T * (d / 8) * 4);
     xscale.ensure((size_t)T * 4);
+    xq.ensure((size_t)T * d * 2);
+    xs.ensure((size_t)T * 4);
+    buckets.ensure((size_t)(1 + moe::kDecodeMaxPairs * moe::kBucketInts) * 4);
+    pair_slot.ensure((size_t)moe::kDecodeMaxPairs * 4);
     if (T > moe::kDecodeMaxTokens) {
       hp.ensure(P * (size_t)f * 4);
       hsw.ensure(P * (size_t)(f / 8) * 4);
@@ -322,7 +334,7 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
   const int32_t k = c->o.top_k;
   const int shared_slot = with_shared ? c->S : -1;
   const int P = T * k + (with_shared ? T : 0);
-  const bool decode = T <= moe::kDecodeMaxTokens && P <= moe::kDecodeMaxPairs;
+  const bool decode = c->decode_ok(T);
   const moe::RecordLayout &L = c->lay;
   moe::GemvArgs a{};
   if (!decode && !tab) {
@@ -335,6 +347,9 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
     a.bucket_pair = (const int32_t *)c->bucket_pair.p;
   }
   a.slots = c->layers[layer].d_slots;
+  a.bt = decode && !tab ? (const int32_t *)c->buckets.p : nullptr;
+  a.xq = (const uint4 *)c->xq.p;
+  a.xs = (const float *)c->xs.p;
   a.xp = (const uint32_t *)c->xp.p;
   a.xsw = (const float *)c->xsw.p;
   a.xscale = (const float *)c->xscale.p;
@@ -384,11 +399,10 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
     }
     return;
   }
-  const int max_tok = T;
-  moe::GemvShape sh1 = moe::choose_gemv(true, a.rows, a.nb, n_buckets, max_tok);
+  moe::GemvShape sh1 = moe::choose_gemv(true, a.nb, T);
   {
     KTime kt(c, MOE_K_GATEUP, st);
-    HIPCHK(moe::launch_gemv(a, view, tab, sh1, true, n_buckets, st));
+    HIPCHK(moe::launch_gemv(a, tab, sh1, true, n_buckets, st));
     kt.end(work_experts * 2.0 * (double)c->f * (double)L.nb_gu * 18.0);
   }
   // down: rows d, K = f, input = h by pair
@@ -400,10 +414,10 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
   b.in = (const float *)c->h.p;
   b.in_by_pair = 1;
   b.out = (float *)c->y.p;
-  moe::GemvShape sh2 = moe::choose_gemv(false, b.rows, b.nb, n_buckets, max_tok);
+  moe::GemvShape sh2 = moe::choose_gemv(false, b.nb, T);
   {
     KTime kt(c, MOE_K_DOWN, st);
-    HIPCHK(moe::launch_gemv(b, view, tab, sh2, false, n_buckets, st));
+    HIPCHK(moe::launch_gemv(b, tab, sh2, false, n_buckets, st));
     kt.end(work_experts * (double)c->d * (double)L.nb_dn * 18.0);
   }
 }
@@ -429,23 +443,34 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   }
   if (host_mode)
     HIPCHK(hipMemcpyAsync(c->h_x.p, x, (size_t)T * d * 4, hipMemcpyDeviceToHost, st));
+  // table published at call start: the hits run on it before the host plans
+  const moe::SlotView pre = make_view(ly.planner->slot_of());
+  const bool dec = c->decode_ok(T);
   {
     KTime kt(c, MOE_K_ROUTER, st);
+    // the decode GEMV takes digit planes, the matrix-core GEMM binary16 pairs
     HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)c->z.p,
-                              (uint32_t *)c->xp.p, (float *)c->xsw.p, (float *)c->xscale.p, st));
+                              dec ? nullptr : (uint32_t *)c->xp.p, (float *)c->xsw.p,
+                              (float *)c->xscale.p, dec ? (uint4 *)c->xq.p : nullptr,
+                              (float *)c->xs.p, st));
     kt.end(4.0 * ((double)E * d + (double)T * d * 2 + (double)T * E + (router_bias ? E : 0)));
   }
   {
     KTime kt(c, MOE_K_TOPK, st);
-    HIPCHK(moe::launch_topk((const float *)c->z.p, T, E, k, c->o.norm_topk, (int32_t *)c->idx.p,
-                            (float *)c->w.p, (int32_t *)c->h_idx.p, (float *)c->h_w.p, st));
+    if (dec)
+      HIPCHK(moe::launch_topk_decode((const float *)c->z.p, T, E, k, c->o.norm_topk,
+                                     (int32_t *)c->idx.p, (float *)c->w.p, (int32_t *)c->h_idx.p,
+                                     (float *)c->h_w.p, pre, ns > 0 ? c->S : -1,
+                                     (int32_t *)c->buckets.p, (int32_t *)c->pair_slot.p, st));
+    else
+      HIPCHK(moe::launch_topk((const float *)c->z.p, T, E, k, c->o.norm_topk, (int32_t *)c->idx.p,
+                              (float *)c->w.p, (int32_t *)c->h_idx.p, (float *)c->h_w.p, st));
     kt.end(4.0 * ((double)T * E + 4.0 * T * k));
   }
   HIPCHK(hipEventRecord(c->ev_idx, st));
 
   // Cached experts (and the shared one) on the table published at call start,
   // enqueued before the host reads the routing.
-  const moe::SlotView pre = make_view(ly.planner->slot_of());
   const int nb_hits = std::min(T * k, c->S) + (ns > 0 ? 1 : 0);
   run_experts(c, layer, T, pre, ns > 0, nb_hits, 0.0, x, st);
   record_compute(c, ly, st);
@@ -467,8 +492,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
     c->kt[MOE_K_DOWN].bytes += n_hit * (double)c->d * (double)c->lay.nb_dn * 18.0;
   }
   bool combined = false;
-  const bool decode_pairs = T <= moe::kDecodeMaxTokens && T * k <= moe::kDecodeMaxPairs;
-  if (!host_mode && decode_pairs) {
+  if (!host_mode && c->decode_ok(T)) {
     // every miss is pulled from the pinned arena into its slot by a copy
     // kernel on the compute stream, then computed there from host-built buckets
     const int32_t *hidx = (const int32_t *)c->h_idx.p;
@@ -558,8 +582,9 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
       {
         KTime kt(c, MOE_K_COMBINE, st);
         HIPCHK(moe::launch_combine((const float *)c->y.p, (const float *)c->w.p,
-                                   (const int32_t *)c->idx.p, pre, 0, T, k, d, ns, host_part, out,
-                                   dbg_gpu, st));
+                                   (const int32_t *)c->idx.p, pre, 0,
+                                   dec ? (const int32_t *)c->pair_slot.p : nullptr, T, k, d, ns,
+                                   host_part, out, dbg_gpu, st));
         kt.end(4.0 * (double)T * d * (k + ns + 2));
       }
       HIPCHK(hipEventRecord(c->partial_ev[b], st));
@@ -572,7 +597,8 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   if (!combined) {
     KTime kt(c, MOE_K_COMBINE, st);
     HIPCHK(moe::launch_combine((const float *)c->y.p, (const float *)c->w.p,
-                               (const int32_t *)c->idx.p, pre, host_mode ? 0 : 1, T, k, d, ns,
+                               (const int32_t *)c->idx.p, pre, host_mode ? 0 : 1,
+                               dec ? (const int32_t *)c->pair_slot.p : nullptr, T, k, d, ns,
                                nullptr, out, dbg_gpu, st));
     kt.end(4.0 * (double)T * d * (k + ns + 1));
   }

@@ -62,6 +62,26 @@ __device__ __forceinline__ void wave_argmax(float &bv, int &be, int sent) {
   be = re;
 }
 
+// Digit planes of 8 values (elements g..g+3, g+16..g+19 of a block) at scale
+// 1/inv, in the layout the decode GEMV multiplies (described there).
+__device__ __forceinline__ uint4 digit_planes8(const float (&v)[8], float inv) {
+  uint32_t z[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = ((uint32_t)((int)rintf(v[i] * inv) + 0x8888) ^ 0x8888u) & 0xFFFFu;
+  uint32_t p[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      w |= ((z[m] >> (4 * k)) & 15u) << (8 * m);
+      w |= ((z[m + 4] >> (4 * k)) & 15u) << (8 * m + 4);
+    }
+    p[k] = w;
+  }
+  return make_uint4(p[0], p[1], p[2], p[3]);
+}
+
 // ============================================================== router logits
 // One wave per (expert, tile of TT tokens).  Lane l accumulates i = l, l+64, ...
 // with the product and the sum rounded separately (no contraction), then a
@@ -76,7 +96,9 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
                                                      float *__restrict__ z,
                                                      uint32_t *__restrict__ xp,
                                                      float *__restrict__ xsw,
-                                                     float *__restrict__ xscale) {
+                                                     float *__restrict__ xscale,
+                                                     uint4 *__restrict__ xq,
+                                                     float *__restrict__ xs) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -129,7 +151,7 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
       if (tt < nt) z[(long long)(t0 + tt) * E + e] = bias ? p[tt] + bias[e] : p[tt];
     }
   }
-  if (xp == nullptr) return;
+  if (xp == nullptr && xq == nullptr) return;
   const int words = d / 8;
   const int gid = e * 64 + lane, stride = E * 64;
 #pragma unroll
@@ -138,6 +160,21 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
     float m = mx[tt];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    const int t = t0 + tt;
+    const float *xt = x + (long long)t * d;
+    if (xq != nullptr) {
+      // decode GEMV input: digit planes of X = rint(x * 30000 / max|x|)
+      const float inv = m > 0.0f ? 30000.0f / m : 0.0f;
+      if (gid == 0) xs[t] = m / 30000.0f;
+      for (int j = gid; j < words; j += stride) {
+        const int b = j >> 2, wq = j & 3;
+        const float4 a = *reinterpret_cast<const float4 *>(xt + b * 32 + 4 * wq);
+        const float4 c = *reinterpret_cast<const float4 *>(xt + b * 32 + 16 + 4 * wq);
+        const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        xq[(long long)t * words + j] = digit_planes8(v, inv);
+      }
+      continue;
+    }
     int ex2 = 0;
     if (m > 0.0f && m <= 3.0e38f) {
       int fe;
@@ -145,9 +182,7 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
       ex2 = max(0, fe - 14);
     }
     const float sc = ldexpf(1.0f, -ex2);
-    const int t = t0 + tt;
     if (gid == 0) xscale[t] = ldexpf(1.0f, ex2);
-    const float *xt = x + (long long)t * d;
     for (int j = gid; j < words; j += stride) {
       const int b = j >> 2, wq = j & 3;
       const float4 a = *reinterpret_cast<const float4 *>(xt + b * 32 + 4 * wq);
@@ -176,29 +211,28 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
 }
 
 hipError_t launch_router(const float *x, int T, int d, const float *W, const float *bias, int E,
-                         float *z, uint32_t *xp, float *xsw, float *xscale, hipStream_t s) {
+                         float *z, uint32_t *xp, float *xsw, float *xscale, uint4 *xq, float *xs,
+                         hipStream_t s) {
   const int gx = (E + 3) / 4;
   if (T <= 1) {
     hipLaunchKernelGGL((router_kernel<1, 32>), dim3(gx, T), dim3(256), 0, s, x, T, d, W, bias, E,
-                       z, xp, xsw, xscale);
+                       z, xp, xsw, xscale, xq, xs);
   } else if (T <= 4) {
     hipLaunchKernelGGL((router_kernel<4, 16>), dim3(gx, 1), dim3(256), 0, s, x, T, d, W, bias, E,
-                       z, xp, xsw, xscale);
+                       z, xp, xsw, xscale, xq, xs);
   } else {
     hipLaunchKernelGGL((router_kernel<8, 8>), dim3(gx, (T + 7) / 8), dim3(256), 0, s, x, T, d, W,
-                       bias, E, z, xp, xsw, xscale);
+                       bias, E, z, xp, xsw, xscale, xq, xs);
   }
   return hipGetLastError();
 }
 
 // ============================================================== top-k + softmax
-// One wave per token; E <= 512, so each lane owns up to 8 logits.
-__global__ __launch_bounds__(64) void topk_kernel(const float *__restrict__ z, int T, int E, int k,
-                                                  int norm_topk, int32_t *__restrict__ idx,
-                                                  float *__restrict__ w, int32_t *h_idx,
-                                                  float *h_w) {
-  const int t = blockIdx.x;
-  const int lane = threadIdx.x;
+// One wave per token; E <= 512, so each lane owns up to 8 logits.  Lane j < k
+// ends with the j-th selection (my_e) and its gating weight (my_w).
+__device__ __forceinline__ void topk_token(const float *__restrict__ z, int t, int E, int k,
+                                           int norm_topk, int &my_e, float &my_w) {
+  const int lane = threadIdx.x & 63;
   float v[8];
   bool ok[8];
 #pragma unroll
@@ -207,7 +241,7 @@ __global__ __launch_bounds__(64) void topk_kernel(const float *__restrict__ z, i
     ok[c] = e < E;
     v[c] = ok[c] ? z[(long long)t * E + e] : 0.0f;
   }
-  int my_e = 0;
+  my_e = 0;
   float my_v = 0.0f;
   for (int j = 0; j < k; ++j) {
     float bv = 0.0f;
@@ -243,20 +277,101 @@ __global__ __launch_bounds__(64) void topk_kernel(const float *__restrict__ z, i
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) denom += __shfl_xor(denom, off, 64);
+  my_w = ex / denom;
+}
+
+__global__ __launch_bounds__(64) void topk_kernel(const float *__restrict__ z, int T, int E, int k,
+                                                  int norm_topk, int32_t *__restrict__ idx,
+                                                  float *__restrict__ w, int32_t *h_idx,
+                                                  float *h_w) {
+  const int t = blockIdx.x, lane = threadIdx.x;
+  int my_e;
+  float my_w;
+  topk_token(z, t, E, k, norm_topk, my_e, my_w);
   if (lane < k) {
     const long long o = (long long)t * k + lane;
-    const float wv = ex / denom;
     idx[o] = my_e;
-    w[o] = wv;
+    w[o] = my_w;
     h_idx[o] = my_e;
-    h_w[o] = wv;
+    h_w[o] = my_w;
   }
+}
+
+// Decode calls (T <= 4 tokens, T*k + shared pairs <= 64): one workgroup, wave t
+// selects token t's experts; then wave 0 maps every pair to its slot through
+// `view` (shared pairs to shared_slot) and lists the buckets: pairs grouped by
+// slot, a bucket per slot in order of its first pair, pairs ascending.
+__global__ __launch_bounds__(256) void topk_decode_kernel(const float *__restrict__ z, int T, int E,
+                                                          int k, int norm_topk,
+                                                          int32_t *__restrict__ idx,
+                                                          float *__restrict__ w, int32_t *h_idx,
+                                                          float *h_w, SlotView view,
+                                                          int shared_slot,
+                                                          int32_t *__restrict__ buckets,
+                                                          int32_t *__restrict__ pair_slot) {
+  __shared__ int sidx[kDecodeMaxPairs];
+  const int t = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int my_e;
+  float my_w;
+  topk_token(z, t, E, k, norm_topk, my_e, my_w);
+  if (lane < k) {
+    const int o = t * k + lane;
+    idx[o] = my_e;
+    w[o] = my_w;
+    h_idx[o] = my_e;
+    h_w[o] = my_w;
+    sidx[o] = my_e;
+  }
+  __syncthreads();
+  if (t != 0) return;
+  const int Pr = T * k;
+  const int P = Pr + (shared_slot >= 0 ? T : 0);
+  int s = -1;
+  if (lane < P) s = lane < Pr ? (int)view.slot[sidx[lane]] : shared_slot;
+  if (lane < Pr) pair_slot[lane] = s;
+  // one pass per distinct slot, in order of its first pair: that pair's lane
+  // leads, the ballot of equal slots gives the bucket's pairs
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint64_t todo = __ballot(s >= 0);
+  int nbk = 0;
+  while (todo) {
+    const int lead = __ffsll((unsigned long long)todo) - 1;
+    const int slot = __builtin_amdgcn_readlane(s, lead);
+    const uint64_t same = __ballot(s == slot);
+    const int cnt = __popcll(same);
+    int32_t *e = buckets + 1 + nbk * kBucketInts;
+    if (s == slot) {
+      const int rank = __popcll(same & below);
+      e[2 + rank] = lane;
+      if (rank == cnt - 1)
+        for (int i = cnt; i < kDecodeMaxTokens; ++i) e[2 + i] = lane;
+      if (rank == 0) {
+        e[0] = slot;
+        e[1] = cnt;
+      }
+    }
+    todo &= ~same;
+    nbk++;
+  }
+  if (lane == 0) buckets[0] = nbk;
 }
 
 hipError_t launch_topk(const float *z, int T, int E, int k, int norm_topk, int32_t *idx, float *w,
                        int32_t *h_idx, float *h_w, hipStream_t s) {
   hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(64), 0, s, z, T, E, k, norm_topk, idx, w, h_idx,
                      h_w);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_decode(const float *z, int T, int E, int k, int norm_topk, int32_t *idx,
+                              float *w, int32_t *h_idx, float *h_w, const SlotView &view,
+                              int shared_slot, int32_t *buckets, int32_t *pair_slot,
+                              hipStream_t s) {
+  if (T < 1 || T > kDecodeMaxTokens ||
+      T * k + (shared_slot >= 0 ? T : 0) > kDecodeMaxPairs)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_decode_kernel, dim3(1), dim3(64 * T), 0, s, z, T, E, k, norm_topk, idx,
+                     w, h_idx, h_w, view, shared_slot, buckets, pair_slot);
   return hipGetLastError();
 }
 
@@ -346,162 +461,43 @@ hipError_t launch_remap(const int32_t *idx, int T, int k, const SlotView &view, 
   return hipGetLastError();
 }
 
-// ============================================================== bucket lookup
-// The (slot, pairs) of bucket b.  With remap metadata it is a table read; on the
-// decode path each wave derives it from the router ids: lane p takes pair p's
-// slot, a pair opens a bucket when no lower pair has its slot, bucket b is the
-// b-th opener, and its pairs are the lanes with the same slot, ascending.
-template <int TT>
-struct Bucket {
-  int slot, off, cnt;
-  int pairs[TT];  // decode path: the bucket's pairs (cnt <= TT)
-  const uint8_t *src;
-};
+// ============================================================== decode GEMV arithmetic
+// Activations enter the decode GEMV as 16-bit fixed point: X = rint(v / s) with
+// s = max|v| / 30000 (per token for x, per 32-element block for h), split into
+// four signed base-16 digits c_0..c_3 in [-8, 7], X = sum_k 16^k c_k.  For
+// X + 0x8888 the digit nibbles are those of ((X + 0x8888) ^ 0x8888), so no
+// carry chain is needed.  A digit plane is laid out like the weights' nibble
+// words: in word j of a block, nibble 2m holds element 4j+m and nibble 2m+1
+// element 4j+m+16.  XOR with 0x88888888 turns a weight word's nibbles q into
+// signed nibbles q - 8, so one v_dot8_i32_i4 per (word, plane) accumulates
+// sum (q - 8) c_k exactly, and the four planes meet with shifts by 4 bits:
+// I = sum_i (q_i - 8) X_i, |I| <= 32 * 8 * 34952 < 2^24, exact in int32 and in
+// its float32 conversion.  A block then contributes d * I (* s for h blocks).
 
-// Modes of a launch: buckets from remap metadata, derived on the device
-// (decode), or given by the host in a BucketTable.
-enum { BK_META = 0, BK_DEVICE = 1, BK_TABLE = 2 };
-
-template <int TT, int MODE>
-__device__ __forceinline__ bool find_bucket(const GemvArgs &a, const SlotView &view,
-                                            const BucketTable &tab, int b, int *sl,
-                                            Bucket<TT> &bk) {
-  if constexpr (MODE == BK_TABLE) {
-    if (b >= tab.n) return false;
-    bk.src = tab.src[b];
-    bk.cnt = tab.cnt[b];
-    bk.off = 0;
-    bk.slot = 0;
-#pragma unroll
-    for (int i = 0; i < TT; ++i) bk.pairs[i] = tab.pairs[b][i < kDecodeMaxTokens ? i : 0];
-    return true;
-  }
-  if constexpr (MODE == BK_META) {
-    if (b >= a.meta[0]) return false;
-    bk.slot = a.meta[2 + b];
-    bk.off = a.meta[2 + kMetaB + b];
-    bk.cnt = a.meta[2 + 2 * kMetaB + b];
-    bk.src = a.slots + (long long)bk.slot * a.rec_bytes;
-    return true;
-  }
-  const int lane = threadIdx.x & 63;
-  const int Pr = a.T * a.k;
-  const int P = Pr + (a.shared_slot >= 0 ? a.T : 0);
-  int s = -1;
-  if (lane < P) s = lane < Pr ? (int)view.slot[a.idx[lane]] : a.shared_slot;
-  sl[lane] = s;
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_s_waitcnt(0);
-  bool first = s >= 0;
-  for (int q = 0; q < lane; ++q)
-    if (sl[q] == s) first = false;
-  uint64_t openers = __ballot(first);
-  if (__popcll(openers) <= b) return false;
-  for (int i = 0; i < b; ++i) openers &= openers - 1;
-  const int L = __ffsll((unsigned long long)openers) - 1;
-  bk.slot = __builtin_amdgcn_readlane(s, L);
-  bk.src = a.slots + (long long)bk.slot * a.rec_bytes;
-  uint64_t same = __ballot(s == bk.slot);
-  bk.cnt = __popcll(same);
-  bk.off = 0;
-  int last = 0;
-#pragma unroll
-  for (int i = 0; i < TT; ++i) {
-    if (same) {
-      last = __ffsll((unsigned long long)same) - 1;
-      same &= same - 1;
-    }
-    bk.pairs[i] = last;
-  }
-  return true;
-}
-
-template <int TT, int MODE>
-__device__ __forceinline__ int bucket_pair_at(const GemvArgs &a, const Bucket<TT> &bk, int i) {
-  if constexpr (MODE == BK_META) return a.bucket_pair[bk.off + i];
-  return bk.pairs[i < TT ? i : TT - 1];
-}
-
-
-
-// ============================================================== Q4 grouped GEMV
-// Workgroup = 4 waves, one slot bucket (blockIdx.y) and a tile of rows
-// (blockIdx.x).  In a wave, G lanes share a row and RG = 64/G rows run side by
-// side; a lane walks its row's units (V consecutive 32-bit nibble words: V = 4 a
-// whole block, V = 2 half a block) and R rows per lane reuse the unit's
-// activations from registers.  The -8 offset of the weights is folded in per
-// unit; partial sums meet across the G lanes with xor shuffles.
-//
-// gate/up (GLU): the K dimension is split over the 4 waves of the workgroup,
-// whose partials meet in LDS in a fixed order.  A nibble word q holds the
-// elements (0,2),(16,18),(1,3),(17,19) of its 4-element group as the low/high
-// nibbles of bytes (0,2) and (1,3); OR-ing each nibble pair into 0x6400 gives two
-// binary16 values 1024 + q, so one v_dot2 against the prepared hi and lo
-// activation pairs accumulates (1024 + q) x in fp32, and 1032 * sum(x) per unit
-// brings it back to (q - 8) x.
-//
-// down: whole K per wave; nibbles become floats with v_cvt_f32_ubyte0..3.
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
-
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
-  return r;
-}
-
-// sum over one word of (1024 + q) * x, x given as hi and lo binary16 pairs
-__device__ __forceinline__ float word_dot_h(uint32_t q, const uint4 &xh, const uint4 &xl,
-                                            float acc) {
-  const uint32_t m = 0x000F000Fu, mag = 0x64006400u;
-  const uint32_t a = and_or(q, m, mag);
-  const uint32_t b = and_or(q >> 4, m, mag);
-  const uint32_t c = and_or(q >> 8, m, mag);
-  const uint32_t d = and_or(q >> 12, m, mag);
-  acc = __builtin_amdgcn_fdot2(as_h2(a), as_h2(xh.x), acc, false);
-  acc = __builtin_amdgcn_fdot2(as_h2(b), as_h2(xh.y), acc, false);
-  acc = __builtin_amdgcn_fdot2(as_h2(c), as_h2(xh.z), acc, false);
-  acc = __builtin_amdgcn_fdot2(as_h2(d), as_h2(xh.w), acc, false);
-  acc = __builtin_amdgcn_fdot2(as_h2(a), as_h2(xl.x), acc, false);
-  acc = __builtin_amdgcn_fdot2(as_h2(b), as_h2(xl.y), acc, false);
-  acc = __builtin_amdgcn_fdot2(as_h2(c), as_h2(xl.z), acc, false);
-  acc = __builtin_amdgcn_fdot2(as_h2(d), as_h2(xl.w), acc, false);
+// sum over one block of (q - 8) * X, X given as digit planes P[word].{x,y,z,w}
+__device__ __forceinline__ int dot_block_i4(const uint4 &w, const uint4 (&P)[4]) {
+  const int w0 = (int)(w.x ^ 0x88888888u), w1 = (int)(w.y ^ 0x88888888u);
+  const int w2 = (int)(w.z ^ 0x88888888u), w3 = (int)(w.w ^ 0x88888888u);
+  int acc = __builtin_amdgcn_sdot8(w0, (int)P[0].w, 0, false);
+  acc = __builtin_amdgcn_sdot8(w1, (int)P[1].w, acc, false);
+  acc = __builtin_amdgcn_sdot8(w2, (int)P[2].w, acc, false);
+  acc = __builtin_amdgcn_sdot8(w3, (int)P[3].w, acc, false);
+  acc <<= 4;
+  acc = __builtin_amdgcn_sdot8(w0, (int)P[0].z, acc, false);
+  acc = __builtin_amdgcn_sdot8(w1, (int)P[1].z, acc, false);
+  acc = __builtin_amdgcn_sdot8(w2, (int)P[2].z, acc, false);
+  acc = __builtin_amdgcn_sdot8(w3, (int)P[3].z, acc, false);
+  acc <<= 4;
+  acc = __builtin_amdgcn_sdot8(w0, (int)P[0].y, acc, false);
+  acc = __builtin_amdgcn_sdot8(w1, (int)P[1].y, acc, false);
+  acc = __builtin_amdgcn_sdot8(w2, (int)P[2].y, acc, false);
+  acc = __builtin_amdgcn_sdot8(w3, (int)P[3].y, acc, false);
+  acc <<= 4;
+  acc = __builtin_amdgcn_sdot8(w0, (int)P[0].x, acc, false);
+  acc = __builtin_amdgcn_sdot8(w1, (int)P[1].x, acc, false);
+  acc = __builtin_amdgcn_sdot8(w2, (int)P[2].x, acc, false);
+  acc = __builtin_amdgcn_sdot8(w3, (int)P[3].x, acc, false);
   return acc;
-}
-
-// sum over one word of q * x in fp32 (x: elements 0..3 and 16..19 of the group)
-__device__ __forceinline__ float word_dot_f(uint32_t q, const float4 &xl, const float4 &xh,
-                                            float acc) {
-  uint32_t lo = q & 0x0F0F0F0Fu;
-  uint32_t hi = (q >> 4) & 0x0F0F0F0Fu;
-  // hide the known-zero high nibbles so each byte converts with one v_cvt_f32_ubyteN
-  asm volatile("" : "+v"(lo), "+v"(hi));
-  acc += (float)(lo & 0xFFu) * xl.x;
-  acc += (float)((lo >> 8) & 0xFFu) * xl.y;
-  acc += (float)((lo >> 16) & 0xFFu) * xl.z;
-  acc += (float)(lo >> 24) * xl.w;
-  acc += (float)(hi & 0xFFu) * xh.x;
-  acc += (float)((hi >> 8) & 0xFFu) * xh.y;
-  acc += (float)((hi >> 16) & 0xFFu) * xh.z;
-  acc += (float)(hi >> 24) * xh.w;
-  return acc;
-}
-
-template <int V>
-__device__ __forceinline__ void load_words(const uint32_t *p, uint32_t (&q)[V]) {
-  if constexpr (V == 4) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(p);
-    q[0] = v.x;
-    q[1] = v.y;
-    q[2] = v.z;
-    q[3] = v.w;
-  } else {
-    const uint2 v = *reinterpret_cast<const uint2 *>(p);
-    q[0] = v.x;
-    q[1] = v.y;
-  }
 }
 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + expf(-v)); }
@@ -510,357 +506,443 @@ __device__ __forceinline__ int pair_row(const GemvArgs &a, int p) {
   return p < a.T * a.k ? p / a.k : p - a.T * a.k;
 }
 
-template <int G, int V, int TT, int R, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8)))
-void q4_gateup_kernel(GemvArgs a, SlotView view, BucketTable tab) {
-  constexpr int RG = 64 / G;
-  constexpr int KS = 4;
-  __shared__ float red[KS][R * RG][TT][2];
-  __shared__ int sl[4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  Bucket<TT> bk;
-  if (!find_bucket<TT, MODE>(a, view, tab, blockIdx.y, sl[wave], bk)) return;
-  const uint8_t *rec = bk.src;
-  const int grp = lane / G, gl = lane % G;
-  const int row0 = blockIdx.x * (R * RG) + grp;
-  const int row_words = a.nb * 4;
-  const int units = row_words / V;
-  const int words_x = a.nb * 4;  // words per activation row
-  // rows past the end read the last row and are never written
-  const uint32_t *qg[R];
-  const uint32_t *qu[R];
-  const __half *sg[R];
-  const __half *su[R];
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const long long r = min(row0 + i * RG, a.rows - 1);
-    qg[i] = reinterpret_cast<const uint32_t *>(rec + a.off_q0) + r * row_words;
-    qu[i] = reinterpret_cast<const uint32_t *>(rec + a.off_q1) + r * row_words;
-    sg[i] = reinterpret_cast<const __half *>(rec + a.off_s0) + r * a.nb;
-    su[i] = reinterpret_cast<const __half *>(rec + a.off_s1) + r * a.nb;
-  }
+// ============================================================== bucket lookup
+// The expert record and pairs of bucket b on the decode path, from the list the
+// decode top-k kernel wrote (BK_LIST; workgroup-uniform, so scalar loads) or
+// from a host-built table passed by value (BK_TABLE).  pairs[i] for i >= cnt
+// repeats the last pair.
+template <int TT>
+struct Bucket {
+  int cnt;
+  int pairs[TT];
+  const uint8_t *src;
+};
 
-  for (int tg = 0; tg < bk.cnt; tg += TT) {
-    const int nt = min(TT, bk.cnt - tg);
-    int prs[TT], tok[TT];
+enum { BK_LIST = 1, BK_TABLE = 2 };
+
+// a[i] for a runtime i without indexing a register array (no scratch)
+template <int N>
+__device__ __forceinline__ int pick(const int (&a)[N], int i) {
+  int r = a[0];
+#pragma unroll
+  for (int q = 1; q < N; ++q) r = i == q ? a[q] : r;
+  return r;
+}
+
+template <int TT, int MODE>
+__device__ __forceinline__ bool find_bucket(const GemvArgs &a, const BucketTable &tab, int b,
+                                            Bucket<TT> &bk) {
+  if constexpr (MODE == BK_TABLE) {
+    if (b >= tab.n) return false;
+    bk.src = tab.src[b];
+    bk.cnt = tab.cnt[b];
+#pragma unroll
+    for (int i = 0; i < TT; ++i) bk.pairs[i] = tab.pairs[b][min(i, bk.cnt - 1)];
+    return true;
+  }
+  if (b >= a.bt[0]) return false;
+  const int32_t *e = a.bt + 1 + b * kBucketInts;
+  bk.src = a.slots + (long long)e[0] * a.rec_bytes;
+  bk.cnt = e[1];
+#pragma unroll
+  for (int i = 0; i < TT; ++i) bk.pairs[i] = e[2 + i];
+  return true;
+}
+
+// ============================================================== decode Q4 GEMV
+// Workgroup = 4 waves, one bucket (blockIdx.y) and a tile of rows (blockIdx.x).
+// G lanes share a row, RW = 64/G rows side by side, R row steps per lane; the
+// K blocks of a row are split over KS waves (block j = gl + G*(ks + KS*it)), so a
+// wave instruction reads G consecutive 16-byte nibble blocks of each of RW rows.
+// The bucket's activation planes (x for gate/up, h for down, up to TT tokens)
+// sit in LDS; their global loads are issued before the weight loads, so waiting
+// for them never waits for HBM.  The next step's weights are loaded before the
+// current step is multiplied.  Partial sums meet across the G lanes with xor
+// shuffles and across the KS waves in LDS, in a fixed order.
+constexpr int kStageChunks = 4;  // 16-byte staging chunks per thread and round
+
+template <int G, int KS, int R, int TT, int MODE>
+__global__ __launch_bounds__(256) void q4_gateup_kernel(GemvArgs a, BucketTable tab) {
+  constexpr int RW = 64 / G;
+  constexpr int RWG = (4 / KS) * RW * R;
+  extern __shared__ uint4 sx[];  // [TT][nb][4]
+  __shared__ float red[4][RW * R][TT][2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ks = wave % KS, rg = wave / KS;
+  Bucket<TT> bk;
+  if (!find_bucket<TT, MODE>(a, tab, blockIdx.y, bk)) return;
+  const uint8_t *rec = bk.src;
+  const int nb = a.nb;
+  const int gl = lane % G;
+  const int rbase = blockIdx.x * RWG + rg * RW * R + lane / G;
+  const uint4 *q0 = reinterpret_cast<const uint4 *>(rec + a.off_q0);
+  const uint4 *q1 = reinterpret_cast<const uint4 *>(rec + a.off_q1);
+  const _Float16 *s0 = reinterpret_cast<const _Float16 *>(rec + a.off_s0);
+  const _Float16 *s1 = reinterpret_cast<const _Float16 *>(rec + a.off_s1);
+  int tok[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) tok[tt] = pair_row(a, bk.pairs[tt]);
+  // rows past the end read the last row and are never written
+  long long ro[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) ro[i] = (long long)min(rbase + RW * i, a.rows - 1) * nb;
+  const int NI = (nb + G * KS - 1) / (G * KS);
+  auto blk_of = [&](int it) { return min(gl + G * (ks + KS * it), nb - 1); };
+  const int n_stage = TT * nb * 4;
+  auto stage_ld = [&](int u) -> uint4 {
+    u = min(u, n_stage - 1);
+    const int tt = u / (nb * 4);
+    return a.xq[(long long)pick(tok, tt) * nb * 4 + (u - tt * nb * 4)];
+  };
+  auto stage_st = [&](int u, const uint4 &v) {
+    if (u < n_stage) sx[u] = v;
+  };
+  static_assert(kStageChunks == 4, "staging is written out for 4 chunks");
+  const int tid = threadIdx.x;
+  uint4 xv0 = stage_ld(tid), xv1 = stage_ld(tid + 256), xv2 = stage_ld(tid + 512),
+        xv3 = stage_ld(tid + 768);
+  // keep the weight loads behind the activation loads
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 wg[R], wu[R];
+  _Float16 cg[R], cu[R];
+  {
+    const int j = blk_of(0);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      wg[i] = q0[ro[i] + j];
+      wu[i] = q1[ro[i] + j];
+      cg[i] = s0[ro[i] + j];
+      cu[i] = s1[ro[i] + j];
+    }
+  }
+  stage_st(tid, xv0);
+  stage_st(tid + 256, xv1);
+  stage_st(tid + 512, xv2);
+  stage_st(tid + 768, xv3);
+  for (int u0 = 1024; u0 < n_stage; u0 += 1024) {
+    xv0 = stage_ld(u0 + tid);
+    xv1 = stage_ld(u0 + tid + 256);
+    xv2 = stage_ld(u0 + tid + 512);
+    xv3 = stage_ld(u0 + tid + 768);
+    stage_st(u0 + tid, xv0);
+    stage_st(u0 + tid + 256, xv1);
+    stage_st(u0 + tid + 512, xv2);
+    stage_st(u0 + tid + 768, xv3);
+  }
+  __syncthreads();
+  float ag[R][TT], au[R][TT];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-      prs[tt] = bucket_pair_at<TT, MODE>(a, bk, tg + min(tt, nt - 1));
-      tok[tt] = pair_row(a, prs[tt]);
+      ag[i][tt] = 0.0f;
+      au[i][tt] = 0.0f;
     }
-    float ag[R][TT], au[R][TT];
+  for (int it = 0; it < NI; ++it) {
+    const int j0 = gl + G * (ks + KS * it);
+    const bool ok = j0 < nb;
+    const int j = min(j0, nb - 1);
+    uint4 cw[R], cv[R];
+    float dg[R], du[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      cw[i] = wg[i];
+      cv[i] = wu[i];
+      dg[i] = ok ? (float)cg[i] : 0.0f;
+      du[i] = ok ? (float)cu[i] : 0.0f;
+    }
+    if (it + 1 < NI) {
+      const int jn = blk_of(it + 1);
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        wg[i] = q0[ro[i] + jn];
+        wu[i] = q1[ro[i] + jn];
+        cg[i] = s0[ro[i] + jn];
+        cu[i] = s1[ro[i] + jn];
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      uint4 P[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) P[w] = sx[(tt * nb + j) * 4 + w];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        ag[i][tt] = __builtin_fmaf((float)dot_block_i4(cw[i], P), dg[i], ag[i][tt]);
+        au[i][tt] = __builtin_fmaf((float)dot_block_i4(cv[i], P), du[i], au[i][tt]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+#pragma unroll
+      for (int o = G / 2; o >= 1; o >>= 1) {
+        ag[i][tt] += __shfl_xor(ag[i][tt], o, 64);
+        au[i][tt] += __shfl_xor(au[i][tt], o, 64);
+      }
+    }
+  if (gl == 0) {
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        ag[i][tt] = 0.0f;
-        au[i][tt] = 0.0f;
+        red[wave][lane / G + RW * i][tt][0] = ag[i][tt];
+        red[wave][lane / G + RW * i][tt][1] = au[i][tt];
       }
-    for (int u = gl + G * wave; u < units; u += G * KS) {
-      const int w0 = u * V;
-      const int blk = w0 >> 2;
-      uint4 xh[TT][V], xl[TT][V];
-      float xs[TT];
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < (4 / KS) * RW * R * TT; o += 256) {
+    const int g = o / (RW * R * TT), rr = (o / TT) % (RW * R), tt = o % TT;
+    const int r = blockIdx.x * RWG + g * RW * R + rr;
+    if (r < a.rows && tt < bk.cnt) {
+      float gg = 0.0f, uu = 0.0f;
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        const uint4 *xq =
-            reinterpret_cast<const uint4 *>(a.xp + ((long long)tok[tt] * words_x + w0) * 8);
-        const float *xw = a.xsw + (long long)tok[tt] * words_x + w0;
-        xs[tt] = 0.0f;
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-          xh[tt][v] = xq[2 * v];
-          xl[tt][v] = xq[2 * v + 1];
-          xs[tt] += xw[v];
-        }
+      for (int q = 0; q < KS; ++q) {
+        gg += red[g * KS + q][rr][tt][0];
+        uu += red[g * KS + q][rr][tt][1];
       }
-      uint32_t q0[R][V], q1[R][V];
-      float s0[R], s1[R];
+      const float sc = a.xs[pick(tok, tt)];
+      a.out[(long long)pick(bk.pairs, tt) * a.rows + r] = silu_f(gg * sc) * (uu * sc);
+    }
+  }
+}
+
+// down: y = D h.  The prologue turns the bucket's h rows (fp32, by pair) into
+// digit planes with one scale per 32-element block (thread = one word of one
+// block; the block's four threads share its max through two xor shuffles).
+template <int G, int KS, int R, int TT, int MODE>
+__global__ __launch_bounds__(256) void q4_down_kernel(GemvArgs a, BucketTable tab) {
+  constexpr int RW = 64 / G;
+  constexpr int RWG = (4 / KS) * RW * R;
+  constexpr int HC = 2;  // prologue units per thread and round
+  extern __shared__ uint4 sh[];  // [TT][nb][4] planes, then [TT][nb] block scales
+  __shared__ float red[4][RW * R][TT];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ks = wave % KS, rg = wave / KS;
+  Bucket<TT> bk;
+  if (!find_bucket<TT, MODE>(a, tab, blockIdx.y, bk)) return;
+  const uint8_t *rec = bk.src;
+  const int nb = a.nb;
+  float *sscale = reinterpret_cast<float *>(sh + TT * nb * 4);
+  const int gl = lane % G;
+  const int rbase = blockIdx.x * RWG + rg * RW * R + lane / G;
+  const uint4 *q0 = reinterpret_cast<const uint4 *>(rec + a.off_q0);
+  const _Float16 *s0 = reinterpret_cast<const _Float16 *>(rec + a.off_s0);
+  long long ro[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) ro[i] = (long long)min(rbase + RW * i, a.rows - 1) * nb;
+  const int NI = (nb + G * KS - 1) / (G * KS);
+  auto blk_of = [&](int it) { return min(gl + G * (ks + KS * it), nb - 1); };
+  const int n_units = TT * nb * 4;
+  auto load_units = [&](int u0, float4 (&v0)[HC], float4 (&v1)[HC]) {
+#pragma unroll
+    for (int c = 0; c < HC; ++c) {
+      const int u = min(u0 + (int)threadIdx.x + 256 * c, n_units - 1);
+      const int tt = u / (nb * 4), rem = u - tt * nb * 4;
+      const int b = rem >> 2, j = rem & 3;
+      const float *hr = a.in + (long long)pick(bk.pairs, tt) * nb * 32 + b * 32 + 4 * j;
+      v0[c] = *reinterpret_cast<const float4 *>(hr);
+      v1[c] = *reinterpret_cast<const float4 *>(hr + 16);
+    }
+  };
+  float4 hv0[HC], hv1[HC];
+  load_units(0, hv0, hv1);
+  // keep the weight loads behind the h loads
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 wd[R];
+  _Float16 cd[R];
+  {
+    const int j = blk_of(0);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      wd[i] = q0[ro[i] + j];
+      cd[i] = s0[ro[i] + j];
+    }
+  }
+  auto put_units = [&](int u0, const float4 (&v0)[HC], const float4 (&v1)[HC]) {
+#pragma unroll
+    for (int c = 0; c < HC; ++c) {
+      const int u = u0 + threadIdx.x + 256 * c;
+      if (u0 + 256 * c >= n_units) break;  // uniform
+      const float v[8] = {v0[c].x, v0[c].y, v0[c].z, v0[c].w, v1[c].x, v1[c].y, v1[c].z, v1[c].w};
+      float m = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      m = fmaxf(m, __shfl_xor(m, 2, 64));
+      const float inv = m > 0.0f ? 30000.0f / m : 0.0f;
+      const uint4 pl = digit_planes8(v, inv);
+      if (u < n_units) {
+        sh[u] = pl;
+        if ((u & 3) == 0) sscale[u >> 2] = m / 30000.0f;
+      }
+    }
+  };
+  put_units(0, hv0, hv1);
+  for (int u0 = 256 * HC; u0 < n_units; u0 += 256 * HC) {
+    float4 gv0[HC], gv1[HC];
+    load_units(u0, gv0, gv1);
+    put_units(u0, gv0, gv1);
+  }
+  __syncthreads();
+  float ac[R][TT];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) ac[i][tt] = 0.0f;
+  for (int it = 0; it < NI; ++it) {
+    const int j0 = gl + G * (ks + KS * it);
+    const bool ok = j0 < nb;
+    const int j = min(j0, nb - 1);
+    uint4 cw[R];
+    float dd[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      cw[i] = wd[i];
+      dd[i] = ok ? (float)cd[i] : 0.0f;
+    }
+    if (it + 1 < NI) {
+      const int jn = blk_of(it + 1);
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        load_words<V>(qg[i] + w0, q0[i]);
-        load_words<V>(qu[i] + w0, q1[i]);
-        s0[i] = __half2float(sg[i][blk]);
-        s1[i] = __half2float(su[i][blk]);
-      }
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          float d0 = -1032.0f * xs[tt], d1 = -1032.0f * xs[tt];
-#pragma unroll
-          for (int v = 0; v < V; ++v) {
-            d0 = word_dot_h(q0[i][v], xh[tt][v], xl[tt][v], d0);
-            d1 = word_dot_h(q1[i][v], xh[tt][v], xl[tt][v], d1);
-          }
-          ag[i][tt] += s0[i] * d0;
-          au[i][tt] += s1[i] * d1;
-        }
+        wd[i] = q0[ro[i] + jn];
+        cd[i] = s0[ro[i] + jn];
       }
     }
 #pragma unroll
-    for (int i = 0; i < R; ++i)
+    for (int tt = 0; tt < TT; ++tt) {
+      uint4 P[4];
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-#pragma unroll
-        for (int o = G / 2; o >= 1; o >>= 1) {
-          ag[i][tt] += __shfl_xor(ag[i][tt], o, 64);
-          au[i][tt] += __shfl_xor(au[i][tt], o, 64);
-        }
-      }
-    if (gl == 0) {
+      for (int w = 0; w < 4; ++w) P[w] = sh[(tt * nb + j) * 4 + w];
+      const float se = sscale[tt * nb + j];
 #pragma unroll
       for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          red[wave][i * RG + grp][tt][0] = ag[i][tt];
-          red[wave][i * RG + grp][tt][1] = au[i][tt];
-        }
+        ac[i][tt] = __builtin_fmaf((float)dot_block_i4(cw[i], P) * se, dd[i], ac[i][tt]);
     }
-    __syncthreads();
-    for (int o = threadIdx.x; o < R * RG * TT; o += 256) {
-      const int rr = o / TT, tt = o % TT;
-      const int r = blockIdx.x * (R * RG) + rr;
-      if (r < a.rows && tt < nt) {
-        const float sc = a.xscale[tok[tt]];
-        const float g = (((red[0][rr][tt][0] + red[1][rr][tt][0]) + red[2][rr][tt][0]) +
-                         red[3][rr][tt][0]) * sc;
-        const float uu = (((red[0][rr][tt][1] + red[1][rr][tt][1]) + red[2][rr][tt][1]) +
-                          red[3][rr][tt][1]) * sc;
-        a.out[(long long)prs[tt] * a.rows + r] = silu_f(g) * uu;
-      }
-    }
-    __syncthreads();
   }
-}
-
-template <int G, int V, int TT, int R, int MODE, int KS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8)))
-void q4_down_kernel(GemvArgs a, SlotView view, BucketTable tab) {
-  constexpr int RG = 64 / G;
-  constexpr int ROWS_WAVE = R * RG;
-  constexpr int NRG = 4 / KS;  // row groups per workgroup; KS waves share a row group's K
-  __shared__ int sl[4][64];
-  __shared__ float red[KS > 1 ? 4 : 1][ROWS_WAVE][TT];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int kslice = wave % KS, rgrp = wave / KS;
-  Bucket<TT> bk;
-  if (!find_bucket<TT, MODE>(a, view, tab, blockIdx.y, sl[wave], bk)) return;
-  const uint8_t *rec = bk.src;
-  const int grp = lane / G, gl = lane % G;
-  const int row0 = (blockIdx.x * NRG + rgrp) * ROWS_WAVE + grp;
-  const int row_words = a.nb * 4;
-  const int units = row_words / V;
-  const int K = a.nb * 32;
-  const uint32_t *qr[R];
-  const __half *sr[R];
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const long long r = min(row0 + i * RG, a.rows - 1);
-    qr[i] = reinterpret_cast<const uint32_t *>(rec + a.off_q0) + r * row_words;
-    sr[i] = reinterpret_cast<const __half *>(rec + a.off_s0) + r * a.nb;
-  }
-
-  for (int tg = 0; tg < bk.cnt; tg += TT) {
-    const int nt = min(TT, bk.cnt - tg);
-    const float *xin[TT];
-    int prs[TT];
+  for (int i = 0; i < R; ++i)
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-      const int p = bucket_pair_at<TT, MODE>(a, bk, tg + min(tt, nt - 1));
-      prs[tt] = p;
-      xin[tt] = a.in + (long long)(a.in_by_pair ? p : pair_row(a, p)) * K;
+#pragma unroll
+      for (int o = G / 2; o >= 1; o >>= 1) ac[i][tt] += __shfl_xor(ac[i][tt], o, 64);
     }
-    float acc[R][TT];
+  if (gl == 0) {
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) acc[i][tt] = 0.0f;
-    for (int u = gl + G * kslice; u < units; u += G * KS) {
-      const int w0 = u * V;
-      const int blk = w0 >> 2;
-      float4 xl[TT][V], xh[TT][V];
-      float xs[TT];
+      for (int tt = 0; tt < TT; ++tt) red[wave][lane / G + RW * i][tt] = ac[i][tt];
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < (4 / KS) * RW * R * TT; o += 256) {
+    const int g = o / (RW * R * TT), rr = (o / TT) % (RW * R), tt = o % TT;
+    const int r = blockIdx.x * RWG + g * RW * R + rr;
+    if (r < a.rows && tt < bk.cnt) {
+      float v = 0.0f;
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        xs[tt] = 0.0f;
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-          const int wb = (w0 + v) & 3;
-          const float *xq = xin[tt] + blk * 32 + 4 * wb;
-          xl[tt][v] = *reinterpret_cast<const float4 *>(xq);
-          xh[tt][v] = *reinterpret_cast<const float4 *>(xq + 16);
-          xs[tt] += ((xl[tt][v].x + xl[tt][v].y) + (xl[tt][v].z + xl[tt][v].w)) +
-                    ((xh[tt][v].x + xh[tt][v].y) + (xh[tt][v].z + xh[tt][v].w));
-        }
-      }
-      uint32_t q0[R][V];
-      float sc0[R];
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        load_words<V>(qr[i] + w0, q0[i]);
-        sc0[i] = __half2float(sr[i][blk]);
-      }
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          float d0 = -8.0f * xs[tt];
-#pragma unroll
-          for (int v = 0; v < V; ++v) d0 = word_dot_f(q0[i][v], xl[tt][v], xh[tt][v], d0);
-          acc[i][tt] += sc0[i] * d0;
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-#pragma unroll
-        for (int o = G / 2; o >= 1; o >>= 1) acc[i][tt] += __shfl_xor(acc[i][tt], o, 64);
-      }
-    if constexpr (KS == 1) {
-      if (gl == 0) {
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const int r = row0 + i * RG;
-          if (r < a.rows) {
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt)
-              if (tt < nt) a.out[(long long)prs[tt] * a.rows + r] = acc[i][tt];
-          }
-        }
-      }
-    } else {
-      // the KS waves of a row group meet in LDS, summed in wave order
-      if (gl == 0) {
-#pragma unroll
-        for (int i = 0; i < R; ++i)
-#pragma unroll
-          for (int tt = 0; tt < TT; ++tt) red[wave][i * RG + grp][tt] = acc[i][tt];
-      }
-      __syncthreads();
-      for (int o = threadIdx.x; o < NRG * ROWS_WAVE * TT; o += 256) {
-        const int g = o / (ROWS_WAVE * TT), rr = (o / TT) % ROWS_WAVE, tt = o % TT;
-        const int r = (blockIdx.x * NRG + g) * ROWS_WAVE + rr;
-        if (r < a.rows && tt < nt) {
-          float v = 0.0f;
-#pragma unroll
-          for (int q = 0; q < KS; ++q) v += red[g * KS + q][rr][tt];
-          a.out[(long long)prs[tt] * a.rows + r] = v;
-        }
-      }
-      __syncthreads();
+      for (int q = 0; q < KS; ++q) v += red[g * KS + q][rr][tt];
+      a.out[(long long)pick(bk.pairs, tt) * a.rows + r] = v;
     }
   }
 }
 
-// Shapes measured on MI355X (cold Infinity Cache) over the decode shapes
-// d x f = 6144 x 2048, 2816 x 704, 2048 x 768 with 8 experts: half-block units
-// (V = 2) always beat whole blocks; gate/up runs best with 32 lanes per row and
-// 4 rows per lane; down with 16 lanes per row and 4 rows per lane, its K split
-// over the workgroup's waves only when the grid is small.  Fewer rows per lane
-// when the grid would otherwise leave the chip idle.
-GemvShape choose_gemv(bool glu, int rows, int nb, int n_buckets, int max_tokens) {
-  GemvShape sh{16, 2, 1, 1, 1};
-  const int units = nb * 2;  // half-block units per row
+// Shapes measured on MI355X for one token per bucket over the decode shapes
+// d x f = 6144 x 2048 and 2816 x 704: gate/up rows of >= 128 blocks run best
+// with 16 lanes per row, shorter ones with 8, K split over the 4 waves, 2 rows
+// per lane; down rows of >= 64 blocks with 16 lanes per row, whole K per wave
+// and 4 rows per lane, shorter ones with 8 lanes and K over 4 waves.  Rows of
+// fewer than 32 gate/up blocks keep K in one wave.
+GemvShape choose_gemv(bool glu, int nb, int tokens) {
+  GemvShape sh{};
+  sh.TT = tokens <= 1 ? 1 : (tokens <= 2 ? 2 : 4);
   if (glu) {
-    sh.KS = 4;
-    sh.G = units >= 128 ? 32 : 16;
+    sh.R = 2;
+    if (nb >= 128) {
+      sh.G = 16;
+      sh.KS = 4;
+    } else if (nb >= 32) {
+      sh.G = 8;
+      sh.KS = 4;
+    } else {
+      sh.G = 8;
+      sh.KS = 1;
+    }
   } else {
-    sh.KS = (long long)rows * n_buckets <= 16384 ? 4 : 1;
-    sh.G = 16;
-  }
-  sh.TT = max_tokens <= 1 ? 1 : (max_tokens <= 2 ? 2 : 4);
-  const int RG = 64 / sh.G;
-  const int rows_wg_per_r = (4 / sh.KS) * RG;
-  sh.R = 1;
-  const int rs[2] = {4, 2};
-  for (int ri = 0; ri < 2; ++ri) {
-    const int R = rs[ri];
-    const long long waves =
-        4LL * n_buckets * ((rows + R * rows_wg_per_r - 1) / (R * rows_wg_per_r));
-    if (waves >= 512) {
-      sh.R = R;
-      break;
+    sh.R = 4;
+    if (nb >= 64) {
+      sh.G = 16;
+      sh.KS = 1;
+    } else {
+      sh.G = 8;
+      sh.KS = 4;
     }
   }
+  sh.rows_wg = (4 / sh.KS) * (64 / sh.G) * sh.R;
   return sh;
 }
 
-struct LaunchCtx {
-  const GemvArgs *a;
-  const SlotView *view;
-  const BucketTable *tab;
-  bool glu;
-  int nbk;
-  hipStream_t s;
-  int ks;
-};
+size_t gemv_lds_bytes(bool glu, int nb, int tokens) {
+  const int TT = tokens <= 1 ? 1 : (tokens <= 2 ? 2 : 4);
+  return glu ? (size_t)TT * nb * 64 : (size_t)TT * nb * 68;
+}
 
-template <int G, int V, int TT, int R, int MODE>
-static hipError_t launch_one(const LaunchCtx &c) {
-  constexpr int RG = 64 / G;
-  const GemvArgs &a = *c.a;
-  if (c.glu) {
-    const dim3 grid((a.rows + R * RG - 1) / (R * RG), c.nbk);
-    hipLaunchKernelGGL((q4_gateup_kernel<G, V, TT, R, MODE>), grid, dim3(256), 0, c.s, a, *c.view,
-                       *c.tab);
-  } else if (c.ks == 4) {
-    constexpr int rows_blk = R * RG;
-    const dim3 grid((a.rows + rows_blk - 1) / rows_blk, c.nbk);
-    hipLaunchKernelGGL((q4_down_kernel<G, V, TT, R, MODE, 4>), grid, dim3(256), 0, c.s, a,
-                       *c.view, *c.tab);
-  } else {
-    constexpr int rows_blk = 4 * R * RG;
-    const dim3 grid((a.rows + rows_blk - 1) / rows_blk, c.nbk);
-    hipLaunchKernelGGL((q4_down_kernel<G, V, TT, R, MODE, 1>), grid, dim3(256), 0, c.s, a,
-                       *c.view, *c.tab);
+template <bool GLU, int G, int KS, int R, int TT, int MODE>
+static void launch_one(const GemvArgs &a, const BucketTable &tab, int nbk, size_t lds,
+                       hipStream_t s) {
+  constexpr int RWG = (4 / KS) * (64 / G) * R;
+  const dim3 grid((a.rows + RWG - 1) / RWG, nbk);
+  if constexpr (GLU)
+    hipLaunchKernelGGL((q4_gateup_kernel<G, KS, R, TT, MODE>), grid, dim3(256), lds, s, a, tab);
+  else
+    hipLaunchKernelGGL((q4_down_kernel<G, KS, R, TT, MODE>), grid, dim3(256), lds, s, a, tab);
+}
+
+template <bool GLU, int G, int KS, int R>
+static void launch_tt(const GemvArgs &a, const BucketTable &tab, int nbk, int TT, size_t lds,
+                      hipStream_t s) {
+  const bool t = tab.n >= 0;
+  switch (TT) {
+    case 1:
+      t ? launch_one<GLU, G, KS, R, 1, BK_TABLE>(a, tab, nbk, lds, s)
+        : launch_one<GLU, G, KS, R, 1, BK_LIST>(a, tab, nbk, lds, s);
+      break;
+    case 2:
+      t ? launch_one<GLU, G, KS, R, 2, BK_TABLE>(a, tab, nbk, lds, s)
+        : launch_one<GLU, G, KS, R, 2, BK_LIST>(a, tab, nbk, lds, s);
+      break;
+    default:
+      t ? launch_one<GLU, G, KS, R, 4, BK_TABLE>(a, tab, nbk, lds, s)
+        : launch_one<GLU, G, KS, R, 4, BK_LIST>(a, tab, nbk, lds, s);
+      break;
+  }
+}
+
+hipError_t launch_gemv(const GemvArgs &a, const BucketTable *tab, const GemvShape &sh, bool glu,
+                       int n_buckets, hipStream_t s) {
+  if (n_buckets <= 0) return hipSuccess;
+  if (!tab && !a.bt) return hipErrorInvalidValue;
+  BucketTable none;
+  none.n = -1;
+  const BucketTable &t = tab ? *tab : none;
+  const size_t lds = gemv_lds_bytes(glu, a.nb, sh.TT);
+  const int key = (glu ? 1000 : 0) + sh.G * 100 + sh.KS * 10 + sh.R;
+  switch (key) {
+    case 1000 + 1600 + 40 + 2: launch_tt<true, 16, 4, 2>(a, t, n_buckets, sh.TT, lds, s); break;
+    case 1000 + 800 + 40 + 2: launch_tt<true, 8, 4, 2>(a, t, n_buckets, sh.TT, lds, s); break;
+    case 1000 + 800 + 10 + 2: launch_tt<true, 8, 1, 2>(a, t, n_buckets, sh.TT, lds, s); break;
+    case 1600 + 10 + 4: launch_tt<false, 16, 1, 4>(a, t, n_buckets, sh.TT, lds, s); break;
+    case 800 + 40 + 4: launch_tt<false, 8, 4, 4>(a, t, n_buckets, sh.TT, lds, s); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int G, int V, int TT, int R>
-static hipError_t launch_m(const LaunchCtx &c) {
-  if (c.tab->n >= 0) return launch_one<G, V, TT, R, BK_TABLE>(c);
-  if (c.a->meta != nullptr) return launch_one<G, V, TT, R, BK_META>(c);
-  return launch_one<G, V, TT, R, BK_DEVICE>(c);
-}
-
-template <int G, int V, int TT>
-static hipError_t launch_r(const LaunchCtx &c, int R) {
-  switch (R) {
-    case 4: return launch_m<G, V, TT, 4>(c);
-    case 2: return launch_m<G, V, TT, 2>(c);
-    default: return launch_m<G, V, TT, 1>(c);
-  }
-}
-
-template <int G, int V>
-static hipError_t launch_t(const LaunchCtx &c, const GemvShape &sh) {
-  switch (sh.TT) {
-    case 1: return launch_r<G, V, 1>(c, sh.R);
-    case 2: return launch_r<G, V, 2>(c, sh.R);
-    default: return launch_r<G, V, 4>(c, sh.R);
-  }
-}
-
-template <int G>
-static hipError_t launch_v(const LaunchCtx &c, const GemvShape &sh) {
-  return sh.V == 4 ? launch_t<G, 4>(c, sh) : launch_t<G, 2>(c, sh);
-}
-
-hipError_t launch_gemv(const GemvArgs &a, const SlotView &view, const BucketTable *tab,
-                       const GemvShape &sh, bool glu, int n_buckets, hipStream_t s) {
-  if (n_buckets <= 0) return hipSuccess;
-  BucketTable none;
-  none.n = -1;
-  const LaunchCtx c{&a, &view, tab ? tab : &none, glu, n_buckets, s, sh.KS};
-  switch (sh.G) {
-    case 64: return launch_v<64>(c, sh);
-    case 32: return launch_v<32>(c, sh);
-    default: return launch_v<16>(c, sh);
-  }
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
 }
 
 // ============================================================== prefill MFMA GEMM
@@ -1167,11 +1249,17 @@ hipError_t launch_pull(const PullList &l, hipStream_t s) {
 }
 
 // ============================================================== combine
+// out[t] = sum_j [pair on GPU] w * y (j ascending) + shared + host part.  A pair
+// is on the GPU when all_gpu, else when pair_slot[p] >= 0 (decode: the decode
+// top-k kernel's table), else when view.slot[idx[p]] >= 0.  The loads of 8
+// pairs are issued together; pairs off the GPU are skipped by select, since
+// their y rows were never written.
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y,
                                                       const float *__restrict__ w,
                                                       const int32_t *__restrict__ idx,
-                                                      SlotView view, int all_gpu, int T, int k,
-                                                      int d, int n_shared,
+                                                      SlotView view, int all_gpu,
+                                                      const int32_t *__restrict__ pair_slot,
+                                                      int T, int k, int d, int n_shared,
                                                       const float *__restrict__ host_part,
                                                       float *__restrict__ out,
                                                       float *__restrict__ dbg_gpu) {
@@ -1179,15 +1267,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= d) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const long long p = (long long)t * k + j;
-    if (all_gpu || view.slot[idx[p]] >= 0) {
-      const float wv = w[p];
-      const float4 yv = *reinterpret_cast<const float4 *>(y + p * d + i);
-      acc.x += wv * yv.x;
-      acc.y += wv * yv.y;
-      acc.z += wv * yv.z;
-      acc.w += wv * yv.w;
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    float4 yv[8];
+    float wv[8];
+    bool on[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = min(j0 + u, k - 1);
+      const long long p = (long long)t * k + j;
+      bool g = j0 + u < k;
+      if (g && !all_gpu) g = pair_slot ? pair_slot[p] >= 0 : view.slot[idx[p]] >= 0;
+      on[u] = g;
+      wv[u] = w[p];
+      yv[u] = *reinterpret_cast<const float4 *>(y + p * d + i);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (on[u]) {
+        acc.x += wv[u] * yv[u].x;
+        acc.y += wv[u] * yv[u].y;
+        acc.z += wv[u] * yv[u].z;
+        acc.w += wv[u] * yv[u].w;
+      }
     }
   }
   if (n_shared) {
@@ -1209,11 +1310,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 }
 
 hipError_t launch_combine(const float *y, const float *w, const int32_t *idx,
-                          const SlotView &view, int all_gpu, int T, int k, int d, int n_shared,
-                          const float *host_part, float *out, float *dbg_gpu, hipStream_t s) {
+                          const SlotView &view, int all_gpu, const int32_t *pair_slot, int T,
+                          int k, int d, int n_shared, const float *host_part, float *out,
+                          float *dbg_gpu, hipStream_t s) {
   const dim3 grid((d / 4 + 255) / 256, T);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, y, w, idx, view, all_gpu, T, k, d,
-                     n_shared, host_part, out, dbg_gpu);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, y, w, idx, view, all_gpu, pair_slot,
+                     T, k, d, n_shared, host_part, out, dbg_gpu);
   return hipGetLastError();
 }
 

@@ -7,6 +7,9 @@
 namespace moe {
 
 constexpr int kMaxExperts = 512;
+// Decode path: at most this many (token, rank) pairs per call, tokens <= 4.
+constexpr int kDecodeMaxPairs = 64;
+constexpr int kDecodeMaxTokens = 4;
 constexpr int kMetaB = 520;  // bucket capacity of the meta block (>= kMaxExperts + 1)
 constexpr int kMetaInts = 2 + 3 * kMetaB;
 
@@ -16,21 +19,40 @@ struct SlotView {
   int16_t slot[kMaxExperts];
 };
 
-// z[t][e] = x[t] . W[e] (+ b[e]) in the fixed fp32 order.  When xp != nullptr
-// every wave also derives its tokens' activation scale and the waves together
-// prepare the activations for the gate/up kernel: a power-of-two scale 2^-e
-// that keeps |x| below 2^14 (xscale[t] = 2^e); the scaled x as binary16 hi and
-// lo pairs in the order the nibble decoder yields weights (for 32-bit word j of
-// block b = j/4 and g = 4*(j%4): (x[g],x[g+2]), (x[g+16],x[g+18]),
-// (x[g+1],x[g+3]), (x[g+17],x[g+19]) of the block, hi then lo); and the sum of
-// each word's 8 scaled values (xsw).
+// z[t][e] = x[t] . W[e] (+ b[e]) in the fixed fp32 order.  The waves also
+// prepare each token's x for the expert kernels, in one of two forms:
+// - xq != nullptr (decode GEMV): digit planes of X = rint(x / s), s = max|x| / 30000
+//   (xs[t] = s); per block b and word j, xq[(t*d/32 + b)*4 + j] holds planes 0..3
+//   as x, y, z, w (the layout is described with the decode GEMV);
+// - xp != nullptr (matrix-core GEMM): a power-of-two scale 2^-e that keeps |x|
+//   below 2^14 (xscale[t] = 2^e); the scaled x as binary16 hi and lo pairs in
+//   the order the nibble decoder yields weights (for 32-bit word j of block
+//   b = j/4 and g = 4*(j%4): (x[g],x[g+2]), (x[g+16],x[g+18]), (x[g+1],x[g+3]),
+//   (x[g+17],x[g+19]) of the block, hi then lo); and the sum of each word's 8
+//   scaled values (xsw).
 hipError_t launch_router(const float *x, int T, int d, const float *W, const float *bias, int E,
-                         float *z, uint32_t *xp, float *xsw, float *xscale, hipStream_t s);
+                         float *z, uint32_t *xp, float *xsw, float *xscale, uint4 *xq, float *xs,
+                         hipStream_t s);
 
 // Per token: k largest logits (ties to the lower id), softmax gating weights,
 // written to device memory (idx, w) and to page-locked host memory (h_idx, h_w).
 hipError_t launch_topk(const float *z, int T, int E, int k, int norm_topk, int32_t *idx,
                        float *w, int32_t *h_idx, float *h_w, hipStream_t s);
+
+// Decode bucket list: buckets[0] = count; bucket b at buckets + 1 + b*kBucketInts
+// holds {slot, pair count, pairs[kDecodeMaxTokens]} (pairs ascending, the last
+// one repeated past the count).
+constexpr int kBucketInts = 6;  // 2 + kDecodeMaxTokens
+
+// launch_topk for decode calls (T <= kDecodeMaxTokens, T*k + shared pairs <=
+// kDecodeMaxPairs; else hipErrorInvalidValue), which also maps each routed pair
+// to its slot through `view` (pair_slot[T*k], -1 when not cached) and writes
+// the bucket list of the cached experts plus, when shared_slot >= 0, one bucket
+// of the shared expert's T pairs (pair T*k + t) at slot shared_slot.
+hipError_t launch_topk_decode(const float *z, int T, int E, int k, int norm_topk, int32_t *idx,
+                              float *w, int32_t *h_idx, float *h_w, const SlotView &view,
+                              int shared_slot, int32_t *buckets, int32_t *pair_slot,
+                              hipStream_t s);
 
 // Expert -> slot remap of the routed pairs (plus one shared pair per token when
 // shared_slot >= 0) and stable bucketing per slot, for batches beyond the
@@ -42,27 +64,28 @@ hipError_t launch_remap(const int32_t *idx, int T, int k, const SlotView &view, 
 
 struct GemvArgs {
   const uint8_t *slots;  // slot arena of the layer
-  const uint32_t *xp;    // gate/up: activation pairs [T][d/8][8]
-  const float *xsw;      // gate/up: per-word sums [T][d/8]
-  const float *xscale;   // gate/up: 2^e per token
+  const uint4 *xq;       // decode gate/up: digit planes of x [T][d/32][4]
+  const float *xs;       // decode gate/up: scale per token
+  const uint32_t *xp;    // matrix-core gate/up: activation pairs [T][d/8][8]
+  const float *xsw;      // matrix-core gate/up: per-word sums [T][d/8]
+  const float *xscale;   // matrix-core gate/up: 2^e per token
   long long rec_bytes;   // slot stride
   long long off_q0, off_s0;  // nibbles / scales of the first matrix in a record
   long long off_q1, off_s1;  // second matrix (up projection) for the fused GLU
   int rows;              // output rows per expert
   int nb;                // blocks per row
-  const float *in;       // input rows of nb*32 floats
+  const float *in;       // decode down: input rows (h by pair) of nb*32 floats
   int in_by_pair;        // 0: input row = token of the pair, 1: input row = pair
   int T, k;              // tokens and top-k (pair -> token)
-  const int32_t *meta;         // buckets from launch_remap, or nullptr: decode path
+  const int32_t *meta;         // matrix-core path: buckets from launch_remap
   const int32_t *bucket_pair;
-  const int32_t *idx;          // decode path: router ids [T*k]
-  int shared_slot;             // decode path: slot of the shared expert or -1
+  const int32_t *idx;          // router ids [T*k]
+  int shared_slot;             // slot of the shared expert or -1
+  const int32_t *bt;           // decode path: bucket list (launch_topk_decode)
   float *out;                  // [pairs][rows]
 };
 
-// Decode path: at most this many (token, rank) pairs per call, tokens <= 4.
-constexpr int kDecodeMaxPairs = 64;
-constexpr int kDecodeMaxTokens = 4;
+static_assert(kBucketInts == 2 + kDecodeMaxTokens, "bucket list entry size");
 
 // Buckets built on the host (stream mode, decode path, after the slot fills):
 // bucket b reads the expert record at src[b] (a device slot).
@@ -75,23 +98,28 @@ struct BucketTable {
 };
 
 struct GemvShape {
-  int G, V, TT, R;
-  int KS;  // waves of a workgroup that split one row group's K (down: 1 or 4; gate/up: 4)
+  int G;        // lanes per row
+  int KS;       // waves of a workgroup that split a row's K blocks
+  int R;        // rows per lane
+  int TT;       // tokens per bucket pass (1, 2 or 4)
+  int rows_wg;  // rows per workgroup
 };
 
-// Chooses lanes per row G, words per unit V, token tile TT and rows per lane R
-// for the gate/up kernel (glu, K split over the 4 waves of a workgroup) or the
-// down kernel (whole K per wave).
-GemvShape choose_gemv(bool glu, int rows, int nb, int n_buckets, int max_tokens);
+// Decode GEMV shape for rows of nb blocks and buckets of up to `tokens` pairs:
+// glu = gate/up (+ SwiGLU), else down.
+GemvShape choose_gemv(bool glu, int nb, int tokens);
 
-// glu = 1: out = silu(G x) * (U x) from the prepared activation pairs;
-// glu = 0: out = M in, in float32.  On the decode path (a.meta == nullptr) each
-// workgroup finds its bucket itself from a.idx and `view`: bucket b is the b-th
-// pair (in pair order) whose slot has not appeared before.
-// With tab != nullptr the buckets come from *tab instead.
+// Dynamic LDS of one decode GEMV workgroup (the bucket's activation planes).
+size_t gemv_lds_bytes(bool glu, int nb, int tokens);
 
-hipError_t launch_gemv(const GemvArgs &a, const SlotView &view, const BucketTable *tab,
-                       const GemvShape &sh, bool glu, int n_buckets, hipStream_t s);
+// Decode GEMV over Q4 slot records with 4-bit integer dot products.  glu = 1:
+// out[pair][r] = silu(G x) * (U x) from the router's digit planes (xq, xs);
+// glu = 0: out[pair][r] = (D h)[r] with h = in[pair] (fp32), turned into digit
+// planes with one scale per 32-element block inside each workgroup.  Buckets
+// come from *tab when tab != nullptr, else from the list at a.bt; a grid of
+// n_buckets columns covers at most that many buckets.
+hipError_t launch_gemv(const GemvArgs &a, const BucketTable *tab, const GemvShape &sh, bool glu,
+                       int n_buckets, hipStream_t s);
 
 // Prefill grouped GEMM on the matrix cores (batches beyond the decode path).
 // Buckets from launch_remap; per workgroup 64 weight rows of one bucket's expert
@@ -121,9 +149,11 @@ struct PullList {
 hipError_t launch_pull(const PullList &l, hipStream_t s);
 
 // out[t] = sum_j [pair on GPU] w * y[t*k+j] (j ascending) + shared + host part,
-// where a pair is on the GPU when all_gpu or view.slot[idx] >= 0.
+// where a pair is on the GPU when all_gpu, else when pair_slot[p] >= 0 (if
+// pair_slot != nullptr), else when view.slot[idx[p]] >= 0.
 hipError_t launch_combine(const float *y, const float *w, const int32_t *idx,
-                          const SlotView &view, int all_gpu, int T, int k, int d, int n_shared,
-                          const float *host_part, float *out, float *dbg_gpu, hipStream_t s);
+                          const SlotView &view, int all_gpu, const int32_t *pair_slot, int T,
+                          int k, int d, int n_shared, const float *host_part, float *out,
+                          float *dbg_gpu, hipStream_t s);
 
 }  // namespace moe
