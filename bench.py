@@ -47,7 +47,7 @@ KERNEL_SRC = os.path.join(ROOT, "expert_cache_host_amd", "csrc", "kernels.hip")
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 # the library's kernel ids -> kernel names in rocprofv3 output
 KERNEL_SYMBOL = {"gateup": "q4_gateup_kernel", "down": "q4_down_kernel", "fill": "pull_kernel",
-                 "router": "router_kernel", "topk": "topk_kernel", "combine": "combine_kernel"}
+                 "router": "router_kernel", "topk": "topk_decode_kernel", "combine": "combine_kernel"}
 
 
 def log(msg):

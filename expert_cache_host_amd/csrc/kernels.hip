@@ -559,77 +559,95 @@ __device__ __forceinline__ bool find_bucket(const GemvArgs &a, const BucketTable
 // for them never waits for HBM.  The next step's weights are loaded before the
 // current step is multiplied.  Partial sums meet across the G lanes with xor
 // shuffles and across the KS waves in LDS, in a fixed order.
-constexpr int kStageChunks = 4;  // 16-byte staging chunks per thread and round
+constexpr int kStageChunks = 6;  // 16-byte staging chunks per thread and round
+constexpr int kHUnits = 2;       // down prologue: h words per thread and round
+constexpr int kScaleChunks = 2;  // down prologue: scale chunks per thread and round
 
-template <int G, int KS, int R, int TT, int MODE>
-__global__ __launch_bounds__(256) void q4_gateup_kernel(GemvArgs a, BucketTable tab) {
+// Bytes of the row scales a workgroup stages: rows [r0, r0 + n) of nb binary16
+// scales, in 16-byte chunks.  r0 is a multiple of the workgroup's row count
+// (>= 8) and a section holds rows * nb * 2 bytes, a multiple of 16 (nb and
+// rows even, one of them a multiple of 8 for every shape the cache admits), so
+// chunks start aligned and never pass the section's end.
+__device__ __forceinline__ int scale_chunks(int rows_here, int nb) {
+  return (rows_here * nb * 2 + 15) / 16;
+}
+
+// gate/up + SwiGLU.  LDS: the bucket's x planes [TT][nb][4], then the gate and
+// the up scales of the workgroup's rows.
+template <int G, int KS, int R, int TT, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW) void q4_gateup_kernel(GemvArgs a, BucketTable tab) {
   constexpr int RW = 64 / G;
-  constexpr int RWG = (4 / KS) * RW * R;
-  extern __shared__ uint4 sx[];  // [TT][nb][4]
-  __shared__ float red[4][RW * R][TT][2];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int RWG = (NW / KS) * RW * R;
+  constexpr int NT = 64 * NW;
+  extern __shared__ uint4 sx[];
+  __shared__ float red[NW][RW * R][TT][2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int ks = wave % KS, rg = wave / KS;
   Bucket<TT> bk;
   if (!find_bucket<TT, MODE>(a, tab, blockIdx.y, bk)) return;
   const uint8_t *rec = bk.src;
   const int nb = a.nb;
   const int gl = lane % G;
-  const int rbase = blockIdx.x * RWG + rg * RW * R + lane / G;
+  const int r0 = blockIdx.x * RWG;
+  const int rows_here = min(RWG, a.rows - r0);
+  const int rbase = r0 + rg * RW * R + lane / G;
   const uint4 *q0 = reinterpret_cast<const uint4 *>(rec + a.off_q0);
   const uint4 *q1 = reinterpret_cast<const uint4 *>(rec + a.off_q1);
-  const _Float16 *s0 = reinterpret_cast<const _Float16 *>(rec + a.off_s0);
-  const _Float16 *s1 = reinterpret_cast<const _Float16 *>(rec + a.off_s1);
+  const uint4 *c0 = reinterpret_cast<const uint4 *>(rec + a.off_s0 + (long long)r0 * nb * 2);
+  const uint4 *c1 = reinterpret_cast<const uint4 *>(rec + a.off_s1 + (long long)r0 * nb * 2);
   int tok[TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) tok[tt] = pair_row(a, bk.pairs[tt]);
   // rows past the end read the last row and are never written
+  int rl[R];  // row within the workgroup's staged scales
   long long ro[R];
 #pragma unroll
-  for (int i = 0; i < R; ++i) ro[i] = (long long)min(rbase + RW * i, a.rows - 1) * nb;
+  for (int i = 0; i < R; ++i) {
+    const int r = min(rbase + RW * i, a.rows - 1);
+    rl[i] = (r - r0) * nb;
+    ro[i] = (long long)r * nb;
+  }
   const int NI = (nb + G * KS - 1) / (G * KS);
   auto blk_of = [&](int it) { return min(gl + G * (ks + KS * it), nb - 1); };
-  const int n_stage = TT * nb * 4;
+  // staging: x planes, gate scales, up scales, as one run of 16-byte units
+  const int n_x = TT * nb * 4, n_s = scale_chunks(rows_here, nb);
+  const int n_stage = n_x + 2 * n_s;
   auto stage_ld = [&](int u) -> uint4 {
     u = min(u, n_stage - 1);
-    const int tt = u / (nb * 4);
-    return a.xq[(long long)pick(tok, tt) * nb * 4 + (u - tt * nb * 4)];
+    if (u < n_x) {
+      const int tt = u / (nb * 4);
+      return a.xq[(long long)pick(tok, tt) * nb * 4 + (u - tt * nb * 4)];
+    }
+    return u < n_x + n_s ? c0[u - n_x] : c1[u - n_x - n_s];
   };
-  auto stage_st = [&](int u, const uint4 &v) {
-    if (u < n_stage) sx[u] = v;
-  };
-  static_assert(kStageChunks == 4, "staging is written out for 4 chunks");
-  const int tid = threadIdx.x;
-  uint4 xv0 = stage_ld(tid), xv1 = stage_ld(tid + 256), xv2 = stage_ld(tid + 512),
-        xv3 = stage_ld(tid + 768);
-  // keep the weight loads behind the activation loads
+  uint4 xv[kStageChunks];
+#pragma unroll
+  for (int c = 0; c < kStageChunks; ++c) xv[c] = stage_ld(tid + NT * c);
+  // keep the weight loads behind the staging loads
   __builtin_amdgcn_sched_barrier(0);
   uint4 wg[R], wu[R];
-  _Float16 cg[R], cu[R];
   {
     const int j = blk_of(0);
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       wg[i] = q0[ro[i] + j];
       wu[i] = q1[ro[i] + j];
-      cg[i] = s0[ro[i] + j];
-      cu[i] = s1[ro[i] + j];
     }
   }
-  stage_st(tid, xv0);
-  stage_st(tid + 256, xv1);
-  stage_st(tid + 512, xv2);
-  stage_st(tid + 768, xv3);
-  for (int u0 = 1024; u0 < n_stage; u0 += 1024) {
-    xv0 = stage_ld(u0 + tid);
-    xv1 = stage_ld(u0 + tid + 256);
-    xv2 = stage_ld(u0 + tid + 512);
-    xv3 = stage_ld(u0 + tid + 768);
-    stage_st(u0 + tid, xv0);
-    stage_st(u0 + tid + 256, xv1);
-    stage_st(u0 + tid + 512, xv2);
-    stage_st(u0 + tid + 768, xv3);
+#pragma unroll
+  for (int c = 0; c < kStageChunks; ++c)
+    if (tid + NT * c < n_stage) sx[tid + NT * c] = xv[c];
+  for (int u0 = NT * kStageChunks; u0 < n_stage; u0 += NT * kStageChunks) {
+    uint4 yv[kStageChunks];
+#pragma unroll
+    for (int c = 0; c < kStageChunks; ++c) yv[c] = stage_ld(u0 + tid + NT * c);
+#pragma unroll
+    for (int c = 0; c < kStageChunks; ++c)
+      if (u0 + tid + NT * c < n_stage) sx[u0 + tid + NT * c] = yv[c];
   }
   __syncthreads();
+  const _Float16 *sg = reinterpret_cast<const _Float16 *>(sx + n_x);
+  const _Float16 *su = reinterpret_cast<const _Float16 *>(sx + n_x + n_s);
   float ag[R][TT], au[R][TT];
 #pragma unroll
   for (int i = 0; i < R; ++i)
@@ -643,13 +661,10 @@ __global__ __launch_bounds__(256) void q4_gateup_kernel(GemvArgs a, BucketTable 
     const bool ok = j0 < nb;
     const int j = min(j0, nb - 1);
     uint4 cw[R], cv[R];
-    float dg[R], du[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       cw[i] = wg[i];
       cv[i] = wu[i];
-      dg[i] = ok ? (float)cg[i] : 0.0f;
-      du[i] = ok ? (float)cu[i] : 0.0f;
     }
     if (it + 1 < NI) {
       const int jn = blk_of(it + 1);
@@ -657,9 +672,13 @@ __global__ __launch_bounds__(256) void q4_gateup_kernel(GemvArgs a, BucketTable 
       for (int i = 0; i < R; ++i) {
         wg[i] = q0[ro[i] + jn];
         wu[i] = q1[ro[i] + jn];
-        cg[i] = s0[ro[i] + jn];
-        cu[i] = s1[ro[i] + jn];
       }
+    }
+    float dg[R], du[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      dg[i] = ok ? (float)sg[rl[i] + j] : 0.0f;
+      du[i] = ok ? (float)su[rl[i] + j] : 0.0f;
     }
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
@@ -693,9 +712,9 @@ __global__ __launch_bounds__(256) void q4_gateup_kernel(GemvArgs a, BucketTable 
       }
   }
   __syncthreads();
-  for (int o = threadIdx.x; o < (4 / KS) * RW * R * TT; o += 256) {
+  for (int o = tid; o < (NW / KS) * RW * R * TT; o += NT) {
     const int g = o / (RW * R * TT), rr = (o / TT) % (RW * R), tt = o % TT;
-    const int r = blockIdx.x * RWG + g * RW * R + rr;
+    const int r = r0 + g * RW * R + rr;
     if (r < a.rows && tt < bk.cnt) {
       float gg = 0.0f, uu = 0.0f;
 #pragma unroll
@@ -711,35 +730,46 @@ __global__ __launch_bounds__(256) void q4_gateup_kernel(GemvArgs a, BucketTable 
 
 // down: y = D h.  The prologue turns the bucket's h rows (fp32, by pair) into
 // digit planes with one scale per 32-element block (thread = one word of one
-// block; the block's four threads share its max through two xor shuffles).
-template <int G, int KS, int R, int TT, int MODE>
-__global__ __launch_bounds__(256) void q4_down_kernel(GemvArgs a, BucketTable tab) {
+// block; the block's four threads share its max through two xor shuffles) and
+// stages the workgroup's row scales.  LDS: planes [TT][nb][4], block scales
+// [TT][nb] (fp32), row scales.
+template <int G, int KS, int R, int TT, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW) void q4_down_kernel(GemvArgs a, BucketTable tab) {
   constexpr int RW = 64 / G;
-  constexpr int RWG = (4 / KS) * RW * R;
-  constexpr int HC = 2;  // prologue units per thread and round
-  extern __shared__ uint4 sh[];  // [TT][nb][4] planes, then [TT][nb] block scales
-  __shared__ float red[4][RW * R][TT];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int RWG = (NW / KS) * RW * R;
+  constexpr int NT = 64 * NW;
+  extern __shared__ uint4 sh[];
+  __shared__ float red[NW][RW * R][TT];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int ks = wave % KS, rg = wave / KS;
   Bucket<TT> bk;
   if (!find_bucket<TT, MODE>(a, tab, blockIdx.y, bk)) return;
   const uint8_t *rec = bk.src;
   const int nb = a.nb;
-  float *sscale = reinterpret_cast<float *>(sh + TT * nb * 4);
+  const int n_units = TT * nb * 4;
+  float *sscale = reinterpret_cast<float *>(sh + n_units);
+  uint4 *srow = sh + n_units + (TT * nb + 3) / 4;
   const int gl = lane % G;
-  const int rbase = blockIdx.x * RWG + rg * RW * R + lane / G;
+  const int r0 = blockIdx.x * RWG;
+  const int rows_here = min(RWG, a.rows - r0);
+  const int rbase = r0 + rg * RW * R + lane / G;
   const uint4 *q0 = reinterpret_cast<const uint4 *>(rec + a.off_q0);
-  const _Float16 *s0 = reinterpret_cast<const _Float16 *>(rec + a.off_s0);
+  const uint4 *c0 = reinterpret_cast<const uint4 *>(rec + a.off_s0 + (long long)r0 * nb * 2);
+  int rl[R];
   long long ro[R];
 #pragma unroll
-  for (int i = 0; i < R; ++i) ro[i] = (long long)min(rbase + RW * i, a.rows - 1) * nb;
+  for (int i = 0; i < R; ++i) {
+    const int r = min(rbase + RW * i, a.rows - 1);
+    rl[i] = (r - r0) * nb;
+    ro[i] = (long long)r * nb;
+  }
   const int NI = (nb + G * KS - 1) / (G * KS);
   auto blk_of = [&](int it) { return min(gl + G * (ks + KS * it), nb - 1); };
-  const int n_units = TT * nb * 4;
-  auto load_units = [&](int u0, float4 (&v0)[HC], float4 (&v1)[HC]) {
+  const int n_s = scale_chunks(rows_here, nb);
+  auto load_units = [&](int u0, float4 (&v0)[kHUnits], float4 (&v1)[kHUnits]) {
 #pragma unroll
-    for (int c = 0; c < HC; ++c) {
-      const int u = min(u0 + (int)threadIdx.x + 256 * c, n_units - 1);
+    for (int c = 0; c < kHUnits; ++c) {
+      const int u = min(u0 + tid + NT * c, n_units - 1);
       const int tt = u / (nb * 4), rem = u - tt * nb * 4;
       const int b = rem >> 2, j = rem & 3;
       const float *hr = a.in + (long long)pick(bk.pairs, tt) * nb * 32 + b * 32 + 4 * j;
@@ -747,25 +777,11 @@ __global__ __launch_bounds__(256) void q4_down_kernel(GemvArgs a, BucketTable ta
       v1[c] = *reinterpret_cast<const float4 *>(hr + 16);
     }
   };
-  float4 hv0[HC], hv1[HC];
-  load_units(0, hv0, hv1);
-  // keep the weight loads behind the h loads
-  __builtin_amdgcn_sched_barrier(0);
-  uint4 wd[R];
-  _Float16 cd[R];
-  {
-    const int j = blk_of(0);
+  auto put_units = [&](int u0, const float4 (&v0)[kHUnits], const float4 (&v1)[kHUnits]) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      wd[i] = q0[ro[i] + j];
-      cd[i] = s0[ro[i] + j];
-    }
-  }
-  auto put_units = [&](int u0, const float4 (&v0)[HC], const float4 (&v1)[HC]) {
-#pragma unroll
-    for (int c = 0; c < HC; ++c) {
-      const int u = u0 + threadIdx.x + 256 * c;
-      if (u0 + 256 * c >= n_units) break;  // uniform
+    for (int c = 0; c < kHUnits; ++c) {
+      const int u = u0 + tid + NT * c;
+      if (u0 + NT * c >= n_units) break;  // uniform
       const float v[8] = {v0[c].x, v0[c].y, v0[c].z, v0[c].w, v1[c].x, v1[c].y, v1[c].z, v1[c].w};
       float m = 0.0f;
 #pragma unroll
@@ -780,13 +796,31 @@ __global__ __launch_bounds__(256) void q4_down_kernel(GemvArgs a, BucketTable ta
       }
     }
   };
+  float4 hv0[kHUnits], hv1[kHUnits];
+  load_units(0, hv0, hv1);
+  static_assert(kScaleChunks == 2, "row scale staging is written out for 2 chunks");
+  const uint4 sv0 = c0[min(tid, n_s - 1)], sv1 = c0[min(tid + NT, n_s - 1)];
+  // keep the weight loads behind the staging loads
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 wd[R];
+  {
+    const int j = blk_of(0);
+#pragma unroll
+    for (int i = 0; i < R; ++i) wd[i] = q0[ro[i] + j];
+  }
+  if (tid < n_s) srow[tid] = sv0;
+  if (tid + NT < n_s) srow[tid + NT] = sv1;
+  for (int u0 = NT * kScaleChunks; u0 < n_s; u0 += NT) {
+    if (u0 + tid < n_s) srow[u0 + tid] = c0[u0 + tid];
+  }
   put_units(0, hv0, hv1);
-  for (int u0 = 256 * HC; u0 < n_units; u0 += 256 * HC) {
-    float4 gv0[HC], gv1[HC];
+  for (int u0 = NT * kHUnits; u0 < n_units; u0 += NT * kHUnits) {
+    float4 gv0[kHUnits], gv1[kHUnits];
     load_units(u0, gv0, gv1);
     put_units(u0, gv0, gv1);
   }
   __syncthreads();
+  const _Float16 *sd = reinterpret_cast<const _Float16 *>(srow);
   float ac[R][TT];
 #pragma unroll
   for (int i = 0; i < R; ++i)
@@ -797,20 +831,16 @@ __global__ __launch_bounds__(256) void q4_down_kernel(GemvArgs a, BucketTable ta
     const bool ok = j0 < nb;
     const int j = min(j0, nb - 1);
     uint4 cw[R];
-    float dd[R];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      cw[i] = wd[i];
-      dd[i] = ok ? (float)cd[i] : 0.0f;
-    }
+    for (int i = 0; i < R; ++i) cw[i] = wd[i];
     if (it + 1 < NI) {
       const int jn = blk_of(it + 1);
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        wd[i] = q0[ro[i] + jn];
-        cd[i] = s0[ro[i] + jn];
-      }
+      for (int i = 0; i < R; ++i) wd[i] = q0[ro[i] + jn];
     }
+    float dd[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) dd[i] = ok ? (float)sd[rl[i] + j] : 0.0f;
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       uint4 P[4];
@@ -836,9 +866,9 @@ __global__ __launch_bounds__(256) void q4_down_kernel(GemvArgs a, BucketTable ta
       for (int tt = 0; tt < TT; ++tt) red[wave][lane / G + RW * i][tt] = ac[i][tt];
   }
   __syncthreads();
-  for (int o = threadIdx.x; o < (4 / KS) * RW * R * TT; o += 256) {
+  for (int o = tid; o < (NW / KS) * RW * R * TT; o += NT) {
     const int g = o / (RW * R * TT), rr = (o / TT) % (RW * R), tt = o % TT;
-    const int r = blockIdx.x * RWG + g * RW * R + rr;
+    const int r = r0 + g * RW * R + rr;
     if (r < a.rows && tt < bk.cnt) {
       float v = 0.0f;
 #pragma unroll
@@ -879,24 +909,30 @@ GemvShape choose_gemv(bool glu, int nb, int tokens) {
       sh.KS = 4;
     }
   }
-  sh.rows_wg = (4 / sh.KS) * (64 / sh.G) * sh.R;
+  sh.NW = 4;
+  sh.rows_wg = (sh.NW / sh.KS) * (64 / sh.G) * sh.R;
   return sh;
 }
 
 size_t gemv_lds_bytes(bool glu, int nb, int tokens) {
-  const int TT = tokens <= 1 ? 1 : (tokens <= 2 ? 2 : 4);
-  return glu ? (size_t)TT * nb * 64 : (size_t)TT * nb * 68;
+  const GemvShape sh = choose_gemv(glu, nb, tokens);
+  const size_t row_scales = ((size_t)sh.rows_wg * nb * 2 + 15) / 16 * 16;
+  if (glu) return (size_t)sh.TT * nb * 64 + 2 * row_scales;
+  return (size_t)sh.TT * nb * 64 + ((size_t)sh.TT * nb + 3) / 4 * 16 + row_scales;
 }
 
 template <bool GLU, int G, int KS, int R, int TT, int MODE>
 static void launch_one(const GemvArgs &a, const BucketTable &tab, int nbk, size_t lds,
                        hipStream_t s) {
-  constexpr int RWG = (4 / KS) * (64 / G) * R;
+  constexpr int NW = 4;
+  constexpr int RWG = (NW / KS) * (64 / G) * R;
   const dim3 grid((a.rows + RWG - 1) / RWG, nbk);
   if constexpr (GLU)
-    hipLaunchKernelGGL((q4_gateup_kernel<G, KS, R, TT, MODE>), grid, dim3(256), lds, s, a, tab);
+    hipLaunchKernelGGL((q4_gateup_kernel<G, KS, R, TT, MODE, NW>), grid, dim3(64 * NW), lds, s, a,
+                       tab);
   else
-    hipLaunchKernelGGL((q4_down_kernel<G, KS, R, TT, MODE>), grid, dim3(256), lds, s, a, tab);
+    hipLaunchKernelGGL((q4_down_kernel<G, KS, R, TT, MODE, NW>), grid, dim3(64 * NW), lds, s, a,
+                       tab);
 }
 
 template <bool GLU, int G, int KS, int R>

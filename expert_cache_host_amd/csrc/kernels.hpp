@@ -102,6 +102,7 @@ struct GemvShape {
   int KS;       // waves of a workgroup that split a row's K blocks
   int R;        // rows per lane
   int TT;       // tokens per bucket pass (1, 2 or 4)
+  int NW;       // waves per workgroup
   int rows_wg;  // rows per workgroup
 };
 
