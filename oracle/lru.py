@@ -30,6 +30,27 @@ Readings taken where the pages are silent:
   id; the views are the full tables at call start (cached -> slot,
   uncached -> -1 / uncached -> own id, cached -> -1); fills are visible from the
   same layer's next call on.
+
+The score policy follows "Keeping the cache fresh" (llama.cpp + MoE expert
+cache): after each step the routing is read back and a usage score per expert
+decays by 0.9 per token; missed experts scoring higher than the weakest slot
+are promoted, within a budget of copies.  Readings:
+
+* score[e] starts at 0.0 (binary64); per call, for each token t in order:
+  every score is multiplied by 0.9, then each expert token t selected gains
+  1.0 -- before any slot decision of the call;
+* protection and the clock are those of the LRU rule (a stage's resident
+  experts and the experts inserted in it are protected for that stage);
+* the weakest slot is the lowest-index empty slot, else the unprotected slot
+  with the smallest (score of its expert, slot index);
+* host mode: the missed experts are candidates in order of (-score, id); a
+  candidate is promoted into the weakest slot only when its score is strictly
+  greater than that slot's (an empty slot always loses), up to max_fills
+  promotions; the first candidate that does not beat the weakest slot ends the
+  call's promotions (later candidates score no higher, and the weakest slot
+  only rises);
+* stream mode: every miss is still filled, stage by stage in ascending id, the
+  victim being the weakest slot instead of the least recently used one.
 """
 from __future__ import annotations
 
@@ -38,6 +59,9 @@ from typing import List, Tuple
 
 STREAM = "stream"
 HOST = "host"
+LRU = "lru"
+SCORE = "score"
+DECAY = 0.9  # usage score factor per token
 
 
 @dataclass
@@ -56,11 +80,15 @@ class PlanResult:
 class LayerSlots:
     """LRU slot state of one layer."""
 
-    def __init__(self, n_experts: int, slots: int):
+    def __init__(self, n_experts: int, slots: int, policy: str = LRU):
         if not 1 <= slots <= n_experts:
             raise ValueError("slots must be in [1, n_experts]")
+        if policy not in (LRU, SCORE):
+            raise ValueError("policy must be 'lru' or 'score'")
         self.E = n_experts
         self.S = slots
+        self.policy = policy
+        self.score = [0.0] * n_experts
         self.expert_in = list(range(slots))
         self.slot_of = [-1] * n_experts
         for s in range(slots):
@@ -74,15 +102,33 @@ class LayerSlots:
 
     # -- victim choice -------------------------------------------------------
     def victim(self):
+        """Lowest-index empty slot, else the unprotected slot with the smallest
+        (last_use, index) under LRU or (score of its expert, index) under the
+        score policy; None when every slot is protected."""
         for s in range(self.S):
             if self.expert_in[s] == -1:
                 return s
         best = None
         for s in range(self.S):
             if self.last_use[s] < self.clock:
-                if best is None or self.last_use[s] < self.last_use[best]:
+                if best is None or self._key(s) < self._key(best):
                     best = s
         return best
+
+    def _key(self, s):
+        if self.policy == SCORE:
+            return (self.score[self.expert_in[s]], s)
+        return (self.last_use[s], s)
+
+    def _update_scores(self, idx, tokens):
+        if tokens < 1 or len(idx) % tokens:
+            raise ValueError("selections must split evenly over the tokens")
+        k = len(idx) // tokens
+        for t in range(tokens):
+            for e in range(self.E):
+                self.score[e] = self.score[e] * DECAY
+            for e in idx[t * k:(t + 1) * k]:
+                self.score[e] = self.score[e] + 1.0
 
     def _insert(self, call, stage, slot, e, log):
         old = self.expert_in[slot]
@@ -98,11 +144,13 @@ class LayerSlots:
         self.stats["fills"] += 1
 
     # -- one call ------------------------------------------------------------
-    def plan(self, idx, mode: str = STREAM, max_fills: int = -1) -> PlanResult:
+    def plan(self, idx, mode: str = STREAM, max_fills: int = -1, tokens: int = 1) -> PlanResult:
         idx = [int(e) for e in idx]
         for e in idx:
             if not 0 <= e < self.E:
                 raise ValueError("expert id out of range")
+        if self.policy == SCORE:
+            self._update_scores(idx, tokens)
         call = self.calls
         self.calls += 1
         uniq = sorted(set(idx))
@@ -145,11 +193,17 @@ class LayerSlots:
             for e in hit_experts:
                 self.last_use[self.slot_of[e]] = self.clock
             placed = 0
-            for e in pending:
+            order = pending
+            if self.policy == SCORE:
+                order = sorted(pending, key=lambda e: (-self.score[e], e))
+            for e in order:
                 if max_fills >= 0 and placed >= max_fills:
                     break
                 v = self.victim()
                 if v is None:
+                    break
+                if self.policy == SCORE and self.expert_in[v] >= 0 and \
+                        not self.score[e] > self.score[self.expert_in[v]]:
                     break
                 self._insert(call, 0, v, e, log)
                 placed += 1

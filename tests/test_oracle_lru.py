@@ -6,7 +6,7 @@ from collections import OrderedDict
 
 import pytest
 
-from oracle.lru import HOST, STREAM, LayerSlots
+from oracle.lru import DECAY, HOST, LRU, SCORE, STREAM, LayerSlots
 
 G = os.path.join(os.path.dirname(__file__), "golden", "lru_traces.txt")
 
@@ -22,7 +22,8 @@ def _parse_traces():
         tr = traces.setdefault(name, {"calls": [], "views": [], "stages": None})
         if parts[1].startswith("E="):
             kv = dict(p.split("=") for p in parts[1].split())
-            tr.update(E=int(kv["E"]), S=int(kv["S"]), mode=kv["mode"], fills=int(kv["fills"]))
+            tr.update(E=int(kv["E"]), S=int(kv["S"]), mode=kv["mode"], fills=int(kv["fills"]),
+                      policy=kv.get("policy", LRU), tokens=int(kv.get("tokens", "1")))
         elif parts[1].startswith("call"):
             idx = [int(v) for v in parts[2].split()[1:]]
             hits = int(parts[3].split()[1])
@@ -35,7 +36,11 @@ def _parse_traces():
             hv = [int(v) for v in parts[3].split()[1:]]
             tr["views"].append((sv, hv))
         elif parts[1] == "stages":
-            tr["stages"] = [[int(e) for e in s.split(":")[1].split(",")] for s in parts[2].split()]
+            # stage members of the call on the line above
+            st = [[int(e) for e in s.split(":")[1].split(",")] for s in parts[2].split()]
+            if tr["stages"] is None:
+                tr["stages"] = {}
+            tr["stages"][len(tr["calls"]) - 1] = st
         elif parts[1] == "final":
             tr["final"] = [int(v) for v in parts[2].split()[1:]]
     return traces
@@ -47,17 +52,17 @@ TRACES = _parse_traces()
 @pytest.mark.parametrize("name", sorted(TRACES))
 def test_golden_trace(name):
     tr = TRACES[name]
-    sim = LayerSlots(tr["E"], tr["S"])
+    sim = LayerSlots(tr["E"], tr["S"], tr["policy"])
     for c, (idx, hits, evs) in enumerate(tr["calls"]):
-        res = sim.plan(idx, tr["mode"], tr["fills"])
+        res = sim.plan(idx, tr["mode"], tr["fills"], tr["tokens"])
         assert res.hits == hits
         assert res.evictions == evs
         if tr["views"]:
             sv, hv = tr["views"][c]
             assert res.stage_views[0] == sv
             assert res.host_view == hv
-        if tr["stages"] is not None:
-            assert res.stage_experts == tr["stages"]
+        if tr["stages"] is not None and c in tr["stages"]:
+            assert res.stage_experts == tr["stages"][c]
         sim.check_invariants()
     assert sim.expert_in == tr["final"]
 
@@ -176,15 +181,16 @@ class _HighTie(LayerSlots):
 
 
 def _trace_passes(cls, tr):
-    sim = cls(tr["E"], tr["S"])
+    sim = cls(tr["E"], tr["S"], tr["policy"])
     try:
         for c, (idx, hits, evs) in enumerate(tr["calls"]):
-            res = sim.plan(idx, tr["mode"], tr["fills"])
+            res = sim.plan(idx, tr["mode"], tr["fills"], tr["tokens"])
             if res.hits != hits or res.evictions != evs:
                 return False
             if tr["views"] and (res.stage_views[0], res.host_view) != tr["views"][c]:
                 return False
-            if tr["stages"] is not None and res.stage_experts != tr["stages"]:
+            if tr["stages"] is not None and c in tr["stages"] and \
+                    res.stage_experts != tr["stages"][c]:
                 return False
     except Exception:
         return False
@@ -196,3 +202,125 @@ def test_planted_victim_mistakes_fail_the_traces(cls):
     """Each plausible slip in the victim rule contradicts at least one hand-worked trace."""
     assert all(_trace_passes(LayerSlots, tr) for tr in TRACES.values())
     assert not all(_trace_passes(cls, tr) for tr in TRACES.values())
+
+
+# ---------------------------------------------------------------- score policy
+
+class _DecayPerCall(LayerSlots):
+    def _update_scores(self, idx, tokens):  # planted mistake: one decay per call
+        return super()._update_scores(idx, 1)
+
+
+class _NoDecay(LayerSlots):
+    def _update_scores(self, idx, tokens):  # planted mistake: plain use counts
+        for e in idx:
+            self.score[e] += 1.0
+
+
+class _ScoreButLruVictim(LayerSlots):
+    def _key(self, s):  # planted mistake: the score policy evicts by recency
+        return (self.last_use[s], s)
+
+
+@pytest.mark.parametrize("cls", [_DecayPerCall, _NoDecay, _ScoreButLruVictim])
+def test_planted_score_mistakes_fail_the_traces(cls):
+    score_traces = [tr for tr in TRACES.values() if tr["policy"] == SCORE]
+    assert score_traces and all(_trace_passes(LayerSlots, tr) for tr in score_traces)
+    assert not all(_trace_passes(cls, tr) for tr in score_traces)
+
+
+def test_score_candidate_order_pinned():
+    # trace G's first call has candidates 1 (0.9) and 2 (1.0): taking them in id
+    # order would put expert 1 in the slot
+    tr = TRACES["G"]
+    sim = LayerSlots(tr["E"], tr["S"], SCORE)
+    res = sim.plan(tr["calls"][0][0], HOST, -1, tr["tokens"])
+    assert [r[4] for r in res.evictions] == [2]
+    assert sim.score[2] > sim.score[1] > 0.0
+
+
+def test_score_closed_forms():
+    # n consecutive single-token uses: sum_{i<n} 0.9^i = (1 - 0.9^n) / 0.1;
+    # one use followed by m calls without it: 0.9^m
+    sim = LayerSlots(8, 2, SCORE)
+    for n in range(1, 40):
+        sim.plan([5], HOST)
+        assert abs(sim.score[5] - (1.0 - DECAY ** n) / (1.0 - DECAY)) < 1e-12
+    sim = LayerSlots(8, 2, SCORE)
+    sim.plan([6], HOST)
+    for m in range(1, 30):
+        sim.plan([0], HOST)
+        assert abs(sim.score[6] - DECAY ** m) < 1e-15
+    # T tokens in one call decay T times
+    sim = LayerSlots(8, 2, SCORE)
+    sim.plan([3, 1, 1, 1], HOST, -1, tokens=4)
+    assert abs(sim.score[3] - DECAY ** 3) < 1e-15
+    assert abs(sim.score[1] - (1.0 + DECAY + DECAY ** 2)) < 1e-15
+
+
+def test_score_admission_needs_a_strictly_higher_score():
+    # "Missed experts that score higher than the weakest slot are promoted":
+    # an equal score does not promote, the next representable one above does
+    import math
+    for cand, promoted in ((1.0, False), (math.nextafter(1.0, 2.0), True), (0.5, False)):
+        sim = LayerSlots(3, 1, SCORE)          # slot 0 holds expert 0
+        sim._update_scores = lambda idx, tokens, c=cand, s=sim: s.score.__setitem__(
+            slice(None), [1.0, 0.0, c])
+        res = sim.plan([2], HOST)
+        assert (res.evictions == [(0, 0, 0, 0, 2)]) == promoted
+
+
+def _full_scan_weakest(sim):
+    empty = [s for s in range(sim.S) if sim.expert_in[s] == -1]
+    if empty:
+        return empty[0]
+    cands = sorted((sim.score[sim.expert_in[s]], s) for s in range(sim.S)
+                   if sim.last_use[s] < sim.clock)
+    return cands[0][1] if cands else None
+
+
+@pytest.mark.parametrize("mode", [STREAM, HOST])
+def test_score_invariants_random(mode):
+    rnd = random.Random(11)
+    for e_count, s_count, k, t in ((8, 4, 2, 1), (32, 5, 4, 3), (64, 8, 8, 1), (20, 2, 3, 2)):
+        sim = LayerSlots(e_count, s_count, SCORE)
+        orig_victim = sim.victim
+        sim.victim = lambda: (lambda v: (v, _assert_eq(v, _full_scan_weakest(sim)))[0])(orig_victim())
+        for _ in range(200):
+            idx = []
+            for _t in range(t):
+                idx += rnd.sample(range(min(e_count, 3 * k)) if rnd.random() < 0.6
+                                  else range(e_count), k)
+            budget = rnd.choice([-1, -1, 0, 1, 2]) if mode == HOST else -1
+            scores_before = None
+            res = sim.plan(idx, mode, budget, tokens=t)
+            sim.check_invariants()
+            assert res.hits + res.misses == len(idx)
+            if mode == HOST:
+                if budget >= 0:
+                    assert len(res.evictions) <= budget
+                hits = [e for e in sorted(set(idx)) if res.stage_views[0][e] >= 0]
+                for (_c, _st, _slot, old, new) in res.evictions:
+                    assert old not in hits
+                    assert old == -1 or sim.score[new] > sim.score[old]
+            else:
+                flat = [e for st in res.stage_experts for e in st]
+                assert sorted(flat) == sorted(set(idx))
+            del scores_before
+
+
+@pytest.mark.parametrize("mode", [STREAM, HOST])
+def test_score_slots_equal_experts_all_hits(mode):
+    rnd = random.Random(12)
+    sim = LayerSlots(16, 16, SCORE)
+    for _ in range(100):
+        res = sim.plan(rnd.sample(range(16), 4), mode)
+        assert res.misses == 0 and res.evictions == []
+
+
+def test_score_budget_zero_never_fills():
+    rnd = random.Random(13)
+    sim = LayerSlots(32, 4, SCORE)
+    for _ in range(200):
+        assert sim.plan(rnd.sample(range(32), 4), HOST, 0).evictions == []
+    assert sim.expert_in == [0, 1, 2, 3]
