@@ -133,6 +133,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="gemma")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--miss-mode", choices=["stream", "host"], default=None,
+                    help="override the workload's miss mode")
+    ap.add_argument("--policy", choices=["lru", "score"], default="lru",
+                    help="slot policy: LRU, or the decayed usage score with admission")
+    ap.add_argument("--max-fills", type=int, default=-1,
+                    help="host mode: slot fills per call (-1 = every admitted miss)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without per-kernel events (no roofline)")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -149,6 +155,9 @@ def main():
     import synth
 
     wl = pick_workload(args.workload)
+    if args.miss_mode is not None:
+        import dataclasses
+        wl = dataclasses.replace(wl, miss_mode=args.miss_mode)
     per_layer = wl.calls_per_layer
     if wl.rho is None:
         steps = args.steps if args.steps is not None else 6
@@ -171,7 +180,8 @@ def main():
     hidden = [synth.gen_hidden(wl, l, need) for l in range(wl.layers)]
     t0 = time.perf_counter()
     cache = m.MoECache(wl.layers, wl.n_experts, wl.slots, wl.d_model, wl.d_ff, weights,
-                       top_k=wl.top_k, miss_mode=wl.miss_mode, n_shared=wl.n_shared)
+                       top_k=wl.top_k, miss_mode=wl.miss_mode, n_shared=wl.n_shared,
+                       policy=args.policy, max_fills_per_call=args.max_fills)
     log(f"[bench] cache created (pinned arena + slot preload) in {time.perf_counter() - t0:.1f} s")
     w_d = [torch.from_numpy(w).to(dev) for w, _ in routers]
     b_d = [torch.from_numpy(b).to(dev) if b is not None else None for _, b in routers]
@@ -301,6 +311,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded Q4_0 experts ~N(0,0.02), AR(1) hidden states, Zipf router bias)",
         "config": {"workload": describe(wl), "layers": wl.layers, "tokens_per_call": wl.batch,
+                   "slot_policy": args.policy, "max_fills_per_call": args.max_fills,
                    "steps_are": "one batch through every layer",
                    "kernel_timing": f"HIP events per launch over {ev_steps} further steps"},
         "roofline": roofline,

@@ -31,7 +31,7 @@ class Opts(ctypes.Structure):
                 ("n_shared", ctypes.c_int32), ("norm_topk", ctypes.c_int32),
                 ("host_threads", ctypes.c_int32), ("max_fills_per_call", ctypes.c_int32),
                 ("keep_debug", ctypes.c_int32), ("timing", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 8)]
+                ("policy", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
 
 
 class Stats(ctypes.Structure):
@@ -80,10 +80,12 @@ def load_library():
         "moe_debug_routing": (I32, [P, I32, P, P]),
         "moe_debug_views": (I32, [P, I32, I32, P, P]),
         "moe_debug_slots": (I32, [P, I32, P, P]),
+        "moe_debug_scores": (I32, [P, I32, P]),
         "moe_debug_evictions": (I32, [P, I32, P, SZ, ctypes.POINTER(SZ)]),
         "moe_debug_partials": (I32, [P, I32, P, P]),
-        "moe_planner_create": (I32, [I32, I32, I32, I32, ctypes.POINTER(P)]),
-        "moe_planner_plan": (I32, [P, P, I32, P, P, P]),
+        "moe_planner_create": (I32, [I32, I32, I32, I32, I32, ctypes.POINTER(P)]),
+        "moe_planner_plan": (I32, [P, P, I32, I32, P, P, P]),
+        "moe_planner_scores": (I32, [P, P]),
         "moe_planner_views": (I32, [P, I32, P, P]),
         "moe_planner_slots": (I32, [P, P, P]),
         "moe_planner_evictions": (I32, [P, P, SZ, ctypes.POINTER(SZ)]),
@@ -96,6 +98,15 @@ def load_library():
         fn.argtypes = args
     _lib = lib
     return lib
+
+
+POLICY_LRU, POLICY_SCORE = 0, 1
+
+
+def _policy(name: str) -> int:
+    if name not in ("lru", "score"):
+        raise ValueError("policy must be 'lru' or 'score'")
+    return POLICY_SCORE if name == "score" else POLICY_LRU
 
 
 def _check(rc: int):
@@ -127,7 +138,8 @@ class MoECache:
     def __init__(self, layers: int, n_experts: int, slots: int, d_model: int, d_ff: int,
                  host_weights: np.ndarray, top_k: int = 8, miss_mode: str = "stream",
                  n_shared: int = 0, norm_topk: bool = True, host_threads: int = 0,
-                 max_fills_per_call: int = -1, keep_debug: bool = False, timing: bool = False):
+                 max_fills_per_call: int = -1, keep_debug: bool = False, timing: bool = False,
+                 policy: str = "lru"):
         lib = load_library()
         w = np.ascontiguousarray(host_weights, dtype=np.uint8)
         need = layers * (n_experts + n_shared) * (3 * d_model * d_ff // 32 * 18)
@@ -143,6 +155,7 @@ class MoECache:
         o.max_fills_per_call = max_fills_per_call
         o.keep_debug = 1 if keep_debug else 0
         o.timing = 1 if timing else 0
+        o.policy = _policy(policy)
         h = ctypes.c_void_p()
         _check(lib.moe_cache_create(layers, n_experts, slots, d_model, d_ff, _ptr(w), ctypes.byref(o),
                                     ctypes.byref(h)))
@@ -150,6 +163,7 @@ class MoECache:
         self.layers, self.n_experts, self.slots = layers, n_experts, slots
         self.d_model, self.d_ff, self.top_k, self.n_shared = d_model, d_ff, top_k, n_shared
         self.miss_mode = miss_mode
+        self.policy = policy
 
     # -- compute ---------------------------------------------------------------
     def forward(self, layer: int, x, router_w, router_bias=None, out=None, stream=None):
@@ -226,6 +240,11 @@ class MoECache:
     def evictions(self, layer: int) -> list:
         return _evictions(load_library().moe_debug_evictions, self._h, layer)
 
+    def scores(self, layer: int) -> np.ndarray:
+        sc = np.empty(self.n_experts, np.float64)
+        _check(load_library().moe_debug_scores(self._h, layer, _ptr(sc)))
+        return sc
+
     def partials(self, layer: int):
         _, t = self.last_call(layer)
         g = np.empty((t, self.d_model), np.float32)
@@ -246,23 +265,29 @@ class MoECache:
 
 
 class Planner:
-    """The library's per-layer LRU planner alone (host only, no GPU)."""
+    """The library's per-layer slot planner alone (host only, no GPU)."""
 
     def __init__(self, n_experts: int, slots: int, miss_mode: str = "stream",
-                 max_fills_per_call: int = -1):
+                 max_fills_per_call: int = -1, policy: str = "lru"):
         h = ctypes.c_void_p()
         _check(load_library().moe_planner_create(n_experts, slots,
                                                  MISS_HOST if miss_mode == "host" else MISS_STREAM,
-                                                 max_fills_per_call, ctypes.byref(h)))
+                                                 max_fills_per_call, _policy(policy),
+                                                 ctypes.byref(h)))
         self._h = h
         self.n_experts, self.slots = n_experts, slots
 
-    def plan(self, idx):
+    def plan(self, idx, tokens: int = 1):
         a = np.ascontiguousarray(idx, dtype=np.int32).ravel()
         ns, hi, mi = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-        _check(load_library().moe_planner_plan(self._h, _ptr(a), a.size, ctypes.byref(ns),
+        _check(load_library().moe_planner_plan(self._h, _ptr(a), a.size, tokens, ctypes.byref(ns),
                                                ctypes.byref(hi), ctypes.byref(mi)))
         return ns.value, hi.value, mi.value
+
+    def scores(self) -> np.ndarray:
+        sc = np.empty(self.n_experts, np.float64)
+        _check(load_library().moe_planner_scores(self._h, _ptr(sc)))
+        return sc
 
     def views(self, stage: int):
         sv = np.empty(self.n_experts, np.int32)

@@ -482,7 +482,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   }
   HIPCHK(hipEventSynchronize(c->ev_idx));
   const double tp = now_s();
-  ly.planner->plan((const int32_t *)c->h_idx.p, T * k, host_mode ? 1 : 0,
+  ly.planner->plan((const int32_t *)c->h_idx.p, T * k, T, host_mode ? 1 : 0,
                    host_mode ? c->o.max_fills_per_call : -1, ly.plan);
   ly.st.plan_s += now_s() - tp;
   if (c->timing) {
@@ -686,7 +686,9 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
   if (o.max_fills_per_call < -1) return fail(MOE_EINVAL, "max_fills_per_call must be >= -1");
   if (o.keep_debug != 0 && o.keep_debug != 1) return fail(MOE_EINVAL, "keep_debug must be 0 or 1");
   if (o.timing != 0 && o.timing != 1) return fail(MOE_EINVAL, "timing must be 0 or 1");
-  for (int i = 0; i < 8; ++i)
+  if (o.policy != MOE_POLICY_LRU && o.policy != MOE_POLICY_SCORE)
+    return fail(MOE_EINVAL, "policy must be MOE_POLICY_LRU or MOE_POLICY_SCORE");
+  for (int i = 0; i < 7; ++i)
     if (o.reserved[i] != 0) return fail(MOE_EINVAL, "reserved fields must be 0");
 
   std::unique_ptr<moe_cache> c;
@@ -738,7 +740,7 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
     c->layers.resize(layers);
     for (int32_t l = 0; l < layers; ++l) {
       LayerState &ly = c->layers[l];
-      ly.planner.reset(new moe::SlotPlanner(n_experts, slots));
+      ly.planner.reset(new moe::SlotPlanner(n_experts, slots, o.policy));
       const size_t nslots = (size_t)slots + o.n_shared;
       he = hipMalloc((void **)&ly.d_slots, nslots * c->rec());
       if (he != hipSuccess) {
@@ -909,6 +911,15 @@ moe_status moe_debug_slots(moe_cache *c, int32_t layer, int32_t *expert_in, uint
   return MOE_OK;
 }
 
+moe_status moe_debug_scores(moe_cache *c, int32_t layer, double *scores) {
+  g_err.clear();
+  if (!c || !scores) return fail(MOE_EINVAL, "NULL argument");
+  if (layer < 0 || layer >= c->L) return fail(MOE_EINVAL, "layer out of range");
+  const auto &p = *c->layers[layer].planner;
+  std::copy(p.scores().begin(), p.scores().end(), scores);
+  return MOE_OK;
+}
+
 static void copy_log(const std::vector<moe::EvictRecord> &log, moe_evict_rec *buf, size_t cap,
                      size_t *n) {
   const size_t m = std::min(cap, log.size());
@@ -960,7 +971,7 @@ struct moe_planner {
 };
 
 moe_status moe_planner_create(int32_t n_experts, int32_t slots, int32_t miss_mode,
-                              int32_t max_fills_per_call, moe_planner **out) {
+                              int32_t max_fills_per_call, int32_t policy, moe_planner **out) {
   g_err.clear();
   if (!out) return fail(MOE_EINVAL, "out is NULL");
   *out = nullptr;
@@ -969,9 +980,10 @@ moe_status moe_planner_create(int32_t n_experts, int32_t slots, int32_t miss_mod
   if (miss_mode != MOE_MISS_STREAM && miss_mode != MOE_MISS_HOST)
     return fail(MOE_EINVAL, "bad miss_mode");
   if (max_fills_per_call < -1) return fail(MOE_EINVAL, "max_fills_per_call must be >= -1");
+  if (policy != MOE_POLICY_LRU && policy != MOE_POLICY_SCORE) return fail(MOE_EINVAL, "bad policy");
   try {
     auto *p = new moe_planner();
-    p->p.reset(new moe::SlotPlanner(n_experts, slots));
+    p->p.reset(new moe::SlotPlanner(n_experts, slots, policy));
     p->mode = miss_mode;
     p->max_fills = max_fills_per_call;
     *out = p;
@@ -981,15 +993,16 @@ moe_status moe_planner_create(int32_t n_experts, int32_t slots, int32_t miss_mod
   return MOE_OK;
 }
 
-moe_status moe_planner_plan(moe_planner *p, const int32_t *idx, int32_t n_sel, int32_t *n_stages,
-                            int32_t *hits, int32_t *misses) {
+moe_status moe_planner_plan(moe_planner *p, const int32_t *idx, int32_t n_sel, int32_t n_tokens,
+                            int32_t *n_stages, int32_t *hits, int32_t *misses) {
   g_err.clear();
   if (!p || (!idx && n_sel > 0)) return fail(MOE_EINVAL, "NULL argument");
   if (n_sel < 1) return fail(MOE_EINVAL, "n_sel must be >= 1");
+  if (n_tokens < 1 || n_sel % n_tokens) return fail(MOE_EINVAL, "n_sel must be a multiple of n_tokens");
   for (int32_t i = 0; i < n_sel; ++i)
     if (idx[i] < 0 || idx[i] >= p->p->n_experts()) return fail(MOE_EINVAL, "expert id out of range");
   try {
-    p->p->plan(idx, n_sel, p->mode, p->max_fills, p->last);
+    p->p->plan(idx, n_sel, n_tokens, p->mode, p->max_fills, p->last);
   } catch (const std::bad_alloc &) {
     return fail(MOE_ENOMEM, "host allocation failed");
   }
@@ -1022,6 +1035,13 @@ moe_status moe_planner_evictions(moe_planner *p, moe_evict_rec *buf, size_t cap,
   if (!p) return fail(MOE_EINVAL, "planner is NULL");
   if (cap && !buf) return fail(MOE_EINVAL, "buf is NULL");
   copy_log(p->p->log(), buf, cap, n);
+  return MOE_OK;
+}
+
+moe_status moe_planner_scores(moe_planner *p, double *scores) {
+  g_err.clear();
+  if (!p || !scores) return fail(MOE_EINVAL, "NULL argument");
+  std::copy(p->p->scores().begin(), p->p->scores().end(), scores);
   return MOE_OK;
 }
 

@@ -4,13 +4,21 @@
 
 namespace moe {
 
-SlotPlanner::SlotPlanner(int32_t n_experts, int32_t slots)
-    : E_(n_experts), S_(slots), expert_in_(slots), slot_of_(n_experts, -1), last_use_(slots, 0),
-      seen_(n_experts, 0) {
+SlotPlanner::SlotPlanner(int32_t n_experts, int32_t slots, int32_t policy)
+    : E_(n_experts), S_(slots), policy_(policy), score_(n_experts, 0.0), expert_in_(slots),
+      slot_of_(n_experts, -1), last_use_(slots, 0), seen_(n_experts, 0) {
   for (int32_t s = 0; s < slots; ++s) {
     expert_in_[s] = s;
     slot_of_[s] = s;
   }
+}
+
+bool SlotPlanner::weaker(int32_t a, int32_t b) const {
+  if (policy_ == kPolicyScore) {
+    const double sa = score_[expert_in_[a]], sb = score_[expert_in_[b]];
+    return sa < sb || (sa == sb && a < b);
+  }
+  return last_use_[a] < last_use_[b] || (last_use_[a] == last_use_[b] && a < b);
 }
 
 int32_t SlotPlanner::victim() const {
@@ -19,9 +27,19 @@ int32_t SlotPlanner::victim() const {
   int32_t best = -1;
   for (int32_t s = 0; s < S_; ++s) {
     if (last_use_[s] >= clock_) continue;
-    if (best < 0 || last_use_[s] < last_use_[best]) best = s;
+    if (best < 0 || weaker(s, best)) best = s;
   }
   return best;
+}
+
+// Per token: every score times 0.9, then +1 for the token's experts (separate
+// roundings; the build keeps floating-point contraction off).
+void SlotPlanner::update_scores(const int32_t *idx, int32_t n_sel, int32_t tokens) {
+  const int32_t k = n_sel / tokens;
+  for (int32_t t = 0; t < tokens; ++t) {
+    for (double &v : score_) v = v * kScoreDecay;
+    for (int32_t j = 0; j < k; ++j) score_[idx[t * k + j]] = score_[idx[t * k + j]] + 1.0;
+  }
 }
 
 void SlotPlanner::insert(int64_t call, int32_t stage, int32_t slot, int32_t e, CallPlan &out) {
@@ -37,8 +55,9 @@ void SlotPlanner::insert(int64_t call, int32_t stage, int32_t slot, int32_t e, C
   out.fills++;
 }
 
-void SlotPlanner::plan(const int32_t *idx, int32_t n_sel, int32_t mode, int32_t max_fills,
-                       CallPlan &out) {
+void SlotPlanner::plan(const int32_t *idx, int32_t n_sel, int32_t tokens, int32_t mode,
+                       int32_t max_fills, CallPlan &out) {
+  if (policy_ == kPolicyScore) update_scores(idx, n_sel, tokens);
   out = CallPlan();
   out.call = calls_++;
   out.mode = mode;
@@ -94,10 +113,17 @@ void SlotPlanner::plan(const int32_t *idx, int32_t n_sel, int32_t mode, int32_t 
       st.members.push_back(e);
     }
     int32_t placed = 0;
-    for (int32_t e : pending) {
+    std::vector<int32_t> order = pending;
+    if (policy_ == kPolicyScore)
+      std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+        return score_[a] > score_[b] || (score_[a] == score_[b] && a < b);
+      });
+    for (int32_t e : order) {
       if (max_fills >= 0 && placed >= max_fills) break;
       const int32_t v = victim();
       if (v < 0) break;
+      if (policy_ == kPolicyScore && expert_in_[v] >= 0 && !(score_[e] > score_[expert_in_[v]]))
+        break;
       insert(out.call, 0, v, e, out);
       st.fills.push_back(Fill{e, v});
       placed++;

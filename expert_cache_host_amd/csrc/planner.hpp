@@ -17,6 +17,17 @@
 //   slot table maps that stage's experts only; the host table is all -1.
 //   host mode: one stage; at most max_fills fills (-1 = no cap) in ascending id;
 //   the tables are the full tables at call start.
+//
+// Score policy ("Keeping the cache fresh", llama.cpp + MoE expert cache: a
+// decayed usage score per expert, x0.9 per token; missed experts scoring higher
+// than the weakest slot are promoted, within a copy budget):
+//   score[e] starts at 0 (binary64); per call, for each token in order, every
+//   score is multiplied by 0.9 and each expert the token selected gains 1, before
+//   any slot decision.  The victim is the lowest-index empty slot, else the
+//   unprotected slot with the smallest (score of its expert, index).  Host mode
+//   takes the misses in order of (-score, id) and promotes one only when its
+//   score is strictly greater than the victim's, up to max_fills; the first
+//   that is not ends the call's promotions.  Stream mode fills every miss.
 #pragma once
 #include <cstdint>
 #include <vector>
@@ -37,6 +48,9 @@ struct PlanStage {
   std::vector<Fill> fills;       // copies that must land before the stage runs
 };
 
+enum Policy : int32_t { kPolicyLru = 0, kPolicyScore = 1 };
+constexpr double kScoreDecay = 0.9;
+
 struct CallPlan {
   int64_t call = -1;
   int32_t hits = 0, misses = 0, unique = 0, fills = 0, evictions = 0;
@@ -48,10 +62,12 @@ struct CallPlan {
 
 class SlotPlanner {
  public:
-  SlotPlanner(int32_t n_experts, int32_t slots);
+  SlotPlanner(int32_t n_experts, int32_t slots, int32_t policy = kPolicyLru);
 
-  // Plans one call; `scratch` marks are internal.  mode: 0 stream, 1 host.
-  void plan(const int32_t *idx, int32_t n_sel, int32_t mode, int32_t max_fills, CallPlan &out);
+  // Plans one call on n_sel = tokens * k router ids (token-major).  mode: 0
+  // stream, 1 host.
+  void plan(const int32_t *idx, int32_t n_sel, int32_t tokens, int32_t mode, int32_t max_fills,
+            CallPlan &out);
 
   // Slot table of stage s of `p` (stream: that stage's members; host: pre_view).
   void stage_view(const CallPlan &p, int32_t s, int32_t *slot_view, int32_t *host_view) const;
@@ -61,14 +77,19 @@ class SlotPlanner {
   const std::vector<int32_t> &expert_in() const { return expert_in_; }
   const std::vector<int32_t> &slot_of() const { return slot_of_; }
   const std::vector<uint64_t> &last_use() const { return last_use_; }
+  const std::vector<double> &scores() const { return score_; }
+  int32_t policy() const { return policy_; }
   const std::vector<EvictRecord> &log() const { return log_; }
   uint64_t clock() const { return clock_; }
 
  private:
   int32_t victim() const;
+  bool weaker(int32_t a, int32_t b) const;  // slot a before slot b as a victim
+  void update_scores(const int32_t *idx, int32_t n_sel, int32_t tokens);
   void insert(int64_t call, int32_t stage, int32_t slot, int32_t e, CallPlan &out);
 
-  int32_t E_, S_;
+  int32_t E_, S_, policy_;
+  std::vector<double> score_;
   std::vector<int32_t> expert_in_, slot_of_;
   std::vector<uint64_t> last_use_;
   std::vector<uint8_t> seen_;

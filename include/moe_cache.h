@@ -55,6 +55,16 @@ typedef int32_t moe_status;
 #define MOE_MISS_STREAM 0
 #define MOE_MISS_HOST 1
 
+/* Slot policy.  MOE_POLICY_LRU: least-recently-used replacement per layer, the
+ * batch's experts protected ("Longhaul MoE loading", introduction and "Current
+ * scope").  MOE_POLICY_SCORE: a decayed usage score per expert, x0.9 per token
+ * and +1 per selection; a missed expert is admitted only when it scores
+ * strictly more than the weakest unprotected slot, within max_fills_per_call
+ * copies per call ("Keeping the cache fresh", llama.cpp + MoE expert cache).
+ * In stream mode every miss is still filled and the weakest slot is the victim. */
+#define MOE_POLICY_LRU 0
+#define MOE_POLICY_SCORE 1
+
 /* Limits of this build. */
 #define MOE_MAX_EXPERTS 512 /* routed experts per layer */
 #define MOE_MAX_TOPK 64
@@ -70,7 +80,8 @@ typedef struct moe_cache_opts {
   int32_t max_fills_per_call; /* host mode: fills per call, -1 = every miss     default -1 */
   int32_t keep_debug;         /* 1: keep per-layer GPU/host partials            default 0 */
   int32_t timing;             /* 1: time fills and compute with HIP events       default 0 */
-  int32_t reserved[8];        /* must be 0 */
+  int32_t policy;             /* MOE_POLICY_LRU or MOE_POLICY_SCORE             default LRU */
+  int32_t reserved[7];        /* must be 0 */
 } moe_cache_opts;
 
 /* Counters since create or the last moe_cache_reset_stats.  A "selection" is one
@@ -232,6 +243,10 @@ moe_status moe_debug_views(moe_cache *c, int32_t layer, int32_t stage, int32_t *
 /* Current slot state: expert_in[slots] (-1 = empty) and last_use[slots]. */
 moe_status moe_debug_slots(moe_cache *c, int32_t layer, int32_t *expert_in, uint64_t *last_use);
 
+/* Usage scores of `layer`'s experts, scores[n_experts] (binary64; all 0 under
+ * MOE_POLICY_LRU). */
+moe_status moe_debug_scores(moe_cache *c, int32_t layer, double *scores);
+
 /* The layer's whole replacement log since create; copies min(cap, total)
  * records into buf (may be NULL when cap == 0) and stores the total in *n. */
 moe_status moe_debug_evictions(moe_cache *c, int32_t layer, moe_evict_rec *buf, size_t cap,
@@ -247,14 +262,19 @@ moe_status moe_debug_partials(moe_cache *c, int32_t layer, float *gpu_part, floa
 typedef struct moe_planner moe_planner; /* the per-layer LRU slot planner alone */
 
 /* A planner with the same rules and initial state as one layer of a cache
- * (slot s holds expert s).  miss_mode as in moe_cache_opts. */
+ * (slot s holds expert s, every score 0).  miss_mode, max_fills_per_call and
+ * policy as in moe_cache_opts. */
 moe_status moe_planner_create(int32_t n_experts, int32_t slots, int32_t miss_mode,
-                              int32_t max_fills_per_call, moe_planner **out);
+                              int32_t max_fills_per_call, int32_t policy, moe_planner **out);
 
-/* Plans one call on the router ids idx[n_sel] (n_sel = tokens * top_k).  After
- * it, *n_stages, *hits and *misses describe the call. */
-moe_status moe_planner_plan(moe_planner *p, const int32_t *idx, int32_t n_sel, int32_t *n_stages,
-                            int32_t *hits, int32_t *misses);
+/* Plans one call on the router ids idx[n_sel], token-major, n_sel = n_tokens *
+ * top_k (n_sel a multiple of n_tokens >= 1).  After it, *n_stages, *hits and
+ * *misses describe the call. */
+moe_status moe_planner_plan(moe_planner *p, const int32_t *idx, int32_t n_sel, int32_t n_tokens,
+                            int32_t *n_stages, int32_t *hits, int32_t *misses);
+
+/* The usage scores after the last call, scores[n_experts] (all 0 under LRU). */
+moe_status moe_planner_scores(moe_planner *p, double *scores);
 
 /* Tables of one stage of the last planned call, as moe_debug_views. */
 moe_status moe_planner_views(moe_planner *p, int32_t stage, int32_t *slot_view,

@@ -2,7 +2,8 @@
 call by call and checks each call against the oracle.
 
 Checked bit for bit: top-k ids of every token, both lookup tables of every
-stage, the slot state and the whole replacement log.  Checked within tolerance
+stage, the slot state, the usage scores (score policy) and the whole
+replacement log.  Checked within tolerance
 (max |out - oracle| <= 2e-3 * RMS(oracle) over the compared block of each call):
 the layer output, on all of it or on a seeded sample of tokens and columns.
 """
@@ -26,7 +27,7 @@ def log(msg):
 
 class Runner:
     def __init__(self, wl, layers, slots=None, mode="stream", max_fills=-1, keep_debug=False,
-                 host_threads=0, weights=None):
+                 host_threads=0, weights=None, policy="lru"):
         import torch
         import expert_cache_host_amd as m
         import synth
@@ -45,8 +46,9 @@ class Runner:
         self.cache = m.MoECache(nl, wl.n_experts, self.S, wl.d_model, wl.d_ff, weights,
                                 top_k=wl.top_k, miss_mode=mode, n_shared=wl.n_shared,
                                 max_fills_per_call=max_fills, keep_debug=keep_debug,
-                                host_threads=host_threads)
-        self.sims = [LayerSlots(wl.n_experts, self.S) for _ in self.layers]
+                                host_threads=host_threads, policy=policy)
+        self.policy = policy
+        self.sims = [LayerSlots(wl.n_experts, self.S, policy) for _ in self.layers]
         self.routers = []
         for l in self.layers:
             w_r, b = synth.gen_router(wl, l)
@@ -73,7 +75,8 @@ class Runner:
             bad = np.argwhere(idx_gpu != idx_ref)[:5]
             raise AssertionError(f"top-k ids differ at {bad.tolist()}")
         # tables and slot state, bit for bit
-        res = self.sims[li].plan(idx_ref.ravel().tolist(), self.mode, self.max_fills)
+        res = self.sims[li].plan(idx_ref.ravel().tolist(), self.mode, self.max_fills,
+                                 tokens=x_np.shape[0])
         ns, nt = self.cache.last_call(li)
         assert nt == x_np.shape[0]
         assert ns == len(res.stage_views), (ns, len(res.stage_views))
@@ -84,6 +87,8 @@ class Runner:
         ein, lu = self.cache.slot_state(li)
         assert ein.tolist() == self.sims[li].expert_in
         assert lu.tolist() == self.sims[li].last_use
+        if self.policy == "score":
+            assert self.cache.scores(li).tolist() == self.sims[li].score
         if check_out:
             xs = x_np if tok_sample is None else x_np[tok_sample]
             ref = moe_layer(xs, w_r, b, self.layer_buf(li), wl.d_model, wl.d_ff, wl.n_experts,

@@ -134,3 +134,44 @@ def test_prefill_ubatch_sampled():
     assert len(res.stage_views) >= 4
     r.check_log()
     r.close()
+
+
+@pytest.mark.parametrize("mode,budget", [("host", -1), ("host", 1), ("host", 0), ("stream", -1)])
+def test_tiny_score_policy(mode, budget):
+    """Decayed-score slots: every call's tables, scores and outputs against the oracle."""
+    wl = synth.WORKLOADS["tiny"]
+    log(f"tiny score policy mode={mode} budget={budget}")
+    r = Runner(wl, [0], slots=3, mode=mode, max_fills=budget, policy="score")
+    x = synth.gen_hidden(wl, 0)
+    for t in range(x.shape[0]):
+        r.call(0, x[t])
+    r.check_log()
+    st = r.cache.stats()
+    if budget == 0:
+        assert st["fills"] == 0
+    r.close()
+
+
+@pytest.mark.parametrize("T", [3, 4])
+def test_multi_token_score_policy(T):
+    wl = synth.Workload("rag", 11, 1, 256, 512, 16, 4, 6, n_shared=1, router_sigma=0.1,
+                        zipf_s=0.5, rho=None, tokens=T * 6, batch=T)
+    log(f"score policy T={T}")
+    r = Runner(wl, [0], mode="host", max_fills=2, policy="score")
+    x = synth.gen_hidden(wl, 0)
+    for c in range(x.shape[0]):
+        r.call(0, x[c])
+    r.check_log()
+    r.close()
+
+
+def test_gemma_shape_score_policy_host():
+    wl = synth.WORKLOADS["gemma"]
+    log("gemma shape, score policy, host mode, one fill per call")
+    r = Runner(wl, [0, 1], mode="host", max_fills=1, policy="score")
+    xs = [synth.gen_hidden(wl, l, 24) for l in (0, 1)]
+    for t in range(24):
+        for li in range(2):
+            r.call(li, xs[li][t], check_out=(t % 4 == 0))
+    r.check_log()
+    r.close()

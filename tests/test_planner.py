@@ -10,10 +10,10 @@ import expert_cache_host_amd as m
 from oracle.lru import LayerSlots
 
 
-def _compare(e_count, s_count, mode, max_fills, calls, seed):
+def _compare(e_count, s_count, mode, max_fills, calls, seed, policy="lru"):
     rnd = random.Random(seed)
-    lib_p = m.Planner(e_count, s_count, mode, max_fills)
-    sim = LayerSlots(e_count, s_count)
+    lib_p = m.Planner(e_count, s_count, mode, max_fills, policy)
+    sim = LayerSlots(e_count, s_count, policy)
     for _ in range(calls):
         t, k = rnd.choice([(1, 1), (1, 2), (1, 8), (2, 4), (4, 8), (3, 3)])
         k = min(k, e_count)
@@ -25,8 +25,8 @@ def _compare(e_count, s_count, mode, max_fills, calls, seed):
                 pool = list(range(hot)) + rnd.sample(range(e_count), min(e_count, k))
                 pool = sorted(set(pool))
             idx += rnd.sample(pool, k) if len(pool) >= k else rnd.sample(range(e_count), k)
-        ns, hits, misses = lib_p.plan(idx)
-        res = sim.plan(idx, mode, max_fills)
+        ns, hits, misses = lib_p.plan(idx, tokens=t)
+        res = sim.plan(idx, mode, max_fills, tokens=t)
         assert (ns, hits, misses) == (len(res.stage_views), res.hits, res.misses)
         for s in range(ns):
             sv, hv = lib_p.views(s)
@@ -38,6 +38,8 @@ def _compare(e_count, s_count, mode, max_fills, calls, seed):
         ein, lu = lib_p.slot_state()
         assert ein.tolist() == sim.expert_in
         assert lu.tolist() == sim.last_use
+        # binary64 scores bit for bit (same operations in the same order)
+        assert lib_p.scores().tolist() == sim.score
     assert lib_p.evictions() == sim.log
 
 
@@ -65,3 +67,22 @@ def test_planner_staging_prefill_like():
         for s in range(ns):
             assert lib_p.views(s)[0].tolist() == res.stage_views[s]
     assert lib_p.evictions() == sim.log
+
+
+@pytest.mark.parametrize("mode", ["stream", "host"])
+@pytest.mark.parametrize("e_count,s_count", [(8, 4), (8, 1), (16, 16), (128, 32), (256, 64), (20, 3)])
+def test_score_planner_matches_oracle(mode, e_count, s_count):
+    _compare(e_count, s_count, mode, -1, 150, seed=e_count * 17 + s_count, policy="score")
+
+
+@pytest.mark.parametrize("max_fills", [0, 1, 2])
+def test_score_planner_budget_matches_oracle(max_fills):
+    _compare(32, 6, "host", max_fills, 200, seed=100 + max_fills, policy="score")
+
+
+def test_planner_rejects_bad_policy_and_token_split():
+    with pytest.raises(ValueError):
+        m.Planner(8, 4, "host", -1, "fifo")
+    p = m.Planner(8, 4, "host", -1, "score")
+    with pytest.raises(m.MoeError):
+        p.plan([0, 1, 2], tokens=2)
