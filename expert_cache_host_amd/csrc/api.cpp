@@ -102,8 +102,10 @@ struct TimingLog {
       free_list.pop_back();
       return e;
     }
+    // timing only: no system-scope fence (no cache writeback / invalidate
+    // around the timed work); these events order nothing
     hipEvent_t e;
-    HIPCHK(hipEventCreate(&e));
+    HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
     return e;
   }
   void collect() {

@@ -574,7 +574,7 @@ __device__ __forceinline__ int scale_chunks(int rows_here, int nb) {
 
 // gate/up + SwiGLU.  LDS: the bucket's x planes [TT][nb][4], then the gate and
 // the up scales of the workgroup's rows.
-template <int G, int KS, int R, int TT, int MODE, int NW>
+template <int G, int KS, int R, int TT, int MODE, int NW, int PF>
 __global__ __launch_bounds__(64 * NW) void q4_gateup_kernel(GemvArgs a, BucketTable tab) {
   constexpr int RW = 64 / G;
   constexpr int RWG = (NW / KS) * RW * R;
@@ -625,13 +625,15 @@ __global__ __launch_bounds__(64 * NW) void q4_gateup_kernel(GemvArgs a, BucketTa
   for (int c = 0; c < kStageChunks; ++c) xv[c] = stage_ld(tid + NT * c);
   // keep the weight loads behind the staging loads
   __builtin_amdgcn_sched_barrier(0);
-  uint4 wg[R], wu[R];
-  {
-    const int j = blk_of(0);
+  // weights of the first PF K steps in flight before the staging completes
+  uint4 wg[PF][R], wu[PF][R];
+#pragma unroll
+  for (int f = 0; f < PF; ++f) {
+    const int j = blk_of(min(f, NI - 1));
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      wg[i] = q0[ro[i] + j];
-      wu[i] = q1[ro[i] + j];
+      wg[f][i] = q0[ro[i] + j];
+      wu[f][i] = q1[ro[i] + j];
     }
   }
 #pragma unroll
@@ -656,39 +658,45 @@ __global__ __launch_bounds__(64 * NW) void q4_gateup_kernel(GemvArgs a, BucketTa
       ag[i][tt] = 0.0f;
       au[i][tt] = 0.0f;
     }
-  for (int it = 0; it < NI; ++it) {
-    const int j0 = gl + G * (ks + KS * it);
-    const bool ok = j0 < nb;
-    const int j = min(j0, nb - 1);
-    uint4 cw[R], cv[R];
+  for (int it0 = 0; it0 < NI; it0 += PF) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      cw[i] = wg[i];
-      cv[i] = wu[i];
-    }
-    if (it + 1 < NI) {
-      const int jn = blk_of(it + 1);
+    for (int f = 0; f < PF; ++f) {
+      const int it = it0 + f;
+      if (it < NI) {
+        const int j0 = gl + G * (ks + KS * it);
+        const bool ok = j0 < nb;
+        const int j = min(j0, nb - 1);
+        uint4 cw[R], cv[R];
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        wg[i] = q0[ro[i] + jn];
-        wu[i] = q1[ro[i] + jn];
-      }
-    }
-    float dg[R], du[R];
+        for (int i = 0; i < R; ++i) {
+          cw[i] = wg[f][i];
+          cv[i] = wu[f][i];
+        }
+        if (it + PF < NI) {
+          const int jn = blk_of(it + PF);
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      dg[i] = ok ? (float)sg[rl[i] + j] : 0.0f;
-      du[i] = ok ? (float)su[rl[i] + j] : 0.0f;
-    }
+          for (int i = 0; i < R; ++i) {
+            wg[f][i] = q0[ro[i] + jn];
+            wu[f][i] = q1[ro[i] + jn];
+          }
+        }
+        float dg[R], du[R];
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      uint4 P[4];
+        for (int i = 0; i < R; ++i) {
+          dg[i] = ok ? (float)sg[rl[i] + j] : 0.0f;
+          du[i] = ok ? (float)su[rl[i] + j] : 0.0f;
+        }
 #pragma unroll
-      for (int w = 0; w < 4; ++w) P[w] = sx[(tt * nb + j) * 4 + w];
+        for (int tt = 0; tt < TT; ++tt) {
+          uint4 P[4];
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        ag[i][tt] = __builtin_fmaf((float)dot_block_i4(cw[i], P), dg[i], ag[i][tt]);
-        au[i][tt] = __builtin_fmaf((float)dot_block_i4(cv[i], P), du[i], au[i][tt]);
+          for (int w = 0; w < 4; ++w) P[w] = sx[(tt * nb + j) * 4 + w];
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            ag[i][tt] = __builtin_fmaf((float)dot_block_i4(cw[i], P), dg[i], ag[i][tt]);
+            au[i][tt] = __builtin_fmaf((float)dot_block_i4(cv[i], P), du[i], au[i][tt]);
+          }
+        }
       }
     }
   }
@@ -733,7 +741,7 @@ __global__ __launch_bounds__(64 * NW) void q4_gateup_kernel(GemvArgs a, BucketTa
 // block; the block's four threads share its max through two xor shuffles) and
 // stages the workgroup's row scales.  LDS: planes [TT][nb][4], block scales
 // [TT][nb] (fp32), row scales.
-template <int G, int KS, int R, int TT, int MODE, int NW>
+template <int G, int KS, int R, int TT, int MODE, int NW, int PF>
 __global__ __launch_bounds__(64 * NW) void q4_down_kernel(GemvArgs a, BucketTable tab) {
   constexpr int RW = 64 / G;
   constexpr int RWG = (NW / KS) * RW * R;
@@ -802,11 +810,13 @@ __global__ __launch_bounds__(64 * NW) void q4_down_kernel(GemvArgs a, BucketTabl
   const uint4 sv0 = c0[min(tid, n_s - 1)], sv1 = c0[min(tid + NT, n_s - 1)];
   // keep the weight loads behind the staging loads
   __builtin_amdgcn_sched_barrier(0);
-  uint4 wd[R];
-  {
-    const int j = blk_of(0);
+  // weights of the first PF K steps in flight before the prologue runs
+  uint4 wd[PF][R];
 #pragma unroll
-    for (int i = 0; i < R; ++i) wd[i] = q0[ro[i] + j];
+  for (int f = 0; f < PF; ++f) {
+    const int j = blk_of(min(f, NI - 1));
+#pragma unroll
+    for (int i = 0; i < R; ++i) wd[f][i] = q0[ro[i] + j];
   }
   if (tid < n_s) srow[tid] = sv0;
   if (tid + NT < n_s) srow[tid + NT] = sv1;
@@ -826,30 +836,36 @@ __global__ __launch_bounds__(64 * NW) void q4_down_kernel(GemvArgs a, BucketTabl
   for (int i = 0; i < R; ++i)
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) ac[i][tt] = 0.0f;
-  for (int it = 0; it < NI; ++it) {
-    const int j0 = gl + G * (ks + KS * it);
-    const bool ok = j0 < nb;
-    const int j = min(j0, nb - 1);
-    uint4 cw[R];
+  for (int it0 = 0; it0 < NI; it0 += PF) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) cw[i] = wd[i];
-    if (it + 1 < NI) {
-      const int jn = blk_of(it + 1);
+    for (int f = 0; f < PF; ++f) {
+      const int it = it0 + f;
+      if (it < NI) {
+        const int j0 = gl + G * (ks + KS * it);
+        const bool ok = j0 < nb;
+        const int j = min(j0, nb - 1);
+        uint4 cw[R];
 #pragma unroll
-      for (int i = 0; i < R; ++i) wd[i] = q0[ro[i] + jn];
-    }
-    float dd[R];
+        for (int i = 0; i < R; ++i) cw[i] = wd[f][i];
+        if (it + PF < NI) {
+          const int jn = blk_of(it + PF);
 #pragma unroll
-    for (int i = 0; i < R; ++i) dd[i] = ok ? (float)sd[rl[i] + j] : 0.0f;
+          for (int i = 0; i < R; ++i) wd[f][i] = q0[ro[i] + jn];
+        }
+        float dd[R];
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      uint4 P[4];
+        for (int i = 0; i < R; ++i) dd[i] = ok ? (float)sd[rl[i] + j] : 0.0f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) P[w] = sh[(tt * nb + j) * 4 + w];
-      const float se = sscale[tt * nb + j];
+        for (int tt = 0; tt < TT; ++tt) {
+          uint4 P[4];
 #pragma unroll
-      for (int i = 0; i < R; ++i)
-        ac[i][tt] = __builtin_fmaf((float)dot_block_i4(cw[i], P) * se, dd[i], ac[i][tt]);
+          for (int w = 0; w < 4; ++w) P[w] = sh[(tt * nb + j) * 4 + w];
+          const float se = sscale[tt * nb + j];
+#pragma unroll
+          for (int i = 0; i < R; ++i)
+            ac[i][tt] = __builtin_fmaf((float)dot_block_i4(cw[i], P) * se, dd[i], ac[i][tt]);
+        }
+      }
     }
   }
 #pragma unroll
@@ -928,10 +944,10 @@ static void launch_one(const GemvArgs &a, const BucketTable &tab, int nbk, size_
   constexpr int RWG = (NW / KS) * (64 / G) * R;
   const dim3 grid((a.rows + RWG - 1) / RWG, nbk);
   if constexpr (GLU)
-    hipLaunchKernelGGL((q4_gateup_kernel<G, KS, R, TT, MODE, NW>), grid, dim3(64 * NW), lds, s, a,
-                       tab);
+    hipLaunchKernelGGL((q4_gateup_kernel<G, KS, R, TT, MODE, NW, 1>), grid, dim3(64 * NW), lds, s,
+                       a, tab);
   else
-    hipLaunchKernelGGL((q4_down_kernel<G, KS, R, TT, MODE, NW>), grid, dim3(64 * NW), lds, s, a,
+    hipLaunchKernelGGL((q4_down_kernel<G, KS, R, TT, MODE, NW, 1>), grid, dim3(64 * NW), lds, s, a,
                        tab);
 }
 
