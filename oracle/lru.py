@@ -51,6 +51,17 @@ are promoted, within a budget of copies.  Readings:
   only rises);
 * stream mode: every miss is still filled, stage by stage in ascending id, the
   victim being the weakest slot instead of the least recently used one.
+
+Usage profile (llama.cpp fork with multi GPU acceleration, "Persistent hot
+experts": the cache saves how often each expert was used and the next start
+preloads each layer's most-used experts).  Readings:
+
+* every selection of a call adds 1 to its expert's lifetime count (uint32);
+* preload(counts): the layer's S most-used experts by (-count, id) take the
+  slots, the least used of them in slot 0 and the most used in slot S-1, so
+  that with equal last_use the least used is the first victim; every slot gets
+  last_use = the current clock (unprotected from the next stage on), usage
+  scores restart at 0, and the loaded counts are added to the lifetime counts.
 """
 from __future__ import annotations
 
@@ -89,6 +100,7 @@ class LayerSlots:
         self.S = slots
         self.policy = policy
         self.score = [0.0] * n_experts
+        self.usage = [0] * n_experts
         self.expert_in = list(range(slots))
         self.slot_of = [-1] * n_experts
         for s in range(slots):
@@ -151,6 +163,8 @@ class LayerSlots:
                 raise ValueError("expert id out of range")
         if self.policy == SCORE:
             self._update_scores(idx, tokens)
+        for e in idx:
+            self.usage[e] = (self.usage[e] + 1) & 0xFFFFFFFF
         call = self.calls
         self.calls += 1
         uniq = sorted(set(idx))
@@ -224,6 +238,20 @@ class LayerSlots:
         return PlanResult(call=call, unique=uniq, hits=hits, misses=misses, stage_views=views,
                           host_view=host_view, evictions=log, fills=len(log),
                           stage_experts=stage_experts)
+
+    def preload(self, counts):
+        """Loads the S most-used experts by (-count, id); see the module notes."""
+        counts = [int(c) for c in counts]
+        if len(counts) != self.E or any(c < 0 or c > 0xFFFFFFFF for c in counts):
+            raise ValueError("counts must be E uint32 values")
+        ranked = sorted(range(self.E), key=lambda e: (-counts[e], e))[:self.S]
+        self.expert_in = list(reversed(ranked))
+        self.slot_of = [-1] * self.E
+        for s, e in enumerate(self.expert_in):
+            self.slot_of[e] = s
+        self.last_use = [self.clock] * self.S
+        self.score = [0.0] * self.E
+        self.usage = [(u + c) & 0xFFFFFFFF for u, c in zip(self.usage, counts)]
 
     def check_invariants(self):
         for s, e in enumerate(self.expert_in):

@@ -41,6 +41,8 @@ def _parse_traces():
             if tr["stages"] is None:
                 tr["stages"] = {}
             tr["stages"][len(tr["calls"]) - 1] = st
+        elif parts[1] == "preload":
+            tr["preload"] = [int(v) for v in parts[2].split()]
         elif parts[1] == "final":
             tr["final"] = [int(v) for v in parts[2].split()[1:]]
     return traces
@@ -53,6 +55,8 @@ TRACES = _parse_traces()
 def test_golden_trace(name):
     tr = TRACES[name]
     sim = LayerSlots(tr["E"], tr["S"], tr["policy"])
+    if "preload" in tr:
+        sim.preload(tr["preload"])
     for c, (idx, hits, evs) in enumerate(tr["calls"]):
         res = sim.plan(idx, tr["mode"], tr["fills"], tr["tokens"])
         assert res.hits == hits
@@ -183,6 +187,8 @@ class _HighTie(LayerSlots):
 def _trace_passes(cls, tr):
     sim = cls(tr["E"], tr["S"], tr["policy"])
     try:
+        if "preload" in tr:
+            sim.preload(tr["preload"])
         for c, (idx, hits, evs) in enumerate(tr["calls"]):
             res = sim.plan(idx, tr["mode"], tr["fills"], tr["tokens"])
             if res.hits != hits or res.evictions != evs:
@@ -324,3 +330,72 @@ def test_score_budget_zero_never_fills():
     for _ in range(200):
         assert sim.plan(rnd.sample(range(32), 4), HOST, 0).evictions == []
     assert sim.expert_in == [0, 1, 2, 3]
+
+
+# ---------------------------------------------------------------- usage profile
+
+class _MostUsedFirst(LayerSlots):
+    def preload(self, counts):  # planted mistake: the most used expert in slot 0
+        super().preload(counts)
+        self.expert_in = list(reversed(self.expert_in))
+        for s, e in enumerate(self.expert_in):
+            self.slot_of[e] = s
+
+
+def test_planted_preload_order_fails_trace():
+    tr = TRACES["H"]
+    assert _trace_passes(LayerSlots, tr)
+    assert not _trace_passes(_MostUsedFirst, tr)
+
+
+def test_preload_takes_the_top_slots_by_brute_force():
+    rnd = random.Random(21)
+    for e_count, s_count in ((8, 3), (32, 32), (64, 5), (128, 32)):
+        counts = [rnd.choice([0, 1, 2, 5, 5, 40, 2 ** 32 - 1]) for _ in range(e_count)]
+        sim = LayerSlots(e_count, s_count)
+        sim.preload(counts)
+        sim.check_invariants()
+        # every kept expert is used at least as often as every dropped one, and
+        # at an equal count the lower id is kept
+        kept = set(sim.expert_in)
+        for a in kept:
+            for b in set(range(e_count)) - kept:
+                assert counts[a] > counts[b] or (counts[a] == counts[b] and a < b)
+        # slot order: non-decreasing rank of use from slot S-1 down to slot 0
+        keys = [(-counts[e], e) for e in sim.expert_in]
+        assert keys == sorted(keys, reverse=True)
+
+
+def test_usage_counts_every_selection():
+    rnd = random.Random(22)
+    sim = LayerSlots(16, 4, SCORE)
+    seen = [0] * 16
+    for _ in range(300):
+        t = rnd.choice([1, 2, 3])
+        idx = []
+        for _t in range(t):
+            idx += rnd.sample(range(16), 3)
+        for e in idx:
+            seen[e] += 1
+        sim.plan(idx, rnd.choice([STREAM, HOST]), -1, tokens=t)
+    assert sim.usage == seen
+    sim.preload([1] * 16)
+    assert sim.usage == [c + 1 for c in seen]
+    assert sim.score == [0.0] * 16
+
+
+def test_preloaded_profile_serves_its_own_routing():
+    # host mode with no fills: after preloading a sequence's own counts, a
+    # selection hits exactly when its expert is among the S most used
+    rnd = random.Random(23)
+    e_count, s_count = 32, 8
+    seq = [rnd.sample(list(range(6)) + rnd.sample(range(32), 4), 4) for _ in range(100)]
+    counts = [0] * e_count
+    for idx in seq:
+        for e in idx:
+            counts[e] += 1
+    top = set(sorted(range(e_count), key=lambda e: (-counts[e], e))[:s_count])
+    sim = LayerSlots(e_count, s_count)
+    sim.preload(counts)
+    hits = sum(sim.plan(idx, HOST, 0).hits for idx in seq)
+    assert hits == sum(1 for idx in seq for e in idx if e in top)
