@@ -126,6 +126,60 @@ def cpu_baseline(wl, weights, routers, hidden, budget_s=12.0, max_calls=64):
             "sample": f"first {n} calls of layer 0 ({n * wl.batch} tokens), fp64 numpy, {dt:.1f} s"}
 
 
+def preload_study(args, first=32, profile_calls=128):
+    """The usage-profile preload on the workload's own routing: a profile gathered
+    on the last `profile_calls` calls of every layer (standing in for earlier runs)
+    is preloaded into a fresh cache, and the hit rate of the first `first` calls is
+    compared with a cold cache (slot s holds expert s)."""
+    import torch
+    import expert_cache_host_amd as m
+    import synth
+    wl = pick_workload(args.workload)
+    if args.miss_mode is not None:
+        import dataclasses
+        wl = dataclasses.replace(wl, miss_mode=args.miss_mode)
+    n = wl.calls_per_layer
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    weights = synth.gen_all_weights(wl)
+    routers = [synth.gen_router(wl, l) for l in range(wl.layers)]
+    hidden = [synth.gen_hidden(wl, l, n) for l in range(wl.layers)]
+    w_d = [torch.from_numpy(w).to(dev) for w, _ in routers]
+    b_d = [torch.from_numpy(b).to(dev) if b is not None else None for _, b in routers]
+    x_d = [torch.from_numpy(h).to(dev) for h in hidden]
+    out = torch.empty((wl.batch, wl.d_model), dtype=torch.float32, device=dev)
+
+    def new_cache():
+        return m.MoECache(wl.layers, wl.n_experts, wl.slots, wl.d_model, wl.d_ff, weights,
+                          top_k=wl.top_k, miss_mode=wl.miss_mode, n_shared=wl.n_shared,
+                          policy=args.policy, max_fills_per_call=args.max_fills)
+
+    def run(cache, calls):
+        cache.reset_stats()
+        for s in calls:
+            for l in range(wl.layers):
+                cache.forward(l, x_d[l][s], w_d[l], b_d[l], out=out)
+        torch.cuda.synchronize()
+        cache.sync()
+        st = cache.stats()
+        return st["hits"] / max(1, st["selections"])
+
+    c = new_cache()
+    run(c, range(n - profile_calls, n))
+    counts = c.usage()
+    c.close()
+    c = new_cache()
+    cold = run(c, range(first))
+    c.close()
+    c = new_cache()
+    c.preload(counts)
+    warm = run(c, range(first))
+    c.close()
+    print(json.dumps({"study": "usage-profile preload", "workload": describe(wl),
+                      "slot_policy": args.policy, "profile": f"calls {n - profile_calls}..{n - 1} of every layer",
+                      "first_calls": first, "hit_rate_cold": cold, "hit_rate_preloaded": warm}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,9 +196,14 @@ def main():
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without per-kernel events (no roofline)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--preload-study", action="store_true",
+                    help="first-call hit rates cold and after preloading a usage profile")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.preload_study:
+        preload_study(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))

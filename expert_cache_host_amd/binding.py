@@ -86,6 +86,10 @@ def load_library():
         "moe_planner_create": (I32, [I32, I32, I32, I32, I32, ctypes.POINTER(P)]),
         "moe_planner_plan": (I32, [P, P, I32, I32, P, P, P]),
         "moe_planner_scores": (I32, [P, P]),
+        "moe_planner_usage": (I32, [P, P]),
+        "moe_planner_preload": (I32, [P, P]),
+        "moe_cache_usage": (I32, [P, P]),
+        "moe_cache_preload": (I32, [P, P]),
         "moe_planner_views": (I32, [P, I32, P, P]),
         "moe_planner_slots": (I32, [P, P, P]),
         "moe_planner_evictions": (I32, [P, P, SZ, ctypes.POINTER(SZ)]),
@@ -245,6 +249,19 @@ class MoECache:
         _check(load_library().moe_debug_scores(self._h, layer, _ptr(sc)))
         return sc
 
+    def usage(self) -> np.ndarray:
+        """Lifetime selection counts [layers, n_experts] (uint32)."""
+        u = np.empty((self.layers, self.n_experts), np.uint32)
+        _check(load_library().moe_cache_usage(self._h, _ptr(u)))
+        return u
+
+    def preload(self, counts):
+        """Puts each layer's most-used experts (counts [layers, n_experts]) in its slots."""
+        a = np.ascontiguousarray(counts, dtype=np.uint32)
+        if a.shape != (self.layers, self.n_experts):
+            raise ValueError("counts must be [layers, n_experts]")
+        _check(load_library().moe_cache_preload(self._h, _ptr(a)))
+
     def partials(self, layer: int):
         _, t = self.last_call(layer)
         g = np.empty((t, self.d_model), np.float32)
@@ -288,6 +305,17 @@ class Planner:
         sc = np.empty(self.n_experts, np.float64)
         _check(load_library().moe_planner_scores(self._h, _ptr(sc)))
         return sc
+
+    def usage(self) -> np.ndarray:
+        u = np.empty(self.n_experts, np.uint32)
+        _check(load_library().moe_planner_usage(self._h, _ptr(u)))
+        return u
+
+    def preload(self, counts):
+        a = np.ascontiguousarray(counts, dtype=np.uint32)
+        if a.shape != (self.n_experts,):
+            raise ValueError("counts must be [n_experts]")
+        _check(load_library().moe_planner_preload(self._h, _ptr(a)))
 
     def views(self, stage: int):
         sv = np.empty(self.n_experts, np.int32)

@@ -869,6 +869,36 @@ moe_status moe_cache_sync(moe_cache *c) {
   });
 }
 
+moe_status moe_cache_usage(moe_cache *c, uint32_t *counts) {
+  g_err.clear();
+  if (!c || !counts) return fail(MOE_EINVAL, "NULL argument");
+  for (int32_t l = 0; l < c->L; ++l) {
+    const auto &u = c->layers[l].planner->usage();
+    std::copy(u.begin(), u.end(), counts + (size_t)l * c->E);
+  }
+  return MOE_OK;
+}
+
+moe_status moe_cache_preload(moe_cache *c, const uint32_t *counts) {
+  g_err.clear();
+  if (!c || !counts) return fail(MOE_EINVAL, "NULL argument");
+  return guarded(c, [&]() {
+    // nothing may read or fill a slot while it is replaced
+    HIPCHK(hipDeviceSynchronize());
+    for (int32_t l = 0; l < c->L; ++l) {
+      LayerState &ly = c->layers[l];
+      ly.planner->preload(counts + (size_t)l * c->E);
+      const auto &ein = ly.planner->expert_in();
+      for (int32_t s = 0; s < c->S; ++s)
+        HIPCHK(hipMemcpy(c->dev_slot(l, s), c->host_record(l, ein[s]), c->rec(),
+                         hipMemcpyHostToDevice));
+      ly.fill_pending = false;
+      ly.fill_used[0] = ly.fill_used[1] = false;
+    }
+    return MOE_OK;
+  });
+}
+
 void moe_cache_destroy(moe_cache *c) { delete c; }
 
 moe_status moe_debug_last_call(moe_cache *c, int32_t layer, int32_t *n_stages, int32_t *n_tokens) {
@@ -1037,6 +1067,20 @@ moe_status moe_planner_evictions(moe_planner *p, moe_evict_rec *buf, size_t cap,
   if (!p) return fail(MOE_EINVAL, "planner is NULL");
   if (cap && !buf) return fail(MOE_EINVAL, "buf is NULL");
   copy_log(p->p->log(), buf, cap, n);
+  return MOE_OK;
+}
+
+moe_status moe_planner_usage(moe_planner *p, uint32_t *counts) {
+  g_err.clear();
+  if (!p || !counts) return fail(MOE_EINVAL, "NULL argument");
+  std::copy(p->p->usage().begin(), p->p->usage().end(), counts);
+  return MOE_OK;
+}
+
+moe_status moe_planner_preload(moe_planner *p, const uint32_t *counts) {
+  g_err.clear();
+  if (!p || !counts) return fail(MOE_EINVAL, "NULL argument");
+  p->p->preload(counts);
   return MOE_OK;
 }
 

@@ -5,7 +5,8 @@
 namespace moe {
 
 SlotPlanner::SlotPlanner(int32_t n_experts, int32_t slots, int32_t policy)
-    : E_(n_experts), S_(slots), policy_(policy), score_(n_experts, 0.0), expert_in_(slots),
+    : E_(n_experts), S_(slots), policy_(policy), score_(n_experts, 0.0), usage_(n_experts, 0),
+      expert_in_(slots),
       slot_of_(n_experts, -1), last_use_(slots, 0), seen_(n_experts, 0) {
   for (int32_t s = 0; s < slots; ++s) {
     expert_in_[s] = s;
@@ -58,6 +59,7 @@ void SlotPlanner::insert(int64_t call, int32_t stage, int32_t slot, int32_t e, C
 void SlotPlanner::plan(const int32_t *idx, int32_t n_sel, int32_t tokens, int32_t mode,
                        int32_t max_fills, CallPlan &out) {
   if (policy_ == kPolicyScore) update_scores(idx, n_sel, tokens);
+  for (int32_t i = 0; i < n_sel; ++i) usage_[idx[i]]++;
   out = CallPlan();
   out.call = calls_++;
   out.mode = mode;
@@ -131,6 +133,22 @@ void SlotPlanner::plan(const int32_t *idx, int32_t n_sel, int32_t tokens, int32_
     out.stages.push_back(std::move(st));
     out.host_experts = pending;
   }
+}
+
+void SlotPlanner::preload(const uint32_t *counts) {
+  std::vector<int32_t> order(E_);
+  for (int32_t e = 0; e < E_; ++e) order[e] = e;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b) { return counts[a] > counts[b]; });
+  std::fill(slot_of_.begin(), slot_of_.end(), -1);
+  for (int32_t s = 0; s < S_; ++s) {
+    const int32_t e = order[S_ - 1 - s];
+    expert_in_[s] = e;
+    slot_of_[e] = s;
+    last_use_[s] = clock_;
+  }
+  std::fill(score_.begin(), score_.end(), 0.0);
+  for (int32_t e = 0; e < E_; ++e) usage_[e] += counts[e];
 }
 
 void SlotPlanner::stage_view(const CallPlan &p, int32_t s, int32_t *slot_view,

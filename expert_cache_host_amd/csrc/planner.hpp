@@ -28,6 +28,13 @@
 //   takes the misses in order of (-score, id) and promotes one only when its
 //   score is strictly greater than the victim's, up to max_fills; the first
 //   that is not ends the call's promotions.  Stream mode fills every miss.
+//
+// Usage profile ("Persistent hot experts", llama.cpp fork with multi GPU
+// acceleration): every selection adds 1 to its expert's lifetime count
+// (uint32).  preload(counts) puts the S most-used experts by (-count, id) in
+// the slots, the least used of them in slot 0 and the most used in slot S-1,
+// gives every slot last_use = clock, resets the scores and adds the counts to
+// the lifetime counts.
 #pragma once
 #include <cstdint>
 #include <vector>
@@ -78,6 +85,10 @@ class SlotPlanner {
   const std::vector<int32_t> &slot_of() const { return slot_of_; }
   const std::vector<uint64_t> &last_use() const { return last_use_; }
   const std::vector<double> &scores() const { return score_; }
+  const std::vector<uint32_t> &usage() const { return usage_; }
+
+  // Loads the usage profile counts[n_experts] (see above).
+  void preload(const uint32_t *counts);
   int32_t policy() const { return policy_; }
   const std::vector<EvictRecord> &log() const { return log_; }
   uint64_t clock() const { return clock_; }
@@ -90,6 +101,7 @@ class SlotPlanner {
 
   int32_t E_, S_, policy_;
   std::vector<double> score_;
+  std::vector<uint32_t> usage_;
   std::vector<int32_t> expert_in_, slot_of_;
   std::vector<uint64_t> last_use_;
   std::vector<uint8_t> seen_;

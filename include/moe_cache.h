@@ -184,6 +184,23 @@ moe_status moe_layer_forward(moe_cache *c, int32_t layer, const float *x, int32_
 moe_status moe_cache_stats(moe_cache *c, int32_t layer, moe_stats *out);
 
 /* Turns the event timing of opts.timing on (1) or off (0) from now on. */
+/* Usage profile ("Persistent hot experts", llama.cpp fork with multi GPU
+ * acceleration: the cache saves how often each expert was used and the next
+ * start preloads each layer's most-used experts).
+ *
+ * moe_cache_usage writes counts[layers * n_experts] (layer-major, uint32): the
+ * selections of each expert since create, plus any counts preloaded.
+ *
+ * moe_cache_preload reads counts[layers * n_experts] from the caller (host
+ * memory, read during the call only).  It waits for the device, then per layer
+ * puts the S most-used experts by (-count, id) in the slots (the least used of
+ * them in slot 0, the most used in slot S-1, so the least used is evicted
+ * first), copies their records in, makes every slot unprotected from the next
+ * call on, resets the usage scores and adds the counts to the lifetime counts.
+ * Meant at start-up, before the first moe_layer_forward; any time is allowed. */
+moe_status moe_cache_usage(moe_cache *c, uint32_t *counts);
+moe_status moe_cache_preload(moe_cache *c, const uint32_t *counts);
+
 moe_status moe_cache_set_timing(moe_cache *c, int32_t on);
 
 /* Kernels timed one launch at a time when timing is on. */
@@ -275,6 +292,11 @@ moe_status moe_planner_plan(moe_planner *p, const int32_t *idx, int32_t n_sel, i
 
 /* The usage scores after the last call, scores[n_experts] (all 0 under LRU). */
 moe_status moe_planner_scores(moe_planner *p, double *scores);
+
+/* Lifetime counts and profile preload of one layer, as moe_cache_usage and
+ * moe_cache_preload (counts[n_experts]). */
+moe_status moe_planner_usage(moe_planner *p, uint32_t *counts);
+moe_status moe_planner_preload(moe_planner *p, const uint32_t *counts);
 
 /* Tables of one stage of the last planned call, as moe_debug_views. */
 moe_status moe_planner_views(moe_planner *p, int32_t stage, int32_t *slot_view,

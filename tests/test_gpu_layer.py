@@ -175,3 +175,30 @@ def test_gemma_shape_score_policy_host():
             r.call(li, xs[li][t], check_out=(t % 4 == 0))
     r.check_log()
     r.close()
+
+
+@pytest.mark.parametrize("mode,policy", [("host", "score"), ("stream", "lru")])
+def test_usage_profile_preload(mode, policy):
+    """Lifetime counts read back; a preloaded profile re-seats the slots on the GPU
+    exactly as the oracle does, and outputs stay exact."""
+    wl = synth.WORKLOADS["gemma"]
+    log(f"usage profile preload mode={mode} policy={policy}")
+    r = Runner(wl, [0, 1], mode=mode, max_fills=1 if mode == "host" else -1, policy=policy)
+    xs = [synth.gen_hidden(wl, l, 20) for l in (0, 1)]
+    for t in range(8):
+        for li in range(2):
+            r.call(li, xs[li][t], check_out=(t % 4 == 0))
+    u = r.cache.usage()
+    assert u.tolist() == [sim.usage for sim in r.sims]
+    rng = np.random.default_rng(5)
+    counts = (u[:, ::-1] + rng.integers(0, 3, size=u.shape)).astype(np.uint32)
+    r.cache.preload(counts)
+    for li in range(2):
+        r.sims[li].preload(counts[li].tolist())
+        ein, _ = r.cache.slot_state(li)
+        assert ein.tolist() == r.sims[li].expert_in
+    for t in range(8, 20):
+        for li in range(2):
+            r.call(li, xs[li][t], check_out=(t % 3 == 0))
+    r.check_log()
+    r.close()

@@ -40,6 +40,7 @@ def _compare(e_count, s_count, mode, max_fills, calls, seed, policy="lru"):
         assert lu.tolist() == sim.last_use
         # binary64 scores bit for bit (same operations in the same order)
         assert lib_p.scores().tolist() == sim.score
+        assert lib_p.usage().tolist() == sim.usage
     assert lib_p.evictions() == sim.log
 
 
@@ -86,3 +87,28 @@ def test_planner_rejects_bad_policy_and_token_split():
     p = m.Planner(8, 4, "host", -1, "score")
     with pytest.raises(m.MoeError):
         p.plan([0, 1, 2], tokens=2)
+
+
+@pytest.mark.parametrize("policy", ["lru", "score"])
+@pytest.mark.parametrize("mode", ["stream", "host"])
+def test_planner_preload_matches_oracle(policy, mode):
+    rnd = random.Random(31)
+    e_count, s_count = 64, 8
+    lib_p = m.Planner(e_count, s_count, mode, -1, policy)
+    sim = LayerSlots(e_count, s_count, policy)
+    for rnd_call in range(120):
+        if rnd_call in (0, 50):
+            counts = np.array([rnd.choice([0, 1, 3, 3, 7, 2 ** 32 - 1]) for _ in range(e_count)],
+                              np.uint32)
+            lib_p.preload(counts)
+            sim.preload(counts.tolist())
+        idx = rnd.sample(range(e_count), 4)
+        ns, hits, misses = lib_p.plan(idx)
+        res = sim.plan(idx, mode, -1)
+        assert (ns, hits) == (len(res.stage_views), res.hits)
+        assert lib_p.views(0)[0].tolist() == res.stage_views[0]
+        ein, lu = lib_p.slot_state()
+        assert ein.tolist() == sim.expert_in and lu.tolist() == sim.last_use
+        assert lib_p.usage().tolist() == sim.usage
+        assert lib_p.scores().tolist() == sim.score
+    assert lib_p.evictions() == sim.log
