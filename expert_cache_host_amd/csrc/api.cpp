@@ -168,7 +168,7 @@ struct moe_cache {
   bool timing = false;
   // device workspace
   int32_t cap_T = 0;
-  DevBuf z, idx, w, meta, bucket_pair, h, y, xp, xsw, xscale, hp, hsw, hscale, xq, xs;
+  DevBuf z, idx, w, meta, bucket_pair, items, h, y, xp, xsw, xscale, hp, hsw, hscale, xq, xs;
   DevBuf buckets, pair_slot;  // decode: bucket list and pair -> slot of the hits
   // pinned host staging
   PinnedBuf h_idx, h_w, h_x, partial[2];
@@ -223,6 +223,7 @@ struct moe_cache {
     w.ensure((size_t)T * k * 4);
     meta.ensure((size_t)moe::kMetaInts * 4);
     bucket_pair.ensure(P * 4);
+    items.ensure(((size_t)moe::gemm_items_bound(moe::kMetaB, (int)P) + 1) * 4);
     h.ensure(P * (size_t)f * 4);
     y.ensure(P * (size_t)d * 4);
     xp.ensure((size_t)T * d * 4);
@@ -343,10 +344,11 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
     KTime kt(c, MOE_K_REMAP, st);
     HIPCHK(moe::launch_remap((const int32_t *)c->idx.p, T, k, view, shared_slot,
                              c->S + c->o.n_shared, (int32_t *)c->meta.p,
-                             (int32_t *)c->bucket_pair.p, st));
+                             (int32_t *)c->bucket_pair.p, (int32_t *)c->items.p, st));
     kt.end((double)P * 8);
     a.meta = (const int32_t *)c->meta.p;
     a.bucket_pair = (const int32_t *)c->bucket_pair.p;
+    a.items = (const int32_t *)c->items.p;
   }
   a.slots = c->layers[layer].d_slots;
   a.bt = decode && !tab ? (const int32_t *)c->buckets.p : nullptr;
@@ -371,10 +373,12 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
   a.in_by_pair = 0;
   a.out = (float *)c->h.p;
   if (!decode && !tab) {
-    // matrix-core grouped GEMM: gate/up + SwiGLU, h -> binary16 pairs, down
+    // matrix-core grouped GEMM: gate/up + SwiGLU, h -> binary16 pairs, down;
+    // one grid column per work item (bucket, token pass), bounded from above
+    const int n_items = moe::gemm_items_bound(std::min(n_buckets, c->S + c->o.n_shared), P);
     {
       KTime kt(c, MOE_K_GATEUP, st);
-      HIPCHK(moe::launch_mfma(a, true, n_buckets, st));
+      HIPCHK(moe::launch_mfma(a, true, n_items, st));
       kt.end(work_experts * 2.0 * (double)c->f * (double)L.nb_gu * 18.0);
     }
     const int P_all = T * k + T * c->o.n_shared;
@@ -396,7 +400,7 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
     b.out = (float *)c->y.p;
     {
       KTime kt(c, MOE_K_DOWN, st);
-      HIPCHK(moe::launch_mfma(b, false, n_buckets, st));
+      HIPCHK(moe::launch_mfma(b, false, n_items, st));
       kt.end(work_experts * (double)c->d * (double)L.nb_dn * 18.0);
     }
     return;

@@ -376,58 +376,63 @@ hipError_t launch_topk_decode(const float *z, int T, int E, int k, int norm_topk
 }
 
 // ============================================================== remap + bucket
-// One workgroup.  Counts pairs per slot, lays buckets out in slot order, then
-// places pairs stably (ascending pair id inside a bucket), 256 pairs at a time.
-__global__ __launch_bounds__(256) void remap_kernel(const int32_t *__restrict__ idx, int T, int k,
-                                                    SlotView view, int shared_slot, int n_ids,
-                                                    int32_t *__restrict__ meta,
-                                                    int32_t *__restrict__ bucket_pair) {
+// One workgroup of 16 waves.  Counts pairs per slot, lays buckets out in slot
+// order with their token passes, then places pairs stably (ascending pair id
+// inside a bucket): wave w owns the slots s = w (mod 16) and walks the pairs,
+// staged through LDS in runs of kRemapRun, with one ballot per 64 pairs.
+constexpr int kRemapWaves = 16;
+constexpr int kRemapRun = 4096;
+
+__global__ __launch_bounds__(64 * kRemapWaves) void remap_kernel(
+    const int32_t *__restrict__ idx, int T, int k, SlotView view, int shared_slot, int n_ids,
+    int32_t *__restrict__ meta, int32_t *__restrict__ bucket_pair, int32_t *__restrict__ items) {
   __shared__ int cnt[kMetaB];
   __shared__ int base[kMetaB];
-  __shared__ int run[kMetaB];
-  __shared__ int sl[256];
-  const int tid = threadIdx.x;
+  __shared__ int16_t sl[kRemapRun];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P_routed = T * k;
   const int P = P_routed + (shared_slot >= 0 ? T : 0);
-  for (int s = tid; s < n_ids; s += 256) {
-    cnt[s] = 0;
-    run[s] = 0;
-  }
+  for (int s = tid; s < n_ids; s += 64 * kRemapWaves) cnt[s] = 0;
   __syncthreads();
   auto slot_of = [&](int p) -> int {
     return p < P_routed ? (int)view.slot[idx[p]] : shared_slot;
   };
-  for (int p = tid; p < P; p += 256) {
+  for (int p = tid; p < P; p += 64 * kRemapWaves) {
     const int s = slot_of(p);
     if (s >= 0) atomicAdd(&cnt[s], 1);
   }
   __syncthreads();
-  if (tid < 64) {
-    const int lane = tid;
+  if (wave == 0) {
+    // each lane scans a run of slots; exclusive prefix of buckets, pairs and
+    // token passes over the lanes
     const int chunk = (n_ids + 63) / 64;
     const int s0 = min(n_ids, lane * chunk), s1 = min(n_ids, s0 + chunk);
-    int na = 0, np = 0;
+    int na = 0, np = 0, ni = 0;
     for (int s = s0; s < s1; ++s)
       if (cnt[s] > 0) {
         na++;
         np += cnt[s];
+        ni += (cnt[s] + kGemmTokens - 1) / kGemmTokens;
       }
-    int ia = na, ip = np;  // inclusive scans
+    int ia = na, ip = np, ii = ni;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int oa = __shfl_up(ia, off, 64), op = __shfl_up(ip, off, 64);
+      const int oa = __shfl_up(ia, off, 64), op = __shfl_up(ip, off, 64),
+                oi = __shfl_up(ii, off, 64);
       if (lane >= off) {
         ia += oa;
         ip += op;
+        ii += oi;
       }
     }
-    int a = ia - na, q = ip - np;
+    int a = ia - na, q = ip - np, it = ii - ni;
     for (int s = s0; s < s1; ++s) {
       if (cnt[s] > 0) {
         meta[2 + a] = s;
         meta[2 + kMetaB + a] = q;
         meta[2 + 2 * kMetaB + a] = cnt[s];
         base[s] = q;
+        for (int j = 0; j * kGemmTokens < cnt[s]; ++j) items[1 + it++] = a | (j << 16);
         q += cnt[s];
         a++;
       }
@@ -435,29 +440,37 @@ __global__ __launch_bounds__(256) void remap_kernel(const int32_t *__restrict__ 
     if (lane == 63) {
       meta[0] = ia;
       meta[1] = ip;
+      items[0] = ii;
     }
   }
   __syncthreads();
-  for (int c = 0; c < P; c += 256) {
-    const int p = c + tid;
-    const int s = p < P ? slot_of(p) : -1;
-    sl[tid] = s;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int c0 = 0; c0 < P; c0 += kRemapRun) {
+    const int n = min(kRemapRun, P - c0);
+    for (int i = tid; i < n; i += 64 * kRemapWaves) sl[i] = (int16_t)slot_of(c0 + i);
     __syncthreads();
-    if (s >= 0) {
-      int rank = 0;
-      for (int i = 0; i < tid; ++i) rank += (sl[i] == s) ? 1 : 0;
-      bucket_pair[base[s] + run[s] + rank] = p;
+    for (int s = wave; s < n_ids; s += kRemapWaves) {
+      if (cnt[s] == 0) continue;
+      int pos = base[s];  // wave-owned: the next free place of bucket s
+      for (int i0 = 0; i0 < n; i0 += 64) {
+        const int i = i0 + lane;
+        const bool mine = i < n && sl[i] == s;
+        const uint64_t m = __ballot(mine);
+        if (mine) bucket_pair[pos + __popcll(m & below)] = c0 + i;
+        pos += __popcll(m);
+      }
+      if (lane == 0) base[s] = pos;
     }
-    __syncthreads();
-    if (s >= 0) atomicAdd(&run[s], 1);
     __syncthreads();
   }
 }
 
 hipError_t launch_remap(const int32_t *idx, int T, int k, const SlotView &view, int shared_slot,
-                        int n_slot_ids, int32_t *meta, int32_t *bucket_pair, hipStream_t s) {
-  hipLaunchKernelGGL(remap_kernel, dim3(1), dim3(256), 0, s, idx, T, k, view, shared_slot,
-                     n_slot_ids, meta, bucket_pair);
+                        int n_slot_ids, int32_t *meta, int32_t *bucket_pair, int32_t *items,
+                        hipStream_t s) {
+  if (n_slot_ids < 1 || n_slot_ids > kMetaB) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(remap_kernel, dim3(1), dim3(64 * kRemapWaves), 0, s, idx, T, k, view,
+                     shared_slot, n_slot_ids, meta, bucket_pair, items);
   return hipGetLastError();
 }
 
@@ -998,217 +1011,258 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
 }
 
 // ============================================================== prefill MFMA GEMM
-// Per workgroup: 4 waves x 2 row blocks of 16 = 128 weight rows of one bucket's
-// expert, and its tokens in passes of up to NT x 16.  The K dimension runs in
-// chunks of KC blocks through two LDS buffers: while the waves multiply chunk c,
-// the chunk c+1 loads (raw nibble words, block scales, the tokens' hi/lo
-// activation pairs and block sums) are in flight and land in the other buffer.
-// A lane turns its nibble word into binary16 (1024 + q) as it builds the MFMA A
-// operand; each 32-weight block is one pair of v_mfma_f32_16x16x32_f16 (x hi,
-// x lo), and d * (C - 1032 * sum x) is folded into the accumulators in fp32.
-// Operand lanes: A lane l = row l%16 and the 8 K values of word l/16 of the
-// block (elements g, g+2, g+16, g+18, g+1, g+3, g+17, g+19 with g = 4*(l/16));
-// B lane l = token l%16 and the same 8 K values; C lane l = rows 4*(l/16)+i,
-// token l%16.
+// Per workgroup: 4 waves x 16 weight rows of one bucket's expert, and one pass of
+// up to 32 of the bucket's tokens (two 16-token tiles).  Each wave streams its
+// own rows through registers: lane l loads the whole 16-byte nibble block
+// 4c + l/16 of row l%16 for K chunk c (4 blocks), two chunks ahead of the one it
+// multiplies.  A 4 x 4 word transpose across the four 16-lane rows of the wave
+// (two rounds of gfx950 lane swaps, no LDS) turns "block per lane row" into the
+// MFMA A layout (lane l: row l%16, word l/16 of each of the 4 blocks); the 16
+// rows' block scales go to the C layout (lane l: rows 4*(l/16)+i) through a
+// small wave-private LDS table of fp32 values.  The activation tiles (binary16
+// hi/lo pairs for the chunk's 4 blocks and the pass's tokens) are staged per
+// chunk for the whole workgroup in two LDS buffers, loaded two chunks ahead,
+// with one barrier per chunk.
+// A lane turns its nibble word into binary16 q - 8 (exact: 1024 + q from the
+// exponent trick, minus 1032); each 32-weight block is one pair of
+// v_mfma_f32_16x16x32_f16 (x hi, x lo) per token tile, and the block scale d
+// multiplies the pair's result into the fp32 accumulators.  Operand lanes: A
+// lane l = row l%16 and the 8 K values of word l/16 of the block (elements g,
+// g+2, g+16, g+18, g+1, g+3, g+17, g+19 with g = 4*(l/16)); B lane l = token
+// l%16 and the same 8 K values; C lane l = rows 4*(l/16)+i, token l%16.
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int K6_RB = 2;                  // 16-row blocks per wave
-constexpr int K6_ROWS = 4 * 16 * K6_RB;   // rows per workgroup
-constexpr int K6_KC = 4;                  // blocks per K chunk
-constexpr int K6_NT = 2;                  // 16-token tiles per pass
-constexpr int K6_AW = K6_KC * 4 + 1;      // words per LDS row (one pad against bank conflicts)
+constexpr int K6_WAVES = 4;
+constexpr int K6_ROWS = K6_WAVES * 16;  // rows per workgroup
+constexpr int K6_KC = 4;                // blocks per K chunk
+constexpr int K6_TOK = kGemmTokens;     // tokens per pass (two tiles of 16)
+constexpr int K6_PD = 2;                // K chunks in flight per wave
 
-__device__ __forceinline__ uint4 decode_word_h(uint32_t q) {
+__device__ __forceinline__ float pick4(const float4 &v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// binary16 pairs of (q - 8) for the 8 nibbles of word w, in the operand order
+__device__ __forceinline__ half8_t decode_word_h(uint32_t w) {
   const uint32_t m = 0x000F000Fu, mag = 0x64006400u;
-  uint4 r;
-  r.x = and_or(q, m, mag);
-  r.y = and_or(q >> 4, m, mag);
-  r.z = and_or(q >> 8, m, mag);
-  r.w = and_or(q >> 12, m, mag);
+  const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  half8_t r;
+  const half2_t p0 = __builtin_bit_cast(half2_t, and_or(w, m, mag)) - off;
+  const half2_t p1 = __builtin_bit_cast(half2_t, and_or(w >> 4, m, mag)) - off;
+  const half2_t p2 = __builtin_bit_cast(half2_t, and_or(w >> 8, m, mag)) - off;
+  const half2_t p3 = __builtin_bit_cast(half2_t, and_or(w >> 12, m, mag)) - off;
+  r[0] = p0[0];
+  r[1] = p0[1];
+  r[2] = p1[0];
+  r[3] = p1[1];
+  r[4] = p2[0];
+  r[5] = p2[1];
+  r[6] = p3[0];
+  r[7] = p3[1];
   return r;
 }
 
-template <int NM>
-struct K6Buf {
-  uint32_t A[NM][K6_ROWS][K6_AW];
-  float S[NM][K6_ROWS][K6_KC];
-  uint4 B[K6_NT * 16][K6_KC * 4][2];
-  float X[K6_NT * 16][K6_KC];
-};
+// 4 x 4 transpose of 32-bit words over the wave's four 16-lane rows: on entry
+// row g holds (w0..w3) of block g, on exit row g holds word g of blocks 0..3.
+// Round 1 swaps the off-diagonal 2 x 2 quarters between lane halves 0-31 and
+// 32-63, round 2 the off-diagonal entries between rows 2j and 2j+1.
+__device__ __forceinline__ uint4 transpose_rows(uint4 v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  return make_uint4(c[0], c[1], d[0], d[1]);
+}
 
 template <int NM>
-struct K6Regs {
-  uint4 w[NM][2];
-  float sc[NM][2];
-  uint4 b[2][2];
-  float4 xs;
+struct K6Lds {
+  // [buf][token][word * 2 + hi/lo]; one spare entry per token row staggers the
+  // rows over the banks (row stride 528 B = 16 B mod 128 B)
+  uint4 B[2][K6_TOK][K6_KC * 8 + 1];
+  float S[K6_WAVES][NM][K6_KC][16];  // block scales [block][row], wave-private
+  int tok[K6_TOK];
 };
 
 template <bool GLU>
-__global__ __launch_bounds__(256) void q4_mfma_kernel(GemvArgs a) {
+__global__ __launch_bounds__(256, 2) void q4_mfma_kernel(GemvArgs a) {
   constexpr int NM = GLU ? 2 : 1;
-  __shared__ K6Buf<NM> buf[2];
-  __shared__ int lTok[K6_NT * 16];
+  __shared__ K6Lds<NM> L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int bucket = blockIdx.y;
-  if (bucket >= a.meta[0]) return;
+  // XCD-aware order: workgroup l of the grid runs on XCD l % 8; each XCD takes a
+  // contiguous run of the (item, row tile) work, so that the row tiles of one
+  // item, which read the same activations, share that XCD's L2.  Workgroups past
+  // their XCD's run exit.
+  const int gx = gridDim.x;
+  const int n_work = a.items[0] * gx;
+  const int lin = blockIdx.y * gx + blockIdx.x;
+  const int xcd = lin & 7, r = lin >> 3;
+  const int q8 = n_work >> 3, rem = n_work & 7;
+  if (r >= q8 + (xcd < rem ? 1 : 0)) return;
+  const int work = xcd * q8 + min(xcd, rem) + r;
+  const int item = a.items[1 + work / gx];
+  const int tile = work % gx;
+  const int bucket = item & 0xFFFF;
+  const int g0 = (item >> 16) * K6_TOK;
   const int slot = a.meta[2 + bucket];
   const int off = a.meta[2 + kMetaB + bucket];
   const int cnt = a.meta[2 + 2 * kMetaB + bucket];
   const uint8_t *rec = a.slots + (long long)slot * a.rec_bytes;
-  const int row_base = blockIdx.x * K6_ROWS;
-  const int words = a.nb * 4;
-  const uint32_t *qb[NM];
-  const __half *sb[NM];
-  qb[0] = reinterpret_cast<const uint32_t *>(rec + a.off_q0);
-  sb[0] = reinterpret_cast<const __half *>(rec + a.off_s0);
-  if constexpr (GLU) {
-    qb[NM - 1] = reinterpret_cast<const uint32_t *>(rec + a.off_q1);
-    sb[NM - 1] = reinterpret_cast<const __half *>(rec + a.off_s1);
+  const int nb = a.nb, words = nb * 4;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int row0 = tile * K6_ROWS + wave * 16;
+  const long long my_row = min(row0 + lr, a.rows - 1);
+  const uint4 *q0row = reinterpret_cast<const uint4 *>(rec + a.off_q0) + my_row * nb;
+  const _Float16 *s0row = reinterpret_cast<const _Float16 *>(rec + a.off_s0) + my_row * nb;
+  const uint4 *q1row = reinterpret_cast<const uint4 *>(rec + a.off_q1) + my_row * nb;
+  const _Float16 *s1row = reinterpret_cast<const _Float16 *>(rec + a.off_s1) + my_row * nb;
+  const int nch = (nb + K6_KC - 1) / K6_KC;
+  const int ntok = min(K6_TOK, cnt - g0);
+  const int n_tiles = (ntok + 15) >> 4;
+  if (tid < K6_TOK) {
+    const int p = a.bucket_pair[off + g0 + min(tid, ntok - 1)];
+    L.tok[tid] = a.in_by_pair ? p : pair_row(a, p);
   }
-  const int m = lane & 15, kg = lane >> 4;
-  const int n_chunks = (a.nb + K6_KC - 1) / K6_KC;
+  __syncthreads();
 
-  for (int g0 = 0; g0 < cnt; g0 += K6_NT * 16) {
-    const int ntok = min(K6_NT * 16, cnt - g0);
-    const int n_tiles = (ntok + 15) >> 4;
-    if (tid < K6_NT * 16) {
-      const int p = a.bucket_pair[off + g0 + min(tid, ntok - 1)];
-      lTok[tid] = a.in_by_pair ? p : pair_row(a, p);
-    }
-    __syncthreads();
-    // staging roles: items (row, block) = 128 x KC per matrix, 2 per thread;
-    // (token, word) = 32 x 4*KC, 2 per thread; (token, block) = 32 x KC, 1 per thread
-    auto load_chunk = [&](int c, K6Regs<NM> &r) {
-      const int kc = c * K6_KC;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int it = tid + 256 * j;
-        const int row = it >> 2, blk = min(kc + (it & 3), a.nb - 1);
-        const long long gr = min(row_base + row, a.rows - 1);
-#pragma unroll
-        for (int q = 0; q < NM; ++q) {
-          r.w[q][j] = *reinterpret_cast<const uint4 *>(qb[q] + gr * words + blk * 4);
-          r.sc[q][j] = __half2float(sb[q][gr * a.nb + blk]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int it = tid + 256 * j;
-        const int t = it >> 4, w = it & 15;
-        const int wq = min(kc * 4 + w, words - 1);
-        const uint4 *src =
-            reinterpret_cast<const uint4 *>(a.xp + ((long long)lTok[t] * words + wq) * 8);
-        r.b[j][0] = src[0];
-        r.b[j][1] = src[1];
-      }
-      {
-        const int t = (tid >> 2) & 31, b = tid & 3;
-        const int blk = min(kc + b, a.nb - 1);
-        r.xs = *reinterpret_cast<const float4 *>(a.xsw + (long long)lTok[t] * words + blk * 4);
-      }
+  // activation staging of chunk c: per token 16 words x (hi, lo) = 512
+  // contiguous bytes, 32 lanes per token, four 16-B loads per thread.  Two
+  // register sets: the loads of chunk c + 2 are issued in step c and stored to
+  // LDS at the end of step c + 1.
+  auto load_b = [&](int c, uint4 &o0, uint4 &o1, uint4 &o2, uint4 &o3)
+      __attribute__((always_inline)) {
+    const int v = tid & 31;
+    const int wd = min(c * 16 + (v >> 1), words - 1);
+    auto src = [&](int j) -> const uint4 * {
+      return reinterpret_cast<const uint4 *>(
+                 a.xp + ((long long)L.tok[(tid >> 5) + 8 * j] * words + wd) * 8) +
+             (v & 1);
     };
-    auto store_chunk = [&](K6Buf<NM> &B, const K6Regs<NM> &r) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int it = tid + 256 * j;
-        const int row = it >> 2, b = it & 3;
-#pragma unroll
-        for (int q = 0; q < NM; ++q) {
-          B.A[q][row][b * 4 + 0] = r.w[q][j].x;
-          B.A[q][row][b * 4 + 1] = r.w[q][j].y;
-          B.A[q][row][b * 4 + 2] = r.w[q][j].z;
-          B.A[q][row][b * 4 + 3] = r.w[q][j].w;
-          B.S[q][row][b] = r.sc[q][j];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int it = tid + 256 * j;
-        B.B[it >> 4][it & 15][0] = r.b[j][0];
-        B.B[it >> 4][it & 15][1] = r.b[j][1];
-      }
-      if (tid < 128) B.X[tid >> 2][tid & 3] = (r.xs.x + r.xs.y) + (r.xs.z + r.xs.w);
-    };
-
-    floatx4 acc[NM][K6_RB][K6_NT];
-#pragma unroll
-    for (int q = 0; q < NM; ++q)
-#pragma unroll
-      for (int rb = 0; rb < K6_RB; ++rb)
-#pragma unroll
-        for (int t = 0; t < K6_NT; ++t) acc[q][rb][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    K6Regs<NM> regs;
-    load_chunk(0, regs);
-    store_chunk(buf[0], regs);
-    __syncthreads();
-    for (int c = 0; c < n_chunks; ++c) {
-      if (c + 1 < n_chunks) load_chunk(c + 1, regs);
-      const K6Buf<NM> &B = buf[c & 1];
-      const int kb_n = min(K6_KC, a.nb - c * K6_KC);
-      for (int kb = 0; kb < kb_n; ++kb) {
-        half8_t Bh[K6_NT], Bl[K6_NT];
-        float o1032[K6_NT];
-#pragma unroll
-        for (int t = 0; t < K6_NT; ++t) {
-          Bh[t] = __builtin_bit_cast(half8_t, B.B[t * 16 + m][kb * 4 + kg][0]);
-          Bl[t] = __builtin_bit_cast(half8_t, B.B[t * 16 + m][kb * 4 + kg][1]);
-          o1032[t] = 1032.0f * B.X[t * 16 + m][kb];
-        }
-#pragma unroll
-        for (int rb = 0; rb < K6_RB; ++rb) {
-          const int rw = wave * (16 * K6_RB) + rb * 16;
-#pragma unroll
-          for (int q = 0; q < NM; ++q) {
-            const half8_t A = __builtin_bit_cast(half8_t, decode_word_h(B.A[q][rw + m][kb * 4 + kg]));
-            float sc[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sc[i] = B.S[q][rw + kg * 4 + i][kb];
-#pragma unroll
-            for (int t = 0; t < K6_NT; ++t) {
-              if (t < n_tiles) {
-                floatx4 cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh[t], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl[t], cc, 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[q][rb][t][i] += sc[i] * (cc[i] - o1032[t]);
-              }
-            }
-          }
-        }
-      }
-      if (c + 1 < n_chunks) store_chunk(buf[(c + 1) & 1], regs);
-      __syncthreads();
+    o0 = *src(0);
+    o1 = *src(1);
+    o2 = *src(2);
+    o3 = *src(3);
+  };
+  auto store_b = [&](int buf, const uint4 &o0, const uint4 &o1, const uint4 &o2,
+                     const uint4 &o3) __attribute__((always_inline)) {
+    const int v = tid & 31, t = tid >> 5;
+    L.B[buf][t][v] = o0;
+    L.B[buf][t + 8][v] = o1;
+    L.B[buf][t + 16][v] = o2;
+    L.B[buf][t + 24][v] = o3;
+  };
+  // this lane's weight block of chunk c, per matrix (the second one only for
+  // the GLU), held in named registers.  Unconditional loads (clamped block):
+  // blocks past the row end get a zero scale when the chunk is used.
+  auto load_a = [&](int c, uint4 &w0, uint4 &w1, _Float16 &s0, _Float16 &s1)
+      __attribute__((always_inline)) {
+    const int bc = min(c * K6_KC + lg, nb - 1);
+    w0 = q0row[bc];
+    s0 = s0row[bc];
+    if constexpr (GLU) {
+      w1 = q1row[bc];
+      s1 = s1row[bc];
     }
-    // C lane layout: rows rw + kg*4 + i, token column m of each tile
+  };
+  static_assert(K6_PD == 2, "the chunk ring is written out for two chunks");
+  uint4 wa0, wa1, wb0, wb1;
+  _Float16 sa0, sa1, sb0, sb1;
+  uint4 ba0, ba1, ba2, ba3, bb0, bb1, bb2, bb3;
+  // issue order as in the steady state (activations, then weights, per chunk)
+  load_b(0, ba0, ba1, ba2, ba3);
+  load_a(0, wa0, wa1, sa0, sa1);
+  load_b(min(1, nch - 1), bb0, bb1, bb2, bb3);
+  load_a(min(1, nch - 1), wb0, wb1, sb0, sb1);
+  store_b(0, ba0, ba1, ba2, ba3);
+  __syncthreads();
+
+  floatx4 acc00 = {0.f, 0.f, 0.f, 0.f}, acc01 = acc00, acc10 = acc00, acc11 = acc00;
+
+  // one matrix of one chunk: transposed words t, scales from the LDS table
+  auto mma = [&](int cur, int q, const uint4 &t, floatx4 &c0, floatx4 &c1)
+      __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < K6_NT; ++t) {
-      const int col = t * 16 + m;
-      if (t < n_tiles && col < ntok) {
-        const int p = a.bucket_pair[off + g0 + col];
-        const float sc = a.xscale[lTok[col]];
+    for (int b = 0; b < K6_KC; ++b) {
+      const uint32_t aw = b == 0 ? t.x : b == 1 ? t.y : b == 2 ? t.z : t.w;
+      const half8_t A = decode_word_h(aw);
+      const float4 d = *reinterpret_cast<const float4 *>(&L.S[wave][q][b][lg * 4]);
+      const half8_t Bh0 = __builtin_bit_cast(half8_t, L.B[cur][lr][(b * 4 + lg) * 2]);
+      const half8_t Bl0 = __builtin_bit_cast(half8_t, L.B[cur][lr][(b * 4 + lg) * 2 + 1]);
+      floatx4 cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh0, floatx4{0.f, 0.f, 0.f, 0.f},
+                                                          0, 0, 0);
+      cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl0, cc, 0, 0, 0);
 #pragma unroll
-        for (int rb = 0; rb < K6_RB; ++rb) {
+      for (int i = 0; i < 4; ++i) c0[i] = __builtin_fmaf(pick4(d, i), cc[i], c0[i]);
+      if (n_tiles > 1) {
+        const half8_t Bh1 = __builtin_bit_cast(half8_t, L.B[cur][16 + lr][(b * 4 + lg) * 2]);
+        const half8_t Bl1 =
+            __builtin_bit_cast(half8_t, L.B[cur][16 + lr][(b * 4 + lg) * 2 + 1]);
+        floatx4 c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            A, Bh1, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl1, c2, 0, 0, 0);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = row_base + wave * (16 * K6_RB) + rb * 16 + kg * 4 + i;
-            if (r < a.rows) {
-              const float v = GLU ? silu_f(acc[0][rb][t][i] * sc) * (acc[NM - 1][rb][t][i] * sc)
-                                  : acc[0][rb][t][i] * sc;
-              a.out[(long long)p * a.rows + r] = v;
-            }
-          }
-        }
+        for (int i = 0; i < 4; ++i) c1[i] = __builtin_fmaf(pick4(d, i), c2[i], c1[i]);
       }
     }
+  };
+
+  // one K chunk: scales to the table, transpose, refill the ring slots,
+  // multiply, stage the next activations, barrier.  (w*, s*): this chunk's
+  // weights, refilled with chunk c + 2; (l*): the activation set that receives
+  // chunk c + 2; (m*): the set holding chunk c + 1.
+  auto step = [&](int c, uint4 &w0, uint4 &w1, _Float16 &s0, _Float16 &s1, uint4 &l0,
+                  uint4 &l1, uint4 &l2, uint4 &l3, const uint4 &m0, const uint4 &m1,
+                  const uint4 &m2, const uint4 &m3) __attribute__((always_inline)) {
+    const int cur = c & 1;
+    const bool live = c * K6_KC + lg < nb;
+    L.S[wave][0][lg][lr] = live ? (float)s0 : 0.0f;
+    if constexpr (GLU) L.S[wave][NM - 1][lg][lr] = live ? (float)s1 : 0.0f;
+    const uint4 t0 = transpose_rows(w0);
+    uint4 t1 = t0;
+    if constexpr (GLU) t1 = transpose_rows(w1);
+    // Loads past the last chunk re-read it (clamped) so that the code stays
+    // straight and the waits exact.
+    load_b(min(c + 2, nch - 1), l0, l1, l2, l3);
+    load_a(min(c + K6_PD, nch - 1), w0, w1, s0, s1);
+    __builtin_amdgcn_wave_barrier();
+    mma(cur, 0, t0, acc00, acc01);
+    if constexpr (GLU) mma(cur, NM - 1, t1, acc10, acc11);
+    store_b(cur ^ 1, m0, m1, m2, m3);  // buffer cur ^ 1 is idle until the barrier
     __syncthreads();
+  };
+  // steps in pairs, unconditionally (straight code keeps the load waits exact);
+  // for an odd chunk count the last step is a chunk past the row end, whose
+  // blocks all have a zero scale
+  for (int c0 = 0; c0 < nch; c0 += K6_PD) {
+    step(c0, wa0, wa1, sa0, sa1, ba0, ba1, ba2, ba3, bb0, bb1, bb2, bb3);
+    step(c0 + 1, wb0, wb1, sb0, sb1, bb0, bb1, bb2, bb3, ba0, ba1, ba2, ba3);
+  }
+  // C lane layout: rows row0 + 4*lg + i, token column t*16 + lr
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int col = t * 16 + lr;
+    if (t < n_tiles && col < ntok) {
+      const int p = a.bucket_pair[off + g0 + col];
+      const float sc = a.xscale[L.tok[col]];
+      const floatx4 g = t == 0 ? acc00 : acc01;
+      const floatx4 u = t == 0 ? acc10 : acc11;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0 + lg * 4 + i;
+        if (r < a.rows) {
+          const float v = GLU ? silu_f(g[i] * sc) * (u[i] * sc) : g[i] * sc;
+          a.out[(long long)p * a.rows + r] = v;
+        }
+      }
+    }
   }
 }
 
-hipError_t launch_mfma(const GemvArgs &a, bool glu, int n_buckets, hipStream_t s) {
-  if (n_buckets <= 0) return hipSuccess;
-  const dim3 grid((a.rows + K6_ROWS - 1) / K6_ROWS, n_buckets);
+hipError_t launch_mfma(const GemvArgs &a, bool glu, int n_items, hipStream_t s) {
+  if (n_items <= 0) return hipSuccess;
+  if (n_items > 65535) return hipErrorInvalidValue;
+  const dim3 grid((a.rows + K6_ROWS - 1) / K6_ROWS, n_items);
   if (glu)
     hipLaunchKernelGGL(q4_mfma_kernel<true>, grid, dim3(256), 0, s, a);
   else

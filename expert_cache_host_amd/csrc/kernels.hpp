@@ -54,13 +54,26 @@ hipError_t launch_topk_decode(const float *z, int T, int E, int k, int norm_topk
                               int shared_slot, int32_t *buckets, int32_t *pair_slot,
                               hipStream_t s);
 
+// Tokens of one bucket that one matrix-core workgroup takes per pass.
+constexpr int kGemmTokens = 32;
+
+// Work items of the matrix-core GEMM for `pairs` pairs in at most `buckets`
+// buckets: one per started pass of kGemmTokens tokens of a bucket.
+inline int gemm_items_bound(int buckets, int pairs) {
+  return buckets + (pairs + kGemmTokens - 1) / kGemmTokens;
+}
+
 // Expert -> slot remap of the routed pairs (plus one shared pair per token when
 // shared_slot >= 0) and stable bucketing per slot, for batches beyond the
 // decode path.  meta: [0] = buckets, [1] = pairs, [2 + b] = slot,
 // [2 + kMetaB + b] = first pair position, [2 + 2 kMetaB + b] = pair count;
-// bucket_pair holds pair ids grouped by bucket, ascending within a bucket.
+// bucket_pair holds pair ids grouped by bucket, ascending within a bucket;
+// items[0] = work items, items[1 + i] = bucket | (pass << 16), buckets in order
+// and passes ascending (room for gemm_items_bound(n_slot_ids, pairs) + 1).
+// n_slot_ids must lie in [1, kMetaB] (else hipErrorInvalidValue).
 hipError_t launch_remap(const int32_t *idx, int T, int k, const SlotView &view, int shared_slot,
-                        int n_slot_ids, int32_t *meta, int32_t *bucket_pair, hipStream_t s);
+                        int n_slot_ids, int32_t *meta, int32_t *bucket_pair, int32_t *items,
+                        hipStream_t s);
 
 struct GemvArgs {
   const uint8_t *slots;  // slot arena of the layer
@@ -79,6 +92,7 @@ struct GemvArgs {
   int T, k;              // tokens and top-k (pair -> token)
   const int32_t *meta;         // matrix-core path: buckets from launch_remap
   const int32_t *bucket_pair;
+  const int32_t *items;        // matrix-core path: work items from launch_remap
   const int32_t *idx;          // router ids [T*k]
   int shared_slot;             // slot of the shared expert or -1
   const int32_t *bt;           // decode path: bucket list (launch_topk_decode)
@@ -123,14 +137,18 @@ hipError_t launch_gemv(const GemvArgs &a, const BucketTable *tab, const GemvShap
                        int n_buckets, hipStream_t s);
 
 // Prefill grouped GEMM on the matrix cores (batches beyond the decode path).
-// Buckets from launch_remap; per workgroup 64 weight rows of one bucket's expert
-// and up to 64 of its tokens at a time.  Weights are decoded chunk by chunk into
-// LDS as binary16 (1024 + q), activations come as binary16 hi/lo pairs in the
-// same K order (xp / xsw / xscale as prepared for the gate/up GEMV, indexed by
-// token for gate/up and by pair for down), each 32-weight block is one pair of
-// v_mfma_f32_16x16x32_f16 (hi, lo) and its scale and the 1032 * sum(x) offset are
-// applied per block in fp32.  glu: out[p][r] = silu(g) * u; else out = M in.
-hipError_t launch_mfma(const GemvArgs &a, bool glu, int n_buckets, hipStream_t s);
+// Work items from launch_remap; per workgroup 64 weight rows of one bucket's
+// expert and one pass of up to kGemmTokens of its tokens.  Each wave streams its
+// 16 rows' nibbles through registers (two K chunks in flight) and decodes them
+// to binary16 (1024 + q) A operands; activations come as binary16 hi/lo pairs in
+// the same K order (xp / xsw / xscale as prepared for the gate/up GEMV, indexed
+// by token for gate/up and by pair for down), staged per chunk in LDS.  Each
+// 32-weight block is one pair of v_mfma_f32_16x16x32_f16 (hi, lo) per 16-token
+// tile, and its scale and the 1032 * sum(x) offset are applied per block in
+// fp32.  glu: out[p][r] = silu(g) * u; else out = M in.  A grid of n_items
+// columns covers at most that many work items (more than 65535:
+// hipErrorInvalidValue).
+hipError_t launch_mfma(const GemvArgs &a, bool glu, int n_items, hipStream_t s);
 
 // Binary16 hi/lo pairs, word sums and power-of-two scale of `rows` float rows of
 // length K (the preparation the router does for x), for the down GEMM's input h.
