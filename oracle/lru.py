@@ -62,6 +62,32 @@ preloads each layer's most-used experts).  Readings:
   that with equal last_use the least used is the first victim; every slot gets
   last_use = the current clock (unprotected from the next stage on), usage
   scores restart at 0, and the loaded counts are added to the lifetime counts.
+
+Prefill preheat (llama.cpp fork with multi GPU acceleration, "Prefill
+preheat": a prompt batch's experts are on the GPU anyway for its matmuls; the
+cache keeps the batch's most-used ones, device to device, in place of cached
+experts the batch used less; an adopt share bounds the share of a layer's
+slots that one batch may replace).  Here the slots themselves are the staging
+area of a call that needs more experts than fit, so the reading is a choice of
+which slots stage and in what order.  Readings, for a stream-mode call whose
+misses outnumber the slots that hold none of its hits (a staged call), when
+adopt >= 0 (per mille; -1 = off, the plain rule above):
+
+* cnt[e] = selections of e in the call; an expert ranks above another by
+  (-cnt, id); F = the call's S top-ranked experts;
+* weakness order of slots: empty slots first (by index), then occupied ones
+  with the lowest-ranked expert first;
+* the pool is the first P = min(#slots holding no expert of F,
+  floor(adopt * S / 1000)) of the slots holding no expert of F, in weakness
+  order; when P = 0 the pool is one slot, the weakest of those slots if any,
+  else the weakest slot (the staging needs a slot);
+* slots outside the pool are never victims in the call (they keep their
+  experts; hits among them run in stage 0);
+* stages as in the plain rule (stage 0 protects the hits), but misses are
+  placed lowest-ranked first, and the victim is the first unprotected pool
+  slot in weakness order;
+* so the pool ends holding the top-ranked misses, and with
+  P = #(slots without an F expert) the layer ends holding exactly F.
 """
 from __future__ import annotations
 
@@ -91,14 +117,17 @@ class PlanResult:
 class LayerSlots:
     """LRU slot state of one layer."""
 
-    def __init__(self, n_experts: int, slots: int, policy: str = LRU):
+    def __init__(self, n_experts: int, slots: int, policy: str = LRU, adopt: int = -1):
         if not 1 <= slots <= n_experts:
             raise ValueError("slots must be in [1, n_experts]")
         if policy not in (LRU, SCORE):
             raise ValueError("policy must be 'lru' or 'score'")
+        if not -1 <= adopt <= 1000:
+            raise ValueError("adopt must be -1 (off) or a share in per mille, 0..1000")
         self.E = n_experts
         self.S = slots
         self.policy = policy
+        self.adopt = adopt
         self.score = [0.0] * n_experts
         self.usage = [0] * n_experts
         self.expert_in = list(range(slots))
@@ -178,6 +207,10 @@ class LayerSlots:
         stage_experts: List[List[int]] = []
 
         if mode == STREAM:
+            pool = None
+            weak = None
+            if self.adopt >= 0 and len(pending) > self.S - len(hit_experts):
+                pool, weak, pending = self._preheat_pool(idx, uniq, pending)
             stage = 0
             while stage == 0 or pending:
                 self.clock += 1
@@ -188,7 +221,7 @@ class LayerSlots:
                         members.append(e)
                 placed = 0
                 for e in pending:
-                    v = self.victim()
+                    v = self.victim() if pool is None else self._pool_victim(pool, weak)
                     if v is None:
                         break
                     self._insert(call, stage, v, e, log)
@@ -238,6 +271,47 @@ class LayerSlots:
         return PlanResult(call=call, unique=uniq, hits=hits, misses=misses, stage_views=views,
                           host_view=host_view, evictions=log, fills=len(log),
                           stage_experts=stage_experts)
+
+    # -- prefill preheat ------------------------------------------------------
+    def _preheat_pool(self, idx, uniq, pending):
+        """Pool slots, weakness key and miss order of a staged call under the
+        adopt share; see the module notes."""
+        cnt = {}
+        for e in idx:
+            cnt[e] = cnt.get(e, 0) + 1
+
+        def rank(e):
+            return (-cnt.get(e, 0), e)
+
+        def weakness(s):
+            e = self.expert_in[s]
+            if e < 0:
+                return (0, s)
+            r = rank(e)
+            return (1, -r[0], -r[1])  # lowest-ranked expert first
+
+        top = set(sorted(uniq, key=rank)[:self.S])
+        others = sorted((s for s in range(self.S) if self.expert_in[s] not in top),
+                        key=weakness)
+        n = min(len(others), self.adopt * self.S // 1000)
+        if n > 0:
+            pool = others[:n]
+        elif others:
+            pool = others[:1]
+        else:
+            pool = [min(range(self.S), key=weakness)]
+        order = sorted(pending, key=rank, reverse=True)
+        return pool, weakness, order
+
+    def _pool_victim(self, pool, weakness):
+        """First unprotected pool slot in weakness order (empty slots first);
+        None when every pool slot is protected."""
+        best = None
+        for s in pool:
+            if self.expert_in[s] == -1 or self.last_use[s] < self.clock:
+                if best is None or weakness(s) < weakness(best):
+                    best = s
+        return best
 
     def preload(self, counts):
         """Loads the S most-used experts by (-count, id); see the module notes."""

@@ -23,7 +23,8 @@ def _parse_traces():
         if parts[1].startswith("E="):
             kv = dict(p.split("=") for p in parts[1].split())
             tr.update(E=int(kv["E"]), S=int(kv["S"]), mode=kv["mode"], fills=int(kv["fills"]),
-                      policy=kv.get("policy", LRU), tokens=int(kv.get("tokens", "1")))
+                      policy=kv.get("policy", LRU), tokens=int(kv.get("tokens", "1")),
+                      adopt=int(kv.get("adopt", "-1")))
         elif parts[1].startswith("call"):
             idx = [int(v) for v in parts[2].split()[1:]]
             hits = int(parts[3].split()[1])
@@ -54,7 +55,7 @@ TRACES = _parse_traces()
 @pytest.mark.parametrize("name", sorted(TRACES))
 def test_golden_trace(name):
     tr = TRACES[name]
-    sim = LayerSlots(tr["E"], tr["S"], tr["policy"])
+    sim = LayerSlots(tr["E"], tr["S"], tr["policy"], tr["adopt"])
     if "preload" in tr:
         sim.preload(tr["preload"])
     for c, (idx, hits, evs) in enumerate(tr["calls"]):
@@ -185,7 +186,7 @@ class _HighTie(LayerSlots):
 
 
 def _trace_passes(cls, tr):
-    sim = cls(tr["E"], tr["S"], tr["policy"])
+    sim = cls(tr["E"], tr["S"], tr["policy"], tr["adopt"])
     try:
         if "preload" in tr:
             sim.preload(tr["preload"])
@@ -399,3 +400,122 @@ def test_preloaded_profile_serves_its_own_routing():
     sim.preload(counts)
     hits = sum(sim.plan(idx, HOST, 0).hits for idx in seq)
     assert hits == sum(1 for idx in seq for e in idx if e in top)
+
+
+# ---------------------------------------------------------------- prefill preheat
+class _PreheatAscending(LayerSlots):
+    def _preheat_pool(self, idx, uniq, pending):  # planted mistake: plain miss order
+        pool, weak, order = super()._preheat_pool(idx, uniq, pending)
+        return pool, weak, sorted(pending)
+
+
+class _PreheatStrongPool(LayerSlots):
+    def _preheat_pool(self, idx, uniq, pending):  # planted mistake: strongest slots pool
+        pool, weak, order = super()._preheat_pool(idx, uniq, pending)
+        others = sorted((s for s in range(self.S) if s not in pool), key=weak, reverse=True)
+        cand = sorted(pool + others, key=weak, reverse=True)
+        return cand[:len(pool)], weak, order
+
+
+class _PreheatLruVictim(LayerSlots):
+    def _pool_victim(self, pool, weakness):  # planted mistake: recency inside the pool
+        c = [s for s in pool if self.expert_in[s] == -1 or self.last_use[s] < self.clock]
+        return min(c, key=lambda s: (self.last_use[s], s)) if c else None
+
+
+class _PreheatNoKeep(LayerSlots):
+    def _pool_victim(self, pool, weakness):  # planted mistake: every slot stages
+        return self.victim()
+
+
+@pytest.mark.parametrize("cls", [_PreheatAscending, _PreheatStrongPool, _PreheatLruVictim,
+                                 _PreheatNoKeep])
+def test_planted_preheat_mistakes_fail_the_traces(cls):
+    assert not all(_trace_passes(cls, tr) for tr in TRACES.values())
+
+
+def _counts(idx):
+    c = {}
+    for e in idx:
+        c[e] = c.get(e, 0) + 1
+    return c
+
+
+def _staged_call(rnd, e_count, k, t):
+    idx = []
+    for _ in range(t):
+        idx += rnd.sample(range(e_count), k)
+    return idx
+
+
+@pytest.mark.parametrize("e_count,s_count,k,t", [(16, 4, 2, 9), (32, 6, 4, 12), (64, 8, 8, 16),
+                                                 (12, 3, 3, 7)])
+def test_preheat_full_share_ends_with_the_call_top_experts(e_count, s_count, k, t):
+    """adopt = 1000: after a staged call the layer holds exactly the call's S
+    top-ranked experts by (-count, id), each miss is filled once, and every stage
+    view maps only its own experts."""
+    rnd = random.Random(31)
+    sim = LayerSlots(e_count, s_count, LRU, 1000)
+    n_staged = 0
+    for _ in range(120):
+        idx = _staged_call(rnd, e_count, k, t)
+        before = list(sim.slot_of)
+        res = sim.plan(idx, STREAM, -1, t)
+        sim.check_invariants()
+        cnt = _counts(idx)
+        uniq = sorted(cnt)
+        hits = [e for e in uniq if before[e] >= 0]
+        misses = [e for e in uniq if before[e] < 0]
+        staged = len(misses) > s_count - len(hits)
+        filled = [r[4] for r in res.evictions]
+        assert sorted(filled) == misses  # each miss exactly once
+        assert sorted(sum(res.stage_experts, [])) == uniq  # each selected expert in one stage
+        if staged:
+            n_staged += 1
+            top = sorted(uniq, key=lambda e: (-cnt[e], e))[:s_count]
+            assert sorted(sim.expert_in) == sorted(top)
+    assert n_staged > 50
+
+
+@pytest.mark.parametrize("adopt", [0, 100, 250, 500, 750])
+def test_preheat_share_bounds_the_replaced_slots(adopt):
+    """Slots outside the pool keep their experts: at most
+    max(1, floor(adopt * S / 1000)) slots change in a staged call, and the pool
+    ends holding the best-ranked misses."""
+    rnd = random.Random(37 + adopt)
+    e_count, s_count, k, t = 40, 8, 4, 10
+    sim = LayerSlots(e_count, s_count, LRU, adopt)
+    cap = max(1, adopt * s_count // 1000)
+    for _ in range(100):
+        idx = _staged_call(rnd, e_count, k, t)
+        before_in = list(sim.expert_in)
+        before = list(sim.slot_of)
+        sim.plan(idx, STREAM, -1, t)
+        cnt = _counts(idx)
+        hits = [e for e in cnt if before[e] >= 0]
+        misses = sorted(e for e in cnt if before[e] < 0)
+        if len(misses) <= s_count - len(hits):
+            continue
+        changed = [s for s in range(s_count) if sim.expert_in[s] != before_in[s]]
+        assert 1 <= len(changed) <= cap
+        ranked = sorted(misses, key=lambda e: (-cnt[e], e))
+        assert sorted(sim.expert_in[s] for s in changed) == sorted(ranked[:len(changed)])
+
+
+def test_preheat_leaves_unstaged_calls_to_the_plain_rule():
+    rnd = random.Random(41)
+    plain = LayerSlots(24, 8, LRU, -1)
+    pre = LayerSlots(24, 8, LRU, 1000)
+    for _ in range(300):
+        idx = rnd.sample(range(24), rnd.choice((1, 2, 3)))
+        a = plain.plan(idx, STREAM)
+        b = pre.plan(idx, STREAM)
+        assert a.evictions == b.evictions and a.stage_views == b.stage_views
+    assert plain.expert_in == pre.expert_in
+
+
+def test_preheat_bad_share_rejected():
+    with pytest.raises(ValueError):
+        LayerSlots(8, 4, LRU, 1001)
+    with pytest.raises(ValueError):
+        LayerSlots(8, 4, LRU, -2)
