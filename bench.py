@@ -180,6 +180,72 @@ def preload_study(args, first=32, profile_calls=128):
                       "first_calls": first, "hit_rate_cold": cold, "hit_rate_preloaded": warm}), flush=True)
 
 
+def preheat_study(args, prompt_ubatches=24, decode_tokens=256, adopts=(-1, 500, 1000)):
+    """Prefill preheat: a prompt of `prompt_ubatches` ubatches of 512 tokens, then
+    `decode_tokens` single-token decode calls, through every layer of the large
+    shape (stream misses), with the decode workload's router (Zipf bias, so
+    expert popularity persists) in both phases.  Reports per adopt share (-1 =
+    off) the prompt time, the decode hit rate and the decode layer-tokens/s."""
+    import torch
+    import expert_cache_host_amd as m
+    import synth
+    dec = synth.WORKLOADS["large"]
+    pre = synth.WORKLOADS["prefill"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    weights = synth.gen_all_weights(dec)
+    routers = [synth.gen_router(dec, l) for l in range(dec.layers)]
+    w_d = [torch.from_numpy(w).to(dev) for w, _ in routers]
+    b_d = [torch.from_numpy(b).to(dev) if b is not None else None for _, b in routers]
+    xp = [torch.from_numpy(synth.gen_hidden(pre, l, prompt_ubatches)).to(dev)
+          for l in range(dec.layers)]
+    xd = [torch.from_numpy(synth.gen_hidden(dec, l, decode_tokens)).to(dev)
+          for l in range(dec.layers)]
+    out_p = torch.empty((pre.batch, dec.d_model), dtype=torch.float32, device=dev)
+    out_d = torch.empty((1, dec.d_model), dtype=torch.float32, device=dev)
+    rows = []
+    for adopt in adopts:
+        c = m.MoECache(dec.layers, dec.n_experts, dec.slots, dec.d_model, dec.d_ff, weights,
+                       top_k=dec.top_k, miss_mode="stream", n_shared=dec.n_shared, adopt=adopt)
+        log(f"preheat study: adopt={adopt}, prompt")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for u in range(prompt_ubatches):
+            for l in range(dec.layers):
+                c.forward(l, xp[l][u], w_d[l], b_d[l], out=out_p)
+        torch.cuda.synchronize()
+        c.sync()
+        t1 = time.perf_counter()
+        stp = c.stats()
+        c.reset_stats()
+        log(f"preheat study: adopt={adopt}, decode")
+        first = None
+        for s in range(decode_tokens):
+            if s == 32:
+                torch.cuda.synchronize()
+                c.sync()
+                st32 = c.stats()
+                first = st32["hits"] / max(1, st32["selections"])
+            for l in range(dec.layers):
+                c.forward(l, xd[l][s], w_d[l], b_d[l], out=out_d)
+        torch.cuda.synchronize()
+        c.sync()
+        t2 = time.perf_counter()
+        st = c.stats()
+        rows.append({"adopt": adopt, "prompt_s": t1 - t0,
+                     "prompt_stages_per_call": stp["stages"] / max(1, stp["calls"]),
+                     "prompt_fills": stp["fills"],
+                     "decode_hit_rate": st["hits"] / max(1, st["selections"]),
+                     "decode_hit_rate_first32": first,
+                     "decode_layer_tokens_per_s": decode_tokens * dec.layers / (t2 - t1),
+                     "decode_fills_per_call": st["fills"] / max(1, st["calls"])})
+        c.close()
+    print(json.dumps({"study": "prefill preheat", "shape": describe(dec),
+                      "prompt": f"{prompt_ubatches} ubatches of {pre.batch} i.i.d. tokens",
+                      "decode": f"{decode_tokens} AR(1) tokens, one per call",
+                      "miss_mode": "stream", "results": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,12 +264,17 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--preload-study", action="store_true",
                     help="first-call hit rates cold and after preloading a usage profile")
+    ap.add_argument("--preheat-study", action="store_true",
+                    help="decode after a long prompt, with and without prefill preheat")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
         return
     if args.preload_study:
         preload_study(args)
+        return
+    if args.preheat_study:
+        preheat_study(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))

@@ -31,7 +31,8 @@ class Opts(ctypes.Structure):
                 ("n_shared", ctypes.c_int32), ("norm_topk", ctypes.c_int32),
                 ("host_threads", ctypes.c_int32), ("max_fills_per_call", ctypes.c_int32),
                 ("keep_debug", ctypes.c_int32), ("timing", ctypes.c_int32),
-                ("policy", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+                ("policy", ctypes.c_int32), ("preheat", ctypes.c_int32),
+                ("adopt", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
 
 
 class Stats(ctypes.Structure):
@@ -85,6 +86,7 @@ def load_library():
         "moe_debug_partials": (I32, [P, I32, P, P]),
         "moe_planner_create": (I32, [I32, I32, I32, I32, I32, ctypes.POINTER(P)]),
         "moe_planner_plan": (I32, [P, P, I32, I32, P, P, P]),
+        "moe_planner_set_adopt": (I32, [P, I32]),
         "moe_planner_scores": (I32, [P, P]),
         "moe_planner_usage": (I32, [P, P]),
         "moe_planner_preload": (I32, [P, P]),
@@ -143,7 +145,8 @@ class MoECache:
                  host_weights: np.ndarray, top_k: int = 8, miss_mode: str = "stream",
                  n_shared: int = 0, norm_topk: bool = True, host_threads: int = 0,
                  max_fills_per_call: int = -1, keep_debug: bool = False, timing: bool = False,
-                 policy: str = "lru"):
+                 policy: str = "lru", adopt: int = -1):
+        """adopt: prefill preheat share of the slots per mille (0..1000), -1 = off."""
         lib = load_library()
         w = np.ascontiguousarray(host_weights, dtype=np.uint8)
         need = layers * (n_experts + n_shared) * (3 * d_model * d_ff // 32 * 18)
@@ -160,6 +163,9 @@ class MoECache:
         o.keep_debug = 1 if keep_debug else 0
         o.timing = 1 if timing else 0
         o.policy = _policy(policy)
+        if adopt >= 0:
+            o.preheat = 1
+            o.adopt = adopt
         h = ctypes.c_void_p()
         _check(lib.moe_cache_create(layers, n_experts, slots, d_model, d_ff, _ptr(w), ctypes.byref(o),
                                     ctypes.byref(h)))
@@ -168,6 +174,7 @@ class MoECache:
         self.d_model, self.d_ff, self.top_k, self.n_shared = d_model, d_ff, top_k, n_shared
         self.miss_mode = miss_mode
         self.policy = policy
+        self.adopt = adopt
 
     # -- compute ---------------------------------------------------------------
     def forward(self, layer: int, x, router_w, router_bias=None, out=None, stream=None):
@@ -285,13 +292,15 @@ class Planner:
     """The library's per-layer slot planner alone (host only, no GPU)."""
 
     def __init__(self, n_experts: int, slots: int, miss_mode: str = "stream",
-                 max_fills_per_call: int = -1, policy: str = "lru"):
+                 max_fills_per_call: int = -1, policy: str = "lru", adopt: int = -1):
         h = ctypes.c_void_p()
         _check(load_library().moe_planner_create(n_experts, slots,
                                                  MISS_HOST if miss_mode == "host" else MISS_STREAM,
                                                  max_fills_per_call, _policy(policy),
                                                  ctypes.byref(h)))
         self._h = h
+        if adopt != -1:
+            _check(load_library().moe_planner_set_adopt(h, adopt))
         self.n_experts, self.slots = n_experts, slots
 
     def plan(self, idx, tokens: int = 1):

@@ -658,6 +658,8 @@ void moe_cache_default_opts(moe_cache_opts *o) {
   o->host_threads = 0;
   o->max_fills_per_call = -1;
   o->keep_debug = 0;
+  o->preheat = 0;
+  o->adopt = 1000;
 }
 
 const char *moe_last_error(void) { return g_err.c_str(); }
@@ -694,7 +696,9 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
   if (o.timing != 0 && o.timing != 1) return fail(MOE_EINVAL, "timing must be 0 or 1");
   if (o.policy != MOE_POLICY_LRU && o.policy != MOE_POLICY_SCORE)
     return fail(MOE_EINVAL, "policy must be MOE_POLICY_LRU or MOE_POLICY_SCORE");
-  for (int i = 0; i < 7; ++i)
+  if (o.preheat != 0 && o.preheat != 1) return fail(MOE_EINVAL, "preheat must be 0 or 1");
+  if (o.adopt < 0 || o.adopt > 1000) return fail(MOE_EINVAL, "adopt must be in [0, 1000]");
+  for (int i = 0; i < 5; ++i)
     if (o.reserved[i] != 0) return fail(MOE_EINVAL, "reserved fields must be 0");
 
   std::unique_ptr<moe_cache> c;
@@ -746,7 +750,8 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
     c->layers.resize(layers);
     for (int32_t l = 0; l < layers; ++l) {
       LayerState &ly = c->layers[l];
-      ly.planner.reset(new moe::SlotPlanner(n_experts, slots, o.policy));
+      ly.planner.reset(
+          new moe::SlotPlanner(n_experts, slots, o.policy, o.preheat ? o.adopt : -1));
       const size_t nslots = (size_t)slots + o.n_shared;
       he = hipMalloc((void **)&ly.d_slots, nslots * c->rec());
       if (he != hipSuccess) {
@@ -1085,6 +1090,14 @@ moe_status moe_planner_preload(moe_planner *p, const uint32_t *counts) {
   g_err.clear();
   if (!p || !counts) return fail(MOE_EINVAL, "NULL argument");
   p->p->preload(counts);
+  return MOE_OK;
+}
+
+moe_status moe_planner_set_adopt(moe_planner *p, int32_t adopt) {
+  g_err.clear();
+  if (!p) return fail(MOE_EINVAL, "planner is NULL");
+  if (adopt < -1 || adopt > 1000) return fail(MOE_EINVAL, "adopt must be -1 or in [0, 1000]");
+  p->p->set_adopt(adopt);
   return MOE_OK;
 }
 

@@ -4,8 +4,9 @@
 
 namespace moe {
 
-SlotPlanner::SlotPlanner(int32_t n_experts, int32_t slots, int32_t policy)
-    : E_(n_experts), S_(slots), policy_(policy), score_(n_experts, 0.0), usage_(n_experts, 0),
+SlotPlanner::SlotPlanner(int32_t n_experts, int32_t slots, int32_t policy, int32_t adopt)
+    : E_(n_experts), S_(slots), policy_(policy), adopt_(adopt), cnt_(n_experts, 0),
+      score_(n_experts, 0.0), usage_(n_experts, 0),
       expert_in_(slots),
       slot_of_(n_experts, -1), last_use_(slots, 0), seen_(n_experts, 0) {
   for (int32_t s = 0; s < slots; ++s) {
@@ -56,6 +57,60 @@ void SlotPlanner::insert(int64_t call, int32_t stage, int32_t slot, int32_t e, C
   out.fills++;
 }
 
+bool SlotPlanner::ranks_above(int32_t a, int32_t b) const {
+  return cnt_[a] > cnt_[b] || (cnt_[a] == cnt_[b] && a < b);
+}
+
+bool SlotPlanner::weaker_slot(int32_t a, int32_t b) const {
+  const int32_t ea = expert_in_[a], eb = expert_in_[b];
+  if (ea < 0 || eb < 0) return ea < 0 && (eb >= 0 || a < b);
+  return ranks_above(eb, ea);  // the lower-ranked expert is the weaker slot
+}
+
+int32_t SlotPlanner::pool_victim(const std::vector<int32_t> &pool) const {
+  int32_t best = -1;
+  for (int32_t s : pool) {
+    if (expert_in_[s] >= 0 && last_use_[s] >= clock_) continue;
+    if (best < 0 || weaker_slot(s, best)) best = s;
+  }
+  return best;
+}
+
+void SlotPlanner::preheat_pool(const int32_t *idx, int32_t n_sel,
+                               const std::vector<int32_t> &uniq, std::vector<int32_t> &pending,
+                               std::vector<int32_t> &pool) {
+  std::fill(cnt_.begin(), cnt_.end(), 0);
+  for (int32_t i = 0; i < n_sel; ++i) cnt_[idx[i]]++;
+  std::vector<int32_t> ranked = uniq;
+  std::sort(ranked.begin(), ranked.end(),
+            [&](int32_t a, int32_t b) { return ranks_above(a, b); });
+  // mark F, the S top-ranked experts of the call
+  const size_t n_top = std::min(ranked.size(), (size_t)S_);
+  for (size_t i = 0; i < n_top; ++i) seen_[ranked[i]] = 1;
+  std::vector<int32_t> others;
+  for (int32_t s = 0; s < S_; ++s)
+    if (expert_in_[s] < 0 || !seen_[expert_in_[s]]) others.push_back(s);
+  for (size_t i = 0; i < n_top; ++i) seen_[ranked[i]] = 0;
+  std::sort(others.begin(), others.end(),
+            [&](int32_t a, int32_t b) { return weaker_slot(a, b); });
+  const size_t share = (size_t)((int64_t)adopt_ * S_ / 1000);
+  const size_t n = std::min(others.size(), share);
+  pool.clear();
+  if (n > 0) {
+    pool.assign(others.begin(), others.begin() + n);
+  } else if (!others.empty()) {
+    pool.push_back(others[0]);
+  } else {
+    int32_t w = 0;
+    for (int32_t s = 1; s < S_; ++s)
+      if (weaker_slot(s, w)) w = s;
+    pool.push_back(w);
+  }
+  // lowest-ranked misses first
+  std::sort(pending.begin(), pending.end(),
+            [&](int32_t a, int32_t b) { return ranks_above(b, a); });
+}
+
 void SlotPlanner::plan(const int32_t *idx, int32_t n_sel, int32_t tokens, int32_t mode,
                        int32_t max_fills, CallPlan &out) {
   if (policy_ == kPolicyScore) update_scores(idx, n_sel, tokens);
@@ -84,6 +139,9 @@ void SlotPlanner::plan(const int32_t *idx, int32_t n_sel, int32_t tokens, int32_
   for (int32_t e : uniq) (slot_of_[e] >= 0 ? hit_experts : pending).push_back(e);
 
   if (mode == 0) {
+    std::vector<int32_t> pool;  // empty: the plain rule
+    if (adopt_ >= 0 && (int64_t)pending.size() > (int64_t)S_ - (int64_t)hit_experts.size())
+      preheat_pool(idx, n_sel, uniq, pending, pool);
     size_t next = 0;
     int32_t stage = 0;
     while (stage == 0 || next < pending.size()) {
@@ -96,7 +154,7 @@ void SlotPlanner::plan(const int32_t *idx, int32_t n_sel, int32_t tokens, int32_
         }
       }
       while (next < pending.size()) {
-        const int32_t v = victim();
+        const int32_t v = pool.empty() ? victim() : pool_victim(pool);
         if (v < 0) break;
         const int32_t e = pending[next++];
         insert(out.call, stage, v, e, out);

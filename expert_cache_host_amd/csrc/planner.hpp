@@ -35,6 +35,19 @@
 // the slots, the least used of them in slot 0 and the most used in slot S-1,
 // gives every slot last_use = clock, resets the scores and adds the counts to
 // the lifetime counts.
+//
+// Prefill preheat ("Prefill preheat", llama.cpp fork with multi GPU
+// acceleration: the cache keeps a prompt batch's most-used experts in place of
+// cached experts the batch used less, within an adopt share of the slots).
+// With adopt >= 0 (per mille; -1 = off), a stream-mode call whose misses
+// outnumber the slots holding none of its hits is staged through a pool:
+//   experts rank by (-count in the call, id); F = the S top-ranked; slot
+//   weakness: empty first, then the lowest-ranked expert first; the pool is the
+//   first min(#slots without an F expert, floor(adopt * S / 1000)) slots without
+//   an F expert in weakness order, or one slot when that is 0 (the weakest
+//   without an F expert, else the weakest); other slots are never victims in
+//   the call; misses are placed lowest-ranked first into the first unprotected
+//   pool slot in weakness order.
 #pragma once
 #include <cstdint>
 #include <vector>
@@ -69,7 +82,8 @@ struct CallPlan {
 
 class SlotPlanner {
  public:
-  SlotPlanner(int32_t n_experts, int32_t slots, int32_t policy = kPolicyLru);
+  SlotPlanner(int32_t n_experts, int32_t slots, int32_t policy = kPolicyLru,
+              int32_t adopt = -1);
 
   // Plans one call on n_sel = tokens * k router ids (token-major).  mode: 0
   // stream, 1 host.
@@ -90,6 +104,8 @@ class SlotPlanner {
   // Loads the usage profile counts[n_experts] (see above).
   void preload(const uint32_t *counts);
   int32_t policy() const { return policy_; }
+  int32_t adopt() const { return adopt_; }
+  void set_adopt(int32_t adopt) { adopt_ = adopt; }  // -1 off, else per mille 0..1000
   const std::vector<EvictRecord> &log() const { return log_; }
   uint64_t clock() const { return clock_; }
 
@@ -98,8 +114,15 @@ class SlotPlanner {
   bool weaker(int32_t a, int32_t b) const;  // slot a before slot b as a victim
   void update_scores(const int32_t *idx, int32_t n_sel, int32_t tokens);
   void insert(int64_t call, int32_t stage, int32_t slot, int32_t e, CallPlan &out);
+  // preheat: pool slots and miss order of a staged stream call
+  void preheat_pool(const int32_t *idx, int32_t n_sel, const std::vector<int32_t> &uniq,
+                    std::vector<int32_t> &pending, std::vector<int32_t> &pool);
+  bool ranks_above(int32_t a, int32_t b) const;   // expert a before expert b
+  bool weaker_slot(int32_t a, int32_t b) const;   // slot a before slot b (weakness)
+  int32_t pool_victim(const std::vector<int32_t> &pool) const;
 
-  int32_t E_, S_, policy_;
+  int32_t E_, S_, policy_, adopt_;
+  std::vector<int32_t> cnt_;  // selections per expert in the current call (preheat)
   std::vector<double> score_;
   std::vector<uint32_t> usage_;
   std::vector<int32_t> expert_in_, slot_of_;

@@ -65,6 +65,20 @@ typedef int32_t moe_status;
 #define MOE_POLICY_LRU 0
 #define MOE_POLICY_SCORE 1
 
+/* Prefill preheat (opts.preheat = 1; "Prefill preheat", llama.cpp fork with
+ * multi GPU acceleration: the cache keeps a prompt batch's most-used experts in
+ * place of cached experts the batch used less, and an adopt share bounds how
+ * many of a layer's slots one batch may replace).  It applies to stream-mode
+ * calls whose misses outnumber the slots holding none of their hits, which run
+ * in stages through the slots.  Experts rank by (-count in the call, id); the
+ * slots holding none of the call's S top-ranked experts, weakest first (lowest
+ * -ranked expert first), give a pool of min(their number, adopt * S / 1000)
+ * slots (at least one: staging needs a slot); only pool slots take fills, the
+ * lowest-ranked misses first, so the pool ends holding the call's best-ranked
+ * misses and the other slots keep their experts.  With adopt = 1000 the layer
+ * ends holding exactly the call's S top-ranked experts.  Other calls, and host
+ * mode, follow the policy's plain rule. */
+
 /* Limits of this build. */
 #define MOE_MAX_EXPERTS 512 /* routed experts per layer */
 #define MOE_MAX_TOPK 64
@@ -81,7 +95,9 @@ typedef struct moe_cache_opts {
   int32_t keep_debug;         /* 1: keep per-layer GPU/host partials            default 0 */
   int32_t timing;             /* 1: time fills and compute with HIP events       default 0 */
   int32_t policy;             /* MOE_POLICY_LRU or MOE_POLICY_SCORE             default LRU */
-  int32_t reserved[7];        /* must be 0 */
+  int32_t preheat;            /* 1: prefill preheat for staged stream calls      default 0 */
+  int32_t adopt;              /* preheat share of the slots, per mille 0..1000   default 1000 */
+  int32_t reserved[5];        /* must be 0 */
 } moe_cache_opts;
 
 /* Counters since create or the last moe_cache_reset_stats.  A "selection" is one
@@ -283,6 +299,10 @@ typedef struct moe_planner moe_planner; /* the per-layer LRU slot planner alone 
  * policy as in moe_cache_opts. */
 moe_status moe_planner_create(int32_t n_experts, int32_t slots, int32_t miss_mode,
                               int32_t max_fills_per_call, int32_t policy, moe_planner **out);
+
+/* Prefill preheat of the planner, as opts.preheat / opts.adopt: adopt = -1 turns
+ * it off (the state after create), 0..1000 turns it on with that share. */
+moe_status moe_planner_set_adopt(moe_planner *p, int32_t adopt);
 
 /* Plans one call on the router ids idx[n_sel], token-major, n_sel = n_tokens *
  * top_k (n_sel a multiple of n_tokens >= 1).  After it, *n_stages, *hits and

@@ -27,7 +27,7 @@ def log(msg):
 
 class Runner:
     def __init__(self, wl, layers, slots=None, mode="stream", max_fills=-1, keep_debug=False,
-                 host_threads=0, weights=None, policy="lru"):
+                 host_threads=0, weights=None, policy="lru", adopt=-1):
         import torch
         import expert_cache_host_amd as m
         import synth
@@ -46,9 +46,9 @@ class Runner:
         self.cache = m.MoECache(nl, wl.n_experts, self.S, wl.d_model, wl.d_ff, weights,
                                 top_k=wl.top_k, miss_mode=mode, n_shared=wl.n_shared,
                                 max_fills_per_call=max_fills, keep_debug=keep_debug,
-                                host_threads=host_threads, policy=policy)
+                                host_threads=host_threads, policy=policy, adopt=adopt)
         self.policy = policy
-        self.sims = [LayerSlots(wl.n_experts, self.S, policy) for _ in self.layers]
+        self.sims = [LayerSlots(wl.n_experts, self.S, policy, adopt) for _ in self.layers]
         self.routers = []
         for l in self.layers:
             w_r, b = synth.gen_router(wl, l)

@@ -84,6 +84,39 @@ def test_staged_small_prefill():
     r.close()
 
 
+@pytest.mark.parametrize("adopt", [0, 500, 1000])
+def test_staged_small_prefill_preheat(adopt):
+    """Prefill preheat: the staging pool, miss order and final slots of every
+    staged call match the oracle, and so do the outputs; decode-sized calls in
+    between follow the plain rule."""
+    wl = synth.Workload("stg", 12, 1, 128, 256, 64, 8, 8, n_shared=1, router_sigma=0.14,
+                        rho=None, tokens=192, batch=64)
+    log(f"staged small prefill, preheat adopt={adopt}")
+    r = Runner(wl, [0], mode="stream", adopt=adopt)
+    x = synth.gen_hidden(wl, 0)
+    for c in range(x.shape[0]):
+        _, res = r.call(0, x[c])
+        assert len(res.stage_views) > 1
+        r.call(0, x[c][:2])
+    r.check_log()
+    r.close()
+
+
+def test_prefill_ubatch_preheat_sampled():
+    wl = synth.WORKLOADS["prefill"]
+    log("prefill shape with preheat, 1 layer x 2 ubatches of 512, sampled tokens and columns")
+    r = Runner(wl, [2], adopt=1000)
+    x = synth.gen_hidden(wl, 2, 2)
+    rng = np.random.default_rng(2)
+    for u in range(2):
+        toks = np.sort(rng.choice(512, 4, replace=False))
+        cols = rng.choice(wl.d_model, 48, replace=False)
+        _, res = r.call(0, x[u], tok_sample=toks, col_sample=cols)
+        assert len(res.stage_views) >= 4
+    r.check_log()
+    r.close()
+
+
 def test_gemma_shape_two_layers():
     wl = synth.WORKLOADS["gemma"]
     log("gemma shape, 2 layers x 6 calls")

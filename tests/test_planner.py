@@ -10,10 +10,10 @@ import expert_cache_host_amd as m
 from oracle.lru import LayerSlots
 
 
-def _compare(e_count, s_count, mode, max_fills, calls, seed, policy="lru"):
+def _compare(e_count, s_count, mode, max_fills, calls, seed, policy="lru", adopt=-1):
     rnd = random.Random(seed)
-    lib_p = m.Planner(e_count, s_count, mode, max_fills, policy)
-    sim = LayerSlots(e_count, s_count, policy)
+    lib_p = m.Planner(e_count, s_count, mode, max_fills, policy, adopt)
+    sim = LayerSlots(e_count, s_count, policy, adopt)
     for _ in range(calls):
         t, k = rnd.choice([(1, 1), (1, 2), (1, 8), (2, 4), (4, 8), (3, 3)])
         k = min(k, e_count)
@@ -112,3 +112,46 @@ def test_planner_preload_matches_oracle(policy, mode):
         assert lib_p.usage().tolist() == sim.usage
         assert lib_p.scores().tolist() == sim.score
     assert lib_p.evictions() == sim.log
+
+
+# ---------------------------------------------------------------- prefill preheat
+@pytest.mark.parametrize("adopt", [0, 1, 250, 500, 1000])
+@pytest.mark.parametrize("e_count,s_count", [(8, 4), (8, 1), (20, 3), (128, 32), (256, 64)])
+def test_preheat_planner_matches_oracle(adopt, e_count, s_count):
+    _compare(e_count, s_count, "stream", -1, 120, seed=e_count * 7 + s_count + adopt,
+             adopt=adopt)
+
+
+@pytest.mark.parametrize("adopt", [250, 1000])
+def test_preheat_planner_score_policy_matches_oracle(adopt):
+    _compare(64, 8, "stream", -1, 150, seed=adopt, policy="score", adopt=adopt)
+
+
+def test_preheat_host_mode_ignores_the_share():
+    _compare(32, 6, "host", 2, 150, seed=3, adopt=1000)
+
+
+@pytest.mark.parametrize("adopt", [125, 1000])
+def test_preheat_planner_prefill_like(adopt):
+    # 512 tokens x top-8 of 256 experts through 64 slots, Zipf-like popularity
+    rng = np.random.default_rng(1)
+    p = 1.0 / np.arange(1, 257) ** 0.8
+    p /= p.sum()
+    lib_p = m.Planner(256, 64, "stream", adopt=adopt)
+    sim = LayerSlots(256, 64, "lru", adopt)
+    for _ in range(4):
+        idx = np.stack([rng.choice(256, 8, replace=False, p=p) for _ in range(512)]).ravel()
+        ns, hits, misses = lib_p.plan(idx, tokens=512)
+        res = sim.plan(idx.tolist(), "stream", -1, 512)
+        assert ns == len(res.stage_views) and (hits, misses) == (res.hits, res.misses)
+        for s in range(ns):
+            assert lib_p.views(s)[0].tolist() == res.stage_views[s]
+        assert lib_p.slot_state()[0].tolist() == sim.expert_in
+    assert lib_p.evictions() == sim.log
+
+
+def test_preheat_bad_share_rejected():
+    with pytest.raises(m.MoeError):
+        m.Planner(8, 4, adopt=1001)
+    with pytest.raises(m.MoeError):
+        m.Planner(8, 4, adopt=-2)
