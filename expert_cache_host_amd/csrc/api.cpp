@@ -135,9 +135,9 @@ struct LayerState {
   uint8_t *d_slots = nullptr;     // (S + n_shared) records
   hipEvent_t fill_ev[2] = {nullptr, nullptr};  // last fills of this layer (side streams)
   bool fill_used[2] = {false, false};
-  hipEvent_t compute_ev = nullptr;  // last kernels that read this layer's slots
   bool fill_pending = false;
-  bool compute_recorded = false;
+  hipStream_t last_stream = nullptr;  // stream of the layer's last call
+  bool called = false;
   moe::CallPlan plan;             // last call
   int32_t last_T = 0;
   std::vector<int32_t> last_idx;
@@ -164,6 +164,10 @@ struct moe_cache {
   std::vector<LayerState> layers;
   hipStream_t side[2] = {nullptr, nullptr};  // slot fills alternate over two copy streams
   hipEvent_t ev_idx = nullptr, ev_ready = nullptr;
+  // decode calls: the top-k kernel stores the call's sequence number here
+  // (page-locked, coherent) once the routing copy is visible to the host
+  uint32_t *h_flag = nullptr;
+  uint32_t flag_seq = 0;
   bool poisoned = false;
   bool timing = false;
   // device workspace
@@ -201,10 +205,10 @@ struct moe_cache {
       if (ly.d_slots) (void)hipFree(ly.d_slots);
       for (auto &e : ly.fill_ev)
         if (e) (void)hipEventDestroy(e);
-      if (ly.compute_ev) (void)hipEventDestroy(ly.compute_ev);
     }
     layers.clear();
     if (h_arena) (void)hipHostFree(h_arena);
+    if (h_flag) (void)hipHostFree(h_flag);
     if (ev_idx) (void)hipEventDestroy(ev_idx);
     if (ev_ready) (void)hipEventDestroy(ev_ready);
     for (auto &e : partial_ev)
@@ -279,14 +283,28 @@ struct KTime {
   }
 };
 
-void record_compute(moe_cache *c, LayerState &ly, hipStream_t st) {
-  HIPCHK(hipEventRecord(ly.compute_ev, st));
-  ly.compute_recorded = true;
+// Waits until the decode top-k kernel has published the call's routing copy
+// (flag == flag_seq, acquire).  A stream that went idle without the flag, or
+// 30 s without it, is an error rather than a hang.
+void wait_routing(moe_cache *c, hipStream_t st) {
+  const uint32_t want = c->flag_seq;
+  const double t0 = now_s();
+  for (uint64_t i = 0;; ++i) {
+    if (__atomic_load_n(c->h_flag, __ATOMIC_ACQUIRE) == want) return;
+    if ((i & 4095) == 4095) {
+      const hipError_t e = hipStreamQuery(st);
+      if (e != hipSuccess && e != hipErrorNotReady) HIPCHK(e);
+      if (__atomic_load_n(c->h_flag, __ATOMIC_ACQUIRE) == want) return;
+      if (e == hipSuccess) throw HipError("routing flag missing after the top-k kernel completed");
+      if (now_s() - t0 > 30.0) throw HipError("routing flag not set within 30 s");
+    }
+    __builtin_ia32_pause();
+  }
 }
 
 // Copies the fills of one stage on the two side streams after every earlier
-// reader of the victim slots (work enqueued so far on `st`, and the layer's last
-// kernels), and records the layer's fill events.
+// reader of the victim slots (all of them are on `st`: see the stream rule at
+// the top of a call), and records the layer's fill events.
 void enqueue_fills(moe_cache *c, int32_t layer, const std::vector<moe::Fill> &fills,
                    hipStream_t st) {
   LayerState &ly = c->layers[layer];
@@ -295,7 +313,6 @@ void enqueue_fills(moe_cache *c, int32_t layer, const std::vector<moe::Fill> &fi
   hipEvent_t t0 = nullptr, t1 = nullptr;
   for (int i = 0; i < n_sd; ++i) {
     HIPCHK(hipStreamWaitEvent(c->side[i], c->ev_ready, 0));
-    if (ly.compute_recorded) HIPCHK(hipStreamWaitEvent(c->side[i], ly.compute_ev, 0));
   }
   if (c->timing) {
     t0 = ly.t_h2d.get();
@@ -436,6 +453,13 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   const bool host_mode = c->o.miss_mode == MOE_MISS_HOST;
   const int ns = c->o.n_shared;
   c->ensure_ws(T);
+  // Stream rule: slot fills (the pull kernel on `st`, copies after an event on
+  // `st`) rely on every earlier reader of the victims being before them on
+  // `st`.  A call on another stream than the layer's last call therefore waits
+  // for the device first (rare; keeps the usual path free of markers).
+  if (ly.called && ly.last_stream != st) HIPCHK(hipDeviceSynchronize());
+  ly.last_stream = st;
+  ly.called = true;
   hipEvent_t g0 = nullptr, g1 = nullptr;
   if (c->timing) {
     g0 = ly.t_gpu.get();
@@ -452,41 +476,58 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   // table published at call start: the hits run on it before the host plans
   const moe::SlotView pre = make_view(ly.planner->slot_of());
   const bool dec = c->decode_ok(T);
-  {
+  if (dec) {
+    // router with the digit planes of the decode GEMV, then the decode top-k
     KTime kt(c, MOE_K_ROUTER, st);
-    // the decode GEMV takes digit planes, the matrix-core GEMM binary16 pairs
-    HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)c->z.p,
-                              dec ? nullptr : (uint32_t *)c->xp.p, (float *)c->xsw.p,
-                              (float *)c->xscale.p, dec ? (uint4 *)c->xq.p : nullptr,
-                              (float *)c->xs.p, st));
+    moe::DecodeTopk a;
+    a.k = k;
+    a.norm_topk = c->o.norm_topk;
+    a.idx = (int32_t *)c->idx.p;
+    a.w = (float *)c->w.p;
+    a.h_idx = (int32_t *)c->h_idx.p;
+    a.h_w = (float *)c->h_w.p;
+    a.view = pre;
+    a.shared_slot = ns > 0 ? c->S : -1;
+    a.buckets = (int32_t *)c->buckets.p;
+    a.pair_slot = (int32_t *)c->pair_slot.p;
+    a.h_flag = c->h_flag;
+    a.seq = ++c->flag_seq;
+    HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)c->z.p, nullptr,
+                              nullptr, nullptr, (uint4 *)c->xq.p, (float *)c->xs.p, st));
     kt.end(4.0 * ((double)E * d + (double)T * d * 2 + (double)T * E + (router_bias ? E : 0)));
-  }
-  {
+    KTime kt2(c, MOE_K_TOPK, st);
+    HIPCHK(moe::launch_topk_decode((const float *)c->z.p, T, E, a, st));
+    kt2.end(4.0 * ((double)T * E + 4.0 * T * k));
+  } else {
+    {
+      KTime kt(c, MOE_K_ROUTER, st);
+      // the matrix-core GEMM takes binary16 pairs
+      HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)c->z.p,
+                                (uint32_t *)c->xp.p, (float *)c->xsw.p, (float *)c->xscale.p,
+                                nullptr, (float *)c->xs.p, st));
+      kt.end(4.0 * ((double)E * d + (double)T * d * 2 + (double)T * E + (router_bias ? E : 0)));
+    }
     KTime kt(c, MOE_K_TOPK, st);
-    if (dec)
-      HIPCHK(moe::launch_topk_decode((const float *)c->z.p, T, E, k, c->o.norm_topk,
-                                     (int32_t *)c->idx.p, (float *)c->w.p, (int32_t *)c->h_idx.p,
-                                     (float *)c->h_w.p, pre, ns > 0 ? c->S : -1,
-                                     (int32_t *)c->buckets.p, (int32_t *)c->pair_slot.p, st));
-    else
-      HIPCHK(moe::launch_topk((const float *)c->z.p, T, E, k, c->o.norm_topk, (int32_t *)c->idx.p,
-                              (float *)c->w.p, (int32_t *)c->h_idx.p, (float *)c->h_w.p, st));
+    HIPCHK(moe::launch_topk((const float *)c->z.p, T, E, k, c->o.norm_topk, (int32_t *)c->idx.p,
+                            (float *)c->w.p, (int32_t *)c->h_idx.p, (float *)c->h_w.p, st));
     kt.end(4.0 * ((double)T * E + 4.0 * T * k));
   }
-  HIPCHK(hipEventRecord(c->ev_idx, st));
+  if (!dec) HIPCHK(hipEventRecord(c->ev_idx, st));
 
   // Cached experts (and the shared one) on the table published at call start,
   // enqueued before the host reads the routing.
   const int nb_hits = std::min(T * k, c->S) + (ns > 0 ? 1 : 0);
   run_experts(c, layer, T, pre, ns > 0, nb_hits, 0.0, x, st);
-  record_compute(c, ly, st);
 
   float *dbg_gpu = nullptr;
   if (c->o.keep_debug) {
     ly.dbg_gpu.ensure((size_t)T * d * 4);
     dbg_gpu = (float *)ly.dbg_gpu.p;
   }
-  HIPCHK(hipEventSynchronize(c->ev_idx));
+  if (dec)
+    wait_routing(c, st);
+  else
+    HIPCHK(hipEventSynchronize(c->ev_idx));
   const double tp = now_s();
   ly.planner->plan((const int32_t *)c->h_idx.p, T * k, T, host_mode ? 1 : 0,
                    host_mode ? c->o.max_fills_per_call : -1, ly.plan);
@@ -499,8 +540,9 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   }
   bool combined = false;
   if (!host_mode && c->decode_ok(T)) {
-    // every miss is pulled from the pinned arena into its slot by a copy
-    // kernel on the compute stream, then computed there from host-built buckets
+    // every miss is pulled from the pinned arena into its slot by a copy kernel
+    // on the compute stream (after every earlier reader of the victims), then
+    // computed there from host-built buckets
     const int32_t *hidx = (const int32_t *)c->h_idx.p;
     for (size_t s = 0; s < ly.plan.stages.size(); ++s) {
       const moe::PlanStage &stg = ly.plan.stages[s];
@@ -521,17 +563,14 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
           for (int i = cnt; i < moe::kDecodeMaxTokens; ++i) tab.pairs[b][i] = tab.pairs[b][0];
         }
         pl.n = tab.n;
-        pl.per_expert = 64;
+        pl.per_expert = 32;
         pl.bytes16 = (long long)c->rec() / 16;
-        // victims may still be read by earlier kernels of this layer on another stream
-        if (ly.compute_recorded) HIPCHK(hipStreamWaitEvent(st, ly.compute_ev, 0));
         {
           KTime kt(c, MOE_K_FILL, st);
           HIPCHK(moe::launch_pull(pl, st));
           kt.end((double)pl.n * (double)c->rec());
         }
         run_experts(c, layer, T, pre, false, tab.n, (double)tab.n, x, st, &tab);
-        record_compute(c, ly, st);
       }
       ly.st.fills += stg.fills.size();
       ly.st.fill_bytes += stg.fills.size() * (uint64_t)c->rec();
@@ -549,7 +588,6 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
       for (const moe::Fill &fl : stg.fills) table[fl.expert] = fl.slot;
       const int nb = (int)stg.fills.size();
       run_experts(c, layer, T, make_view(table), false, nb, (double)nb, x, st);
-      record_compute(c, ly, st);
     }
     if (c->o.keep_debug) ly.dbg_host.assign((size_t)T * d, 0.0f);
   } else {
@@ -746,7 +784,12 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
     for (auto &sd : c->side) HIPCHK(hipStreamCreateWithFlags(&sd, hipStreamNonBlocking));
     HIPCHK(hipEventCreateWithFlags(&c->ev_idx, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&c->ev_ready, hipEventDisableTiming));
-    for (auto &e : c->partial_ev) HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    // completion only (the host or the copy streams wait for readers to finish):
+    // no system-scope fence
+    for (auto &e : c->partial_ev)
+      HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence));
+    HIPCHK(hipHostMalloc((void **)&c->h_flag, 64, hipHostMallocCoherent));
+    *c->h_flag = 0;
     c->layers.resize(layers);
     for (int32_t l = 0; l < layers; ++l) {
       LayerState &ly = c->layers[l];
@@ -760,7 +803,6 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
         return fail(MOE_ENOMEM, "device slot arena allocation failed");
       }
       for (auto &e : ly.fill_ev) HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-      HIPCHK(hipEventCreateWithFlags(&ly.compute_ev, hipEventDisableTiming));
       // preload: slot s <- expert s; shared slot S <- expert E
       for (int32_t s = 0; s < slots; ++s)
         HIPCHK(hipMemcpyAsync(c->dev_slot(l, s), c->host_record(l, s), c->rec(),

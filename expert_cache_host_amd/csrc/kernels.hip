@@ -26,40 +26,64 @@ __device__ __forceinline__ int mov_dpp(int v) {
   return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 
-// (value, id) order for top-k: larger value first, then lower id; id == sent
-// marks "no candidate".
-__device__ __forceinline__ void take_better(float &bv, int &be, float ov, int oe, int sent) {
-  if (oe != sent && (be == sent || ov > bv || (ov == bv && oe < be))) {
-    bv = ov;
-    be = oe;
-  }
+// Top-k order as one unsigned 64-bit comparison: the logit's bits mapped to an
+// order-preserving integer (-0 taken as +0) above the complemented expert id,
+// so that a larger value wins and, at equal values, the lower id.  0 is "no
+// candidate": no logit maps to it.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+  uint32_t b = __builtin_bit_cast(uint32_t, v + 0.0f);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
 }
+
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t b = (uint32_t)(k >> 32);
+  return __builtin_bit_cast(float, (b & 0x80000000u) ? (b & 0x7FFFFFFFu) : ~b);
+}
+
+__device__ __forceinline__ int key_id(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
+
+__device__ __forceinline__ uint64_t kmax(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
 template <int CTRL>
-__device__ __forceinline__ void argmax_step(float &bv, int &be, int sent) {
-  const float ov = __builtin_bit_cast(float, mov_dpp<CTRL>(__builtin_bit_cast(int, bv)));
-  const int oe = mov_dpp<CTRL>(be);
-  take_better(bv, be, ov, oe, sent);
+__device__ __forceinline__ uint64_t dpp_key(uint64_t k) {
+  const uint32_t lo = (uint32_t)mov_dpp<CTRL>((int)(uint32_t)k);
+  const uint32_t hi = (uint32_t)mov_dpp<CTRL>((int)(uint32_t)(k >> 32));
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// Best (value, id) over the wave, uniform in every lane: DPP within rows of 16
-// lanes (xor 1, xor 2, half-row mirror, row mirror), then the four row results.
-__device__ __forceinline__ void wave_argmax(float &bv, int &be, int sent) {
-  argmax_step<0xB1>(bv, be, sent);   // quad_perm [1,0,3,2]
-  argmax_step<0x4E>(bv, be, sent);   // quad_perm [2,3,0,1]
-  argmax_step<0x141>(bv, be, sent);  // row_half_mirror
-  argmax_step<0x140>(bv, be, sent);  // row_mirror
-  float rv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 0));
-  int re = __builtin_amdgcn_readlane(be, 0);
-#pragma unroll
-  for (int r = 1; r < 4; ++r) {
-    const float ov =
-        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 16 * r));
-    const int oe = __builtin_amdgcn_readlane(be, 16 * r);
-    take_better(rv, re, ov, oe, sent);
+// max(k, k of the partner lane) across 16-lane rows (ROWS = 16: rows 2j and
+// 2j+1) or wave halves (ROWS = 32), with the gfx950 lane swaps: swapping a
+// register with itself leaves, per lane, its own value in one result and the
+// partner's in the other, so the larger of the two results is the pair maximum.
+template <int ROWS>
+__device__ __forceinline__ uint64_t swap_max_key(uint64_t k) {
+  const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+  uint32_t l0, l1, h0, h1;
+  if constexpr (ROWS == 16) {
+    const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    l0 = a[0], l1 = a[1], h0 = b[0], h1 = b[1];
+  } else {
+    const auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    l0 = a[0], l1 = a[1], h0 = b[0], h1 = b[1];
   }
-  bv = rv;
-  be = re;
+  return kmax(((uint64_t)h0 << 32) | l0, ((uint64_t)h1 << 32) | l1);
+}
+
+// Largest key over the wave, branch free: DPP within rows of 16 lanes (xor 1,
+// xor 2, half-row mirror, row mirror), then lane swaps across rows and halves.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  k = kmax(k, dpp_key<0xB1>(k));   // quad_perm [1,0,3,2]
+  k = kmax(k, dpp_key<0x4E>(k));   // quad_perm [2,3,0,1]
+  k = kmax(k, dpp_key<0x141>(k));  // row_half_mirror
+  k = kmax(k, dpp_key<0x140>(k));  // row_mirror
+  k = swap_max_key<16>(k);
+  k = swap_max_key<32>(k);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)k);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(k >> 32));
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Digit planes of 8 values (elements g..g+3, g+16..g+19 of a block) at scale
@@ -228,38 +252,33 @@ hipError_t launch_router(const float *x, int T, int d, const float *W, const flo
 }
 
 // ============================================================== top-k + softmax
-// One wave per token; E <= 512, so each lane owns up to 8 logits.  Lane j < k
-// ends with the j-th selection (my_e) and its gating weight (my_w).
-__device__ __forceinline__ void topk_token(const float *__restrict__ z, int t, int E, int k,
-                                           int norm_topk, int &my_e, float &my_w) {
+// One wave per token; E <= 512, so each lane owns NC <= 8 logits (expert
+// lane + 64c).  k rounds of a wave-wide maximum over the remaining keys; lane
+// j < k ends with the j-th selection (my_e) and its gating weight (my_w).
+template <int NC>
+__device__ __forceinline__ void topk_token_nc(const float *z, int t, int E, int k, int norm_topk,
+                                              int &my_e, float &my_w) {
   const int lane = threadIdx.x & 63;
-  float v[8];
-  bool ok[8];
+  float v[NC];
+  uint64_t key[NC];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const int e = lane + 64 * c;
-    ok[c] = e < E;
-    v[c] = ok[c] ? z[(long long)t * E + e] : 0.0f;
+    v[c] = e < E ? z[(long long)t * E + e] : 0.0f;
+    key[c] = e < E ? topk_key(v[c], e) : 0ull;
   }
   my_e = 0;
   float my_v = 0.0f;
   for (int j = 0; j < k; ++j) {
-    float bv = 0.0f;
-    int be = E;  // sentinel: nothing yet
+    uint64_t m = key[0];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      if (ok[c] && (be == E || v[c] > bv)) {
-        bv = v[c];
-        be = lane + 64 * c;
-      }
-    }
-    wave_argmax(bv, be, E);
+    for (int c = 1; c < NC; ++c) m = kmax(m, key[c]);
+    m = wave_max_key(m);
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      if (lane + 64 * c == be) ok[c] = false;
+    for (int c = 0; c < NC; ++c) key[c] = key[c] == m ? 0ull : key[c];
     if (lane == j) {
-      my_e = be;
-      my_v = bv;
+      my_e = key_id(m);
+      my_v = key_value(m);
     }
   }
   const float zmax =
@@ -272,12 +291,24 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ z, int t, i
   } else {
     denom = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int c = 0; c < NC; ++c)
       if (lane + 64 * c < E) denom += expf(v[c] - zmax);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) denom += __shfl_xor(denom, off, 64);
   my_w = ex / denom;
+}
+
+__device__ __forceinline__ void topk_token(const float *z, int t, int E, int k, int norm_topk,
+                                           int &my_e, float &my_w) {
+  if (E <= 64)
+    topk_token_nc<1>(z, t, E, k, norm_topk, my_e, my_w);
+  else if (E <= 128)
+    topk_token_nc<2>(z, t, E, k, norm_topk, my_e, my_w);
+  else if (E <= 256)
+    topk_token_nc<4>(z, t, E, k, norm_topk, my_e, my_w);
+  else
+    topk_token_nc<8>(z, t, E, k, norm_topk, my_e, my_w);
 }
 
 __global__ __launch_bounds__(64) void topk_kernel(const float *__restrict__ z, int T, int E, int k,
@@ -299,36 +330,40 @@ __global__ __launch_bounds__(64) void topk_kernel(const float *__restrict__ z, i
 
 // Decode calls (T <= 4 tokens, T*k + shared pairs <= 64): one workgroup, wave t
 // selects token t's experts; then wave 0 maps every pair to its slot through
-// `view` (shared pairs to shared_slot) and lists the buckets: pairs grouped by
-// slot, a bucket per slot in order of its first pair, pairs ascending.
-__global__ __launch_bounds__(256) void topk_decode_kernel(const float *__restrict__ z, int T, int E,
-                                                          int k, int norm_topk,
-                                                          int32_t *__restrict__ idx,
-                                                          float *__restrict__ w, int32_t *h_idx,
-                                                          float *h_w, SlotView view,
-                                                          int shared_slot,
-                                                          int32_t *__restrict__ buckets,
-                                                          int32_t *__restrict__ pair_slot) {
+// `view` (shared pairs to shared_slot), lists the buckets (pairs grouped by slot,
+// a bucket per slot in order of its first pair, pairs ascending), writes the
+// page-locked routing copy and raises the host flag.  Every thread of the
+// workgroup (at least 64 * T) calls it.
+__device__ void topk_decode_block(const float *z, int T, int E, const DecodeTopk &a) {
   __shared__ int sidx[kDecodeMaxPairs];
+  __shared__ float sw[kDecodeMaxPairs];
   const int t = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int my_e;
-  float my_w;
-  topk_token(z, t, E, k, norm_topk, my_e, my_w);
-  if (lane < k) {
-    const int o = t * k + lane;
-    idx[o] = my_e;
-    w[o] = my_w;
-    h_idx[o] = my_e;
-    h_w[o] = my_w;
-    sidx[o] = my_e;
+  const int k = a.k;
+  if (t < T) {
+    int my_e;
+    float my_w;
+    topk_token(z, t, E, k, a.norm_topk, my_e, my_w);
+    if (lane < k) {
+      const int o = t * k + lane;
+      a.idx[o] = my_e;
+      a.w[o] = my_w;
+      sidx[o] = my_e;
+      sw[o] = my_w;
+    }
   }
   __syncthreads();
   if (t != 0) return;
   const int Pr = T * k;
-  const int P = Pr + (shared_slot >= 0 ? T : 0);
+  const int P = Pr + (a.shared_slot >= 0 ? T : 0);
+  // wave 0 alone writes the page-locked routing copy, so that its own fence
+  // publishes all of it before the flag
+  if (lane < Pr) {
+    a.h_idx[lane] = sidx[lane];
+    a.h_w[lane] = sw[lane];
+  }
   int s = -1;
-  if (lane < P) s = lane < Pr ? (int)view.slot[sidx[lane]] : shared_slot;
-  if (lane < Pr) pair_slot[lane] = s;
+  if (lane < P) s = lane < Pr ? (int)a.view.slot[sidx[lane]] : a.shared_slot;
+  if (lane < Pr) a.pair_slot[lane] = s;
   // one pass per distinct slot, in order of its first pair: that pair's lane
   // leads, the ballot of equal slots gives the bucket's pairs
   const uint64_t below = (1ull << lane) - 1ull;
@@ -339,7 +374,7 @@ __global__ __launch_bounds__(256) void topk_decode_kernel(const float *__restric
     const int slot = __builtin_amdgcn_readlane(s, lead);
     const uint64_t same = __ballot(s == slot);
     const int cnt = __popcll(same);
-    int32_t *e = buckets + 1 + nbk * kBucketInts;
+    int32_t *e = a.buckets + 1 + nbk * kBucketInts;
     if (s == slot) {
       const int rank = __popcll(same & below);
       e[2 + rank] = lane;
@@ -353,7 +388,15 @@ __global__ __launch_bounds__(256) void topk_decode_kernel(const float *__restric
     todo &= ~same;
     nbk++;
   }
-  if (lane == 0) buckets[0] = nbk;
+  if (lane == 0) a.buckets[0] = nbk;
+  // publish the routing copy to the host: system-scope release, then the flag
+  __threadfence_system();
+  if (lane == 0) __hip_atomic_store(a.h_flag, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+__global__ __launch_bounds__(256) void topk_decode_kernel(const float *z, int T, int E,
+                                                          DecodeTopk a) {
+  topk_decode_block(z, T, E, a);
 }
 
 hipError_t launch_topk(const float *z, int T, int E, int k, int norm_topk, int32_t *idx, float *w,
@@ -363,17 +406,17 @@ hipError_t launch_topk(const float *z, int T, int E, int k, int norm_topk, int32
   return hipGetLastError();
 }
 
-hipError_t launch_topk_decode(const float *z, int T, int E, int k, int norm_topk, int32_t *idx,
-                              float *w, int32_t *h_idx, float *h_w, const SlotView &view,
-                              int shared_slot, int32_t *buckets, int32_t *pair_slot,
-                              hipStream_t s) {
-  if (T < 1 || T > kDecodeMaxTokens ||
-      T * k + (shared_slot >= 0 ? T : 0) > kDecodeMaxPairs)
-    return hipErrorInvalidValue;
-  hipLaunchKernelGGL(topk_decode_kernel, dim3(1), dim3(64 * T), 0, s, z, T, E, k, norm_topk, idx,
-                     w, h_idx, h_w, view, shared_slot, buckets, pair_slot);
+static bool decode_args_ok(int T, const DecodeTopk &a) {
+  return T >= 1 && T <= kDecodeMaxTokens &&
+         T * a.k + (a.shared_slot >= 0 ? T : 0) <= kDecodeMaxPairs && a.h_flag != nullptr;
+}
+
+hipError_t launch_topk_decode(const float *z, int T, int E, const DecodeTopk &a, hipStream_t s) {
+  if (!decode_args_ok(T, a)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_decode_kernel, dim3(1), dim3(64 * T), 0, s, z, T, E, a);
   return hipGetLastError();
 }
+
 
 // ============================================================== remap + bucket
 // One workgroup of 16 waves.  Counts pairs per slot, lays buckets out in slot
@@ -1332,19 +1375,18 @@ __global__ __launch_bounds__(256) void pull_kernel(PullList l) {
   const long long b = part * per, end = min(b + per, l.bytes16);
   const uint4 *__restrict__ src = reinterpret_cast<const uint4 *>(l.src[e]);
   uint4 *__restrict__ dst = reinterpret_cast<uint4 *>(l.dst[e]);
-  constexpr int U = 8;
-  for (long long i = b + threadIdx.x; i < end; i += 256 * U) {
-    uint4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const long long j = i + (long long)u * 256;
-      if (j < end) v[u] = src[j];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const long long j = i + (long long)u * 256;
-      if (j < end) dst[j] = v[u];
-    }
+  // two 16-B loads in flight per lane.  Measured on page-locked records: more
+  // requests in flight (more loads per lane, or more workgroups per expert)
+  // lowers the PCIe read rate; 32 workgroups x 256 lanes x 2 is near the best.
+  // A load past the end is skipped, not clamped, so no host byte is read twice.
+#pragma unroll 1
+  for (long long i = b + threadIdx.x; i < end; i += 512) {
+    const uint4 v0 = src[i];
+    const bool k1 = i + 256 < end;
+    uint4 v1;
+    if (k1) v1 = src[i + 256];
+    dst[i] = v0;
+    if (k1) dst[i + 256] = v1;
   }
 }
 

@@ -44,15 +44,28 @@ hipError_t launch_topk(const float *z, int T, int E, int k, int norm_topk, int32
 // one repeated past the count).
 constexpr int kBucketInts = 6;  // 2 + kDecodeMaxTokens
 
-// launch_topk for decode calls (T <= kDecodeMaxTokens, T*k + shared pairs <=
-// kDecodeMaxPairs; else hipErrorInvalidValue), which also maps each routed pair
-// to its slot through `view` (pair_slot[T*k], -1 when not cached) and writes
-// the bucket list of the cached experts plus, when shared_slot >= 0, one bucket
-// of the shared expert's T pairs (pair T*k + t) at slot shared_slot.
-hipError_t launch_topk_decode(const float *z, int T, int E, int k, int norm_topk, int32_t *idx,
-                              float *w, int32_t *h_idx, float *h_w, const SlotView &view,
-                              int shared_slot, int32_t *buckets, int32_t *pair_slot,
-                              hipStream_t s);
+// Decode top-k (T <= kDecodeMaxTokens, T*k + shared pairs <= kDecodeMaxPairs,
+// h_flag set; else hipErrorInvalidValue): as launch_topk (idx, w on the device,
+// h_idx, h_w page-locked), and also maps each routed pair to its slot through
+// `view` (pair_slot[T*k], -1 when not cached) and writes the bucket list of the
+// cached experts plus, when shared_slot >= 0, one bucket of the shared expert's
+// T pairs (pair T*k + t) at slot shared_slot.  When h_idx / h_w are complete and
+// visible to the host, seq is stored into *h_flag (page-locked, coherent) with
+// a system-scope release, so that the host can wait on the flag instead of an
+// event with a full-device fence.
+struct DecodeTopk {
+  int k, norm_topk;
+  int32_t *idx;
+  float *w;
+  int32_t *h_idx;
+  float *h_w;
+  SlotView view;
+  int shared_slot;
+  int32_t *buckets, *pair_slot;
+  uint32_t *h_flag;
+  uint32_t seq;
+};
+hipError_t launch_topk_decode(const float *z, int T, int E, const DecodeTopk &a, hipStream_t s);
 
 // Tokens of one bucket that one matrix-core workgroup takes per pass.
 constexpr int kGemmTokens = 32;
@@ -157,7 +170,8 @@ hipError_t launch_prep_pairs(const float *in, int rows, int K, uint32_t *xp, flo
 
 // Copies n expert records (bytes16 x 16 bytes each) from the page-locked host
 // arena into device slots; `per_expert` workgroups each read one contiguous
-// chunk with wide loads (PCIe reads stay long and in flight).
+// chunk, two 16-byte loads in flight per lane (more requests in flight read
+// page-locked memory more slowly).
 struct PullList {
   const uint8_t *src[kTabMax];
   uint8_t *dst[kTabMax];

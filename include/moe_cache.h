@@ -178,17 +178,22 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
  * Each selected expert computes y = D (silu(G x) * (U x)); shared experts add
  * with weight 1; out[t] = sum_j w[t,j] y_{idx[t,j]} + shared.
  *
- * MOE_MISS_STREAM: the call waits for the routing (a device->host copy of the
- * ids), plans, copies missed experts into slots on a side stream and computes
- * every selected expert on the GPU, in stages when more experts are selected
- * than slots exist.  MOE_MISS_HOST: GPU work on cached experts is enqueued
+ * MOE_MISS_STREAM: the call waits for the routing (the top-k kernel writes
+ * the ids to page-locked memory and raises a flag), plans, copies missed
+ * experts into slots (decode-sized calls: a copy kernel on `stream`; larger
+ * calls: the copy engines on side streams) and computes every selected expert
+ * on the GPU, in stages when more experts are selected than slots exist.
+ * MOE_MISS_HOST: GPU work on cached experts is enqueued
  * before the routing reaches the host; host threads then compute the misses,
  * the misses' slot fills are queued on the side stream and become visible at
  * the same layer's next call, and the GPU adds the host partial; the call
  * returns when the host partial has been handed to `stream`.
  *
  * x, router_w, router_bias and out must stay valid until `stream` has passed
- * this call's work.  Requirements: 0 <= layer < layers; 1 <= n_tokens; the
+ * this call's work.  A layer's calls are ordered on their stream; a call on
+ * another stream than the same layer's previous call first waits for the whole
+ * device (hipDeviceSynchronize), so that no earlier reader of a slot can race
+ * with its refill.  Requirements: 0 <= layer < layers; 1 <= n_tokens; the
  * pointers non-NULL except router_bias and stream.
  */
 moe_status moe_layer_forward(moe_cache *c, int32_t layer, const float *x, int32_t n_tokens,
