@@ -201,8 +201,9 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
     }
     int ex2 = 0;
     if (m > 0.0f && m <= 3.0e38f) {
-      int fe;
-      (void)frexpf(m, &fe);  // m = f * 2^fe, f in [0.5, 1)
+      // m = f * 2^fe with f in [0.5, 1) for normal m; a subnormal m gives a
+      // smaller fe, and ex2 = 0 either way
+      const int fe = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xFFu) - 126;
       ex2 = max(0, fe - 14);
     }
     const float sc = ldexpf(1.0f, -ex2);
@@ -585,6 +586,21 @@ __device__ __forceinline__ int pick(const int (&a)[N], int i) {
   return r;
 }
 
+// Pair tt of bucket b for a lane-varying tt: a select chain for TT <= 2; above
+// that the compiler turns selects back into an indexed register array (which
+// lives in scratch), so the pair is read again from the list or the table.
+template <int TT, int MODE>
+__device__ __forceinline__ int pair_at(const GemvArgs &a, const BucketTable &tab, int b,
+                                       const Bucket<TT> &bk, int tt) {
+  if constexpr (TT <= 2) {
+    return pick(bk.pairs, tt);
+  } else if constexpr (MODE == BK_TABLE) {
+    return tab.pairs[b][min(tt, bk.cnt - 1)];
+  } else {
+    return a.bt[1 + b * kBucketInts + 2 + tt];
+  }
+}
+
 template <int TT, int MODE>
 __device__ __forceinline__ bool find_bucket(const GemvArgs &a, const BucketTable &tab, int b,
                                             Bucket<TT> &bk) {
@@ -672,7 +688,9 @@ __global__ __launch_bounds__(64 * NW) void q4_gateup_kernel(GemvArgs a, BucketTa
     u = min(u, n_stage - 1);
     if (u < n_x) {
       const int tt = u / (nb * 4);
-      return a.xq[(long long)pick(tok, tt) * nb * 4 + (u - tt * nb * 4)];
+      const int row =
+          TT <= 2 ? pick(tok, tt) : pair_row(a, pair_at<TT, MODE>(a, tab, blockIdx.y, bk, tt));
+      return a.xq[(long long)row * nb * 4 + (u - tt * nb * 4)];
     }
     return u < n_x + n_s ? c0[u - n_x] : c1[u - n_x - n_s];
   };
@@ -786,8 +804,9 @@ __global__ __launch_bounds__(64 * NW) void q4_gateup_kernel(GemvArgs a, BucketTa
         gg += red[g * KS + q][rr][tt][0];
         uu += red[g * KS + q][rr][tt][1];
       }
-      const float sc = a.xs[pick(tok, tt)];
-      a.out[(long long)pick(bk.pairs, tt) * a.rows + r] = silu_f(gg * sc) * (uu * sc);
+      const int p = pair_at<TT, MODE>(a, tab, blockIdx.y, bk, tt);
+      const float sc = a.xs[pair_row(a, p)];
+      a.out[(long long)p * a.rows + r] = silu_f(gg * sc) * (uu * sc);
     }
   }
 }
@@ -836,7 +855,8 @@ __global__ __launch_bounds__(64 * NW) void q4_down_kernel(GemvArgs a, BucketTabl
       const int u = min(u0 + tid + NT * c, n_units - 1);
       const int tt = u / (nb * 4), rem = u - tt * nb * 4;
       const int b = rem >> 2, j = rem & 3;
-      const float *hr = a.in + (long long)pick(bk.pairs, tt) * nb * 32 + b * 32 + 4 * j;
+      const float *hr =
+          a.in + (long long)pair_at<TT, MODE>(a, tab, blockIdx.y, bk, tt) * nb * 32 + b * 32 + 4 * j;
       v0[c] = *reinterpret_cast<const float4 *>(hr);
       v1[c] = *reinterpret_cast<const float4 *>(hr + 16);
     }
@@ -945,7 +965,7 @@ __global__ __launch_bounds__(64 * NW) void q4_down_kernel(GemvArgs a, BucketTabl
       float v = 0.0f;
 #pragma unroll
       for (int q = 0; q < KS; ++q) v += red[g * KS + q][rr][tt];
-      a.out[(long long)pick(bk.pairs, tt) * a.rows + r] = v;
+      a.out[(long long)pair_at<TT, MODE>(a, tab, blockIdx.y, bk, tt) * a.rows + r] = v;
     }
   }
 }

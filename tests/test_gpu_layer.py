@@ -117,6 +117,36 @@ def test_prefill_ubatch_preheat_sampled():
     r.close()
 
 
+@pytest.mark.parametrize("T", [1, 3, 17])
+def test_topk_exact_ties(T):
+    """Exact logit ties through the whole layer: duplicated router rows give equal
+    logits (the lower id must win), two zero rows tie at 0 and a negated row
+    mirrors another; a bias of -100 keeps every other expert out, so the ties
+    decide the selection.  The top-k ids must match the oracle bit for bit."""
+    import torch
+    wl = synth.Workload("ties", 13, 1, 256, 512, 32, 6, 6, router_sigma=0.1, rho=0.9,
+                        tokens=24, batch=T)
+    log(f"top-k exact ties, T={T}")
+    r = Runner(wl, [0], mode="stream")
+    w_r, b, _, _ = r.routers[0]
+    w_r = w_r.copy()
+    w_r[5] = w_r[2]      # ties between experts 2 and 5
+    w_r[9] = w_r[4]      # and 4, 9, 30
+    w_r[30] = w_r[4]
+    w_r[11] = 0.0        # two logits of exactly 0
+    w_r[12] = 0.0
+    w_r[20] = -w_r[21]   # exact negation: z20 = -z21
+    # only these nine compete
+    b = np.full(wl.n_experts, -100.0, np.float32)
+    b[[2, 4, 5, 9, 11, 12, 20, 21, 30]] = 0.0
+    r.routers[0] = (w_r, b, torch.from_numpy(w_r).cuda(), torch.from_numpy(b).cuda())
+    x = synth.gen_hidden(wl, 0, 8)
+    for c in range(x.shape[0]):
+        r.call(0, x[c])
+    r.check_log()
+    r.close()
+
+
 def test_gemma_shape_two_layers():
     wl = synth.WORKLOADS["gemma"]
     log("gemma shape, 2 layers x 6 calls")
