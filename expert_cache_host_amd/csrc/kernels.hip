@@ -971,20 +971,19 @@ __global__ __launch_bounds__(64 * NW) void q4_down_kernel(GemvArgs a, BucketTabl
 }
 
 // Shapes measured on MI355X for one token per bucket over the decode shapes
-// d x f = 6144 x 2048 and 2816 x 704 at 6-8 experts per launch: gate/up rows
-// of >= 128 blocks run best with 32 lanes per row and K split over 2 waves,
-// shorter ones with 8 lanes and K over the 4 waves, 2 rows per lane; down rows
-// of >= 64 blocks with 16 lanes per row, whole K per wave and 4 rows per lane,
-// shorter ones with 8 lanes and K over 4 waves.  Rows of fewer than 32 gate/up
-// blocks keep K in one wave.
+// d x f = 6144 x 2048 and 2816 x 704: gate/up rows of >= 128 blocks run best
+// with 16 lanes per row, shorter ones with 8, K split over the 4 waves, 2 rows
+// per lane; down rows of >= 64 blocks with 16 lanes per row, whole K per wave
+// and 4 rows per lane, shorter ones with 8 lanes and K over 4 waves.  Rows of
+// fewer than 32 gate/up blocks keep K in one wave.
 GemvShape choose_gemv(bool glu, int nb, int tokens) {
   GemvShape sh{};
   sh.TT = tokens <= 1 ? 1 : (tokens <= 2 ? 2 : 4);
   if (glu) {
     sh.R = 2;
     if (nb >= 128) {
-      sh.G = 32;
-      sh.KS = 2;
+      sh.G = 16;
+      sh.KS = 4;
     } else if (nb >= 32) {
       sh.G = 8;
       sh.KS = 4;
@@ -1058,7 +1057,7 @@ hipError_t launch_gemv(const GemvArgs &a, const BucketTable *tab, const GemvShap
   const size_t lds = gemv_lds_bytes(glu, a.nb, sh.TT);
   const int key = (glu ? 1000 : 0) + sh.G * 100 + sh.KS * 10 + sh.R;
   switch (key) {
-    case 1000 + 3200 + 20 + 2: launch_tt<true, 32, 2, 2>(a, t, n_buckets, sh.TT, lds, s); break;
+    case 1000 + 1600 + 40 + 2: launch_tt<true, 16, 4, 2>(a, t, n_buckets, sh.TT, lds, s); break;
     case 1000 + 800 + 40 + 2: launch_tt<true, 8, 4, 2>(a, t, n_buckets, sh.TT, lds, s); break;
     case 1000 + 800 + 10 + 2: launch_tt<true, 8, 1, 2>(a, t, n_buckets, sh.TT, lds, s); break;
     case 1600 + 10 + 4: launch_tt<false, 16, 1, 4>(a, t, n_buckets, sh.TT, lds, s); break;
