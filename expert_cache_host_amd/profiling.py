@@ -5,11 +5,20 @@
     python -m expert_cache_host_amd.profiling traffic <out.json> <copy fetch dir> <copy write dir> \
         <workload>=<fetch dir>,<write dir> [...]
 
+    python -m expert_cache_host_amd.profiling copies <rocprof dir> <record bytes> <title> <command...>
+    python -m expert_cache_host_amd.profiling mfma <rocprof dir> <title> <command...>
+    python -m expert_cache_host_amd.profiling timeline <rocprof dir> <first kernel> <count>
+
 `stats` reads the *_kernel_stats.csv of a `rocprofv3 --kernel-trace --stats
 --output-format csv` run; `pmc` reads the *_counter_collection.csv of a
 `rocprofv3 --pmc <counter> --output-format csv` run and averages the counter
-per dispatch and kernel.  Both print markdown with the command that produced
-the data.
+per dispatch and kernel.  `copies` reads the *_memory_copy_trace.csv of a
+`--memory-copy-trace` run: every host-to-device copy that starts after the
+first expert kernel is a slot fill of one record, and the link rate is the
+bytes over the time at least one such copy is in flight.  `mfma` reads a
+`--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_BUSY_CYCLES
+GRBM_GUI_ACTIVE` run.  All print markdown with the command that produced the
+data.
 """
 from __future__ import annotations
 
@@ -59,6 +68,82 @@ def pmc_md(d: str, counter: str, title: str, command: str) -> str:
            f"| kernel | dispatches | mean {counter} per dispatch (KiB) |", "|---|---|---|"]
     for k, (v, n) in sorted(t.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
         out.append(f"| `{short(k)}` | {n} | {v:.1f} |")
+    return "\n".join(out) + "\n"
+
+
+def copies_md(d: str, record_bytes: int, title: str, command: str) -> str:
+    kt = list(csv.DictReader(open(_find(d, "kernel_trace.csv"))))
+    first = min(int(r["Start_Timestamp"]) for r in kt if "q4_" in r["Kernel_Name"])
+    rows = [r for r in csv.DictReader(open(_find(d, "memory_copy_trace.csv")))
+            if r["Direction"] == "MEMORY_COPY_HOST_TO_DEVICE" and int(r["Start_Timestamp"]) >= first]
+    iv = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows)
+    busy, cur_s, cur_e = 0, None, None
+    for a, b in iv:
+        if cur_e is None or a > cur_e:
+            if cur_e is not None:
+                busy += cur_e - cur_s
+            cur_s, cur_e = a, b
+        else:
+            cur_e = max(cur_e, b)
+    if cur_e is not None:
+        busy += cur_e - cur_s
+    n = len(iv)
+    per = [b - a for a, b in iv]
+    mean_us = sum(per) / n / 1e3 if n else 0.0
+    out = [f"# {title}", "", "Command:", "", "```", command, "```", "",
+           "Host-to-device slot fills on the copy engines (one record each, "
+           f"{record_bytes:,} bytes), after the first expert kernel:", "",
+           "| fills | mean copy (us) | per-copy GB/s | link busy (ms) | link GB/s while busy |",
+           "|---|---|---|---|---|"]
+    if n:
+        out.append(f"| {n} | {mean_us:.1f} | {record_bytes / (mean_us * 1e3):.1f} | {busy / 1e6:.1f} | "
+                   f"{n * record_bytes / busy:.1f} |")
+    return "\n".join(out) + "\n"
+
+
+def timeline_md(d: str, anchor: str, count: int) -> str:
+    """One call's kernels: `count` dispatches from the first `anchor` kernel at or
+    after the middle of the trace, with start and end relative to the first."""
+    rows = sorted(csv.DictReader(open(_find(d, "kernel_trace.csv"))),
+                  key=lambda r: int(r["Start_Timestamp"]))
+    i = next(j for j in range(len(rows) // 2, len(rows)) if anchor in rows[j]["Kernel_Name"])
+    t0 = int(rows[i]["Start_Timestamp"])
+    out = ["| kernel | start us | end us |", "|---|---|---|"]
+    for r in rows[i:i + count]:
+        name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        out.append(f"| `{name}` | {(int(r['Start_Timestamp']) - t0) / 1e3:.1f} | "
+                   f"{(int(r['End_Timestamp']) - t0) / 1e3:.1f} |")
+    return "\n".join(out) + "\n"
+
+
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_BUSY_CYCLES",
+                 "GRBM_GUI_ACTIVE")
+XCDS, SIMDS = 8, 1024  # MI355X: 8 accelerator dies, 256 CUs x 4 SIMDs
+
+
+def mfma_md(d: str, title: str, command: str) -> str:
+    f = _find(d, "counter_collection.csv")
+    acc = defaultdict(lambda: defaultdict(float))
+    n = defaultdict(int)
+    dur = defaultdict(float)
+    for r in csv.DictReader(open(f)):
+        k = r["Kernel_Name"]
+        acc[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+            n[k] += 1
+            dur[k] += (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    out = [f"# {title}", "", "Command:", "", "```", command, "```", "",
+           "GRBM_GUI_ACTIVE is summed over the 8 dies, so one die's active cycles are the sum / 8; "
+           "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (die cycles x 1024 SIMDs); matrix flops = "
+           "SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 (they count the hi/lo split and padded token rows).", "",
+           "| kernel | dispatches | mean us | MFMA busy % | matrix TFLOP/s |", "|---|---|---|---|---|"]
+    for k in sorted(acc, key=lambda q: -dur[q]):
+        c = acc[k]
+        if not c.get("SQ_INSTS_VALU_MFMA_MOPS_F16"):
+            continue
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] / XCDS * SIMDS) * 100
+        tf = c["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512 / (dur[k] * 1e-6) / 1e12
+        out.append(f"| `{short(k)}` | {n[k]} | {dur[k] / n[k]:.1f} | {busy:.1f} | {tf:.0f} |")
     return "\n".join(out) + "\n"
 
 
@@ -114,6 +199,12 @@ def main(argv):
         print(stats_md(argv[1], argv[2], " ".join(argv[3:])), end="")
     elif len(argv) >= 5 and argv[0] == "pmc":
         print(pmc_md(argv[1], argv[2], argv[3], " ".join(argv[4:])), end="")
+    elif len(argv) >= 5 and argv[0] == "copies":
+        print(copies_md(argv[1], int(argv[2]), argv[3], " ".join(argv[4:])), end="")
+    elif len(argv) == 4 and argv[0] == "timeline":
+        print(timeline_md(argv[1], argv[2], int(argv[3])), end="")
+    elif len(argv) >= 4 and argv[0] == "mfma":
+        print(mfma_md(argv[1], argv[2], " ".join(argv[3:])), end="")
     elif len(argv) >= 5 and argv[0] == "traffic":
         pairs = {}
         for a in argv[4:]:
