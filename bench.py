@@ -323,8 +323,24 @@ def main():
             for l in range(wl.layers):
                 cache.forward(l, x_d[l][s], w_d[l], b_d[l], out=out)
 
-    run(0, warmup)
+    # Warm-up, untimed.  Each call's routing is read back (which waits for the
+    # call) for the stickiness |S_t & S_t-1| / k of every stream (decode).
+    prev = [None] * wl.layers
+    acc = [0, 0]
+    for s_ in range(warmup):
+        for l in range(wl.layers):
+            cache.forward(l, x_d[l][s_], w_d[l], b_d[l], out=out)
+            if wl.rho is None:
+                continue
+            idx, _ = cache.routing(l)
+            if prev[l] is not None:
+                for b_ in range(idx.shape[0]):
+                    acc[0] += len(set(idx[b_].tolist()) & set(prev[l][b_].tolist()))
+                    acc[1] += wl.top_k
+            prev[l] = idx
+    stick = acc[0] / acc[1] if acc[1] else None
     torch.cuda.synchronize()
+    st0 = cache.stats()  # the warm-up calls: slots start from the preload
     cache.reset_stats()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -345,13 +361,33 @@ def main():
         ks = cache.kernel_stats()
         st2 = cache.stats()
         log(f"[bench] kernel-event pass of {ev_steps} steps done")
-
+    # Warm-up, untimed.  Each call's routing is read back (which waits for the
+    # call) for the stickiness |S_t & S_t-1| / k of every stream (decode).
+    prev = [None] * wl.layers
+    acc = [0, 0]
+    for s_ in range(warmup):
+        for l in range(wl.layers):
+            cache.forward(l, x_d[l][s_], w_d[l], b_d[l], out=out)
+            if wl.rho is None:
+                continue
+            idx, _ = cache.routing(l)
+            if prev[l] is not None:
+                for b_ in range(idx.shape[0]):
+                    acc[0] += len(set(idx[b_].tolist()) & set(prev[l][b_].tolist()))
+                    acc[1] += wl.top_k
+            prev[l] = idx
+    stick = acc[0] / acc[1] if acc[1] else None
+    torch.cuda.synchronize()
+    st0 = cache.stats()  # the warm-up calls: slots start from the preload
     layer_tokens = steps * wl.batch * wl.layers
     value = layer_tokens / wall
     sel = max(1, st["selections"])
     extra = {
         "stack_tokens_per_s": steps * wl.batch / wall,
         "hit_rate": st["hits"] / sel,
+        "hit_rate_warmup_calls": st0["hits"] / max(1, st0["selections"]),
+        "warmup_calls_per_layer": warmup,
+        "stickiness_warmup_calls": stick,
         "fills_per_call": st["fills"] / max(1, st["calls"]),
         "fill_GB": st["fill_bytes"] / 1e9,
         "stages_per_call": st["stages"] / max(1, st["calls"]),

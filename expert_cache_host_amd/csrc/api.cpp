@@ -237,7 +237,12 @@ struct moe_cache {
     xs.ensure((size_t)T * 4);
     buckets.ensure((size_t)(1 + moe::kDecodeMaxPairs * moe::kBucketInts) * 4);
     pair_slot.ensure((size_t)moe::kDecodeMaxPairs * 4);
-    if (T > moe::kDecodeMaxTokens) {
+    // h as binary16 pairs for the matrix-core down GEMM: every call that does
+    // not take the decode path (a call of up to kDecodeMaxTokens tokens takes
+    // the matrix cores too when its pairs or its LDS do not fit the decode
+    // GEMV).  decode_ok only turns false as T grows, so the buffers sized at the
+    // largest T seen serve every smaller matrix-core call.
+    if (!decode_ok(T)) {
       hp.ensure(P * (size_t)f * 4);
       hsw.ensure(P * (size_t)(f / 8) * 4);
       hscale.ensure(P * 4);
@@ -355,6 +360,25 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
   const int shared_slot = with_shared ? c->S : -1;
   const int P = T * k + (with_shared ? T : 0);
   const bool decode = c->decode_ok(T);
+  // the workspace the kernels below index, checked before any launch
+  {
+    const size_t P_all = (size_t)T * k + (size_t)T * c->o.n_shared;
+    auto need = [&](const DevBuf &b, size_t bytes, const char *what) {
+      if (!b.p || b.bytes < bytes)
+        throw HipError(std::string("workspace ") + what + " too small for this call");
+    };
+    need(c->h, P_all * (size_t)c->f * 4, "h");
+    need(c->y, P_all * (size_t)c->d * 4, "y");
+    if (!decode && !tab) {
+      need(c->xp, (size_t)T * c->d * 4, "xp");
+      need(c->hp, P_all * (size_t)c->f * 4, "hp");
+      need(c->hsw, P_all * (size_t)(c->f / 8) * 4, "hsw");
+      need(c->hscale, P_all * 4, "hscale");
+      need(c->bucket_pair, P_all * 4, "bucket_pair");
+    } else {
+      need(c->xq, (size_t)T * c->d * 2, "xq");
+    }
+  }
   const moe::RecordLayout &L = c->lay;
   moe::GemvArgs a{};
   if (!decode && !tab) {

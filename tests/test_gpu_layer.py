@@ -265,3 +265,42 @@ def test_usage_profile_preload(mode, policy):
             r.call(li, xs[li][t], check_out=(t % 3 == 0))
     r.check_log()
     r.close()
+
+
+# Degenerate and maximum cases: every selection, one selection, the most experts
+# the boundary takes, the smallest shapes it takes, the decode path's pair limit
+# and one pair past it (the matrix-core path), slots for every expert.
+EDGE = {
+    # name: (d, f, E, k, S, shared, tokens per call)
+    "k_eq_E": (256, 512, 8, 8, 4, 0, 1),
+    "k_eq_E_slots_all": (256, 512, 8, 8, 8, 0, 1),
+    "k_1": (256, 512, 8, 1, 2, 0, 1),
+    "E_512": (64, 64, 512, 8, 32, 0, 1),
+    "E_512_T4": (64, 64, 512, 8, 32, 1, 4),
+    "min_shape": (64, 32, 16, 4, 4, 1, 3),
+    "pairs_64": (128, 128, 64, 15, 16, 1, 4),
+    "pairs_68": (128, 128, 64, 16, 16, 1, 4),
+    "slots_eq_E": (128, 256, 16, 4, 16, 1, 2),
+}
+
+
+@pytest.mark.parametrize("mode", ["stream", "host"])
+@pytest.mark.parametrize("case", sorted(EDGE))
+def test_edge_shapes(case, mode):
+    d, f, E, k, S, ns, T = EDGE[case]
+    wl = synth.Workload("edge_" + case, 20 + sorted(EDGE).index(case), 1, d, f, E, k, S,
+                        n_shared=ns, router_sigma=0.3, zipf_s=0.8, rho=0.5, tokens=10, batch=T)
+    log(f"edge {case} mode={mode}: d={d} f={f} E={E} k={k} S={S} shared={ns} T={T}")
+    r = Runner(wl, [0], mode=mode)
+    x = synth.gen_hidden(wl, 0)
+    for c in range(x.shape[0]):
+        _, res = r.call(0, x[c])
+        if S == E:
+            assert res.fills == 0 and res.misses == 0 and set(res.host_view) == {-1}
+    r.check_log()
+    st = r.cache.stats()
+    assert st["selections"] == 10 * T * k
+    assert st["hits"] + st["misses"] == st["selections"]
+    if S == E:
+        assert st["hits"] == st["selections"] and st["evictions"] == 0
+    r.close()
