@@ -1148,11 +1148,17 @@ struct K6Lds {
   int tok[K6_TOK];
 };
 
+// The pass body for NT token tiles of 16: a pass of up to 16 tokens stages and
+// multiplies half the activation rows.  NT = 1 and 2 are straight code; NT = 0
+// takes the tile count at run time (and stages all 32 rows).
+template <bool GLU, int NT>
+__device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds<GLU ? 2 : 1> &L, int item,
+                                          int tile);
+
 template <bool GLU>
 __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(GemvArgs a) {
   constexpr int NM = GLU ? 2 : 1;
   __shared__ K6Lds<NM> L;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // XCD-aware order: workgroup l of the grid runs on XCD l % 8; each XCD takes a
   // contiguous run of the (item, row tile) work, so that the row tiles of one
   // item, which read the same activations, share that XCD's L2.  Workgroups past
@@ -1166,6 +1172,23 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(GemvArgs a) {
   const int work = xcd * q8 + min(xcd, rem) + r;
   const int item = a.items[1 + work / gx];
   const int tile = work % gx;
+  const int ntok = min(K6_TOK, a.meta[2 + 2 * kMetaB + (item & 0xFFFF)] - (item >> 16) * K6_TOK);
+  // gate/up: one body for both tile counts (the two-tile form alone needs
+  // every register and spills; so would two forms in one kernel); down: a
+  // straight body per tile count, both within 90 registers
+  if constexpr (GLU)
+    mfma_pass<GLU, 0>(a, L, item, tile);
+  else if (ntok > 16)
+    mfma_pass<GLU, 2>(a, L, item, tile);
+  else
+    mfma_pass<GLU, 1>(a, L, item, tile);
+}
+
+template <bool GLU, int NT>
+__device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds<GLU ? 2 : 1> &L, int item,
+                                          int tile) {
+  constexpr int NM = GLU ? 2 : 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bucket = item & 0xFFFF;
   const int g0 = (item >> 16) * K6_TOK;
   const int slot = a.meta[2 + bucket];
@@ -1182,7 +1205,7 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(GemvArgs a) {
   const _Float16 *s1row = reinterpret_cast<const _Float16 *>(rec + a.off_s1) + my_row * nb;
   const int nch = (nb + K6_KC - 1) / K6_KC;
   const int ntok = min(K6_TOK, cnt - g0);
-  const int n_tiles = (ntok + 15) >> 4;
+  const int n_tiles = NT ? NT : (ntok + 15) >> 4;
   if (tid < K6_TOK) {
     const int p = a.bucket_pair[off + g0 + min(tid, ntok - 1)];
     L.tok[tid] = a.in_by_pair ? p : pair_row(a, p);
@@ -1204,16 +1227,20 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(GemvArgs a) {
     };
     o0 = *src(0);
     o1 = *src(1);
-    o2 = *src(2);
-    o3 = *src(3);
+    if constexpr (NT != 1) {
+      o2 = *src(2);
+      o3 = *src(3);
+    }
   };
   auto store_b = [&](int buf, const uint4 &o0, const uint4 &o1, const uint4 &o2,
                      const uint4 &o3) __attribute__((always_inline)) {
     const int v = tid & 31, t = tid >> 5;
     L.B[buf][t][v] = o0;
     L.B[buf][t + 8][v] = o1;
-    L.B[buf][t + 16][v] = o2;
-    L.B[buf][t + 24][v] = o3;
+    if constexpr (NT != 1) {
+      L.B[buf][t + 16][v] = o2;
+      L.B[buf][t + 24][v] = o3;
+    }
   };
   // this lane's weight block of chunk c, per matrix (the second one only for
   // the GLU), held in named registers.  Unconditional loads (clamped block):
@@ -1257,7 +1284,7 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(GemvArgs a) {
       cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl0, cc, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) c0[i] = __builtin_fmaf(pick4(d, i), cc[i], c0[i]);
-      if (n_tiles > 1) {
+      if (NT == 2 || (NT == 0 && n_tiles > 1)) {
         const half8_t Bh1 = __builtin_bit_cast(half8_t, L.B[cur][16 + lr][(b * 4 + lg) * 2]);
         const half8_t Bl1 =
             __builtin_bit_cast(half8_t, L.B[cur][16 + lr][(b * 4 + lg) * 2 + 1]);
@@ -1303,7 +1330,7 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(GemvArgs a) {
   }
   // C lane layout: rows row0 + 4*lg + i, token column t*16 + lr
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < (NT ? NT : 2); ++t) {
     const int col = t * 16 + lr;
     if (t < n_tiles && col < ntok) {
       const int p = a.bucket_pair[off + g0 + col];
