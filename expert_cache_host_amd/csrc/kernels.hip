@@ -972,10 +972,11 @@ __global__ __launch_bounds__(64 * NW) void q4_down_kernel(GemvArgs a, BucketTabl
 
 // Shapes measured on MI355X for one token per bucket over the decode shapes
 // d x f = 6144 x 2048 and 2816 x 704: gate/up rows of >= 128 blocks run best
-// with 16 lanes per row, shorter ones with 8, K split over the 4 waves, 2 rows
-// per lane; down rows of >= 64 blocks with 16 lanes per row, whole K per wave
-// and 4 rows per lane, shorter ones with 8 lanes and K over 4 waves.  Rows of
-// fewer than 32 gate/up blocks keep K in one wave.
+// with 16 lanes per row and 2 rows per lane, rows of 32-127 blocks with 8 lanes
+// and 1 row per lane, K split over the 4 waves; down rows of >= 64 blocks with
+// 16 lanes per row, whole K per wave and 4 rows per lane, shorter ones with 8
+// lanes and K over 4 waves.  Rows of fewer than 32 gate/up blocks keep K in one
+// wave.
 GemvShape choose_gemv(bool glu, int nb, int tokens) {
   GemvShape sh{};
   sh.TT = tokens <= 1 ? 1 : (tokens <= 2 ? 2 : 4);
@@ -987,6 +988,7 @@ GemvShape choose_gemv(bool glu, int nb, int tokens) {
     } else if (nb >= 32) {
       sh.G = 8;
       sh.KS = 4;
+      sh.R = 1;
     } else {
       sh.G = 8;
       sh.KS = 1;
@@ -1013,36 +1015,36 @@ size_t gemv_lds_bytes(bool glu, int nb, int tokens) {
   return (size_t)sh.TT * nb * 64 + ((size_t)sh.TT * nb + 3) / 4 * 16 + row_scales;
 }
 
-template <bool GLU, int G, int KS, int R, int TT, int MODE>
+template <bool GLU, int G, int KS, int R, int TT, int MODE, int PF>
 static void launch_one(const GemvArgs &a, const BucketTable &tab, int nbk, size_t lds,
                        hipStream_t s) {
   constexpr int NW = 4;
   constexpr int RWG = (NW / KS) * (64 / G) * R;
   const dim3 grid((a.rows + RWG - 1) / RWG, nbk);
   if constexpr (GLU)
-    hipLaunchKernelGGL((q4_gateup_kernel<G, KS, R, TT, MODE, NW, 1>), grid, dim3(64 * NW), lds, s,
+    hipLaunchKernelGGL((q4_gateup_kernel<G, KS, R, TT, MODE, NW, PF>), grid, dim3(64 * NW), lds, s,
                        a, tab);
   else
-    hipLaunchKernelGGL((q4_down_kernel<G, KS, R, TT, MODE, NW, 1>), grid, dim3(64 * NW), lds, s, a,
-                       tab);
+    hipLaunchKernelGGL((q4_down_kernel<G, KS, R, TT, MODE, NW, PF>), grid, dim3(64 * NW), lds, s,
+                       a, tab);
 }
 
-template <bool GLU, int G, int KS, int R>
+template <bool GLU, int G, int KS, int R, int PF = 1>
 static void launch_tt(const GemvArgs &a, const BucketTable &tab, int nbk, int TT, size_t lds,
                       hipStream_t s) {
   const bool t = tab.n >= 0;
   switch (TT) {
     case 1:
-      t ? launch_one<GLU, G, KS, R, 1, BK_TABLE>(a, tab, nbk, lds, s)
-        : launch_one<GLU, G, KS, R, 1, BK_LIST>(a, tab, nbk, lds, s);
+      t ? launch_one<GLU, G, KS, R, 1, BK_TABLE, PF>(a, tab, nbk, lds, s)
+        : launch_one<GLU, G, KS, R, 1, BK_LIST, PF>(a, tab, nbk, lds, s);
       break;
     case 2:
-      t ? launch_one<GLU, G, KS, R, 2, BK_TABLE>(a, tab, nbk, lds, s)
-        : launch_one<GLU, G, KS, R, 2, BK_LIST>(a, tab, nbk, lds, s);
+      t ? launch_one<GLU, G, KS, R, 2, BK_TABLE, PF>(a, tab, nbk, lds, s)
+        : launch_one<GLU, G, KS, R, 2, BK_LIST, PF>(a, tab, nbk, lds, s);
       break;
     default:
-      t ? launch_one<GLU, G, KS, R, 4, BK_TABLE>(a, tab, nbk, lds, s)
-        : launch_one<GLU, G, KS, R, 4, BK_LIST>(a, tab, nbk, lds, s);
+      t ? launch_one<GLU, G, KS, R, 4, BK_TABLE, PF>(a, tab, nbk, lds, s)
+        : launch_one<GLU, G, KS, R, 4, BK_LIST, PF>(a, tab, nbk, lds, s);
       break;
   }
 }
@@ -1058,7 +1060,14 @@ hipError_t launch_gemv(const GemvArgs &a, const BucketTable *tab, const GemvShap
   const int key = (glu ? 1000 : 0) + sh.G * 100 + sh.KS * 10 + sh.R;
   switch (key) {
     case 1000 + 1600 + 40 + 2: launch_tt<true, 16, 4, 2>(a, t, n_buckets, sh.TT, lds, s); break;
-    case 1000 + 800 + 40 + 2: launch_tt<true, 8, 4, 2>(a, t, n_buckets, sh.TT, lds, s); break;
+    case 1000 + 800 + 40 + 1:
+      // a launch of one or two buckets (the fills of a call) is latency bound:
+      // all three K steps of a Gemma-sized row in flight at once
+      if (n_buckets <= 2)
+        launch_tt<true, 8, 4, 1, 3>(a, t, n_buckets, sh.TT, lds, s);
+      else
+        launch_tt<true, 8, 4, 1>(a, t, n_buckets, sh.TT, lds, s);
+      break;
     case 1000 + 800 + 10 + 2: launch_tt<true, 8, 1, 2>(a, t, n_buckets, sh.TT, lds, s); break;
     case 1600 + 10 + 4: launch_tt<false, 16, 1, 4>(a, t, n_buckets, sh.TT, lds, s); break;
     case 800 + 40 + 4: launch_tt<false, 8, 4, 4>(a, t, n_buckets, sh.TT, lds, s); break;
