@@ -277,7 +277,7 @@ def main():
         preheat_study(args)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU (the layer and its cache live on one device); --gpus must be 1"}))
         sys.exit(2)
 
     import torch

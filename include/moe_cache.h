@@ -79,7 +79,7 @@ typedef int32_t moe_status;
  * ends holding exactly the call's S top-ranked experts.  Other calls, and host
  * mode, follow the policy's plain rule. */
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define MOE_MAX_EXPERTS 512 /* routed experts per layer */
 #define MOE_MAX_TOPK 64
 

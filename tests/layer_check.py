@@ -3,7 +3,8 @@ call by call and checks each call against the oracle.
 
 Checked bit for bit: top-k ids of every token, both lookup tables of every
 stage, the slot state, the usage scores (score policy) and the whole
-replacement log.  Checked within tolerance
+replacement log; and that the tables map every selected expert exactly once
+(one stage's slot table or the host table).  Checked within tolerance
 (max |out - oracle| <= 2e-3 * RMS(oracle) over the compared block of each call):
 the layer output, on all of it or on a seeded sample of tokens and columns.
 """
@@ -84,6 +85,17 @@ class Runner:
             sv, hv = self.cache.views(li, s)
             assert sv.tolist() == res.stage_views[s], f"slot table differs in stage {s}"
             assert hv.tolist() == res.host_view, f"host table differs in stage {s}"
+        # every selected expert is computed exactly once: mapped by exactly one of
+        # the call's tables (one stage's slot table, or the host table).  Work
+        # follows the selected pairs; the tables also place experts nobody
+        # selected (in host mode they split all experts between slot and host).
+        mapped = {e: 0 for e in set(idx_ref.ravel().tolist())}
+        for s in range(ns):
+            sv, hv = self.cache.views(li, s)
+            for e in mapped:
+                mapped[e] += int(sv[e] >= 0) + (int(hv[e] >= 0) if s == 0 else 0)
+        for e, n in mapped.items():
+            assert n == 1, (e, n)
         ein, lu = self.cache.slot_state(li)
         assert ein.tolist() == self.sims[li].expert_in
         assert lu.tolist() == self.sims[li].last_use

@@ -304,3 +304,21 @@ def test_edge_shapes(case, mode):
     if S == E:
         assert st["hits"] == st["selections"] and st["evictions"] == 0
     r.close()
+
+
+def test_decode_and_matrix_core_calls_alternate():
+    """One cache takes decode calls and matrix-core calls of up to 4 tokens in
+    any order (4 tokens x (16 + 1 shared) = 68 pairs exceed the decode path; 1-3
+    tokens do not): the workspace follows the path, both miss modes."""
+    wl = synth.Workload("alt", 31, 1, 128, 128, 64, 16, 16, n_shared=1, router_sigma=0.3,
+                        zipf_s=0.8, rho=0.5, tokens=14, batch=1)
+    x = synth.gen_hidden(wl, 0)[:, 0, :]
+    for mode in ("stream", "host"):
+        log(f"decode / matrix-core alternation mode={mode}")
+        r = Runner(wl, [0], mode=mode)
+        c = 0
+        for T in (1, 4, 2, 4, 3, 1, 4):
+            r.call(0, x[c:c + T])
+            c += T % 3
+        r.check_log()
+        r.close()
