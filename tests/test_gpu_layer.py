@@ -322,3 +322,42 @@ def test_decode_and_matrix_core_calls_alternate():
             c += T % 3
         r.check_log()
         r.close()
+
+
+def test_invalid_calls_leave_the_cache_unchanged():
+    """Invalid arguments to a live cache return MOE_EINVAL with a message and
+    change nothing: the next valid calls still match the oracle, table for table,
+    and the replacement log has no entry from the rejected calls."""
+    import ctypes
+
+    import torch
+
+    from expert_cache_host_amd.binding import load_library
+    wl = synth.WORKLOADS["tiny"]
+    log("invalid calls on a live cache")
+    r = Runner(wl, [0], slots=2, mode="stream")
+    x = synth.gen_hidden(wl, 0)
+    r.call(0, x[0])
+    lib = load_library()
+    h = r.cache._h
+    xd = torch.from_numpy(np.ascontiguousarray(x[1])).cuda()
+    w = r.routers[0][2]
+    out = torch.empty_like(xd)
+    st = torch.cuda.current_stream().cuda_stream
+    bad = [
+        (1, xd.data_ptr(), 1, w.data_ptr(), out.data_ptr()),    # layer past the last
+        (-1, xd.data_ptr(), 1, w.data_ptr(), out.data_ptr()),   # negative layer
+        (0, xd.data_ptr(), 0, w.data_ptr(), out.data_ptr()),    # no tokens
+        (0, None, 1, w.data_ptr(), out.data_ptr()),             # no x
+        (0, xd.data_ptr(), 1, None, out.data_ptr()),            # no router
+        (0, xd.data_ptr(), 1, w.data_ptr(), None),              # no output
+    ]
+    for layer, xp, T, wp, op in bad:
+        rc = lib.moe_layer_forward(h, layer, xp, T, wp, None, op, st)
+        assert rc == -1, (layer, T, rc)
+        assert lib.moe_last_error()
+    assert r.cache.stats()["calls"] == 1
+    for t in range(1, 8):
+        r.call(0, x[t])
+    r.check_log()
+    r.close()
