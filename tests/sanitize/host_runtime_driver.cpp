@@ -1,0 +1,159 @@
+// Drives the host-only runtime (the slot planner and the host-miss experts)
+// through many random calls, for a build under AddressSanitizer and
+// UndefinedBehaviorSanitizer.  Checks the planner's invariants after every
+// call (slot_of and expert_in inverse, every selected expert placed exactly
+// once, fills only into slots the call does not hold protected) and the
+// host-miss partial sum against a plain scalar evaluation of the same bytes.
+// Exit status 0 and "ok" on success.
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <random>
+#include <set>
+#include <vector>
+
+#include "../../expert_cache_host_amd/csrc/host_expert.hpp"
+#include "../../expert_cache_host_amd/csrc/layout.hpp"
+#include "../../expert_cache_host_amd/csrc/planner.hpp"
+
+#define CHECK(c)                                                   \
+  do {                                                             \
+    if (!(c)) {                                                    \
+      std::fprintf(stderr, "check failed: %s (line %d)\n", #c, __LINE__); \
+      std::exit(1);                                                \
+    }                                                              \
+  } while (0)
+
+static void planner_runs(std::mt19937_64 &rng) {
+  for (int trial = 0; trial < 60; ++trial) {
+    const int E = 2 + (int)(rng() % 40), S = 1 + (int)(rng() % E), k = 1 + (int)(rng() % std::min(E, 8));
+    const int policy = (int)(rng() % 2), adopt = (rng() % 3 == 0) ? -1 : (int)(rng() % 1001);
+    moe::SlotPlanner p(E, S, policy, adopt);
+    if (rng() % 4 == 0) {
+      std::vector<uint32_t> counts(E);
+      for (auto &c : counts) c = (uint32_t)(rng() % 50);
+      p.preload(counts.data());
+    }
+    moe::CallPlan plan;
+    for (int call = 0; call < 40; ++call) {
+      const int T = 1 + (int)(rng() % 6), mode = (int)(rng() % 2);
+      const int max_fills = mode == 1 ? (int)(rng() % 4) - 1 : -1;
+      std::vector<int32_t> idx((size_t)T * k);
+      for (int t = 0; t < T; ++t) {
+        std::set<int32_t> used;
+        for (int j = 0; j < k; ++j) {
+          int32_t e;
+          do e = (int32_t)(rng() % E); while (used.count(e));
+          used.insert(e);
+          idx[(size_t)t * k + j] = e;
+        }
+      }
+      p.plan(idx.data(), T * k, T, mode, max_fills, plan);
+      // slot_of and expert_in are inverse maps
+      for (int s = 0; s < S; ++s)
+        if (p.expert_in()[s] >= 0) CHECK(p.slot_of()[p.expert_in()[s]] == s);
+      for (int e = 0; e < E; ++e)
+        if (p.slot_of()[e] >= 0) CHECK(p.expert_in()[p.slot_of()[e]] == e);
+      // every selected expert is placed exactly once over the call's tables
+      std::vector<int32_t> sv(E), hv(E);
+      std::vector<int> placed(E, 0);
+      for (size_t s = 0; s < plan.stages.size(); ++s) {
+        p.stage_view(plan, (int32_t)s, sv.data(), hv.data());
+        for (int e = 0; e < E; ++e) {
+          CHECK(sv[e] >= -1 && sv[e] < S);
+          placed[e] += sv[e] >= 0;
+          if (s == 0) placed[e] += hv[e] >= 0;
+        }
+      }
+      std::set<int32_t> sel(idx.begin(), idx.end());
+      for (int32_t e : sel) CHECK(placed[e] == 1);
+      CHECK(plan.hits + plan.misses == T * k);
+      if (mode == 0) CHECK((int)plan.stages.size() >= 1);
+      if (max_fills >= 0) CHECK(plan.fills <= max_fills);
+    }
+  }
+}
+
+static float half_to_float_ref(uint16_t h) {
+  const int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  float v = e == 0 ? std::ldexp((float)m, -24) : std::ldexp((float)(m | 1024), e - 25);
+  return s ? -v : v;
+}
+
+static void host_expert_runs(std::mt19937_64 &rng) {
+  moe::ThreadPool pool(3);
+  for (int trial = 0; trial < 8; ++trial) {
+    const int64_t d = 64 * (1 + (int64_t)(rng() % 4)), f = 32 * (1 + (int64_t)(rng() % 5));
+    const int T = 1 + (int)(rng() % 4), k = 2, n_jobs = 1 + (int)(rng() % 3);
+    const moe::RecordLayout L = moe::RecordLayout::make(d, f);
+    std::vector<std::vector<uint8_t>> recs(n_jobs, std::vector<uint8_t>((size_t)L.bytes));
+    for (auto &r : recs) {
+      std::vector<uint8_t> inter((size_t)L.interchange_bytes);
+      for (size_t i = 0; i < inter.size(); ++i) inter[i] = (uint8_t)rng();
+      for (size_t b = 0; b + 18 <= inter.size(); b += 18) {  // small finite scales
+        const uint16_t sc = (uint16_t)(0x1800 + rng() % 0x400);
+        std::memcpy(&inter[b], &sc, 2);
+      }
+      moe::repack_expert(inter.data(), L, r.data());
+    }
+    std::vector<float> x((size_t)T * d), w((size_t)T * k), part((size_t)T * d), h;
+    std::normal_distribution<float> nd(0.f, 1.f);
+    for (auto &v : x) v = nd(rng);
+    std::vector<moe::HostExpertJob> jobs(n_jobs);
+    std::vector<int32_t> rank((size_t)T * k, -1);
+    for (int j = 0; j < n_jobs; ++j) jobs[j].record = recs[j].data();
+    for (int t = 0; t < T; ++t)
+      for (int j = 0; j < k; ++j) {
+        const int jb = (int)(rng() % (n_jobs + 1)) - 1;  // -1: the pair is not on the host
+        rank[(size_t)t * k + j] = jb;
+        w[(size_t)t * k + j] = 0.5f + 0.1f * j;
+        if (jb >= 0 && (jobs[jb].tokens.empty() || jobs[jb].tokens.back() != t))
+          jobs[jb].tokens.push_back(t);
+      }
+    moe::host_moe_partial(pool, L, jobs, rank.data(), w.data(), T, k, x.data(), part.data(), h);
+    // scalar reference over the same slot-layout bytes
+    for (int t = 0; t < T; ++t) {
+      std::vector<double> ref((size_t)d, 0.0);
+      for (int j = 0; j < k; ++j) {
+        const int jb = rank[(size_t)t * k + j];
+        if (jb < 0) continue;
+        const uint8_t *r = recs[jb].data();
+        auto wgt = [&](int64_t off_q, int64_t off_s, int64_t row, int64_t nb, int64_t i) {
+          const uint8_t byte = r[off_q + (row * nb + i / 32) * 16 + (i % 32) % 16];
+          const int q = (i % 32) < 16 ? (byte & 15) : (byte >> 4);
+          uint16_t sc;
+          std::memcpy(&sc, r + off_s + (row * nb + i / 32) * 2, 2);
+          return (double)half_to_float_ref(sc) * (q - 8);
+        };
+        std::vector<double> hh((size_t)f);
+        for (int64_t rr = 0; rr < f; ++rr) {
+          double g = 0, u = 0;
+          for (int64_t i = 0; i < d; ++i) {
+            g += wgt(L.off_gq, L.off_gs, rr, L.nb_gu, i) * x[(size_t)t * d + i];
+            u += wgt(L.off_uq, L.off_us, rr, L.nb_gu, i) * x[(size_t)t * d + i];
+          }
+          hh[(size_t)rr] = g / (1.0 + std::exp(-g)) * u;
+        }
+        for (int64_t i = 0; i < d; ++i) {
+          double y = 0;
+          for (int64_t rr = 0; rr < f; ++rr) y += wgt(L.off_dq, L.off_ds, i, L.nb_dn, rr) * hh[(size_t)rr];
+          ref[(size_t)i] += w[(size_t)t * k + j] * y;
+        }
+      }
+      double rms = 0, err = 0;
+      for (int64_t i = 0; i < d; ++i) rms += ref[(size_t)i] * ref[(size_t)i];
+      rms = std::sqrt(rms / d);
+      for (int64_t i = 0; i < d; ++i) err = std::max(err, std::fabs(part[(size_t)t * d + i] - ref[(size_t)i]));
+      CHECK(err <= 1e-4 * rms + 1e-12);
+    }
+  }
+}
+
+int main() {
+  std::mt19937_64 rng(12345);
+  planner_runs(rng);
+  host_expert_runs(rng);
+  std::printf("ok\n");
+  return 0;
+}
