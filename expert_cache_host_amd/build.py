@@ -57,7 +57,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("libmoecache build failed:\n" + msg)
     objs = [os.path.join(BUILD, n) for n in ("kernels.o", "api.o", "planner.o", "host_expert.o")]
     tmp = OUT + f".tmp{os.getpid()}"
-    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs + ["-pthread"]
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs + [
+        "-L" + os.path.join(ROCM, "lib"), "-lrocprofiler-sdk-roctx", "-pthread"]
     if verbose:
         print(" ".join(link), flush=True)
     r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)

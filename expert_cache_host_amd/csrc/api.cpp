@@ -10,6 +10,7 @@
 // the slot; host mode: the same layer's next call), which makes every table a
 // deterministic function of the routing history.
 #include <hip/hip_runtime_api.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <algorithm>
 #include <atomic>
@@ -37,6 +38,16 @@ moe_status fail(moe_status st, const std::string &msg) {
   g_err = msg;
   return st;
 }
+
+// A named range of host time for tracing tools (rocprofv3 --marker-trace):
+// the call, the wait for the routing, the plan, the fill enqueue, the
+// host-miss experts.  Costs a few nanoseconds when no tool is attached.
+struct TraceRange {
+  explicit TraceRange(const char *name) { roctxRangePushA(name); }
+  ~TraceRange() { roctxRangePop(); }
+  TraceRange(const TraceRange &) = delete;
+  TraceRange &operator=(const TraceRange &) = delete;
+};
 
 struct HipError : std::runtime_error {
   using std::runtime_error::runtime_error;
@@ -548,13 +559,19 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
     ly.dbg_gpu.ensure((size_t)T * d * 4);
     dbg_gpu = (float *)ly.dbg_gpu.p;
   }
-  if (dec)
-    wait_routing(c, st);
-  else
-    HIPCHK(hipEventSynchronize(c->ev_idx));
+  {
+    TraceRange tr("moe.wait_routing");
+    if (dec)
+      wait_routing(c, st);
+    else
+      HIPCHK(hipEventSynchronize(c->ev_idx));
+  }
   const double tp = now_s();
-  ly.planner->plan((const int32_t *)c->h_idx.p, T * k, T, host_mode ? 1 : 0,
-                   host_mode ? c->o.max_fills_per_call : -1, ly.plan);
+  {
+    TraceRange tr("moe.plan");
+    ly.planner->plan((const int32_t *)c->h_idx.p, T * k, T, host_mode ? 1 : 0,
+                     host_mode ? c->o.max_fills_per_call : -1, ly.plan);
+  }
   ly.st.plan_s += now_s() - tp;
   if (c->timing) {
     const double n_hit = (double)(ly.plan.stages[0].members.size() -
@@ -590,6 +607,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
         pl.per_expert = 32;
         pl.bytes16 = (long long)c->rec() / 16;
         {
+          TraceRange tr("moe.fill_pull");
           KTime kt(c, MOE_K_FILL, st);
           HIPCHK(moe::launch_pull(pl, st));
           kt.end((double)pl.n * (double)c->rec());
@@ -606,7 +624,10 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
     for (size_t s = 0; s < ly.plan.stages.size(); ++s) {
       const moe::PlanStage &stg = ly.plan.stages[s];
       if (stg.fills.empty()) continue;
-      enqueue_fills(c, layer, stg.fills, st);
+      {
+        TraceRange tr("moe.fill_copies");
+        enqueue_fills(c, layer, stg.fills, st);
+      }
       wait_fills(c, ly, st);
       std::fill(table.begin(), table.end(), -1);
       for (const moe::Fill &fl : stg.fills) table[fl.expert] = fl.slot;
@@ -617,7 +638,10 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   } else {
     const moe::PlanStage &stg = ly.plan.stages[0];
     if (!stg.fills.empty()) {
-      enqueue_fills(c, layer, stg.fills, st);
+      {
+        TraceRange tr("moe.fill_copies");
+        enqueue_fills(c, layer, stg.fills, st);
+      }
       ly.fill_pending = true;
     }
     if (!ly.plan.host_experts.empty()) {
@@ -641,8 +665,11 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
           rank_job[(size_t)t * k + j] = jb;
           if (jb >= 0) jobs[jb].tokens.push_back(t);
         }
-      moe::host_moe_partial(*c->pool, c->lay, jobs, rank_job.data(), (const float *)c->h_w.p, T, k,
-                            (const float *)c->h_x.p, (float *)c->partial[b].p, c->h_scratch);
+      {
+        TraceRange tr("moe.host_experts");
+        moe::host_moe_partial(*c->pool, c->lay, jobs, rank_job.data(), (const float *)c->h_w.p, T,
+                              k, (const float *)c->h_x.p, (float *)c->partial[b].p, c->h_scratch);
+      }
       const float *host_part = (const float *)c->partial[b].p;
       if (c->o.keep_debug) ly.dbg_host.assign(host_part, host_part + (size_t)T * d);
       ly.st.host_s += now_s() - th;
@@ -853,6 +880,7 @@ moe_status moe_layer_forward(moe_cache *c, int32_t layer, const float *x, int32_
   if (n_tokens > (1 << 20)) return fail(MOE_EINVAL, "n_tokens too large");
   if (!x || !router_w || !out) return fail(MOE_EINVAL, "x, router_w and out must be non-NULL");
   return guarded(c, [&]() {
+    TraceRange tr("moe.layer_forward");
     return forward_impl(c, layer, x, n_tokens, router_w, router_bias, out, (hipStream_t)stream);
   });
 }

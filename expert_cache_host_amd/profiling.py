@@ -8,6 +8,7 @@
     python -m expert_cache_host_amd.profiling copies <rocprof dir> <record bytes> <title> <command...>
     python -m expert_cache_host_amd.profiling mfma <rocprof dir> <title> <command...>
     python -m expert_cache_host_amd.profiling timeline <rocprof dir> <first kernel> <count>
+    python -m expert_cache_host_amd.profiling markers <rocprof dir> <title> <command...>
 
 `stats` reads the *_kernel_stats.csv of a `rocprofv3 --kernel-trace --stats
 --output-format csv` run; `pmc` reads the *_counter_collection.csv of a
@@ -116,6 +117,22 @@ def timeline_md(d: str, anchor: str, count: int) -> str:
     return "\n".join(out) + "\n"
 
 
+def markers_md(d: str, title: str, command: str) -> str:
+    """Host-side ranges of a `--marker-trace` run: count, median, mean, p90 (us)."""
+    import statistics
+    by = defaultdict(list)
+    for r in csv.DictReader(open(_find(d, "marker_api_trace.csv"))):
+        by[r["Function"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = [f"# {title}", "", "Command:", "", "```", command, "```", "",
+           "Host time of the library's named ranges (one per call, or per fill enqueue):", "",
+           "| range | count | median us | mean us | p90 us |", "|---|---|---|---|---|"]
+    for name in sorted(by, key=lambda k: -statistics.mean(by[k])):
+        v = sorted(by[name])
+        out.append(f"| `{name}` | {len(v)} | {statistics.median(v):.1f} | {statistics.mean(v):.1f} | "
+                   f"{v[int(0.9 * (len(v) - 1))]:.1f} |")
+    return "\n".join(out) + "\n"
+
+
 MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_BUSY_CYCLES",
                  "GRBM_GUI_ACTIVE")
 XCDS, SIMDS = 8, 1024  # MI355X: 8 accelerator dies, 256 CUs x 4 SIMDs
@@ -201,6 +218,8 @@ def main(argv):
         print(pmc_md(argv[1], argv[2], argv[3], " ".join(argv[4:])), end="")
     elif len(argv) >= 5 and argv[0] == "copies":
         print(copies_md(argv[1], int(argv[2]), argv[3], " ".join(argv[4:])), end="")
+    elif len(argv) >= 4 and argv[0] == "markers":
+        print(markers_md(argv[1], argv[2], " ".join(argv[3:])), end="")
     elif len(argv) == 4 and argv[0] == "timeline":
         print(timeline_md(argv[1], argv[2], int(argv[3])), end="")
     elif len(argv) >= 4 and argv[0] == "mfma":
