@@ -84,6 +84,7 @@ def load_library():
         "moe_debug_scores": (I32, [P, I32, P]),
         "moe_debug_evictions": (I32, [P, I32, P, SZ, ctypes.POINTER(SZ)]),
         "moe_debug_partials": (I32, [P, I32, P, P]),
+        "moe_debug_logits": (I32, [P, I32, P]),
         "moe_planner_create": (I32, [I32, I32, I32, I32, I32, ctypes.POINTER(P)]),
         "moe_planner_plan": (I32, [P, P, I32, I32, P, P, P]),
         "moe_planner_set_adopt": (I32, [P, I32]),
@@ -275,6 +276,12 @@ class MoECache:
         h = np.empty((t, self.d_model), np.float32)
         _check(load_library().moe_debug_partials(self._h, layer, _ptr(g), _ptr(h)))
         return g, h
+
+    def logits(self, layer: int):
+        _, t = self.last_call(layer)
+        z = np.empty((t, self.n_experts), np.float32)
+        _check(load_library().moe_debug_logits(self._h, layer, _ptr(z)))
+        return z
 
     def close(self):
         if getattr(self, "_h", None):

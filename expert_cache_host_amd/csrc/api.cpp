@@ -155,6 +155,7 @@ struct LayerState {
   std::vector<float> last_w;
   std::vector<float> dbg_host;    // keep_debug: host partial
   DevBuf dbg_gpu;                 // keep_debug: GPU partial
+  DevBuf dbg_z;                   // keep_debug: router logits
   moe_stats st{};
   TimingLog t_gpu, t_h2d;
 };
@@ -548,6 +549,10 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
     kt.end(4.0 * ((double)T * E + 4.0 * T * k));
   }
   if (!dec) HIPCHK(hipEventRecord(c->ev_idx, st));
+  if (c->o.keep_debug) {
+    ly.dbg_z.ensure((size_t)T * E * 4);
+    HIPCHK(hipMemcpyAsync(ly.dbg_z.p, c->z.p, (size_t)T * E * 4, hipMemcpyDeviceToDevice, st));
+  }
 
   // Cached experts (and the shared one) on the table published at call start,
   // enqueued before the host reads the routing.
@@ -1092,6 +1097,20 @@ moe_status moe_debug_partials(moe_cache *c, int32_t layer, float *gpu_part, floa
       HIPCHK(hipMemcpy(gpu_part, ly.dbg_gpu.p, n * 4, hipMemcpyDeviceToHost));
     }
     if (host_part) std::copy(ly.dbg_host.begin(), ly.dbg_host.begin() + n, host_part);
+    return MOE_OK;
+  });
+}
+
+moe_status moe_debug_logits(moe_cache *c, int32_t layer, float *z) {
+  g_err.clear();
+  if (!c || !z) return fail(MOE_EINVAL, "cache and z must be non-NULL");
+  if (layer < 0 || layer >= c->L) return fail(MOE_EINVAL, "layer out of range");
+  if (!c->o.keep_debug) return fail(MOE_EINVAL, "create the cache with keep_debug = 1");
+  LayerState &ly = c->layers[layer];
+  if (!ly.last_T) return fail(MOE_EINVAL, "layer has no call yet");
+  return guarded(c, [&]() {
+    HIPCHK(hipDeviceSynchronize());
+    HIPCHK(hipMemcpy(z, ly.dbg_z.p, (size_t)ly.last_T * c->E * 4, hipMemcpyDeviceToHost));
     return MOE_OK;
   });
 }

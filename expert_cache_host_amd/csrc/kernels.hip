@@ -235,9 +235,136 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
   }
 }
 
+// Decode router: one workgroup per expert for calls of up to four tokens.  The
+// workgroup loads the expert's router row and the tokens' x in the pieces the
+// decode GEMV's digit planes group (unit j: elements 32b + 4q .. +3 and
+// 32b + 16 + 4q .. +3 of block b = j / 4, q = j % 4), all in flight together,
+// rounds every product x_i * w_i to fp32 and stores it in LDS at index i.  Wave
+// tt then adds token tt's products in the order of router_kernel (lane l:
+// i = l, l + 64, ... ascending, the halving tree, the bias), so the logits are
+// the same bits.  max|x| per token comes from the same loads, and workgroup e
+// turns units 256 e .. 256 e + 255 into digit planes from the registers that
+// loaded them.  Needs tokens * d * 4 bytes of LDS (<= 64 KiB) and d / 8 <= 256 E.
+template <int TT>
+__global__ __launch_bounds__(256) void router_decode_kernel(const float *__restrict__ x, int T,
+                                                            int d, const float *__restrict__ W,
+                                                            const float *__restrict__ bias, int E,
+                                                            float *__restrict__ z,
+                                                            uint4 *__restrict__ xq,
+                                                            float *__restrict__ xs) {
+#pragma clang fp contract(off)
+  extern __shared__ float sprod[];  // [TT][d] products
+  __shared__ float smax[TT][4];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int words = d >> 3;
+  const float *wr = W + (long long)e * d;
+  float mx[TT], px[TT][8];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    mx[tt] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) px[tt][i] = 0.0f;
+  }
+  constexpr int CH = 4;
+  for (int u0 = 0; u0 < words; u0 += 256 * CH) {
+    float4 wa[CH], wb[CH], xa[TT][CH], xb[TT][CH];
+#pragma unroll
+    for (int jj = 0; jj < CH; ++jj) {
+      const int j = min(u0 + tid + 256 * jj, words - 1);
+      const int o = (j >> 2) * 32 + (j & 3) * 4;
+      wa[jj] = *reinterpret_cast<const float4 *>(wr + o);
+      wb[jj] = *reinterpret_cast<const float4 *>(wr + o + 16);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const float *xr = x + (long long)min(tt, T - 1) * d + o;
+        xa[tt][jj] = *reinterpret_cast<const float4 *>(xr);
+        xb[tt][jj] = *reinterpret_cast<const float4 *>(xr + 16);
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < CH; ++jj) {
+      const int j = u0 + tid + 256 * jj;
+      if (j < words) {
+        const int o = (j >> 2) * 32 + (j & 3) * 4;
+        const bool mine = u0 + 256 * jj == 256 * e;  // uniform
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          if (tt < T) {
+            const float4 a = xa[tt][jj], c = xb[tt][jj], p = wa[jj], q = wb[jj];
+            float4 r, s;
+            r.x = a.x * p.x;
+            r.y = a.y * p.y;
+            r.z = a.z * p.z;
+            r.w = a.w * p.w;
+            s.x = c.x * q.x;
+            s.y = c.y * q.y;
+            s.z = c.z * q.z;
+            s.w = c.w * q.w;
+            *reinterpret_cast<float4 *>(sprod + tt * d + o) = r;
+            *reinterpret_cast<float4 *>(sprod + tt * d + o + 16) = s;
+            mx[tt] = fmaxf(mx[tt], fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+            mx[tt] = fmaxf(mx[tt], fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w))));
+            if (mine) {
+              px[tt][0] = a.x, px[tt][1] = a.y, px[tt][2] = a.z, px[tt][3] = a.w;
+              px[tt][4] = c.x, px[tt][5] = c.y, px[tt][6] = c.z, px[tt][7] = c.w;
+            }
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    float m = mx[tt];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (lane == 0) smax[tt][wave] = m;
+  }
+  __syncthreads();
+  if (wave < T) {
+    const float *pr = sprod + wave * d + lane;
+    const int M = d >> 6;
+    float p = 0.0f;
+    for (int m = 0; m < M; ++m) p = p + pr[64 * m];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float o = __shfl_down(p, off, 64);
+      if (lane < off) p = p + o;
+    }
+    if (lane == 0) z[(long long)wave * E + e] = bias ? p + bias[e] : p;
+  }
+  // decode GEMV input: digit planes of X = rint(x * 30000 / max|x|)
+  const int j = tid + 256 * e;
+  if (j < words) {
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      if (tt >= T) break;
+      const float m = fmaxf(fmaxf(smax[tt][0], smax[tt][1]), fmaxf(smax[tt][2], smax[tt][3]));
+      const float inv = m > 0.0f ? 30000.0f / m : 0.0f;
+      if (j == 0) xs[tt] = m / 30000.0f;
+      xq[(long long)tt * words + j] = digit_planes8(px[tt], inv);
+    }
+  }
+}
+
 hipError_t launch_router(const float *x, int T, int d, const float *W, const float *bias, int E,
                          float *z, uint32_t *xp, float *xsw, float *xscale, uint4 *xq, float *xs,
                          hipStream_t s) {
+  const int tt = T <= 1 ? 1 : (T <= 2 ? 2 : 4);
+  const size_t lds = (size_t)tt * d * 4;
+  if (xq != nullptr && xp == nullptr && T >= 1 && T <= 4 && lds <= 64 * 1024 &&
+      d / 8 <= 256 * E) {
+    if (tt == 1)
+      hipLaunchKernelGGL(router_decode_kernel<1>, dim3(E), dim3(256), lds, s, x, T, d, W, bias, E,
+                         z, xq, xs);
+    else if (tt == 2)
+      hipLaunchKernelGGL(router_decode_kernel<2>, dim3(E), dim3(256), lds, s, x, T, d, W, bias, E,
+                         z, xq, xs);
+    else
+      hipLaunchKernelGGL(router_decode_kernel<4>, dim3(E), dim3(256), lds, s, x, T, d, W, bias, E,
+                         z, xq, xs);
+    return hipGetLastError();
+  }
   const int gx = (E + 3) / 4;
   if (T <= 1) {
     hipLaunchKernelGGL((router_kernel<1, 32>), dim3(gx, T), dim3(256), 0, s, x, T, d, W, bias, E,

@@ -9,6 +9,7 @@
     python -m expert_cache_host_amd.profiling mfma <rocprof dir> <title> <command...>
     python -m expert_cache_host_amd.profiling timeline <rocprof dir> <first kernel> <count>
     python -m expert_cache_host_amd.profiling markers <rocprof dir> <title> <command...>
+    python -m expert_cache_host_amd.profiling pulls <rocprof dir> <record bytes> <workgroups per record>
 
 `stats` reads the *_kernel_stats.csv of a `rocprofv3 --kernel-trace --stats
 --output-format csv` run; `pmc` reads the *_counter_collection.csv of a
@@ -117,6 +118,23 @@ def timeline_md(d: str, anchor: str, count: int) -> str:
     return "\n".join(out) + "\n"
 
 
+def pulls_md(d: str, record_bytes: int, wg_per_record: int) -> str:
+    """Pull-kernel launches grouped by the records they carry (grid size / workgroups per record)."""
+    import statistics
+    by = defaultdict(list)
+    for r in csv.DictReader(open(_find(d, "kernel_trace.csv"))):
+        if "pull_kernel" not in r["Kernel_Name"]:
+            continue
+        n = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]) // wg_per_record
+        by[n].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = ["| records per launch | launches | median us | us per record | GB/s (median) |",
+           "|---|---|---|---|---|"]
+    for n in sorted(by):
+        med = statistics.median(by[n])
+        out.append(f"| {n} | {len(by[n])} | {med:.1f} | {med / n:.1f} | {n * record_bytes / med / 1e3:.1f} |")
+    return "\n".join(out) + "\n"
+
+
 def markers_md(d: str, title: str, command: str) -> str:
     """Host-side ranges of a `--marker-trace` run: count, median, mean, p90 (us)."""
     import statistics
@@ -218,6 +236,8 @@ def main(argv):
         print(pmc_md(argv[1], argv[2], argv[3], " ".join(argv[4:])), end="")
     elif len(argv) >= 5 and argv[0] == "copies":
         print(copies_md(argv[1], int(argv[2]), argv[3], " ".join(argv[4:])), end="")
+    elif len(argv) == 4 and argv[0] == "pulls":
+        print(pulls_md(argv[1], int(argv[2]), int(argv[3])), end="")
     elif len(argv) >= 4 and argv[0] == "markers":
         print(markers_md(argv[1], argv[2], " ".join(argv[3:])), end="")
     elif len(argv) == 4 and argv[0] == "timeline":

@@ -295,6 +295,12 @@ moe_status moe_debug_evictions(moe_cache *c, int32_t layer, moe_evict_rec *buf, 
  * stream mode).  out == gpu_part + host_part element by element. */
 moe_status moe_debug_partials(moe_cache *c, int32_t layer, float *gpu_part, float *host_part);
 
+/* Requires opts.keep_debug.  z [n_tokens*n_experts] float32: the router logits
+ * of the last call of `layer` (bias included), in the fixed summation order of
+ * the router (routing: "llama.cpp + MoE expert cache", *How it works*), for
+ * bit-for-bit comparison.  Synchronises the device. */
+moe_status moe_debug_logits(moe_cache *c, int32_t layer, float *z);
+
 /* ---- host-only pieces, callable without a GPU ---- */
 
 typedef struct moe_planner moe_planner; /* the per-layer LRU slot planner alone */

@@ -6,6 +6,7 @@ import pytest
 
 import synth
 from layer_check import Runner, check_close, log
+from oracle.routing import router_logits_fp32
 
 pytestmark = pytest.mark.gpu
 
@@ -359,5 +360,44 @@ def test_invalid_calls_leave_the_cache_unchanged():
     assert r.cache.stats()["calls"] == 1
     for t in range(1, 8):
         r.call(0, x[t])
+    r.check_log()
+    r.close()
+
+
+# Router logits, bit for bit: (d_model, n_experts, top_k, tokens per call, Zipf s).
+# Decode calls of 1-4 tokens take the one-workgroup-per-expert router unless the
+# tokens' products exceed 64 KiB of LDS (6144 x 4 tokens); those and longer
+# calls take the tiled router.  Both must give the oracle's fixed-order sums.
+ROUTER = {
+    "gemma_T1": (2816, 128, 8, 1, 1.1),
+    "large_T1": (6144, 256, 8, 1, 1.2),
+    "large_T4": (6144, 256, 8, 4, 1.2),
+    "qwen_T2": (2048, 128, 8, 2, 1.0),
+    "qwen_T3": (2048, 128, 8, 3, 1.0),
+    "E512_T1": (256, 512, 8, 1, None),
+    "d64_T4": (64, 16, 2, 4, None),
+    "T17": (1024, 64, 4, 17, 1.0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(ROUTER))
+def test_router_logits_bit_exact(case):
+    """The GPU's router logits (bias included) equal the oracle's fixed-order
+    float32 sums bit for bit, on every call, for both router kernels."""
+    d, E, k, T, zipf = ROUTER[case]
+    wl = synth.Workload("router_" + case, 40 + sorted(ROUTER).index(case), 1, d, 64, E, k,
+                        min(E, 16), router_sigma=1.6 / np.sqrt(d), zipf_s=zipf, rho=0.8,
+                        tokens=4, batch=T)
+    log(f"router logits {case}: d={d} E={E} T={T}")
+    r = Runner(wl, [0], mode="stream", keep_debug=True)
+    w_r, b, _, _ = r.routers[0]
+    x = synth.gen_hidden(wl, 0, 3)
+    for c in range(x.shape[0]):
+        r.call(0, x[c])
+        z = r.cache.logits(0)
+        ref = router_logits_fp32(x[c], w_r, b)
+        assert z.shape == ref.shape
+        bad = np.argwhere(z.view(np.uint32) != ref.view(np.uint32))
+        assert bad.size == 0, f"call {c}: {len(bad)} logits differ, first {bad[:4].tolist()}"
     r.check_log()
     r.close()
