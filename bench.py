@@ -47,7 +47,7 @@ KERNEL_SRC = os.path.join(ROOT, "expert_cache_host_amd", "csrc", "kernels.hip")
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 # the library's kernel ids -> kernel names in rocprofv3 output
 KERNEL_SYMBOL = {"gateup": "q4_gateup_kernel", "down": "q4_down_kernel", "fill": "pull_kernel",
-                 "router": "router_kernel", "topk": "topk_decode_kernel", "combine": "combine_kernel"}
+                 "router": "router_decode_kernel", "topk": "topk_decode_kernel", "combine": "combine_kernel"}
 
 
 def log(msg):
@@ -100,6 +100,49 @@ def copy_calibration():
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}))
+
+
+def probes(torch, dev, launch_bytes, record_bytes):
+    """References measured on this GPU outside the timed region with plain torch
+    operations: the HBM read rate of a float32 sum over `launch_bytes` (the
+    bytes of one decode GEMV pair) and over 1 GiB, every slice fresh (rotating
+    over 4 GiB, far more than the 256 MB last-level cache), and the rate of
+    page-locked host -> device copies of one expert record, one after another."""
+    res = {"op": "torch.sum over float32 slices; torch copy_ from pinned memory"}
+    pool = torch.zeros((4 << 30) // 4, dtype=torch.float32, device=dev)
+
+    def read_rate(nbytes, reps):
+        n = max(1, nbytes // 4)
+        k = pool.numel() // n
+        torch.sum(pool[:n])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            j = (i + 1) % k
+            torch.sum(pool[j * n:(j + 1) * n])
+        e1.record()
+        torch.cuda.synchronize()
+        return n * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    if launch_bytes:
+        res["read_bytes_per_op"] = int(launch_bytes)
+        res["read_GB_per_s"] = read_rate(int(launch_bytes), 16)
+    res["read_GB_per_s_1GiB"] = read_rate(1 << 30, 8)
+    del pool
+    src = torch.empty(record_bytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(record_bytes, dtype=torch.uint8, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(8):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    res["h2d_record_bytes"] = record_bytes
+    res["h2d_GB_per_s"] = record_bytes * 8 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    return res
 
 
 def cpu_baseline(wl, weights, routers, hidden, budget_s=12.0, max_calls=64):
@@ -361,24 +404,6 @@ def main():
         ks = cache.kernel_stats()
         st2 = cache.stats()
         log(f"[bench] kernel-event pass of {ev_steps} steps done")
-    # Warm-up, untimed.  Each call's routing is read back (which waits for the
-    # call) for the stickiness |S_t & S_t-1| / k of every stream (decode).
-    prev = [None] * wl.layers
-    acc = [0, 0]
-    for s_ in range(warmup):
-        for l in range(wl.layers):
-            cache.forward(l, x_d[l][s_], w_d[l], b_d[l], out=out)
-            if wl.rho is None:
-                continue
-            idx, _ = cache.routing(l)
-            if prev[l] is not None:
-                for b_ in range(idx.shape[0]):
-                    acc[0] += len(set(idx[b_].tolist()) & set(prev[l][b_].tolist()))
-                    acc[1] += wl.top_k
-            prev[l] = idx
-    stick = acc[0] / acc[1] if acc[1] else None
-    torch.cuda.synchronize()
-    st0 = cache.stats()  # the warm-up calls: slots start from the preload
     layer_tokens = steps * wl.batch * wl.layers
     value = layer_tokens / wall
     sel = max(1, st["selections"])
@@ -457,6 +482,18 @@ def main():
                              "hbm_GB_per_s": (by + by2) / t_mm / 1e9,
                              "hbm_frac": (by + by2) / t_mm / 1e9 / HBM_PEAK_GBS}
             roofline = roofline_mfma
+
+    launch_bytes = None
+    if wl.batch <= 4 and ks["gateup"][0]:
+        launch_bytes = (ks["gateup"][2] + ks["down"][2]) / ks["gateup"][0]
+    extra["probes"] = probes(torch, dev, launch_bytes, wl.expert_bytes)
+    if roofline is not None and launch_bytes and extra["probes"].get("read_GB_per_s"):
+        roofline["vs_read_probe"] = roofline["achieved"] / extra["probes"]["read_GB_per_s"]
+    if roofline_fill is not None:
+        roofline_fill["vs_h2d_probe"] = roofline_fill["achieved"] / extra["probes"]["h2d_GB_per_s"]
+    if "fill_copy_engine_GB_per_s" in extra:
+        extra["fill_copy_engine_vs_h2d_probe"] = (extra["fill_copy_engine_GB_per_s"] /
+                                                  extra["probes"]["h2d_GB_per_s"])
 
     cpu = None
     if not args.no_cpu_baseline:

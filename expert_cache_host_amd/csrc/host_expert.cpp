@@ -3,12 +3,27 @@
 #include <immintrin.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <cstring>
 
 namespace moe {
 
 // ---------------------------------------------------------------- thread pool
+// Decode calls come every few hundred microseconds, and waking a sleeping
+// thread through the kernel costs tens of microseconds on a virtual machine.
+// So workers spin (with pause and yield, leaving the core to any other
+// runnable thread) for a while after each job before they sleep on the
+// condition variable, and the caller spins for the end of a run.
+
+namespace {
+constexpr auto kSpinFor = std::chrono::microseconds(250);
+
+inline void relax(unsigned &i) {
+  _mm_pause();
+  if ((++i & 63u) == 0) std::this_thread::yield();
+}
+}  // namespace
 
 ThreadPool::ThreadPool(int n) : n_(std::max(1, n)) {
   for (int i = 1; i < n_; ++i) th_.emplace_back([this, i] { loop(i); });
@@ -17,7 +32,7 @@ ThreadPool::ThreadPool(int n) : n_(std::max(1, n)) {
 ThreadPool::~ThreadPool() {
   {
     std::lock_guard<std::mutex> g(m_);
-    stop_ = true;
+    stop_.store(true);
   }
   cv_.notify_all();
   for (auto &t : th_) t.join();
@@ -31,33 +46,39 @@ void ThreadPool::run(const std::function<void(int)> &f) {
   {
     std::lock_guard<std::mutex> g(m_);
     job_ = &f;
-    pending_ = n_ - 1;
-    gen_++;
+    pending_.store(n_ - 1, std::memory_order_relaxed);
+    gen_.fetch_add(1, std::memory_order_release);
   }
-  cv_.notify_all();
+  cv_.notify_all();  // only sleeping workers need it
   f(0);
-  std::unique_lock<std::mutex> lk(m_);
-  done_.wait(lk, [&] { return pending_ == 0; });
-  job_ = nullptr;
+  unsigned i = 0;
+  while (pending_.load(std::memory_order_acquire) != 0) relax(i);
 }
 
 void ThreadPool::loop(int id) {
   uint64_t seen = 0;
   for (;;) {
-    const std::function<void(int)> *f;
-    {
-      std::unique_lock<std::mutex> lk(m_);
-      cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
-      if (stop_) return;
-      seen = gen_;
-      f = job_;
+    auto t0 = std::chrono::steady_clock::now();
+    unsigned i = 0;
+    while (gen_.load(std::memory_order_acquire) == seen && !stop_.load(std::memory_order_relaxed)) {
+      relax(i);
+      if ((i & 255u) == 0 && std::chrono::steady_clock::now() - t0 > kSpinFor) {
+        std::unique_lock<std::mutex> lk(m_);
+        cv_.wait(lk, [&] { return stop_.load() || gen_.load() != seen; });
+        t0 = std::chrono::steady_clock::now();
+      }
     }
-    (*f)(id);
-    {
-      std::lock_guard<std::mutex> g(m_);
-      if (--pending_ == 0) done_.notify_one();
-    }
+    if (stop_.load()) return;
+    seen = gen_.load(std::memory_order_acquire);
+    (*job_)(id);
+    pending_.fetch_sub(1, std::memory_order_release);
   }
+}
+
+void SpinBarrier::arrive_and_wait() {
+  arrived_.fetch_add(1, std::memory_order_acq_rel);
+  unsigned i = 0;
+  while (arrived_.load(std::memory_order_acquire) < n_) relax(i);
 }
 
 // ---------------------------------------------------------------- row dots
@@ -214,10 +235,14 @@ void host_moe_partial(ThreadPool &pool, const RecordLayout &L, const std::vector
       pair_row[(size_t)t * k + j] = h_base[jb] + pos;
     }
 
-  // phase 1: gate/up rows, chunks of kRowChunk rows of one job
+  // One run of the pool: gate/up rows (chunks of kRowChunk rows of one job),
+  // a barrier (down needs every row of h), then down rows; every output
+  // element summed in rank order.
   const int64_t chunks_f = (f + kRowChunk - 1) / kRowChunk;
-  std::atomic<int64_t> next1{0};
   const int64_t total1 = chunks_f * (int64_t)jobs.size();
+  const int64_t chunks_d = (d + kRowChunk - 1) / kRowChunk;
+  std::atomic<int64_t> next1{0}, next2{0};
+  SpinBarrier h_done(pool.size());
   pool.run([&](int) {
     for (;;) {
       const int64_t u = next1.fetch_add(1);
@@ -239,12 +264,7 @@ void host_moe_partial(ThreadPool &pool, const RecordLayout &L, const std::vector
         }
       }
     }
-  });
-
-  // phase 2: down rows; every output element summed in rank order
-  const int64_t chunks_d = (d + kRowChunk - 1) / kRowChunk;
-  std::atomic<int64_t> next2{0};
-  pool.run([&](int) {
+    h_done.arrive_and_wait();
     std::vector<float> dots((size_t)h_base.back());
     for (;;) {
       const int64_t u = next2.fetch_add(1);

@@ -21,6 +21,8 @@ class ThreadPool {
   ~ThreadPool();
   int size() const { return n_; }
   // Runs f(tid) on every worker, the caller being tid 0; returns when all ended.
+  // Every worker calls f exactly once per run, so f may hold a barrier over
+  // size() threads.
   void run(const std::function<void(int)> &f);
 
  private:
@@ -28,11 +30,22 @@ class ThreadPool {
   int n_;
   std::vector<std::thread> th_;
   std::mutex m_;
-  std::condition_variable cv_, done_;
-  const std::function<void(int)> *job_ = nullptr;
-  uint64_t gen_ = 0;
-  int pending_ = 0;
-  bool stop_ = false;
+  std::condition_variable cv_;
+  const std::function<void(int)> *job_ = nullptr;  // published by gen_
+  std::atomic<uint64_t> gen_{0};
+  std::atomic<int> pending_{0};
+  std::atomic<bool> stop_{false};
+};
+
+// Spin barrier over a fixed number of threads, for one use.
+class SpinBarrier {
+ public:
+  explicit SpinBarrier(int n) : n_(n) {}
+  void arrive_and_wait();
+
+ private:
+  const int n_;
+  std::atomic<int> arrived_{0};
 };
 
 // One host-side selection: token t picked expert `expert` with weight w at rank j.

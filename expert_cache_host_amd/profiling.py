@@ -184,7 +184,7 @@ def mfma_md(d: str, title: str, command: str) -> str:
 
 # kernel classes of the library, as the benchmark names them, and their symbols
 CLASSES = {"gateup": "q4_gateup_kernel", "down": "q4_down_kernel", "fill": "pull_kernel",
-           "router": "router_kernel", "topk": "topk_", "combine": "combine_kernel",
+           "router": "router_", "topk": "topk_", "combine": "combine_kernel",
            "mfma": "q4_mfma_kernel"}
 COPY_BYTES = 256 << 20  # bytes read and written by each calibration copy
 
