@@ -507,11 +507,14 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
     wait_fills(c, ly, st);
     ly.fill_pending = false;
   }
-  if (host_mode)
-    HIPCHK(hipMemcpyAsync(c->h_x.p, x, (size_t)T * d * 4, hipMemcpyDeviceToHost, st));
   // table published at call start: the hits run on it before the host plans
   const moe::SlotView pre = make_view(ly.planner->slot_of());
   const bool dec = c->decode_ok(T);
+  // host mode: the host experts read x from page-locked memory; the decode
+  // router writes that copy itself, else a copy on the stream does
+  const bool router_x = host_mode && dec && moe::router_decode_fits(T, d, E);
+  if (host_mode && !router_x)
+    HIPCHK(hipMemcpyAsync(c->h_x.p, x, (size_t)T * d * 4, hipMemcpyDeviceToHost, st));
   if (dec) {
     // router with the digit planes of the decode GEMV, then the decode top-k
     KTime kt(c, MOE_K_ROUTER, st);
@@ -529,7 +532,8 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
     a.h_flag = c->h_flag;
     a.seq = ++c->flag_seq;
     HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)c->z.p, nullptr,
-                              nullptr, nullptr, (uint4 *)c->xq.p, (float *)c->xs.p, st));
+                              nullptr, nullptr, (uint4 *)c->xq.p, (float *)c->xs.p, st,
+                              router_x ? (float *)c->h_x.p : nullptr));
     kt.end(4.0 * ((double)E * d + (double)T * d * 2 + (double)T * E + (router_bias ? E : 0)));
     KTime kt2(c, MOE_K_TOPK, st);
     HIPCHK(moe::launch_topk_decode((const float *)c->z.p, T, E, a, st));
@@ -641,14 +645,16 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
     }
     if (c->o.keep_debug) ly.dbg_host.assign((size_t)T * d, 0.0f);
   } else {
+    // Fills land at the layer's next call, so the calling thread enqueues
+    // them while the other workers start on the missed experts.
     const moe::PlanStage &stg = ly.plan.stages[0];
-    if (!stg.fills.empty()) {
-      {
-        TraceRange tr("moe.fill_copies");
-        enqueue_fills(c, layer, stg.fills, st);
-      }
+    const std::function<void()> fills = [&]() {
+      if (stg.fills.empty()) return;
+      TraceRange tr("moe.fill_copies");
+      enqueue_fills(c, layer, stg.fills, st);
       ly.fill_pending = true;
-    }
+    };
+    if (ly.plan.host_experts.empty()) fills();
     if (!ly.plan.host_experts.empty()) {
       const double th = now_s();
       const int b = c->partial_cur;
@@ -673,7 +679,8 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
       {
         TraceRange tr("moe.host_experts");
         moe::host_moe_partial(*c->pool, c->lay, jobs, rank_job.data(), (const float *)c->h_w.p, T,
-                              k, (const float *)c->h_x.p, (float *)c->partial[b].p, c->h_scratch);
+                              k, (const float *)c->h_x.p, (float *)c->partial[b].p, c->h_scratch,
+                              &fills);
       }
       const float *host_part = (const float *)c->partial[b].p;
       if (c->o.keep_debug) ly.dbg_host.assign(host_part, host_part + (size_t)T * d);

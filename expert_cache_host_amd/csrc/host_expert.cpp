@@ -6,6 +6,7 @@
 #include <chrono>
 #include <cmath>
 #include <cstring>
+#include <exception>
 
 namespace moe {
 
@@ -218,7 +219,8 @@ static constexpr int64_t kRowChunk = 32;
 
 void host_moe_partial(ThreadPool &pool, const RecordLayout &L, const std::vector<HostExpertJob> &jobs,
                       const int32_t *rank_job, const float *weights, int32_t T, int32_t k,
-                      const float *x, float *partial, std::vector<float> &h) {
+                      const float *x, float *partial, std::vector<float> &h,
+                      const std::function<void()> *caller_first) {
   const int64_t d = L.d, f = L.f;
   // h rows: one per (job, token) in job order
   std::vector<int64_t> h_base(jobs.size() + 1, 0);
@@ -243,7 +245,15 @@ void host_moe_partial(ThreadPool &pool, const RecordLayout &L, const std::vector
   const int64_t chunks_d = (d + kRowChunk - 1) / kRowChunk;
   std::atomic<int64_t> next1{0}, next2{0};
   SpinBarrier h_done(pool.size());
-  pool.run([&](int) {
+  std::exception_ptr first_err;
+  pool.run([&](int tid) {
+    if (tid == 0 && caller_first) {
+      try {
+        (*caller_first)();
+      } catch (...) {
+        first_err = std::current_exception();
+      }
+    }
     for (;;) {
       const int64_t u = next1.fetch_add(1);
       if (u >= total1) break;
@@ -289,6 +299,7 @@ void host_moe_partial(ThreadPool &pool, const RecordLayout &L, const std::vector
       }
     }
   });
+  if (first_err) std::rethrow_exception(first_err);
 }
 
 void host_expert_forward(ThreadPool &pool, const RecordLayout &L, const uint8_t *record,

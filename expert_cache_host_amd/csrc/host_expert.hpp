@@ -63,9 +63,13 @@ struct HostExpertJob {
 // w * y_e(x_t)[i];  tokens without host pairs get 0.
 //   jobs: one per host expert; rank_expert[t*k + j] = index into jobs or -1;
 //   weights[t*k + j] the gating weights.
+//   caller_first: when non-null, the calling thread runs it before it joins
+//   the work (the other workers start at once); an exception it throws is
+//   rethrown once every worker has finished.
 void host_moe_partial(ThreadPool &pool, const RecordLayout &L, const std::vector<HostExpertJob> &jobs,
                       const int32_t *rank_job, const float *weights, int32_t T, int32_t k,
-                      const float *x, float *partial, std::vector<float> &h_scratch);
+                      const float *x, float *partial, std::vector<float> &h_scratch,
+                      const std::function<void()> *caller_first = nullptr);
 
 // y [T][d] = expert(x) for one record (used by moe_host_expert_forward).
 void host_expert_forward(ThreadPool &pool, const RecordLayout &L, const uint8_t *record,

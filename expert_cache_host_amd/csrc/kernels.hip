@@ -244,14 +244,15 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
 // i = l, l + 64, ... ascending, the halving tree, the bias), so the logits are
 // the same bits.  max|x| per token comes from the same loads, and workgroup e
 // turns units 256 e .. 256 e + 255 into digit planes from the registers that
-// loaded them.  Needs tokens * d * 4 bytes of LDS (<= 64 KiB) and d / 8 <= 256 E.
+// loaded them, and, when h_x is given, copies those x values to page-locked
+// host memory.  Needs tokens * d * 4 bytes of LDS (<= 64 KiB) and d / 8 <= 256 E.
 template <int TT>
 __global__ __launch_bounds__(256) void router_decode_kernel(const float *__restrict__ x, int T,
                                                             int d, const float *__restrict__ W,
                                                             const float *__restrict__ bias, int E,
                                                             float *__restrict__ z,
                                                             uint4 *__restrict__ xq,
-                                                            float *__restrict__ xs) {
+                                                            float *__restrict__ xs, float *h_x) {
 #pragma clang fp contract(off)
   extern __shared__ float sprod[];  // [TT][d] products
   __shared__ float smax[TT][4];
@@ -343,28 +344,42 @@ __global__ __launch_bounds__(256) void router_decode_kernel(const float *__restr
       const float inv = m > 0.0f ? 30000.0f / m : 0.0f;
       if (j == 0) xs[tt] = m / 30000.0f;
       xq[(long long)tt * words + j] = digit_planes8(px[tt], inv);
+      if (h_x != nullptr) {
+        const int o = (j >> 2) * 32 + (j & 3) * 4;
+        float *hx = h_x + (long long)tt * d + o;
+        *reinterpret_cast<float4 *>(hx) = make_float4(px[tt][0], px[tt][1], px[tt][2], px[tt][3]);
+        *reinterpret_cast<float4 *>(hx + 16) =
+            make_float4(px[tt][4], px[tt][5], px[tt][6], px[tt][7]);
+      }
     }
+    // the host reads h_x once a later kernel raises its flag
+    if (h_x != nullptr) __threadfence_system();
   }
+}
+
+bool router_decode_fits(int T, int d, int E) {
+  const int tt = T <= 1 ? 1 : (T <= 2 ? 2 : 4);
+  return T >= 1 && T <= 4 && (size_t)tt * d * 4 <= 64 * 1024 && d / 8 <= 256 * E;
 }
 
 hipError_t launch_router(const float *x, int T, int d, const float *W, const float *bias, int E,
                          float *z, uint32_t *xp, float *xsw, float *xscale, uint4 *xq, float *xs,
-                         hipStream_t s) {
+                         hipStream_t s, float *h_x) {
   const int tt = T <= 1 ? 1 : (T <= 2 ? 2 : 4);
   const size_t lds = (size_t)tt * d * 4;
-  if (xq != nullptr && xp == nullptr && T >= 1 && T <= 4 && lds <= 64 * 1024 &&
-      d / 8 <= 256 * E) {
+  if (xq != nullptr && xp == nullptr && router_decode_fits(T, d, E)) {
     if (tt == 1)
       hipLaunchKernelGGL(router_decode_kernel<1>, dim3(E), dim3(256), lds, s, x, T, d, W, bias, E,
-                         z, xq, xs);
+                         z, xq, xs, h_x);
     else if (tt == 2)
       hipLaunchKernelGGL(router_decode_kernel<2>, dim3(E), dim3(256), lds, s, x, T, d, W, bias, E,
-                         z, xq, xs);
+                         z, xq, xs, h_x);
     else
       hipLaunchKernelGGL(router_decode_kernel<4>, dim3(E), dim3(256), lds, s, x, T, d, W, bias, E,
-                         z, xq, xs);
+                         z, xq, xs, h_x);
     return hipGetLastError();
   }
+  if (h_x != nullptr) return hipErrorInvalidValue;
   const int gx = (E + 3) / 4;
   if (T <= 1) {
     hipLaunchKernelGGL((router_kernel<1, 32>), dim3(gx, T), dim3(256), 0, s, x, T, d, W, bias, E,

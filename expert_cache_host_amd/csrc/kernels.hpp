@@ -30,9 +30,13 @@ struct SlotView {
 //   b = j/4 and g = 4*(j%4): (x[g],x[g+2]), (x[g+16],x[g+18]), (x[g+1],x[g+3]),
 //   (x[g+17],x[g+19]) of the block, hi then lo); and the sum of each word's 8
 //   scaled values (xsw).
+// h_x (decode planes only, when router_decode_fits): page-locked host copy of
+// x [T][d], visible to the host once a later kernel raises its flag.
 hipError_t launch_router(const float *x, int T, int d, const float *W, const float *bias, int E,
                          float *z, uint32_t *xp, float *xsw, float *xscale, uint4 *xq, float *xs,
-                         hipStream_t s);
+                         hipStream_t s, float *h_x = nullptr);
+// The one-workgroup-per-expert decode router handles this call.
+bool router_decode_fits(int T, int d, int E);
 
 // Per token: k largest logits (ties to the lower id), softmax gating weights,
 // written to device memory (idx, w) and to page-locked host memory (h_idx, h_w).
