@@ -103,45 +103,46 @@ def copy_calibration():
 
 
 def probes(torch, dev, launch_bytes, record_bytes):
-    """References measured on this GPU outside the timed region with plain torch
-    operations: the HBM read rate of a float32 sum over `launch_bytes` (the
-    bytes of one decode GEMV pair) and over 1 GiB, every slice fresh (rotating
-    over 4 GiB, far more than the 256 MB last-level cache), and the rate of
-    page-locked host -> device copies of one expert record, one after another."""
-    res = {"op": "torch.sum over float32 slices; torch copy_ from pinned memory"}
-    pool = torch.zeros((4 << 30) // 4, dtype=torch.float32, device=dev)
+    """References measured on this GPU outside the timed region, each operation
+    timed alone between two events on its stream: device-to-device copies
+    (torch copy_, the runtime's copy kernel; read + write bytes counted, the
+    STREAM convention) of `launch_bytes` (the bytes one decode GEMV pair reads)
+    and of 1 GiB, every slice fresh (rotating over 2 x 2 GiB, far more than the
+    256 MB last-level cache), and page-locked host -> device copies of one
+    expert record."""
+    res = {"op": "torch copy_ device-to-device (read + write bytes) and from pinned host memory"}
+    pool = torch.empty((4 << 30) // 4, dtype=torch.float32, device=dev)
+    half = pool.numel() // 2
 
-    def read_rate(nbytes, reps):
-        n = max(1, nbytes // 4)
-        k = pool.numel() // n
-        torch.sum(pool[:n])
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+    def timed(fn, reps):
+        evs = []
         for i in range(reps):
-            j = (i + 1) % k
-            torch.sum(pool[j * n:(j + 1) * n])
-        e1.record()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn(i)
+            e1.record()
+            evs.append((e0, e1))
         torch.cuda.synchronize()
-        return n * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        return sum(a.elapsed_time(b) for a, b in evs) * 1e-3 / reps
+
+    def copy_rate(nbytes, reps):
+        n = max(1, nbytes // 4)
+        k = half // n
+        fn = lambda i: pool[half + (i % k) * n:half + (i % k + 1) * n].copy_(
+            pool[((i + 1) % k) * n:((i + 1) % k + 1) * n])
+        fn(0)
+        return 2 * n * 4 / timed(fn, reps) / 1e9
 
     if launch_bytes:
-        res["read_bytes_per_op"] = int(launch_bytes)
-        res["read_GB_per_s"] = read_rate(int(launch_bytes), 16)
-    res["read_GB_per_s_1GiB"] = read_rate(1 << 30, 8)
+        res["copy_bytes_per_op"] = int(launch_bytes)
+        res["copy_GB_per_s"] = copy_rate(int(launch_bytes), 12)
+    res["copy_GB_per_s_1GiB"] = copy_rate(1 << 30, 6)
     del pool
     src = torch.empty(record_bytes, dtype=torch.uint8, pin_memory=True)
     dst = torch.empty(record_bytes, dtype=torch.uint8, device=dev)
     dst.copy_(src, non_blocking=True)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(8):
-        dst.copy_(src, non_blocking=True)
-    e1.record()
-    torch.cuda.synchronize()
     res["h2d_record_bytes"] = record_bytes
-    res["h2d_GB_per_s"] = record_bytes * 8 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    res["h2d_GB_per_s"] = record_bytes / timed(lambda i: dst.copy_(src, non_blocking=True), 8) / 1e9
     return res
 
 
@@ -487,8 +488,8 @@ def main():
     if wl.batch <= 4 and ks["gateup"][0]:
         launch_bytes = (ks["gateup"][2] + ks["down"][2]) / ks["gateup"][0]
     extra["probes"] = probes(torch, dev, launch_bytes, wl.expert_bytes)
-    if roofline is not None and launch_bytes and extra["probes"].get("read_GB_per_s"):
-        roofline["vs_read_probe"] = roofline["achieved"] / extra["probes"]["read_GB_per_s"]
+    if roofline is not None and launch_bytes and extra["probes"].get("copy_GB_per_s"):
+        roofline["vs_copy_probe"] = roofline["achieved"] / extra["probes"]["copy_GB_per_s"]
     if roofline_fill is not None:
         roofline_fill["vs_h2d_probe"] = roofline_fill["achieved"] / extra["probes"]["h2d_GB_per_s"]
     if "fill_copy_engine_GB_per_s" in extra:

@@ -110,10 +110,13 @@ def timeline_md(d: str, anchor: str, count: int) -> str:
                   key=lambda r: int(r["Start_Timestamp"]))
     i = next(j for j in range(len(rows) // 2, len(rows)) if anchor in rows[j]["Kernel_Name"])
     t0 = int(rows[i]["Start_Timestamp"])
-    out = ["| kernel | start us | end us |", "|---|---|---|"]
+    out = ["| kernel | workgroups | start us | end us |", "|---|---|---|---|"]
     for r in rows[i:i + count]:
         name = r["Kernel_Name"].split("(")[0].replace("void ", "")
-        out.append(f"| `{name}` | {(int(r['Start_Timestamp']) - t0) / 1e3:.1f} | "
+        wg = 1
+        for a in "XYZ":
+            wg *= max(1, int(r["Grid_Size_" + a]) // max(1, int(r["Workgroup_Size_" + a])))
+        out.append(f"| `{name}` | {wg} | {(int(r['Start_Timestamp']) - t0) / 1e3:.1f} | "
                    f"{(int(r['End_Timestamp']) - t0) / 1e3:.1f} |")
     return "\n".join(out) + "\n"
 
