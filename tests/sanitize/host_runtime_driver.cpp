@@ -4,11 +4,22 @@
 // call (slot_of and expert_in inverse, every selected expert placed exactly
 // once, fills only into slots the call does not hold protected) and the
 // host-miss partial sum against a plain scalar evaluation of the same bytes.
-// Exit status 0 and "ok" on success.
+// Also drives the thread pool (every worker runs each job once, a spin barrier
+// orders the workers' writes, idle gaps long enough for the workers to fall
+// asleep) and the caller's first task of a host partial (runs once; an
+// exception it throws surfaces after the run, whose results are complete).
+// Built under ThreadSanitizer with the argument "threads": the pool and the
+// host partial only.  Exit status 0 and "ok" on success.
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
+#include <atomic>
+#include <chrono>
+#include <stdexcept>
+#include <string>
+#include <thread>
 #include <random>
 #include <set>
 #include <vector>
@@ -150,10 +161,80 @@ static void host_expert_runs(std::mt19937_64 &rng) {
   }
 }
 
-int main() {
+static void pool_runs(std::mt19937_64 &rng) {
+  for (int n : {1, 2, 5}) {
+    moe::ThreadPool pool(n);
+    for (int run = 0; run < 240; ++run) {
+      std::vector<int> ran((size_t)n, 0), mark((size_t)n, 0);
+      std::atomic<int> after{0};
+      moe::SpinBarrier bar(pool.size());
+      const int tag = (int)(rng() % 1000) + 1;
+      pool.run([&](int tid) {
+        ran[(size_t)tid] += 1;
+        mark[(size_t)tid] = tag;  // plain writes, ordered by the barrier
+        bar.arrive_and_wait();
+        for (int j = 0; j < n; ++j) CHECK(mark[(size_t)j] == tag);
+        after.fetch_add(1);
+      });
+      CHECK(after.load() == n);
+      for (int j = 0; j < n; ++j) CHECK(ran[(size_t)j] == 1);
+      // now and then idle past the workers' spin, so that they sleep
+      if (run % 40 == 39) std::this_thread::sleep_for(std::chrono::milliseconds(2));
+    }
+  }
+}
+
+// The caller's first task of host_moe_partial: runs once on the calling
+// thread; its exception surfaces after the run, and the partial is complete.
+static void caller_first_runs(std::mt19937_64 &rng) {
+  moe::ThreadPool pool(4);
+  const int64_t d = 128, f = 64;
+  const int T = 2, k = 2;
+  const moe::RecordLayout L = moe::RecordLayout::make(d, f);
+  std::vector<uint8_t> inter((size_t)L.interchange_bytes), rec((size_t)L.bytes);
+  for (size_t i = 0; i < inter.size(); ++i) inter[i] = (uint8_t)rng();
+  for (size_t b = 0; b + 18 <= inter.size(); b += 18) {
+    const uint16_t sc = (uint16_t)(0x1800 + rng() % 0x400);
+    std::memcpy(&inter[b], &sc, 2);
+  }
+  moe::repack_expert(inter.data(), L, rec.data());
+  std::vector<float> x((size_t)T * d), w((size_t)T * k, 0.5f), a((size_t)T * d), b((size_t)T * d), h;
+  std::normal_distribution<float> nd(0.f, 1.f);
+  for (auto &v : x) v = nd(rng);
+  std::vector<moe::HostExpertJob> jobs(1);
+  jobs[0].record = rec.data();
+  jobs[0].tokens = {0, 1};
+  std::vector<int32_t> rank = {0, -1, -1, 0};
+  moe::host_moe_partial(pool, L, jobs, rank.data(), w.data(), T, k, x.data(), a.data(), h);
+  int calls = 0;
+  const std::thread::id me = std::this_thread::get_id();
+  const std::function<void()> first = [&]() {
+    CHECK(std::this_thread::get_id() == me);
+    ++calls;
+  };
+  moe::host_moe_partial(pool, L, jobs, rank.data(), w.data(), T, k, x.data(), b.data(), h, &first);
+  CHECK(calls == 1);
+  CHECK(std::memcmp(a.data(), b.data(), a.size() * 4) == 0);
+  std::fill(b.begin(), b.end(), 0.0f);
+  const std::function<void()> throws = [&]() { throw std::runtime_error("first task failed"); };
+  bool caught = false;
+  try {
+    moe::host_moe_partial(pool, L, jobs, rank.data(), w.data(), T, k, x.data(), b.data(), h,
+                          &throws);
+  } catch (const std::runtime_error &e) {
+    caught = std::string(e.what()) == "first task failed";
+  }
+  CHECK(caught);
+  CHECK(std::memcmp(a.data(), b.data(), a.size() * 4) == 0);
+}
+
+int main(int argc, char **argv) {
   std::mt19937_64 rng(12345);
-  planner_runs(rng);
-  host_expert_runs(rng);
+  const bool threads_only = argc > 1 && std::string(argv[1]) == "threads";
+  if (!threads_only) planner_runs(rng);
+  pool_runs(rng);
+  caller_first_runs(rng);
+  if (!threads_only) host_expert_runs(rng);
   std::printf("ok\n");
   return 0;
 }
