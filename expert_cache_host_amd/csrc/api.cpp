@@ -19,6 +19,7 @@
 #include <cstring>
 #include <memory>
 #include <new>
+#include <optional>
 #include <stdexcept>
 #include <string>
 #include <thread>
@@ -496,6 +497,8 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   if (ly.called && ly.last_stream != st) HIPCHK(hipDeviceSynchronize());
   ly.last_stream = st;
   ly.called = true;
+  std::optional<TraceRange> enqueue_range;
+  enqueue_range.emplace("moe.enqueue");
   hipEvent_t g0 = nullptr, g1 = nullptr;
   if (c->timing) {
     g0 = ly.t_gpu.get();
@@ -562,6 +565,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   // enqueued before the host reads the routing.
   const int nb_hits = std::min(T * k, c->S) + (ns > 0 ? 1 : 0);
   run_experts(c, layer, T, pre, ns > 0, nb_hits, 0.0, x, st);
+  enqueue_range.reset();
 
   float *dbg_gpu = nullptr;
   if (c->o.keep_debug) {
@@ -687,6 +691,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
       ly.st.host_s += now_s() - th;
       ly.st.host_selections += ly.plan.misses;
       {
+        TraceRange tr("moe.combine");
         KTime kt(c, MOE_K_COMBINE, st);
         HIPCHK(moe::launch_combine((const float *)c->y.p, (const float *)c->w.p,
                                    (const int32_t *)c->idx.p, pre, 0,
@@ -702,6 +707,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
     }
   }
   if (!combined) {
+    TraceRange tr("moe.combine");
     KTime kt(c, MOE_K_COMBINE, st);
     HIPCHK(moe::launch_combine((const float *)c->y.p, (const float *)c->w.p,
                                (const int32_t *)c->idx.p, pre, host_mode ? 0 : 1,
