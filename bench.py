@@ -6,7 +6,9 @@
 One step = one batch (decode: one token per stream; prefill: one ubatch) through
 every layer of the workload, layer after layer, through the C ABI.  The default
 workload is the Gemma-4-26B-A4B-like decode (30 layers, d_model 2816, d_ff 704,
-128 experts, top-8, 32 slots per layer, batch 1, misses streamed into slots).
+128 experts, top-8, 32 slots per layer, LRU, batch 1, misses computed on the
+host cores while their slot fills stream in the background; `--miss-mode
+stream` streams them into slots first).
 
 Prints one JSON line.  `value` = MoE-layer tokens/s (tokens x layers / wall
 time) over exactly K timed steps, inputs resident in HBM and expert weights in
@@ -439,7 +441,7 @@ def main():
         if not na or sa + sb <= 0:
             return None
         ach = (ba + bb) / (sa + sb) / 1e9
-        tr = [pmc_traffic(wl.name, k, 0, 0) for k in (a, b)]
+        tr = [pmc_traffic(f"{wl.name}/{wl.miss_mode}", k, 0, 0) for k in (a, b)]
         traffic = None if None in tr else (tr[0] * na + tr[1] * nb_) / na
         return {"bound": "hbm", "kernel": f"{KERNEL_SYMBOL[a]} + {KERNEL_SYMBOL[b]}",
                 "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
@@ -456,7 +458,7 @@ def main():
             ach = by / sec / 1e12
         else:
             ach = by / sec / 1e9
-        tr = pmc_traffic(wl.name, name, n, by / n)
+        tr = pmc_traffic(f"{wl.name}/{wl.miss_mode}", name, n, by / n)
         return {"bound": bound, "kernel": KERNEL_SYMBOL.get(name, name), "achieved": ach,
                 "peak": peak, "unit": unit, "frac": ach / peak,
                 "traffic": tr, "avg_launch_us": 1e6 * sec / n, "launches": n,

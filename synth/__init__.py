@@ -103,7 +103,7 @@ WORKLOADS = {
                      tokens=64, batch=1, modes=("stream", "host")),
     "gemma": Workload("gemma", 2, 30, 2816, 704, 128, 8, 32,
                       router_sigma=1.6 / math.sqrt(2816), zipf_s=1.1, rho=0.8,
-                      tokens=512, batch=1),
+                      tokens=512, batch=1, miss_mode="host", modes=("host", "stream")),
     "qwen": Workload("qwen", 3, 48, 2048, 768, 128, 8, 16,
                      router_sigma=1.6 / math.sqrt(2048), zipf_s=1.0, rho=0.7,
                      tokens=256, batch=1),
