@@ -19,8 +19,10 @@ timed region would cost ~30% of the throughput, since the host enqueues on the
 critical path).  `roofline` is the decode expert GEMV (gate/up + SwiGLU and
 down launches of a call taken together: expert bytes read / their device time)
 against HBM, or for prefill the grouped GEMM against the fp16 matrix-core peak;
-`roofline_fill` is the slot-fill kernel against PCIe Gen5 x16, which under pure
-LRU holds the most device time (`dominant_kernel_by_device_time`).  `traffic` comes from the
+`roofline_fill` is the slot-fill kernel against PCIe Gen5 x16 when misses are
+streamed (it then holds the most device time, `dominant_kernel_by_device_time`);
+with host misses the fills run on the copy engines
+(`extra.fill_copy_engine_GB_per_s`).  `traffic` comes from the
 rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in profiles/pmc_traffic.json
 and is null when the kernel source changed since.  The oracle is timed on a
 bounded sample of the same workload as the CPU baseline.
