@@ -401,3 +401,20 @@ def test_router_logits_bit_exact(case):
         assert bad.size == 0, f"call {c}: {len(bad)} logits differ, first {bad[:4].tolist()}"
     r.check_log()
     r.close()
+
+
+@pytest.mark.parametrize("d,T", [(6144, 1), (6144, 3), (2048, 4)])
+def test_host_misses_read_x_copied_by_router_or_stream(d, T):
+    """Host misses read a page-locked copy of x: written by the decode router
+    when its products fit in LDS (6144 x 1, 2048 x 4 tokens), else copied on
+    the stream (6144 x 3 and 4 tokens).  Outputs, tables and log against the
+    oracle on every call."""
+    wl = synth.Workload(f"hx_{d}_{T}", 50 + d // 1024 + T, 1, d, 64, 16, 2, 4,
+                        router_sigma=1.6 / np.sqrt(d), zipf_s=1.0, rho=0.8, tokens=6, batch=T)
+    log(f"host misses, x copy: d={d} T={T}")
+    r = Runner(wl, [0], mode="host")
+    x = synth.gen_hidden(wl, 0, 6)
+    for c in range(x.shape[0]):
+        r.call(0, x[c])
+    r.check_log()
+    r.close()
