@@ -148,8 +148,6 @@ struct LayerState {
   hipEvent_t fill_ev[2] = {nullptr, nullptr};  // last fills of this layer (side streams)
   bool fill_used[2] = {false, false};
   bool fill_pending = false;
-  hipStream_t last_stream = nullptr;  // stream of the layer's last call
-  bool called = false;
   moe::CallPlan plan;             // last call
   int32_t last_T = 0;
   std::vector<int32_t> last_idx;
@@ -187,6 +185,9 @@ struct moe_cache {
   int32_t cap_T = 0;
   DevBuf z, idx, w, meta, bucket_pair, items, h, y, xp, xsw, xscale, hp, hsw, hscale, xq, xs;
   DevBuf buckets, pair_slot;  // decode: bucket list and pair -> slot of the hits
+  // stream of the last call: the workspace above is shared by every layer
+  hipStream_t last_stream = nullptr;
+  bool called = false;
   // pinned host staging
   PinnedBuf h_idx, h_w, h_x, partial[2];
   hipEvent_t partial_ev[2] = {nullptr, nullptr};
@@ -492,11 +493,13 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   c->ensure_ws(T);
   // Stream rule: slot fills (the pull kernel on `st`, copies after an event on
   // `st`) rely on every earlier reader of the victims being before them on
-  // `st`.  A call on another stream than the layer's last call therefore waits
-  // for the device first (rare; keeps the usual path free of markers).
-  if (ly.called && ly.last_stream != st) HIPCHK(hipDeviceSynchronize());
-  ly.last_stream = st;
-  ly.called = true;
+  // `st`, and every layer's calls share the cache's workspace (logits, planes,
+  // bucket list, partial results).  A call on another stream than the cache's
+  // last call therefore waits for the device first (rare; keeps the usual
+  // path free of markers).
+  if (c->called && c->last_stream != st) HIPCHK(hipDeviceSynchronize());
+  c->last_stream = st;
+  c->called = true;
   std::optional<TraceRange> enqueue_range;
   enqueue_range.emplace("moe.enqueue");
   hipEvent_t g0 = nullptr, g1 = nullptr;

@@ -190,10 +190,11 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
  * returns when the host partial has been handed to `stream`.
  *
  * x, router_w, router_bias and out must stay valid until `stream` has passed
- * this call's work.  A layer's calls are ordered on their stream; a call on
- * another stream than the same layer's previous call first waits for the whole
- * device (hipDeviceSynchronize), so that no earlier reader of a slot can race
- * with its refill.  Requirements: 0 <= layer < layers; 1 <= n_tokens; the
+ * this call's work.  Calls are ordered on their stream; a call on another
+ * stream than the cache's previous call (of any layer) first waits for the
+ * whole device (hipDeviceSynchronize), since every layer shares the cache's
+ * workspace and no earlier reader of a slot may race with its refill.
+ * Requirements: 0 <= layer < layers; 1 <= n_tokens; the
  * pointers non-NULL except router_bias and stream.
  */
 moe_status moe_layer_forward(moe_cache *c, int32_t layer, const float *x, int32_t n_tokens,
