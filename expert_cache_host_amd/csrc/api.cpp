@@ -174,6 +174,7 @@ struct moe_cache {
   uint8_t *h_arena = nullptr;   // L * (E + n_shared) records, page-locked
   std::vector<LayerState> layers;
   hipStream_t side[2] = {nullptr, nullptr};  // slot fills alternate over two copy streams
+  int fill_rr = 0;                           // copy stream of the next fill
   hipEvent_t ev_idx = nullptr, ev_ready = nullptr;
   // decode calls: the top-k kernel stores the call's sequence number here
   // (page-locked, coherent) once the routing copy is visible to the host
@@ -328,29 +329,35 @@ void enqueue_fills(moe_cache *c, int32_t layer, const std::vector<moe::Fill> &fi
                    hipStream_t st) {
   LayerState &ly = c->layers[layer];
   HIPCHK(hipEventRecord(c->ev_ready, st));
+  // the calls' fills alternate over the two copy streams (a call of one fill
+  // takes the stream the previous call's last fill did not), so that both
+  // copy engines stay loaded
   const int n_sd = fills.size() > 1 ? 2 : 1;
+  const int r0 = c->fill_rr;
+  c->fill_rr = (c->fill_rr + (int)fills.size()) & 1;
+  auto phys = [&](int i) { return (r0 + i) & 1; };  // the i-th stream this call uses
   hipEvent_t t0 = nullptr, t1 = nullptr;
   for (int i = 0; i < n_sd; ++i) {
-    HIPCHK(hipStreamWaitEvent(c->side[i], c->ev_ready, 0));
+    HIPCHK(hipStreamWaitEvent(c->side[phys(i)], c->ev_ready, 0));
   }
   if (c->timing) {
     t0 = ly.t_h2d.get();
     t1 = ly.t_h2d.get();
-    HIPCHK(hipEventRecord(t0, c->side[0]));
-    if (n_sd > 1) HIPCHK(hipStreamWaitEvent(c->side[1], t0, 0));
+    HIPCHK(hipEventRecord(t0, c->side[phys(0)]));
+    if (n_sd > 1) HIPCHK(hipStreamWaitEvent(c->side[phys(1)], t0, 0));
   }
   for (size_t i = 0; i < fills.size(); ++i) {
     const moe::Fill &fl = fills[i];
     HIPCHK(hipMemcpyAsync(c->dev_slot(layer, fl.slot), c->host_record(layer, fl.expert), c->rec(),
-                          hipMemcpyHostToDevice, c->side[i % n_sd]));
+                          hipMemcpyHostToDevice, c->side[phys((int)i % n_sd)]));
   }
-  for (int i = 0; i < 2; ++i) {
-    ly.fill_used[i] = i < n_sd;
-    if (i < n_sd) HIPCHK(hipEventRecord(ly.fill_ev[i], c->side[i]));
+  for (int p = 0; p < 2; ++p) {
+    ly.fill_used[p] = n_sd == 2 || p == phys(0);
+    if (ly.fill_used[p]) HIPCHK(hipEventRecord(ly.fill_ev[p], c->side[p]));
   }
   if (c->timing) {
-    if (n_sd > 1) HIPCHK(hipStreamWaitEvent(c->side[0], ly.fill_ev[1], 0));
-    HIPCHK(hipEventRecord(t1, c->side[0]));
+    if (n_sd > 1) HIPCHK(hipStreamWaitEvent(c->side[phys(0)], ly.fill_ev[phys(1)], 0));
+    HIPCHK(hipEventRecord(t1, c->side[phys(0)]));
     ly.t_h2d.pending.emplace_back(t0, t1);
   }
   ly.st.fills += fills.size();
