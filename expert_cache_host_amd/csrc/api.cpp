@@ -142,11 +142,14 @@ struct TimingLog {
 
 }  // namespace
 
+// Copy streams the slot fills rotate over (each keeps a copy engine busy).
+constexpr int kCopyStreams = 2;
+
 struct LayerState {
   std::unique_ptr<moe::SlotPlanner> planner;
   uint8_t *d_slots = nullptr;     // (S + n_shared) records
-  hipEvent_t fill_ev[2] = {nullptr, nullptr};  // last fills of this layer (side streams)
-  bool fill_used[2] = {false, false};
+  hipEvent_t fill_ev[kCopyStreams] = {};  // last fills of this layer (side streams)
+  bool fill_used[kCopyStreams] = {};
   bool fill_pending = false;
   moe::CallPlan plan;             // last call
   int32_t last_T = 0;
@@ -173,8 +176,8 @@ struct moe_cache {
   int device = 0;
   uint8_t *h_arena = nullptr;   // L * (E + n_shared) records, page-locked
   std::vector<LayerState> layers;
-  hipStream_t side[2] = {nullptr, nullptr};  // slot fills alternate over two copy streams
-  int fill_rr = 0;                           // copy stream of the next fill
+  hipStream_t side[kCopyStreams] = {};  // slot fills rotate over the copy streams
+  int fill_rr = 0;                      // copy stream of the next fill
   hipEvent_t ev_idx = nullptr, ev_ready = nullptr;
   // decode calls: the top-k kernel stores the call's sequence number here
   // (page-locked, coherent) once the routing copy is visible to the host
@@ -329,13 +332,13 @@ void enqueue_fills(moe_cache *c, int32_t layer, const std::vector<moe::Fill> &fi
                    hipStream_t st) {
   LayerState &ly = c->layers[layer];
   HIPCHK(hipEventRecord(c->ev_ready, st));
-  // the calls' fills alternate over the two copy streams (a call of one fill
-  // takes the stream the previous call's last fill did not), so that both
-  // copy engines stay loaded
-  const int n_sd = fills.size() > 1 ? 2 : 1;
+  // the calls' fills rotate over the copy streams (a call's first fill takes
+  // the stream after the previous call's last one), so that every copy engine
+  // stays loaded
+  const int n_sd = (int)std::min<size_t>(fills.size(), kCopyStreams);
   const int r0 = c->fill_rr;
-  c->fill_rr = (c->fill_rr + (int)fills.size()) & 1;
-  auto phys = [&](int i) { return (r0 + i) & 1; };  // the i-th stream this call uses
+  c->fill_rr = (int)((c->fill_rr + fills.size()) % kCopyStreams);
+  auto phys = [&](int i) { return (r0 + i) % kCopyStreams; };  // i-th stream of this call
   hipEvent_t t0 = nullptr, t1 = nullptr;
   for (int i = 0; i < n_sd; ++i) {
     HIPCHK(hipStreamWaitEvent(c->side[phys(i)], c->ev_ready, 0));
@@ -344,19 +347,21 @@ void enqueue_fills(moe_cache *c, int32_t layer, const std::vector<moe::Fill> &fi
     t0 = ly.t_h2d.get();
     t1 = ly.t_h2d.get();
     HIPCHK(hipEventRecord(t0, c->side[phys(0)]));
-    if (n_sd > 1) HIPCHK(hipStreamWaitEvent(c->side[phys(1)], t0, 0));
+    for (int i = 1; i < n_sd; ++i) HIPCHK(hipStreamWaitEvent(c->side[phys(i)], t0, 0));
   }
   for (size_t i = 0; i < fills.size(); ++i) {
     const moe::Fill &fl = fills[i];
     HIPCHK(hipMemcpyAsync(c->dev_slot(layer, fl.slot), c->host_record(layer, fl.expert), c->rec(),
-                          hipMemcpyHostToDevice, c->side[phys((int)i % n_sd)]));
+                          hipMemcpyHostToDevice, c->side[phys((int)(i % n_sd))]));
   }
-  for (int p = 0; p < 2; ++p) {
-    ly.fill_used[p] = n_sd == 2 || p == phys(0);
-    if (ly.fill_used[p]) HIPCHK(hipEventRecord(ly.fill_ev[p], c->side[p]));
+  for (int p = 0; p < kCopyStreams; ++p) ly.fill_used[p] = false;
+  for (int i = 0; i < n_sd; ++i) {
+    ly.fill_used[phys(i)] = true;
+    HIPCHK(hipEventRecord(ly.fill_ev[phys(i)], c->side[phys(i)]));
   }
   if (c->timing) {
-    if (n_sd > 1) HIPCHK(hipStreamWaitEvent(c->side[phys(0)], ly.fill_ev[phys(1)], 0));
+    for (int i = 1; i < n_sd; ++i)
+      HIPCHK(hipStreamWaitEvent(c->side[phys(0)], ly.fill_ev[phys(i)], 0));
     HIPCHK(hipEventRecord(t1, c->side[phys(0)]));
     ly.t_h2d.pending.emplace_back(t0, t1);
   }
@@ -365,7 +370,7 @@ void enqueue_fills(moe_cache *c, int32_t layer, const std::vector<moe::Fill> &fi
 }
 
 void wait_fills(moe_cache *c, LayerState &ly, hipStream_t st) {
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kCopyStreams; ++i)
     if (ly.fill_used[i]) HIPCHK(hipStreamWaitEvent(st, ly.fill_ev[i], 0));
 }
 
@@ -1024,7 +1029,7 @@ moe_status moe_cache_preload(moe_cache *c, const uint32_t *counts) {
         HIPCHK(hipMemcpy(c->dev_slot(l, s), c->host_record(l, ein[s]), c->rec(),
                          hipMemcpyHostToDevice));
       ly.fill_pending = false;
-      ly.fill_used[0] = ly.fill_used[1] = false;
+      for (bool &u : ly.fill_used) u = false;
     }
     return MOE_OK;
   });
