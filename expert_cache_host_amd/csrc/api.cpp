@@ -150,6 +150,10 @@ struct LayerState {
   uint8_t *d_slots = nullptr;     // (S + n_shared) records
   hipEvent_t fill_ev[kCopyStreams] = {};  // last fills of this layer (side streams)
   bool fill_used[kCopyStreams] = {};
+  // host mode: recorded on the compute stream at the end of each call, after
+  // its readers of the layer's slots
+  hipEvent_t read_done = nullptr;
+  bool read_done_set = false;
   bool fill_pending = false;
   moe::CallPlan plan;             // last call
   int32_t last_T = 0;
@@ -223,6 +227,7 @@ struct moe_cache {
       if (ly.d_slots) (void)hipFree(ly.d_slots);
       for (auto &e : ly.fill_ev)
         if (e) (void)hipEventDestroy(e);
+      if (ly.read_done) (void)hipEventDestroy(ly.read_done);
     }
     layers.clear();
     if (h_arena) (void)hipHostFree(h_arena);
@@ -325,13 +330,17 @@ void wait_routing(moe_cache *c, hipStream_t st) {
   }
 }
 
-// Copies the fills of one stage on the two side streams after every earlier
-// reader of the victim slots (all of them are on `st`: see the stream rule at
-// the top of a call), and records the layer's fill events.
+// Copies the fills of one stage on the side streams after every earlier reader
+// of the victim slots (all of them are on `st`: see the stream rule at the top
+// of a call), and records the layer's fill events.  Staged calls wait for the
+// work enqueued so far on `st` (a stage's victims may be the previous stage's
+// slots).  Host-mode calls (after_prev_call) wait only for the layer's previous
+// call and fills: no slot a call reads is its own victim, so the copies need
+// not wait for the call's own kernels.
 void enqueue_fills(moe_cache *c, int32_t layer, const std::vector<moe::Fill> &fills,
-                   hipStream_t st) {
+                   hipStream_t st, bool after_prev_call = false) {
   LayerState &ly = c->layers[layer];
-  HIPCHK(hipEventRecord(c->ev_ready, st));
+  if (!after_prev_call) HIPCHK(hipEventRecord(c->ev_ready, st));
   // the calls' fills rotate over the copy streams (a call's first fill takes
   // the stream after the previous call's last one), so that every copy engine
   // stays loaded
@@ -341,7 +350,14 @@ void enqueue_fills(moe_cache *c, int32_t layer, const std::vector<moe::Fill> &fi
   auto phys = [&](int i) { return (r0 + i) % kCopyStreams; };  // i-th stream of this call
   hipEvent_t t0 = nullptr, t1 = nullptr;
   for (int i = 0; i < n_sd; ++i) {
-    HIPCHK(hipStreamWaitEvent(c->side[phys(i)], c->ev_ready, 0));
+    hipStream_t sd = c->side[phys(i)];
+    if (!after_prev_call) {
+      HIPCHK(hipStreamWaitEvent(sd, c->ev_ready, 0));
+      continue;
+    }
+    if (ly.read_done_set) HIPCHK(hipStreamWaitEvent(sd, ly.read_done, 0));
+    for (int p = 0; p < kCopyStreams; ++p)
+      if (ly.fill_used[p] && p != phys(i)) HIPCHK(hipStreamWaitEvent(sd, ly.fill_ev[p], 0));
   }
   if (c->timing) {
     t0 = ly.t_h2d.get();
@@ -670,7 +686,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
     const std::function<void()> fills = [&]() {
       if (stg.fills.empty()) return;
       TraceRange tr("moe.fill_copies");
-      enqueue_fills(c, layer, stg.fills, st);
+      enqueue_fills(c, layer, stg.fills, st, true);
       ly.fill_pending = true;
     };
     if (ly.plan.host_experts.empty()) fills();
@@ -729,6 +745,11 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
                                dec ? (const int32_t *)c->pair_slot.p : nullptr, T, k, d, ns,
                                nullptr, out, dbg_gpu, st));
     kt.end(4.0 * (double)T * d * (k + ns + 1));
+  }
+  if (host_mode) {
+    // the layer's next fills start after this call's readers of its slots
+    HIPCHK(hipEventRecord(ly.read_done, st));
+    ly.read_done_set = true;
   }
   if (c->timing) {
     HIPCHK(hipEventRecord(g1, st));
@@ -887,6 +908,8 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
         return fail(MOE_ENOMEM, "device slot arena allocation failed");
       }
       for (auto &e : ly.fill_ev) HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+      HIPCHK(hipEventCreateWithFlags(&ly.read_done,
+                                     hipEventDisableTiming | hipEventDisableSystemFence));
       // preload: slot s <- expert s; shared slot S <- expert E
       for (int32_t s = 0; s < slots; ++s)
         HIPCHK(hipMemcpyAsync(c->dev_slot(l, s), c->host_record(l, s), c->rec(),
