@@ -106,7 +106,7 @@ WORKLOADS = {
                       tokens=512, batch=1, miss_mode="host", modes=("host", "stream")),
     "qwen": Workload("qwen", 3, 48, 2048, 768, 128, 8, 16,
                      router_sigma=1.6 / math.sqrt(2048), zipf_s=1.0, rho=0.7,
-                     tokens=256, batch=1),
+                     tokens=256, batch=1, miss_mode="host", modes=("host", "stream")),
     "large": Workload("large", 4, 8, 6144, 2048, 256, 8, 64, n_shared=1,
                       router_sigma=1.6 / math.sqrt(6144), zipf_s=1.2, rho=0.8,
                       tokens=256, batch=1, miss_mode="host", modes=("host",)),
