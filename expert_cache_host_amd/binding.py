@@ -71,6 +71,7 @@ def load_library():
         "moe_cache_stats": (I32, [P, I32, ctypes.POINTER(Stats)]),
         "moe_cache_reset_stats": (I32, [P]),
         "moe_cache_set_timing": (I32, [P, I32]),
+        "moe_cache_set_kernel_timing": (I32, [P, ctypes.c_uint32]),
         "moe_cache_kernel_stats": (I32, [P, I32, ctypes.POINTER(ctypes.c_int64),
                                          ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
         "moe_cache_sync": (I32, [P]),
@@ -208,6 +209,13 @@ class MoECache:
 
     def set_timing(self, on: bool):
         _check(load_library().moe_cache_set_timing(self._h, 1 if on else 0))
+
+    def set_kernel_timing(self, kernels):
+        """Times only the named kernels (names from KERNELS) from now on."""
+        mask = 0
+        for k in kernels:
+            mask |= 1 << self.KERNELS.index(k)
+        _check(load_library().moe_cache_set_kernel_timing(self._h, mask))
 
     def kernel_stats(self) -> dict:
         """{kernel: (launches, device seconds, algorithmic bytes)} while timing was on."""

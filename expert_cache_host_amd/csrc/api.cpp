@@ -188,10 +188,11 @@ struct moe_cache {
   uint32_t *h_flag = nullptr;
   uint32_t flag_seq = 0;
   bool poisoned = false;
-  bool timing = false;
+  bool timing = false;   // per-layer compute and fill events
+  uint32_t kmask = 0;    // kernels timed one launch at a time (bit MOE_K_*)
   // device workspace
   int32_t cap_T = 0;
-  DevBuf z, idx, w, meta, bucket_pair, items, h, y, xp, xsw, xscale, hp, hsw, hscale, xq, xs;
+  DevBuf z, idx, w, meta, bucket_pair, items, h, y, xp, xscale, hp, hscale, xq, xs;
   DevBuf buckets, pair_slot;  // decode: bucket list and pair -> slot of the hits
   // stream of the last call: the workspace above is shared by every layer
   hipStream_t last_stream = nullptr;
@@ -254,10 +255,9 @@ struct moe_cache {
     h.ensure(P * (size_t)f * 4);
     y.ensure(P * (size_t)d * 4);
     xp.ensure((size_t)T * d * 4);
-    xsw.ensure((size_t)T * (d / 8) * 4);
     xscale.ensure((size_t)T * 4);
     xq.ensure((size_t)T * d * 2);
-    xs.ensure((size_t)T * 4);
+    xs.ensure((size_t)T * moe::xs_units(d / 32) * 16);
     buckets.ensure((size_t)(1 + moe::kDecodeMaxPairs * moe::kBucketInts) * 4);
     pair_slot.ensure((size_t)moe::kDecodeMaxPairs * 4);
     // h as binary16 pairs for the matrix-core down GEMM: every call that does
@@ -267,7 +267,6 @@ struct moe_cache {
     // largest T seen serve every smaller matrix-core call.
     if (!decode_ok(T)) {
       hp.ensure(P * (size_t)f * 4);
-      hsw.ensure(P * (size_t)(f / 8) * 4);
       hscale.ensure(P * 4);
     }
     h_idx.ensure((size_t)T * k * 4);
@@ -296,13 +295,13 @@ struct KTime {
   hipStream_t st;
   hipEvent_t a = nullptr;
   KTime(moe_cache *c_, int kid_, hipStream_t st_) : c(c_), kid(kid_), st(st_) {
-    if (c->timing) {
+    if (c->kmask & (1u << kid)) {
       a = c->kt[kid].log.get();
       HIPCHK(hipEventRecord(a, st));
     }
   }
   void end(double bytes) {
-    if (!c->timing) return;
+    if (!(c->kmask & (1u << kid))) return;
     hipEvent_t b = c->kt[kid].log.get();
     HIPCHK(hipEventRecord(b, st));
     c->kt[kid].log.pending.emplace_back(a, b);
@@ -414,7 +413,6 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
     if (!decode && !tab) {
       need(c->xp, (size_t)T * c->d * 4, "xp");
       need(c->hp, P_all * (size_t)c->f * 4, "hp");
-      need(c->hsw, P_all * (size_t)(c->f / 8) * 4, "hsw");
       need(c->hscale, P_all * 4, "hscale");
       need(c->bucket_pair, P_all * 4, "bucket_pair");
     } else {
@@ -438,7 +436,6 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
   a.xq = (const uint4 *)c->xq.p;
   a.xs = (const float *)c->xs.p;
   a.xp = (const uint32_t *)c->xp.p;
-  a.xsw = (const float *)c->xsw.p;
   a.xscale = (const float *)c->xscale.p;
   a.rec_bytes = L.bytes;
   a.T = T;
@@ -468,7 +465,7 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
     {
       KTime kt(c, MOE_K_PREP, st);
       HIPCHK(moe::launch_prep_pairs((const float *)c->h.p, P_all, c->f, (uint32_t *)c->hp.p,
-                                    (float *)c->hsw.p, (float *)c->hscale.p, st));
+                                    (float *)c->hscale.p, st));
       kt.end((double)P_all * c->f * 8.0);
     }
     moe::GemvArgs b = a;
@@ -477,7 +474,6 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
     b.rows = c->d;
     b.nb = (int)L.nb_dn;
     b.xp = (const uint32_t *)c->hp.p;
-    b.xsw = (const float *)c->hsw.p;
     b.xscale = (const float *)c->hscale.p;
     b.in_by_pair = 1;
     b.out = (float *)c->y.p;
@@ -566,7 +562,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
     a.h_flag = c->h_flag;
     a.seq = ++c->flag_seq;
     HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)c->z.p, nullptr,
-                              nullptr, nullptr, (uint4 *)c->xq.p, (float *)c->xs.p, st,
+                              nullptr, (uint4 *)c->xq.p, (float *)c->xs.p, st,
                               router_x ? (float *)c->h_x.p : nullptr));
     kt.end(4.0 * ((double)E * d + (double)T * d * 2 + (double)T * E + (router_bias ? E : 0)));
     KTime kt2(c, MOE_K_TOPK, st);
@@ -577,8 +573,8 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
       KTime kt(c, MOE_K_ROUTER, st);
       // the matrix-core GEMM takes binary16 pairs
       HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)c->z.p,
-                                (uint32_t *)c->xp.p, (float *)c->xsw.p, (float *)c->xscale.p,
-                                nullptr, (float *)c->xs.p, st));
+                                (uint32_t *)c->xp.p, (float *)c->xscale.p, nullptr,
+                                (float *)c->xs.p, st));
       kt.end(4.0 * ((double)E * d + (double)T * d * 2 + (double)T * E + (router_bias ? E : 0)));
     }
     KTime kt(c, MOE_K_TOPK, st);
@@ -617,11 +613,13 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
                      host_mode ? c->o.max_fills_per_call : -1, ly.plan);
   }
   ly.st.plan_s += now_s() - tp;
-  if (c->timing) {
+  if (c->kmask & ((1u << MOE_K_GATEUP) | (1u << MOE_K_DOWN))) {
     const double n_hit = (double)(ly.plan.stages[0].members.size() -
                                   (host_mode ? 0 : ly.plan.stages[0].fills.size())) + ns;
-    c->kt[MOE_K_GATEUP].bytes += n_hit * 2.0 * (double)c->f * (double)c->lay.nb_gu * 18.0;
-    c->kt[MOE_K_DOWN].bytes += n_hit * (double)c->d * (double)c->lay.nb_dn * 18.0;
+    if (c->kmask & (1u << MOE_K_GATEUP))
+      c->kt[MOE_K_GATEUP].bytes += n_hit * 2.0 * (double)c->f * (double)c->lay.nb_gu * 18.0;
+    if (c->kmask & (1u << MOE_K_DOWN))
+      c->kt[MOE_K_DOWN].bytes += n_hit * (double)c->d * (double)c->lay.nb_dn * 18.0;
   }
   bool combined = false;
   if (!host_mode && c->decode_ok(T)) {
@@ -857,6 +855,7 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
   c->f = d_ff;
   c->o = o;
   c->timing = o.timing != 0;
+  c->kmask = o.timing ? (1u << MOE_K_COUNT) - 1u : 0u;
   c->lay = moe::RecordLayout::make(d_model, d_ff);
   moe_status rc = guarded(nullptr, [&]() -> moe_status {
     HIPCHK(hipGetDevice(&c->device));
@@ -980,6 +979,15 @@ moe_status moe_cache_set_timing(moe_cache *c, int32_t on) {
   if (!c) return fail(MOE_EINVAL, "cache is NULL");
   if (on != 0 && on != 1) return fail(MOE_EINVAL, "on must be 0 or 1");
   c->timing = on != 0;
+  c->kmask = on ? (1u << MOE_K_COUNT) - 1u : 0u;
+  return MOE_OK;
+}
+
+moe_status moe_cache_set_kernel_timing(moe_cache *c, uint32_t kernel_mask) {
+  g_err.clear();
+  if (!c) return fail(MOE_EINVAL, "cache is NULL");
+  if (kernel_mask >> MOE_K_COUNT) return fail(MOE_EINVAL, "kernel_mask has bits past MOE_K_COUNT");
+  c->kmask = kernel_mask;
   return MOE_OK;
 }
 

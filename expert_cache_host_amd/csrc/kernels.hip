@@ -106,6 +106,37 @@ __device__ __forceinline__ uint4 digit_planes8(const float (&v)[8], float inv) {
   return make_uint4(p[0], p[1], p[2], p[3]);
 }
 
+// Smallest block maximum the 16-bit encoding scales by: keeps 30000 / m finite
+// (a block whose values all lie below it is encoded on this coarser scale).
+constexpr float kMinBlockMax = 0x1p-100f;
+
+// Digit planes of 8 values of one 32-element block with the block's own scale:
+// the block's four units sit in four consecutive active lanes (u % 4 = lane % 4),
+// which share their max through two xor shuffles.  X = rint(v * 30000 / m), the
+// scale m / 30000 goes to sb (0 for an all-zero block).
+__device__ __forceinline__ uint4 block_planes8(const float (&v)[8], float &sb) {
+  float m = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  m = fmaxf(m, __shfl_xor(m, 2, 64));
+  const float ms = fmaxf(m, kMinBlockMax);
+  sb = m > 0.0f ? ms / 30000.0f : 0.0f;
+  return digit_planes8(v, m > 0.0f ? 30000.0f / ms : 0.0f);
+}
+
+// Exponent e of the power-of-two scale 2^-e that brings a row maximum m into
+// [2^13, 2^14) before the binary16 hi/lo split (m = f 2^fe, f in [0.5, 1)), so
+// that every row keeps the split's 22 significant bits whatever its magnitude.
+// Clamped to [-126, 127] so that 2^e and 2^-e stay finite normal floats; 0 for
+// m = 0 or a non-finite m.
+__device__ __forceinline__ int pow2_exponent(float m) {
+  if (!(m > 0.0f) || !(m <= 3.4e38f)) return 0;
+  int fe;
+  (void)frexpf(m, &fe);
+  return min(127, max(-126, fe - 14));
+}
+
 // ============================================================== router logits
 // One wave per (expert, tile of TT tokens).  Lane l accumulates i = l, l+64, ...
 // with the product and the sum rounded separately (no contraction), then a
@@ -119,7 +150,6 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
                                                      const float *__restrict__ bias, int E,
                                                      float *__restrict__ z,
                                                      uint32_t *__restrict__ xp,
-                                                     float *__restrict__ xsw,
                                                      float *__restrict__ xscale,
                                                      uint4 *__restrict__ xq,
                                                      float *__restrict__ xs) {
@@ -187,25 +217,24 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
     const int t = t0 + tt;
     const float *xt = x + (long long)t * d;
     if (xq != nullptr) {
-      // decode GEMV input: digit planes of X = rint(x * 30000 / max|x|)
-      const float inv = m > 0.0f ? 30000.0f / m : 0.0f;
-      if (gid == 0) xs[t] = m / 30000.0f;
+      // decode GEMV input: digit planes with one scale per 32-element block.
+      // The four units of a block are four consecutive lanes (j = gid + stride
+      // * i, gid and stride multiples of 4 at lane 0, words a multiple of 8), all
+      // active together, so two xor shuffles give the block's max.
+      const int nbq = xs_units(d >> 5);
       for (int j = gid; j < words; j += stride) {
         const int b = j >> 2, wq = j & 3;
         const float4 a = *reinterpret_cast<const float4 *>(xt + b * 32 + 4 * wq);
         const float4 c = *reinterpret_cast<const float4 *>(xt + b * 32 + 16 + 4 * wq);
         const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-        xq[(long long)t * words + j] = digit_planes8(v, inv);
+        float sb;
+        const uint4 pl = block_planes8(v, sb);
+        if (wq == 0) xs[(long long)t * nbq * 4 + b] = sb;
+        xq[(long long)t * words + j] = pl;
       }
       continue;
     }
-    int ex2 = 0;
-    if (m > 0.0f && m <= 3.0e38f) {
-      // m = f * 2^fe with f in [0.5, 1) for normal m; a subnormal m gives a
-      // smaller fe, and ex2 = 0 either way
-      const int fe = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xFFu) - 126;
-      ex2 = max(0, fe - 14);
-    }
+    const int ex2 = pow2_exponent(m);
     const float sc = ldexpf(1.0f, -ex2);
     if (gid == 0) xscale[t] = ldexpf(1.0f, ex2);
     for (int j = gid; j < words; j += stride) {
@@ -230,7 +259,6 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
       uint4 *dst = reinterpret_cast<uint4 *>(xp + ((long long)t * words + j) * 8);
       dst[0] = hi;
       dst[1] = lo;
-      xsw[(long long)t * words + j] = ((e0 + e1) + (e2 + e3)) + ((f0 + f1) + (f2 + f3));
     }
   }
 }
@@ -255,14 +283,12 @@ __global__ __launch_bounds__(256) void router_decode_kernel(const float *__restr
                                                             float *__restrict__ xs, float *h_x) {
 #pragma clang fp contract(off)
   extern __shared__ float sprod[];  // [TT][d] products
-  __shared__ float smax[TT][4];
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int words = d >> 3;
   const float *wr = W + (long long)e * d;
-  float mx[TT], px[TT][8];
+  float px[TT][8];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
-    mx[tt] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) px[tt][i] = 0.0f;
   }
@@ -303,8 +329,6 @@ __global__ __launch_bounds__(256) void router_decode_kernel(const float *__restr
             s.w = c.w * q.w;
             *reinterpret_cast<float4 *>(sprod + tt * d + o) = r;
             *reinterpret_cast<float4 *>(sprod + tt * d + o + 16) = s;
-            mx[tt] = fmaxf(mx[tt], fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
-            mx[tt] = fmaxf(mx[tt], fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w))));
             if (mine) {
               px[tt][0] = a.x, px[tt][1] = a.y, px[tt][2] = a.z, px[tt][3] = a.w;
               px[tt][4] = c.x, px[tt][5] = c.y, px[tt][6] = c.z, px[tt][7] = c.w;
@@ -313,13 +337,6 @@ __global__ __launch_bounds__(256) void router_decode_kernel(const float *__restr
         }
       }
     }
-  }
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    float m = mx[tt];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    if (lane == 0) smax[tt][wave] = m;
   }
   __syncthreads();
   if (wave < T) {
@@ -334,16 +351,19 @@ __global__ __launch_bounds__(256) void router_decode_kernel(const float *__restr
     }
     if (lane == 0) z[(long long)wave * E + e] = bias ? p + bias[e] : p;
   }
-  // decode GEMV input: digit planes of X = rint(x * 30000 / max|x|)
+  // decode GEMV input: digit planes with one scale per 32-element block (the
+  // block's four units are four consecutive threads; words is a multiple of 8,
+  // so they pass the test below together)
   const int j = tid + 256 * e;
   if (j < words) {
+    const int nbq = xs_units(d >> 5);
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       if (tt >= T) break;
-      const float m = fmaxf(fmaxf(smax[tt][0], smax[tt][1]), fmaxf(smax[tt][2], smax[tt][3]));
-      const float inv = m > 0.0f ? 30000.0f / m : 0.0f;
-      if (j == 0) xs[tt] = m / 30000.0f;
-      xq[(long long)tt * words + j] = digit_planes8(px[tt], inv);
+      float sb;
+      const uint4 pl = block_planes8(px[tt], sb);
+      if ((j & 3) == 0) xs[(long long)tt * nbq * 4 + (j >> 2)] = sb;
+      xq[(long long)tt * words + j] = pl;
       if (h_x != nullptr) {
         const int o = (j >> 2) * 32 + (j & 3) * 4;
         float *hx = h_x + (long long)tt * d + o;
@@ -363,7 +383,7 @@ bool router_decode_fits(int T, int d, int E) {
 }
 
 hipError_t launch_router(const float *x, int T, int d, const float *W, const float *bias, int E,
-                         float *z, uint32_t *xp, float *xsw, float *xscale, uint4 *xq, float *xs,
+                         float *z, uint32_t *xp, float *xscale, uint4 *xq, float *xs,
                          hipStream_t s, float *h_x) {
   const int tt = T <= 1 ? 1 : (T <= 2 ? 2 : 4);
   const size_t lds = (size_t)tt * d * 4;
@@ -383,13 +403,13 @@ hipError_t launch_router(const float *x, int T, int d, const float *W, const flo
   const int gx = (E + 3) / 4;
   if (T <= 1) {
     hipLaunchKernelGGL((router_kernel<1, 32>), dim3(gx, T), dim3(256), 0, s, x, T, d, W, bias, E,
-                       z, xp, xsw, xscale, xq, xs);
+                       z, xp, xscale, xq, xs);
   } else if (T <= 4) {
     hipLaunchKernelGGL((router_kernel<4, 16>), dim3(gx, 1), dim3(256), 0, s, x, T, d, W, bias, E,
-                       z, xp, xsw, xscale, xq, xs);
+                       z, xp, xscale, xq, xs);
   } else {
     hipLaunchKernelGGL((router_kernel<8, 8>), dim3(gx, (T + 7) / 8), dim3(256), 0, s, x, T, d, W,
-                       bias, E, z, xp, xsw, xscale, xq, xs);
+                       bias, E, z, xp, xscale, xq, xs);
   }
   return hipGetLastError();
 }
@@ -662,7 +682,8 @@ hipError_t launch_remap(const int32_t *idx, int T, int k, const SlotView &view, 
 
 // ============================================================== decode GEMV arithmetic
 // Activations enter the decode GEMV as 16-bit fixed point: X = rint(v / s) with
-// s = max|v| / 30000 (per token for x, per 32-element block for h), split into
+// one scale per 32-element block, s = max|v over the block| / 30000 (for x and
+// for h alike, so that one large channel costs only its own block), split into
 // four signed base-16 digits c_0..c_3 in [-8, 7], X = sum_k 16^k c_k.  For
 // X + 0x8888 the digit nibbles are those of ((X + 0x8888) ^ 0x8888), so no
 // carry chain is needed.  A digit plane is laid out like the weights' nibble
@@ -671,7 +692,7 @@ hipError_t launch_remap(const int32_t *idx, int T, int k, const SlotView &view, 
 // signed nibbles q - 8, so one v_dot8_i32_i4 per (word, plane) accumulates
 // sum (q - 8) c_k exactly, and the four planes meet with shifts by 4 bits:
 // I = sum_i (q_i - 8) X_i, |I| <= 32 * 8 * 34952 < 2^24, exact in int32 and in
-// its float32 conversion.  A block then contributes d * I (* s for h blocks).
+// its float32 conversion.  A block then contributes d * s * I.
 
 // sum over one block of (q - 8) * X, X given as digit planes P[word].{x,y,z,w}
 __device__ __forceinline__ int dot_block_i4(const uint4 &w, const uint4 (&P)[4]) {
@@ -786,8 +807,8 @@ __device__ __forceinline__ int scale_chunks(int rows_here, int nb) {
   return (rows_here * nb * 2 + 15) / 16;
 }
 
-// gate/up + SwiGLU.  LDS: the bucket's x planes [TT][nb][4], then the gate and
-// the up scales of the workgroup's rows.
+// gate/up + SwiGLU.  LDS: the bucket's x planes [TT][nb][4], its x block scales
+// [TT][4 * xs_units(nb)], then the gate and the up scales of the workgroup's rows.
 template <int G, int KS, int R, int TT, int MODE, int NW, int PF>
 __global__ __launch_bounds__(64 * NW) void q4_gateup_kernel(GemvArgs a, BucketTable tab) {
   constexpr int RW = 64 / G;
@@ -823,18 +844,28 @@ __global__ __launch_bounds__(64 * NW) void q4_gateup_kernel(GemvArgs a, BucketTa
   }
   const int NI = (nb + G * KS - 1) / (G * KS);
   auto blk_of = [&](int it) { return min(gl + G * (ks + KS * it), nb - 1); };
-  // staging: x planes, gate scales, up scales, as one run of 16-byte units
-  const int n_x = TT * nb * 4, n_s = scale_chunks(rows_here, nb);
-  const int n_stage = n_x + 2 * n_s;
+  // staging: x planes, x block scales, gate scales, up scales, as one run of
+  // 16-byte units
+  const int nbq = xs_units(nb);
+  const int n_x = TT * nb * 4, n_xs = TT * nbq, n_s = scale_chunks(rows_here, nb);
+  const int n_stage = n_x + n_xs + 2 * n_s;
+  const uint4 *xs4 = reinterpret_cast<const uint4 *>(a.xs);
+  auto row_of = [&](int tt) {
+    return TT <= 2 ? pick(tok, tt) : pair_row(a, pair_at<TT, MODE>(a, tab, blockIdx.y, bk, tt));
+  };
   auto stage_ld = [&](int u) -> uint4 {
     u = min(u, n_stage - 1);
     if (u < n_x) {
       const int tt = u / (nb * 4);
-      const int row =
-          TT <= 2 ? pick(tok, tt) : pair_row(a, pair_at<TT, MODE>(a, tab, blockIdx.y, bk, tt));
-      return a.xq[(long long)row * nb * 4 + (u - tt * nb * 4)];
+      return a.xq[(long long)row_of(tt) * nb * 4 + (u - tt * nb * 4)];
     }
-    return u < n_x + n_s ? c0[u - n_x] : c1[u - n_x - n_s];
+    u -= n_x;
+    if (u < n_xs) {
+      const int tt = u / nbq;
+      return xs4[(long long)row_of(tt) * nbq + (u - tt * nbq)];
+    }
+    u -= n_xs;
+    return u < n_s ? c0[u] : c1[u - n_s];
   };
   uint4 xv[kStageChunks];
 #pragma unroll
@@ -864,8 +895,9 @@ __global__ __launch_bounds__(64 * NW) void q4_gateup_kernel(GemvArgs a, BucketTa
       if (u0 + tid + NT * c < n_stage) sx[u0 + tid + NT * c] = yv[c];
   }
   __syncthreads();
-  const _Float16 *sg = reinterpret_cast<const _Float16 *>(sx + n_x);
-  const _Float16 *su = reinterpret_cast<const _Float16 *>(sx + n_x + n_s);
+  const float *sxs = reinterpret_cast<const float *>(sx + n_x);
+  const _Float16 *sg = reinterpret_cast<const _Float16 *>(sx + n_x + n_xs);
+  const _Float16 *su = reinterpret_cast<const _Float16 *>(sx + n_x + n_xs + n_s);
   float ag[R][TT], au[R][TT];
 #pragma unroll
   for (int i = 0; i < R; ++i)
@@ -907,10 +939,11 @@ __global__ __launch_bounds__(64 * NW) void q4_gateup_kernel(GemvArgs a, BucketTa
           uint4 P[4];
 #pragma unroll
           for (int w = 0; w < 4; ++w) P[w] = sx[(tt * nb + j) * 4 + w];
+          const float se = sxs[tt * nbq * 4 + j];
 #pragma unroll
           for (int i = 0; i < R; ++i) {
-            ag[i][tt] = __builtin_fmaf((float)dot_block_i4(cw[i], P), dg[i], ag[i][tt]);
-            au[i][tt] = __builtin_fmaf((float)dot_block_i4(cv[i], P), du[i], au[i][tt]);
+            ag[i][tt] = __builtin_fmaf((float)dot_block_i4(cw[i], P) * se, dg[i], ag[i][tt]);
+            au[i][tt] = __builtin_fmaf((float)dot_block_i4(cv[i], P) * se, du[i], au[i][tt]);
           }
         }
       }
@@ -947,8 +980,7 @@ __global__ __launch_bounds__(64 * NW) void q4_gateup_kernel(GemvArgs a, BucketTa
         uu += red[g * KS + q][rr][tt][1];
       }
       const int p = pair_at<TT, MODE>(a, tab, blockIdx.y, bk, tt);
-      const float sc = a.xs[pair_row(a, p)];
-      a.out[(long long)p * a.rows + r] = silu_f(gg * sc) * (uu * sc);
+      a.out[(long long)p * a.rows + r] = silu_f(gg) * uu;
     }
   }
 }
@@ -1009,16 +1041,11 @@ __global__ __launch_bounds__(64 * NW) void q4_down_kernel(GemvArgs a, BucketTabl
       const int u = u0 + tid + NT * c;
       if (u0 + NT * c >= n_units) break;  // uniform
       const float v[8] = {v0[c].x, v0[c].y, v0[c].z, v0[c].w, v1[c].x, v1[c].y, v1[c].z, v1[c].w};
-      float m = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
-      m = fmaxf(m, __shfl_xor(m, 1, 64));
-      m = fmaxf(m, __shfl_xor(m, 2, 64));
-      const float inv = m > 0.0f ? 30000.0f / m : 0.0f;
-      const uint4 pl = digit_planes8(v, inv);
+      float sb;
+      const uint4 pl = block_planes8(v, sb);
       if (u < n_units) {
         sh[u] = pl;
-        if ((u & 3) == 0) sscale[u >> 2] = m / 30000.0f;
+        if ((u & 3) == 0) sscale[u >> 2] = sb;
       }
     }
   };
@@ -1153,7 +1180,7 @@ GemvShape choose_gemv(bool glu, int nb, int tokens) {
 size_t gemv_lds_bytes(bool glu, int nb, int tokens) {
   const GemvShape sh = choose_gemv(glu, nb, tokens);
   const size_t row_scales = ((size_t)sh.rows_wg * nb * 2 + 15) / 16 * 16;
-  if (glu) return (size_t)sh.TT * nb * 64 + 2 * row_scales;
+  if (glu) return (size_t)sh.TT * nb * 64 + (size_t)sh.TT * xs_units(nb) * 16 + 2 * row_scales;
   return (size_t)sh.TT * nb * 64 + ((size_t)sh.TT * nb + 3) / 4 * 16 + row_scales;
 }
 
@@ -1514,7 +1541,6 @@ hipError_t launch_mfma(const GemvArgs &a, bool glu, int n_items, hipStream_t s) 
 // One wave per row: scale, binary16 hi/lo pairs in the decoder's order, word sums.
 __global__ __launch_bounds__(64) void prep_pairs_kernel(const float *__restrict__ in, int rows, int K,
                                                         uint32_t *__restrict__ xp,
-                                                        float *__restrict__ xsw,
                                                         float *__restrict__ xscale) {
   const int r = blockIdx.x, lane = threadIdx.x;
   if (r >= rows) return;
@@ -1523,12 +1549,7 @@ __global__ __launch_bounds__(64) void prep_pairs_kernel(const float *__restrict_
   for (int i = lane; i < K; i += 64) m = fmaxf(m, fabsf(xt[i]));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  int ex2 = 0;
-  if (m > 0.0f && m <= 3.0e38f) {
-    int fe;
-    (void)frexpf(m, &fe);
-    ex2 = max(0, fe - 14);
-  }
+  const int ex2 = pow2_exponent(m);
   const float sc = ldexpf(1.0f, -ex2);
   if (lane == 0) xscale[r] = ldexpf(1.0f, ex2);
   const int words = K / 8;
@@ -1554,14 +1575,13 @@ __global__ __launch_bounds__(64) void prep_pairs_kernel(const float *__restrict_
     uint4 *dst = reinterpret_cast<uint4 *>(xp + ((long long)r * words + j) * 8);
     dst[0] = hi;
     dst[1] = lo;
-    xsw[(long long)r * words + j] = ((e0 + e1) + (e2 + e3)) + ((f0 + f1) + (f2 + f3));
   }
 }
 
-hipError_t launch_prep_pairs(const float *in, int rows, int K, uint32_t *xp, float *xsw,
-                             float *xscale, hipStream_t s) {
+hipError_t launch_prep_pairs(const float *in, int rows, int K, uint32_t *xp, float *xscale,
+                             hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(prep_pairs_kernel, dim3(rows), dim3(64), 0, s, in, rows, K, xp, xsw, xscale);
+  hipLaunchKernelGGL(prep_pairs_kernel, dim3(rows), dim3(64), 0, s, in, rows, K, xp, xscale);
   return hipGetLastError();
 }
 

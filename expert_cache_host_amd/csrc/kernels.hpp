@@ -19,21 +19,27 @@ struct SlotView {
   int16_t slot[kMaxExperts];
 };
 
+// 16-byte units of one token's decode block scales: nb floats padded to a
+// multiple of 4 (the row stride of xs is 4 * xs_units(nb) floats).
+inline constexpr int xs_units(int nb) { return (nb + 3) / 4; }
+
 // z[t][e] = x[t] . W[e] (+ b[e]) in the fixed fp32 order.  The waves also
 // prepare each token's x for the expert kernels, in one of two forms:
-// - xq != nullptr (decode GEMV): digit planes of X = rint(x / s), s = max|x| / 30000
-//   (xs[t] = s); per block b and word j, xq[(t*d/32 + b)*4 + j] holds planes 0..3
-//   as x, y, z, w (the layout is described with the decode GEMV);
-// - xp != nullptr (matrix-core GEMM): a power-of-two scale 2^-e that keeps |x|
-//   below 2^14 (xscale[t] = 2^e); the scaled x as binary16 hi and lo pairs in
-//   the order the nibble decoder yields weights (for 32-bit word j of block
-//   b = j/4 and g = 4*(j%4): (x[g],x[g+2]), (x[g+16],x[g+18]), (x[g+1],x[g+3]),
-//   (x[g+17],x[g+19]) of the block, hi then lo); and the sum of each word's 8
-//   scaled values (xsw).
+// - xq != nullptr (decode GEMV): digit planes of X = rint(x / s) with one scale
+//   per 32-element block b, s = max|x over the block| / 30000 (xs[t][b], row
+//   stride 4 * xs_units(d/32)); per block b and word j,
+//   xq[(t*d/32 + b)*4 + j] holds planes 0..3 as x, y, z, w (the layout is
+//   described with the decode GEMV);
+// - xp != nullptr (matrix-core GEMM): a power-of-two scale 2^-e that brings
+//   max|x| into [2^13, 2^14) (xscale[t] = 2^e, e in [-126, 127]); the scaled x
+//   as binary16 hi and lo pairs in the order the nibble decoder yields weights
+//   (for 32-bit word j of block b = j/4 and g = 4*(j%4): (x[g],x[g+2]),
+//   (x[g+16],x[g+18]), (x[g+1],x[g+3]), (x[g+17],x[g+19]) of the block, hi then
+//   lo).
 // h_x (decode planes only, when router_decode_fits): page-locked host copy of
 // x [T][d], visible to the host once a later kernel raises its flag.
 hipError_t launch_router(const float *x, int T, int d, const float *W, const float *bias, int E,
-                         float *z, uint32_t *xp, float *xsw, float *xscale, uint4 *xq, float *xs,
+                         float *z, uint32_t *xp, float *xscale, uint4 *xq, float *xs,
                          hipStream_t s, float *h_x = nullptr);
 // The one-workgroup-per-expert decode router handles this call.
 bool router_decode_fits(int T, int d, int E);
@@ -95,9 +101,8 @@ hipError_t launch_remap(const int32_t *idx, int T, int k, const SlotView &view, 
 struct GemvArgs {
   const uint8_t *slots;  // slot arena of the layer
   const uint4 *xq;       // decode gate/up: digit planes of x [T][d/32][4]
-  const float *xs;       // decode gate/up: scale per token
+  const float *xs;       // decode gate/up: block scales [T][4 * xs_units(d/32)]
   const uint32_t *xp;    // matrix-core gate/up: activation pairs [T][d/8][8]
-  const float *xsw;      // matrix-core gate/up: per-word sums [T][d/8]
   const float *xscale;   // matrix-core gate/up: 2^e per token
   long long rec_bytes;   // slot stride
   long long off_q0, off_s0;  // nibbles / scales of the first matrix in a record
@@ -145,7 +150,8 @@ GemvShape choose_gemv(bool glu, int nb, int tokens);
 size_t gemv_lds_bytes(bool glu, int nb, int tokens);
 
 // Decode GEMV over Q4 slot records with 4-bit integer dot products.  glu = 1:
-// out[pair][r] = silu(G x) * (U x) from the router's digit planes (xq, xs);
+// out[pair][r] = silu(G x) * (U x) from the router's digit planes and block
+// scales (xq, xs);
 // glu = 0: out[pair][r] = (D h)[r] with h = in[pair] (fp32), turned into digit
 // planes with one scale per 32-element block inside each workgroup.  Buckets
 // come from *tab when tab != nullptr, else from the list at a.bt; a grid of
@@ -157,20 +163,19 @@ hipError_t launch_gemv(const GemvArgs &a, const BucketTable *tab, const GemvShap
 // Work items from launch_remap; per workgroup 64 weight rows of one bucket's
 // expert and one pass of up to kGemmTokens of its tokens.  Each wave streams its
 // 16 rows' nibbles through registers (two K chunks in flight) and decodes them
-// to binary16 (1024 + q) A operands; activations come as binary16 hi/lo pairs in
-// the same K order (xp / xsw / xscale as prepared for the gate/up GEMV, indexed
+// to exact binary16 (q - 8) A operands; activations come as binary16 hi/lo pairs
+// in the same K order (xp / xscale as prepared for the gate/up GEMM, indexed
 // by token for gate/up and by pair for down), staged per chunk in LDS.  Each
 // 32-weight block is one pair of v_mfma_f32_16x16x32_f16 (hi, lo) per 16-token
-// tile, and its scale and the 1032 * sum(x) offset are applied per block in
-// fp32.  glu: out[p][r] = silu(g) * u; else out = M in.  A grid of n_items
-// columns covers at most that many work items (more than 65535:
-// hipErrorInvalidValue).
+// tile, and its scale is applied per block in fp32.  glu: out[p][r] =
+// silu(g) * u; else out = M in.  A grid of n_items columns covers at most that
+// many work items (more than 65535: hipErrorInvalidValue).
 hipError_t launch_mfma(const GemvArgs &a, bool glu, int n_items, hipStream_t s);
 
-// Binary16 hi/lo pairs, word sums and power-of-two scale of `rows` float rows of
-// length K (the preparation the router does for x), for the down GEMM's input h.
-hipError_t launch_prep_pairs(const float *in, int rows, int K, uint32_t *xp, float *xsw,
-                             float *xscale, hipStream_t s);
+// Binary16 hi/lo pairs and power-of-two scale of `rows` float rows of length K
+// (the preparation the router does for x), for the down GEMM's input h.
+hipError_t launch_prep_pairs(const float *in, int rows, int K, uint32_t *xp, float *xscale,
+                             hipStream_t s);
 
 // Copies n expert records (bytes16 x 16 bytes each) from the page-locked host
 // arena into device slots; `per_expert` workgroups each read one contiguous

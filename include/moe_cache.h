@@ -236,6 +236,14 @@ moe_status moe_cache_set_timing(moe_cache *c, int32_t on);
 #define MOE_K_PREP 7    /* binary16 hi/lo preparation of h for the prefill down GEMM */
 #define MOE_K_COUNT 8
 
+/* Times only the kernels whose bit (1 << MOE_K_*) is set in kernel_mask, one
+ * launch at a time, from now on; the per-layer compute and fill timings of
+ * moe_cache_set_timing stay as they are.  moe_cache_set_timing(c, 1) sets every
+ * bit, (c, 0) clears them.  Each timed launch costs two event records on its
+ * stream (host time on the calling thread), so a narrow mask perturbs the
+ * calls least.  MOE_EINVAL for bits at or past MOE_K_COUNT. */
+moe_status moe_cache_set_kernel_timing(moe_cache *c, uint32_t kernel_mask);
+
 /* Launches, summed device seconds (HIP events on the launching stream, read
  * when this is called) and summed algorithmic bytes of kernel `kernel` since the
  * last reset.  Algorithmic bytes: router = W_r + x + logits; Q4 kernels = the

@@ -28,10 +28,11 @@ def decode_blocks(raw: np.ndarray) -> np.ndarray:
         raise ValueError("last axis must hold 18-byte blocks")
     d = raw[..., 0:2].copy().view("<f2")[..., 0].astype(np.float64)
     qs = raw[..., 2:18]
-    lo = (qs & 0x0F).astype(np.int64)
-    hi = (qs >> 4).astype(np.int64)
-    q = np.concatenate([lo, hi], axis=-1)          # elements 0..15 then 16..31
-    return d[..., None] * (q - 8).astype(np.float64)
+    q = np.empty(raw.shape[:-1] + (BLOCK,), dtype=np.int8)
+    q[..., :16] = qs & 0x0F                        # elements 0..15: low nibbles
+    q[..., 16:] = qs >> 4                          # elements 16..31: high nibbles
+    q -= 8                                         # q - 8 in [-8, 7]
+    return d[..., None] * q                        # float64, exact
 
 
 def decode_matrix(buf: np.ndarray, rows: int, cols: int) -> np.ndarray:
@@ -46,15 +47,3 @@ def decode_matrix(buf: np.ndarray, rows: int, cols: int) -> np.ndarray:
 
 def expert_nbytes(d_model: int, d_ff: int) -> int:
     return 3 * d_model * d_ff // BLOCK * BLOCK_BYTES
-
-
-def expert_matrices(buf: np.ndarray, expert: int, d_model: int, d_ff: int):
-    """(G [f,d], U [f,d], D [d,f]) in float64 for `expert` of a layer buffer."""
-    eb = expert_nbytes(d_model, d_ff)
-    gu = d_ff * d_model // BLOCK * BLOCK_BYTES
-    base = expert * eb
-    b = np.asarray(buf, dtype=np.uint8)
-    g = decode_matrix(b[base:base + gu], d_ff, d_model)
-    u = decode_matrix(b[base + gu:base + 2 * gu], d_ff, d_model)
-    dn = decode_matrix(b[base + 2 * gu:base + eb], d_model, d_ff)
-    return g, u, dn

@@ -454,3 +454,160 @@ def test_calls_alternating_between_two_streams(mode):
         r.sims[li].plan(ref["idx"].ravel().tolist(), mode, -1, tokens=1)
     r.check_log()
     r.close()
+
+
+# ---------------------------------------------------------------- activation corners
+# The decode GEMV encodes activations as 16-bit fixed point with one scale per
+# 32-element block; the matrix-core GEMM splits them into binary16 hi/lo parts
+# after a power-of-two row scale.  Inputs with one large channel, and inputs far
+# from unit scale, must still meet the bar (tolerance unchanged).
+
+def _with_outlier(x, factor, ch=701):
+    x = np.array(x, copy=True)
+    x[..., ch] *= factor
+    return x
+
+
+@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("outlier", [10, 100, 1000])
+def test_decode_outlier_channel_gemma_shape(T, outlier):
+    """Gemma-like expert shape, one hidden channel at 10x-1000x the rest, decode
+    calls of 1 and 4 tokens (the one-workgroup-per-expert router prepares x)."""
+    wl = synth.Workload("outlier", 60, 1, 2816, 704, 128, 8, 32, router_sigma=1.6 / np.sqrt(2816),
+                        zipf_s=1.1, rho=0.8, tokens=4, batch=T, weight_wid=2)
+    log(f"decode outlier channel x{outlier}, T={T}, Gemma-like shape")
+    r = Runner(wl, [0], mode="host")
+    x = synth.gen_hidden(wl, 0, 4)
+    for c in range(x.shape[0]):
+        r.call(0, _with_outlier(x[c], outlier))
+    r.check_log()
+    r.close()
+
+
+@pytest.mark.parametrize("outlier", [100, 1000])
+def test_decode_outlier_channel_tiled_router(outlier):
+    """d_model 6144 at 4 tokens: the tokens' products exceed the decode router's
+    LDS, so the tiled router prepares the block-scaled planes."""
+    wl = synth.Workload("outlier6144", 61, 1, 6144, 256, 16, 4, 8, n_shared=1,
+                        router_sigma=1.6 / np.sqrt(6144), zipf_s=1.0, rho=0.8, tokens=4, batch=4)
+    log(f"decode outlier channel x{outlier}, T=4, d_model 6144 (tiled router)")
+    r = Runner(wl, [0], mode="stream")
+    x = synth.gen_hidden(wl, 0, 4)
+    for c in range(x.shape[0]):
+        r.call(0, _with_outlier(x[c], outlier, ch=4097))
+    r.check_log()
+    r.close()
+
+
+@pytest.mark.parametrize("scale", [2.0 ** -20, 2.0 ** 20])
+@pytest.mark.parametrize("mode", ["stream", "host"])
+def test_matrix_core_extreme_scales(scale, mode):
+    """17-token calls (matrix-core GEMM) on inputs scaled by 2^-20 and 2^20."""
+    wl = synth.Workload("rag", 11, 1, 256, 512, 16, 4, 6, n_shared=1, router_sigma=0.1,
+                        zipf_s=0.5, rho=None, tokens=17 * 4, batch=17)
+    log(f"matrix-core path, T=17, inputs x {scale:g}, mode={mode}")
+    r = Runner(wl, [0], mode=mode)
+    x = synth.gen_hidden(wl, 0)
+    for c in range(x.shape[0]):
+        r.call(0, (x[c] * scale).astype(np.float32))
+    r.check_log()
+    r.close()
+
+
+@pytest.mark.parametrize("scale", [2.0 ** -20, 1.0 / 3000.0])
+def test_decode_extreme_scales(scale):
+    """Decode calls on inputs far below unit scale (the block scales follow)."""
+    wl = synth.Workload("outlier", 60, 1, 2816, 704, 128, 8, 32, router_sigma=1.6 / np.sqrt(2816),
+                        zipf_s=1.1, rho=0.8, tokens=4, batch=1, weight_wid=2)
+    log(f"decode, inputs x {scale:g}")
+    r = Runner(wl, [0], mode="stream")
+    x = synth.gen_hidden(wl, 0, 4)
+    for c in range(x.shape[0]):
+        r.call(0, (x[c] * scale).astype(np.float32))
+    r.check_log()
+    r.close()
+
+
+def test_prefill_ubatch_small_scale_sampled():
+    wl = synth.WORKLOADS["prefill"]
+    log("prefill shape, 1 ubatch of 512 scaled by 2^-20, sampled tokens and columns")
+    r = Runner(wl, [1])
+    x = (synth.gen_hidden(wl, 1, 1)[0] * 2.0 ** -20).astype(np.float32)
+    rng = np.random.default_rng(3)
+    toks = np.sort(rng.choice(512, 6, replace=False))
+    cols = rng.choice(wl.d_model, 96, replace=False)
+    _, res = r.call(0, x, tok_sample=toks, col_sample=cols)
+    assert len(res.stage_views) >= 4
+    r.check_log()
+    r.close()
+
+
+def _prefill_check_tokens(idx, k):
+    """32 tokens of a 512-token ubatch: one in every 32-token pass of the shared
+    expert (whose bucket holds all 512 tokens), and 16 that sit in the second
+    16-token tile of a routed expert's bucket (bucket position >= 16: pairs are
+    bucketed in ascending (token, rank) order)."""
+    T = idx.shape[0]
+    toks = [32 * p + (7 * p) % 32 for p in range(T // 32)]
+    counts = np.bincount(idx.ravel(), minlength=idx.max() + 1)
+    second = []
+    for e in np.argsort(-counts, kind="stable"):
+        if counts[e] < 17 or len(second) >= 16:
+            break
+        members = np.nonzero((idx == e).any(axis=1))[0]
+        for t in members[16:20]:
+            if int(t) not in toks and int(t) not in second:
+                second.append(int(t))
+    assert len(second) >= 8, "no routed bucket with a second 16-token tile"
+    return np.array(sorted(set(toks) | set(second[:16])))
+
+
+def test_prefill_ubatch_all_columns():
+    """One 512-token ubatch through 64 slots (4+ stages), all 6144 output
+    columns of 32 tokens: every 32-token pass of the shared expert and the
+    second 16-token tiles of the largest routed buckets."""
+    from oracle.routing import topk
+    wl = synth.WORKLOADS["prefill"]
+    log("prefill shape, 1 ubatch of 512, all columns of 32 tokens")
+    r = Runner(wl, [0])
+    x = synth.gen_hidden(wl, 0, 1)[0]
+    w_r, b, _, _ = r.routers[0]
+    toks = _prefill_check_tokens(topk(router_logits_fp32(x, w_r, b), wl.top_k), wl.top_k)
+    assert len(toks) >= 24
+    log(f"  checking tokens {toks.tolist()}")
+    _, res = r.call(0, x, tok_sample=toks)
+    assert len(res.stage_views) >= 4
+    r.check_log()
+    r.close()
+
+
+def test_gemma_shape_host_lru_two_layers():
+    """The Gemma-like decode as benchmarked: host misses, LRU, two layers called
+    token-major for 16 calls; every call's output against the oracle."""
+    wl = synth.WORKLOADS["gemma"]
+    log("gemma shape, host misses, LRU, 2 layers x 16 calls")
+    r = Runner(wl, [3, 11], mode="host", keep_debug=True)
+    xs = [synth.gen_hidden(wl, l, 16) for l in (3, 11)]
+    saw_host = False
+    for t in range(16):
+        for li in range(2):
+            out, res = r.call(li, xs[li][t])
+            g, h = r.cache.partials(li)
+            np.testing.assert_array_equal(g + h, out)
+            saw_host |= res.misses > 0
+    assert saw_host
+    r.check_log()
+    r.close()
+
+
+def test_large_host_lru_all_columns():
+    """The large-expert decode as benchmarked (host misses, LRU, shared expert):
+    8 calls of one layer, every output column."""
+    wl = synth.WORKLOADS["large"]
+    log("large shape, host misses, LRU, 1 layer x 8 calls, all columns")
+    r = Runner(wl, [5], mode="host")
+    x = synth.gen_hidden(wl, 5, 8)
+    for t in range(8):
+        r.call(0, x[t])
+    r.check_log()
+    r.close()
