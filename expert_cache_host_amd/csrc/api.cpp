@@ -30,6 +30,7 @@
 #include "kernels.hpp"
 #include "layout.hpp"
 #include "planner.hpp"
+#include "workspace.hpp"
 
 namespace {
 
@@ -190,10 +191,8 @@ struct moe_cache {
   bool poisoned = false;
   bool timing = false;   // per-layer compute and fill events
   uint32_t kmask = 0;    // kernels timed one launch at a time (bit MOE_K_*)
-  // device workspace
-  int32_t cap_T = 0;
-  DevBuf z, idx, w, meta, bucket_pair, items, h, y, xp, xscale, hp, hscale, xq, xs;
-  DevBuf buckets, pair_slot;  // decode: bucket list and pair -> slot of the hits
+  // device workspace of moe_layer_forward (grown on demand)
+  DevBuf arena;
   // stream of the last call: the workspace above is shared by every layer
   hipStream_t last_stream = nullptr;
   bool called = false;
@@ -203,16 +202,13 @@ struct moe_cache {
   bool partial_used[2] = {false, false};
   int partial_cur = 0;
   std::vector<float> h_scratch;
+  // host-mode bookkeeping, reused across calls
+  std::vector<moe::HostExpertJob> jobs;
+  std::vector<int32_t> job_of, rank_job;
   std::unique_ptr<moe::ThreadPool> pool;
 
   size_t rec() const { return (size_t)lay.bytes; }
-  // T tokens per call take the decode GEMV (workgroups find their own buckets)
-  bool decode_ok(int32_t T) const {
-    constexpr size_t kLdsBudget = 60 * 1024;  // dynamic LDS per workgroup
-    return T <= moe::kDecodeMaxTokens && T * (o.top_k + o.n_shared) <= moe::kDecodeMaxPairs &&
-           moe::gemv_lds_bytes(true, (int)lay.nb_gu, T) <= kLdsBudget &&
-           moe::gemv_lds_bytes(false, (int)lay.nb_dn, T) <= kLdsBudget;
-  }
+  moe::WsParams ws_params(int32_t T) const { return {T, E, o.top_k, o.n_shared, d, f}; }
   int32_t n_total() const { return E + o.n_shared; }
   const uint8_t *host_record(int32_t l, int32_t e) const {
     return h_arena + ((size_t)l * n_total() + e) * rec();
@@ -241,45 +237,52 @@ struct moe_cache {
       if (sd) (void)hipStreamDestroy(sd);
   }
 
-  void ensure_ws(int32_t T) {
-    if (T <= cap_T) return;
+  // Page-locked buffers of a call of T tokens: the routing copy and, in host
+  // mode, the x copy and the two alternating host partials.
+  bool pinned_fits(int32_t T) const {
+    const size_t nk = (size_t)T * o.top_k * 4, nx = (size_t)T * d * 4;
+    if (h_idx.bytes < nk || h_w.bytes < nk) return false;
+    if (o.miss_mode == MOE_MISS_HOST)
+      return h_x.bytes >= nx && partial[0].bytes >= nx && partial[1].bytes >= nx;
+    return true;
+  }
+  // Grows them (waiting for the device first: earlier calls may still use them).
+  void ensure_pinned(int32_t T) {
+    if (pinned_fits(T)) return;
     HIPCHK(hipDeviceSynchronize());
-    const size_t k = (size_t)o.top_k;
-    const size_t P = (size_t)T * k + (size_t)T * o.n_shared;
-    z.ensure((size_t)T * E * 4);
-    idx.ensure((size_t)T * k * 4);
-    w.ensure((size_t)T * k * 4);
-    meta.ensure((size_t)moe::kMetaInts * 4);
-    bucket_pair.ensure(P * 4);
-    items.ensure(((size_t)moe::gemm_items_bound(moe::kMetaB, (int)P) + 1) * 4);
-    h.ensure(P * (size_t)f * 4);
-    y.ensure(P * (size_t)d * 4);
-    xp.ensure((size_t)T * d * 4);
-    xscale.ensure((size_t)T * 4);
-    xq.ensure((size_t)T * d * 2);
-    xs.ensure((size_t)T * moe::xs_units(d / 32) * 16);
-    buckets.ensure((size_t)(1 + moe::kDecodeMaxPairs * moe::kBucketInts) * 4);
-    pair_slot.ensure((size_t)moe::kDecodeMaxPairs * 4);
-    // h as binary16 pairs for the matrix-core down GEMM: every call that does
-    // not take the decode path (a call of up to kDecodeMaxTokens tokens takes
-    // the matrix cores too when its pairs or its LDS do not fit the decode
-    // GEMV).  decode_ok only turns false as T grows, so the buffers sized at the
-    // largest T seen serve every smaller matrix-core call.
-    if (!decode_ok(T)) {
-      hp.ensure(P * (size_t)f * 4);
-      hscale.ensure(P * 4);
-    }
-    h_idx.ensure((size_t)T * k * 4);
-    h_w.ensure((size_t)T * k * 4);
+    const size_t nk = (size_t)T * o.top_k * 4, nx = (size_t)T * d * 4;
+    h_idx.ensure(nk);
+    h_w.ensure(nk);
     if (o.miss_mode == MOE_MISS_HOST) {
-      h_x.ensure((size_t)T * d * 4);
-      for (auto &pb : partial) pb.ensure((size_t)T * d * 4);
+      h_x.ensure(nx);
+      for (auto &pb : partial) pb.ensure(nx);
     }
-    cap_T = T;
+  }
+  void ensure_arena(size_t bytes) {
+    if (bytes <= arena.bytes) return;
+    HIPCHK(hipDeviceSynchronize());
+    arena.ensure(bytes);
   }
 };
 
 namespace {
+
+// Device pointers of one call's workspace, carved from `base` by its layout.
+struct Ws {
+  void *z, *idx, *w, *h, *y;
+  void *xq, *xs, *buckets, *pair_slot;
+  void *meta, *bucket_pair, *items, *xp, *xscale, *hp, *hscale;
+};
+
+Ws carve(void *base, const moe::WsLayout &L) {
+  auto at = [&](const moe::WsRegion &r) -> void * {
+    return r.bytes ? (void *)((uint8_t *)base + r.off) : nullptr;
+  };
+  return Ws{at(L.z),    at(L.idx),         at(L.w),     at(L.h),  at(L.y),
+            at(L.xq),   at(L.xs),          at(L.buckets), at(L.pair_slot),
+            at(L.meta), at(L.bucket_pair), at(L.items), at(L.xp), at(L.xscale),
+            at(L.hp),   at(L.hscale)};
+}
 
 moe::SlotView make_view(const std::vector<int32_t> &table) {
   moe::SlotView v;
@@ -395,52 +398,37 @@ void wait_fills(moe_cache *c, LayerState &ly, hipStream_t st) {
 // once with the remap kernel.  work_experts: experts read (byte counters).
 void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &view,
                  bool with_shared, int n_buckets, double work_experts, const float *x,
-                 hipStream_t st, const moe::BucketTable *tab = nullptr) {
+                 hipStream_t st, const Ws &ws, const moe::WsLayout &WL,
+                 const moe::BucketTable *tab = nullptr) {
   if (n_buckets <= 0) return;
   const int32_t k = c->o.top_k;
   const int shared_slot = with_shared ? c->S : -1;
   const int P = T * k + (with_shared ? T : 0);
-  const bool decode = c->decode_ok(T);
-  // the workspace the kernels below index, checked before any launch
-  {
-    const size_t P_all = (size_t)T * k + (size_t)T * c->o.n_shared;
-    auto need = [&](const DevBuf &b, size_t bytes, const char *what) {
-      if (!b.p || b.bytes < bytes)
-        throw HipError(std::string("workspace ") + what + " too small for this call");
-    };
-    need(c->h, P_all * (size_t)c->f * 4, "h");
-    need(c->y, P_all * (size_t)c->d * 4, "y");
-    if (!decode && !tab) {
-      need(c->xp, (size_t)T * c->d * 4, "xp");
-      need(c->hp, P_all * (size_t)c->f * 4, "hp");
-      need(c->hscale, P_all * 4, "hscale");
-      need(c->bucket_pair, P_all * 4, "bucket_pair");
-    } else {
-      need(c->xq, (size_t)T * c->d * 2, "xq");
-    }
-  }
+  // the layout was checked against every launch of the call (ws_check)
+  const bool decode = WL.decode;
+  if (tab && !decode) throw HipError("host-built buckets need the decode path");
   const moe::RecordLayout &L = c->lay;
   moe::GemvArgs a{};
   if (!decode && !tab) {
     KTime kt(c, MOE_K_REMAP, st);
-    HIPCHK(moe::launch_remap((const int32_t *)c->idx.p, T, k, view, shared_slot,
-                             c->S + c->o.n_shared, (int32_t *)c->meta.p,
-                             (int32_t *)c->bucket_pair.p, (int32_t *)c->items.p, st));
+    HIPCHK(moe::launch_remap((const int32_t *)ws.idx, T, k, view, shared_slot,
+                             c->S + c->o.n_shared, (int32_t *)ws.meta,
+                             (int32_t *)ws.bucket_pair, (int32_t *)ws.items, st));
     kt.end((double)P * 8);
-    a.meta = (const int32_t *)c->meta.p;
-    a.bucket_pair = (const int32_t *)c->bucket_pair.p;
-    a.items = (const int32_t *)c->items.p;
+    a.meta = (const int32_t *)ws.meta;
+    a.bucket_pair = (const int32_t *)ws.bucket_pair;
+    a.items = (const int32_t *)ws.items;
   }
   a.slots = c->layers[layer].d_slots;
-  a.bt = decode && !tab ? (const int32_t *)c->buckets.p : nullptr;
-  a.xq = (const uint4 *)c->xq.p;
-  a.xs = (const float *)c->xs.p;
-  a.xp = (const uint32_t *)c->xp.p;
-  a.xscale = (const float *)c->xscale.p;
+  a.bt = decode && !tab ? (const int32_t *)ws.buckets : nullptr;
+  a.xq = (const uint4 *)ws.xq;
+  a.xs = (const float *)ws.xs;
+  a.xp = (const uint32_t *)ws.xp;
+  a.xscale = (const float *)ws.xscale;
   a.rec_bytes = L.bytes;
   a.T = T;
   a.k = k;
-  a.idx = (const int32_t *)c->idx.p;
+  a.idx = (const int32_t *)ws.idx;
   a.shared_slot = shared_slot;
   // gate/up + SwiGLU: rows f, K = d, input = prepared x by token
   a.off_q0 = L.off_gq;
@@ -451,7 +439,7 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
   a.nb = (int)L.nb_gu;
   a.in = x;
   a.in_by_pair = 0;
-  a.out = (float *)c->h.p;
+  a.out = (float *)ws.h;
   if (!decode && !tab) {
     // matrix-core grouped GEMM: gate/up + SwiGLU, h -> binary16 pairs, down;
     // one grid column per work item (bucket, token pass), bounded from above
@@ -464,8 +452,8 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
     const int P_all = T * k + T * c->o.n_shared;
     {
       KTime kt(c, MOE_K_PREP, st);
-      HIPCHK(moe::launch_prep_pairs((const float *)c->h.p, P_all, c->f, (uint32_t *)c->hp.p,
-                                    (float *)c->hscale.p, st));
+      HIPCHK(moe::launch_prep_pairs((const float *)ws.h, P_all, c->f, (uint32_t *)ws.hp,
+                                    (float *)ws.hscale, st));
       kt.end((double)P_all * c->f * 8.0);
     }
     moe::GemvArgs b = a;
@@ -473,10 +461,10 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
     b.off_s0 = L.off_ds;
     b.rows = c->d;
     b.nb = (int)L.nb_dn;
-    b.xp = (const uint32_t *)c->hp.p;
-    b.xscale = (const float *)c->hscale.p;
+    b.xp = (const uint32_t *)ws.hp;
+    b.xscale = (const float *)ws.hscale;
     b.in_by_pair = 1;
-    b.out = (float *)c->y.p;
+    b.out = (float *)ws.y;
     {
       KTime kt(c, MOE_K_DOWN, st);
       HIPCHK(moe::launch_mfma(b, false, n_items, st));
@@ -496,9 +484,9 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
   b.off_s0 = L.off_ds;
   b.rows = c->d;
   b.nb = (int)L.nb_dn;
-  b.in = (const float *)c->h.p;
+  b.in = (const float *)ws.h;
   b.in_by_pair = 1;
-  b.out = (float *)c->y.p;
+  b.out = (float *)ws.y;
   moe::GemvShape sh2 = moe::choose_gemv(false, b.nb, T);
   {
     KTime kt(c, MOE_K_DOWN, st);
@@ -507,6 +495,7 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
   }
 }
 
+// One layer call; the cache's arena and page-locked buffers grow as needed.
 moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
                         const float *router_w, const float *router_bias, float *out,
                         hipStream_t st) {
@@ -514,7 +503,13 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   const int32_t k = c->o.top_k, E = c->E, d = c->d;
   const bool host_mode = c->o.miss_mode == MOE_MISS_HOST;
   const int ns = c->o.n_shared;
-  c->ensure_ws(T);
+  const moe::WsParams wp = c->ws_params(T);
+  const moe::WsLayout WL = moe::ws_layout(wp);
+  if (const char *bad = moe::ws_check(WL, wp))
+    throw HipError(std::string("workspace region ") + bad + " does not cover the call");
+  c->ensure_pinned(T);
+  c->ensure_arena(WL.total);
+  const Ws ws = carve(c->arena.p, WL);
   // Stream rule: slot fills (the pull kernel on `st`, copies after an event on
   // `st`) rely on every earlier reader of the victims being before them on
   // `st`, and every layer's calls share the cache's workspace (logits, planes,
@@ -539,7 +534,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   }
   // table published at call start: the hits run on it before the host plans
   const moe::SlotView pre = make_view(ly.planner->slot_of());
-  const bool dec = c->decode_ok(T);
+  const bool dec = WL.decode;
   // host mode: the host experts read x from page-locked memory; the decode
   // router writes that copy itself, else a copy on the stream does
   const bool router_x = host_mode && dec && moe::router_decode_fits(T, d, E);
@@ -551,47 +546,47 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
     moe::DecodeTopk a;
     a.k = k;
     a.norm_topk = c->o.norm_topk;
-    a.idx = (int32_t *)c->idx.p;
-    a.w = (float *)c->w.p;
+    a.idx = (int32_t *)ws.idx;
+    a.w = (float *)ws.w;
     a.h_idx = (int32_t *)c->h_idx.p;
     a.h_w = (float *)c->h_w.p;
     a.view = pre;
     a.shared_slot = ns > 0 ? c->S : -1;
-    a.buckets = (int32_t *)c->buckets.p;
-    a.pair_slot = (int32_t *)c->pair_slot.p;
+    a.buckets = (int32_t *)ws.buckets;
+    a.pair_slot = (int32_t *)ws.pair_slot;
     a.h_flag = c->h_flag;
     a.seq = ++c->flag_seq;
-    HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)c->z.p, nullptr,
-                              nullptr, (uint4 *)c->xq.p, (float *)c->xs.p, st,
+    HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)ws.z, nullptr,
+                              nullptr, (uint4 *)ws.xq, (float *)ws.xs, st,
                               router_x ? (float *)c->h_x.p : nullptr));
     kt.end(4.0 * ((double)E * d + (double)T * d * 2 + (double)T * E + (router_bias ? E : 0)));
     KTime kt2(c, MOE_K_TOPK, st);
-    HIPCHK(moe::launch_topk_decode((const float *)c->z.p, T, E, a, st));
+    HIPCHK(moe::launch_topk_decode((const float *)ws.z, T, E, a, st));
     kt2.end(4.0 * ((double)T * E + 4.0 * T * k));
   } else {
     {
       KTime kt(c, MOE_K_ROUTER, st);
       // the matrix-core GEMM takes binary16 pairs
-      HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)c->z.p,
-                                (uint32_t *)c->xp.p, (float *)c->xscale.p, nullptr,
-                                (float *)c->xs.p, st));
+      HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)ws.z,
+                                (uint32_t *)ws.xp, (float *)ws.xscale, nullptr,
+                                (float *)ws.xs, st));
       kt.end(4.0 * ((double)E * d + (double)T * d * 2 + (double)T * E + (router_bias ? E : 0)));
     }
     KTime kt(c, MOE_K_TOPK, st);
-    HIPCHK(moe::launch_topk((const float *)c->z.p, T, E, k, c->o.norm_topk, (int32_t *)c->idx.p,
-                            (float *)c->w.p, (int32_t *)c->h_idx.p, (float *)c->h_w.p, st));
+    HIPCHK(moe::launch_topk((const float *)ws.z, T, E, k, c->o.norm_topk, (int32_t *)ws.idx,
+                            (float *)ws.w, (int32_t *)c->h_idx.p, (float *)c->h_w.p, st));
     kt.end(4.0 * ((double)T * E + 4.0 * T * k));
   }
   if (!dec) HIPCHK(hipEventRecord(c->ev_idx, st));
   if (c->o.keep_debug) {
     ly.dbg_z.ensure((size_t)T * E * 4);
-    HIPCHK(hipMemcpyAsync(ly.dbg_z.p, c->z.p, (size_t)T * E * 4, hipMemcpyDeviceToDevice, st));
+    HIPCHK(hipMemcpyAsync(ly.dbg_z.p, ws.z, (size_t)T * E * 4, hipMemcpyDeviceToDevice, st));
   }
 
   // Cached experts (and the shared one) on the table published at call start,
   // enqueued before the host reads the routing.
   const int nb_hits = std::min(T * k, c->S) + (ns > 0 ? 1 : 0);
-  run_experts(c, layer, T, pre, ns > 0, nb_hits, 0.0, x, st);
+  run_experts(c, layer, T, pre, ns > 0, nb_hits, 0.0, x, st, ws, WL);
   enqueue_range.reset();
 
   float *dbg_gpu = nullptr;
@@ -622,7 +617,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
       c->kt[MOE_K_DOWN].bytes += n_hit * (double)c->d * (double)c->lay.nb_dn * 18.0;
   }
   bool combined = false;
-  if (!host_mode && c->decode_ok(T)) {
+  if (!host_mode && WL.decode) {
     // every miss is pulled from the pinned arena into its slot by a copy kernel
     // on the compute stream (after every earlier reader of the victims), then
     // computed there from host-built buckets
@@ -654,7 +649,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
           HIPCHK(moe::launch_pull(pl, st));
           kt.end((double)pl.n * (double)c->rec());
         }
-        run_experts(c, layer, T, pre, false, tab.n, (double)tab.n, x, st, &tab);
+        run_experts(c, layer, T, pre, false, tab.n, (double)tab.n, x, st, ws, WL, &tab);
       }
       ly.st.fills += stg.fills.size();
       ly.st.fill_bytes += stg.fills.size() * (uint64_t)c->rec();
@@ -674,7 +669,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
       std::fill(table.begin(), table.end(), -1);
       for (const moe::Fill &fl : stg.fills) table[fl.expert] = fl.slot;
       const int nb = (int)stg.fills.size();
-      run_experts(c, layer, T, make_view(table), false, nb, (double)nb, x, st);
+      run_experts(c, layer, T, make_view(table), false, nb, (double)nb, x, st, ws, WL);
     }
     if (c->o.keep_debug) ly.dbg_host.assign((size_t)T * d, 0.0f);
   } else {
@@ -693,16 +688,20 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
       const int b = c->partial_cur;
       c->partial_cur ^= 1;
       if (c->partial_used[b]) HIPCHK(hipEventSynchronize(c->partial_ev[b]));
-      // host jobs: one per missed expert, its tokens ascending
-      std::vector<moe::HostExpertJob> jobs(ly.plan.host_experts.size());
-      std::vector<int32_t> job_of(E, -1);
+      // host jobs: one per missed expert, its tokens ascending (the cache's
+      // vectors, reused from call to call)
+      std::vector<moe::HostExpertJob> &jobs = c->jobs;
+      std::vector<int32_t> &job_of = c->job_of, &rank_job = c->rank_job;
+      jobs.resize(ly.plan.host_experts.size());
+      job_of.assign(E, -1);
       for (size_t i = 0; i < jobs.size(); ++i) {
         const int32_t e = ly.plan.host_experts[i];
         job_of[e] = (int32_t)i;
         jobs[i].record = c->host_record(layer, e);
+        jobs[i].tokens.clear();
       }
       const int32_t *hidx = (const int32_t *)c->h_idx.p;
-      std::vector<int32_t> rank_job((size_t)T * k, -1);
+      rank_job.assign((size_t)T * k, -1);
       for (int32_t t = 0; t < T; ++t)
         for (int32_t j = 0; j < k; ++j) {
           const int32_t jb = job_of[hidx[t * k + j]];
@@ -722,9 +721,9 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
       {
         TraceRange tr("moe.combine");
         KTime kt(c, MOE_K_COMBINE, st);
-        HIPCHK(moe::launch_combine((const float *)c->y.p, (const float *)c->w.p,
-                                   (const int32_t *)c->idx.p, pre, 0,
-                                   dec ? (const int32_t *)c->pair_slot.p : nullptr, T, k, d, ns,
+        HIPCHK(moe::launch_combine((const float *)ws.y, (const float *)ws.w,
+                                   (const int32_t *)ws.idx, pre, 0,
+                                   dec ? (const int32_t *)ws.pair_slot : nullptr, T, k, d, ns,
                                    host_part, out, dbg_gpu, st));
         kt.end(4.0 * (double)T * d * (k + ns + 2));
       }
@@ -738,9 +737,9 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   if (!combined) {
     TraceRange tr("moe.combine");
     KTime kt(c, MOE_K_COMBINE, st);
-    HIPCHK(moe::launch_combine((const float *)c->y.p, (const float *)c->w.p,
-                               (const int32_t *)c->idx.p, pre, host_mode ? 0 : 1,
-                               dec ? (const int32_t *)c->pair_slot.p : nullptr, T, k, d, ns,
+    HIPCHK(moe::launch_combine((const float *)ws.y, (const float *)ws.w,
+                               (const int32_t *)ws.idx, pre, host_mode ? 0 : 1,
+                               dec ? (const int32_t *)ws.pair_slot : nullptr, T, k, d, ns,
                                nullptr, out, dbg_gpu, st));
     kt.end(4.0 * (double)T * d * (k + ns + 1));
   }
@@ -894,6 +893,12 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
       HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence));
     HIPCHK(hipHostMalloc((void **)&c->h_flag, 64, hipHostMallocCoherent));
     *c->h_flag = 0;
+    // page-locked buffers and host bookkeeping of a decode call
+    c->ensure_pinned(moe::kDecodeMaxTokens);
+    c->jobs.resize((size_t)n_experts);
+    for (auto &j : c->jobs) j.tokens.reserve(moe::kDecodeMaxTokens);
+    c->job_of.reserve((size_t)n_experts);
+    c->rank_job.reserve((size_t)moe::kDecodeMaxTokens * o.top_k);
     c->layers.resize(layers);
     for (int32_t l = 0; l < layers; ++l) {
       LayerState &ly = c->layers[l];

@@ -51,9 +51,21 @@ void ThreadPool::run(const std::function<void(int)> &f) {
     gen_.fetch_add(1, std::memory_order_release);
   }
   cv_.notify_all();  // only sleeping workers need it
-  f(0);
+  std::exception_ptr mine;
+  try {
+    f(0);
+  } catch (...) {
+    mine = std::current_exception();
+  }
   unsigned i = 0;
   while (pending_.load(std::memory_order_acquire) != 0) relax(i);
+  std::exception_ptr e;
+  {
+    std::lock_guard<std::mutex> g(err_m_);
+    e = err_ ? err_ : mine;
+    err_ = nullptr;
+  }
+  if (e) std::rethrow_exception(e);
 }
 
 void ThreadPool::loop(int id) {
@@ -71,7 +83,12 @@ void ThreadPool::loop(int id) {
     }
     if (stop_.load()) return;
     seen = gen_.load(std::memory_order_acquire);
-    (*job_)(id);
+    try {
+      (*job_)(id);
+    } catch (...) {
+      std::lock_guard<std::mutex> g(err_m_);
+      if (!err_) err_ = std::current_exception();
+    }
     pending_.fetch_sub(1, std::memory_order_release);
   }
 }
@@ -245,58 +262,71 @@ void host_moe_partial(ThreadPool &pool, const RecordLayout &L, const std::vector
   const int64_t chunks_d = (d + kRowChunk - 1) / kRowChunk;
   std::atomic<int64_t> next1{0}, next2{0};
   SpinBarrier h_done(pool.size());
+  std::mutex err_m;
   std::exception_ptr first_err;
+  auto keep = [&](std::exception_ptr e) {
+    std::lock_guard<std::mutex> g(err_m);
+    if (!first_err) first_err = e;
+  };
   pool.run([&](int tid) {
     if (tid == 0 && caller_first) {
       try {
         (*caller_first)();
       } catch (...) {
-        first_err = std::current_exception();
+        keep(std::current_exception());
       }
     }
-    for (;;) {
-      const int64_t u = next1.fetch_add(1);
-      if (u >= total1) break;
-      const int64_t jb = u / chunks_f, r0 = (u % chunks_f) * kRowChunk;
-      const int64_t r1 = std::min(f, r0 + kRowChunk);
-      const uint8_t *rec = jobs[jb].record;
-      const auto &toks = jobs[jb].tokens;
-      for (int64_t r = r0; r < r1; ++r) {
-        const uint8_t *gq = rec + L.off_gq + r * L.nb_gu * 16;
-        const uint8_t *uq = rec + L.off_uq + r * L.nb_gu * 16;
-        const uint16_t *gs = (const uint16_t *)(rec + L.off_gs) + r * L.nb_gu;
-        const uint16_t *us = (const uint16_t *)(rec + L.off_us) + r * L.nb_gu;
-        for (size_t ti = 0; ti < toks.size(); ++ti) {
-          const float *xt = x + (int64_t)toks[ti] * d;
-          const float g = row_dot(gq, gs, xt, L.nb_gu);
-          const float uu = row_dot(uq, us, xt, L.nb_gu);
-          h[(size_t)((h_base[jb] + (int64_t)ti) * f + r)] = silu(g) * uu;
+    try {
+      for (;;) {
+        const int64_t u = next1.fetch_add(1);
+        if (u >= total1) break;
+        const int64_t jb = u / chunks_f, r0 = (u % chunks_f) * kRowChunk;
+        const int64_t r1 = std::min(f, r0 + kRowChunk);
+        const uint8_t *rec = jobs[jb].record;
+        const auto &toks = jobs[jb].tokens;
+        for (int64_t r = r0; r < r1; ++r) {
+          const uint8_t *gq = rec + L.off_gq + r * L.nb_gu * 16;
+          const uint8_t *uq = rec + L.off_uq + r * L.nb_gu * 16;
+          const uint16_t *gs = (const uint16_t *)(rec + L.off_gs) + r * L.nb_gu;
+          const uint16_t *us = (const uint16_t *)(rec + L.off_us) + r * L.nb_gu;
+          for (size_t ti = 0; ti < toks.size(); ++ti) {
+            const float *xt = x + (int64_t)toks[ti] * d;
+            const float g = row_dot(gq, gs, xt, L.nb_gu);
+            const float uu = row_dot(uq, us, xt, L.nb_gu);
+            h[(size_t)((h_base[jb] + (int64_t)ti) * f + r)] = silu(g) * uu;
+          }
         }
       }
+    } catch (...) {
+      keep(std::current_exception());
     }
     h_done.arrive_and_wait();
-    std::vector<float> dots((size_t)h_base.back());
-    for (;;) {
-      const int64_t u = next2.fetch_add(1);
-      if (u >= chunks_d) break;
-      const int64_t i0 = u * kRowChunk, i1 = std::min(d, i0 + kRowChunk);
-      for (int64_t i = i0; i < i1; ++i) {
-        for (size_t jb = 0; jb < jobs.size(); ++jb) {
-          const uint8_t *rec = jobs[jb].record;
-          const uint8_t *dq = rec + L.off_dq + i * L.nb_dn * 16;
-          const uint16_t *ds = (const uint16_t *)(rec + L.off_ds) + i * L.nb_dn;
-          for (int64_t r = h_base[jb]; r < h_base[jb + 1]; ++r)
-            dots[(size_t)r] = row_dot(dq, ds, h.data() + r * f, L.nb_dn);
-        }
-        for (int32_t t = 0; t < T; ++t) {
-          float acc = 0.0f;
-          for (int32_t j = 0; j < k; ++j) {
-            const int64_t r = pair_row[(size_t)t * k + j];
-            if (r >= 0) acc += weights[t * k + j] * dots[(size_t)r];
+    try {
+      std::vector<float> dots((size_t)h_base.back());
+      for (;;) {
+        const int64_t u = next2.fetch_add(1);
+        if (u >= chunks_d) break;
+        const int64_t i0 = u * kRowChunk, i1 = std::min(d, i0 + kRowChunk);
+        for (int64_t i = i0; i < i1; ++i) {
+          for (size_t jb = 0; jb < jobs.size(); ++jb) {
+            const uint8_t *rec = jobs[jb].record;
+            const uint8_t *dq = rec + L.off_dq + i * L.nb_dn * 16;
+            const uint16_t *ds = (const uint16_t *)(rec + L.off_ds) + i * L.nb_dn;
+            for (int64_t r = h_base[jb]; r < h_base[jb + 1]; ++r)
+              dots[(size_t)r] = row_dot(dq, ds, h.data() + r * f, L.nb_dn);
           }
-          partial[(int64_t)t * d + i] = acc;
+          for (int32_t t = 0; t < T; ++t) {
+            float acc = 0.0f;
+            for (int32_t j = 0; j < k; ++j) {
+              const int64_t r = pair_row[(size_t)t * k + j];
+              if (r >= 0) acc += weights[t * k + j] * dots[(size_t)r];
+            }
+            partial[(int64_t)t * d + i] = acc;
+          }
         }
       }
+    } catch (...) {
+      keep(std::current_exception());
     }
   });
   if (first_err) std::rethrow_exception(first_err);

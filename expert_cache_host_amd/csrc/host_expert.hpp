@@ -6,6 +6,7 @@
 #include <atomic>
 #include <condition_variable>
 #include <cstdint>
+#include <exception>
 #include <functional>
 #include <mutex>
 #include <thread>
@@ -22,7 +23,8 @@ class ThreadPool {
   int size() const { return n_; }
   // Runs f(tid) on every worker, the caller being tid 0; returns when all ended.
   // Every worker calls f exactly once per run, so f may hold a barrier over
-  // size() threads.
+  // size() threads.  An exception thrown by f on any thread is rethrown here
+  // once every worker has finished (the first one, if several threw).
   void run(const std::function<void(int)> &f);
 
  private:
@@ -35,6 +37,8 @@ class ThreadPool {
   std::atomic<uint64_t> gen_{0};
   std::atomic<int> pending_{0};
   std::atomic<bool> stop_{false};
+  std::mutex err_m_;
+  std::exception_ptr err_;  // first exception of the current run
 };
 
 // Spin barrier over a fixed number of threads, for one use.
@@ -64,8 +68,10 @@ struct HostExpertJob {
 //   jobs: one per host expert; rank_expert[t*k + j] = index into jobs or -1;
 //   weights[t*k + j] the gating weights.
 //   caller_first: when non-null, the calling thread runs it before it joins
-//   the work (the other workers start at once); an exception it throws is
-//   rethrown once every worker has finished.
+//   the work (the other workers start at once).
+//   An exception on any thread (caller_first's, or an allocation failure of a
+//   worker) is rethrown once every worker has finished; every worker still
+//   passes the barrier between the gate/up and the down rows.
 void host_moe_partial(ThreadPool &pool, const RecordLayout &L, const std::vector<HostExpertJob> &jobs,
                       const int32_t *rank_job, const float *weights, int32_t T, int32_t k,
                       const float *x, float *partial, std::vector<float> &h_scratch,

@@ -1139,51 +1139,6 @@ __global__ __launch_bounds__(64 * NW) void q4_down_kernel(GemvArgs a, BucketTabl
   }
 }
 
-// Shapes measured on MI355X for one token per bucket over the decode shapes
-// d x f = 6144 x 2048 and 2816 x 704: gate/up rows of >= 128 blocks run best
-// with 16 lanes per row and 2 rows per lane, rows of 32-127 blocks with 8 lanes
-// and 1 row per lane, K split over the 4 waves; down rows of >= 64 blocks with
-// 16 lanes per row, whole K per wave and 4 rows per lane, shorter ones with 8
-// lanes and K over 4 waves.  Rows of fewer than 32 gate/up blocks keep K in one
-// wave.
-GemvShape choose_gemv(bool glu, int nb, int tokens) {
-  GemvShape sh{};
-  sh.TT = tokens <= 1 ? 1 : (tokens <= 2 ? 2 : 4);
-  if (glu) {
-    sh.R = 2;
-    if (nb >= 128) {
-      sh.G = 16;
-      sh.KS = 4;
-    } else if (nb >= 32) {
-      sh.G = 8;
-      sh.KS = 4;
-      sh.R = 1;
-    } else {
-      sh.G = 8;
-      sh.KS = 1;
-    }
-  } else {
-    sh.R = 4;
-    if (nb >= 64) {
-      sh.G = 16;
-      sh.KS = 1;
-    } else {
-      sh.G = 8;
-      sh.KS = 4;
-    }
-  }
-  sh.NW = 4;
-  sh.rows_wg = (sh.NW / sh.KS) * (64 / sh.G) * sh.R;
-  return sh;
-}
-
-size_t gemv_lds_bytes(bool glu, int nb, int tokens) {
-  const GemvShape sh = choose_gemv(glu, nb, tokens);
-  const size_t row_scales = ((size_t)sh.rows_wg * nb * 2 + 15) / 16 * 16;
-  if (glu) return (size_t)sh.TT * nb * 64 + (size_t)sh.TT * xs_units(nb) * 16 + 2 * row_scales;
-  return (size_t)sh.TT * nb * 64 + ((size_t)sh.TT * nb + 3) / 4 * 16 + row_scales;
-}
-
 template <bool GLU, int G, int KS, int R, int TT, int MODE, int PF>
 static void launch_one(const GemvArgs &a, const BucketTable &tab, int nbk, size_t lds,
                        hipStream_t s) {

@@ -4,24 +4,15 @@
 
 #include <cstdint>
 
-namespace moe {
+#include "shapes.hpp"
 
-constexpr int kMaxExperts = 512;
-// Decode path: at most this many (token, rank) pairs per call, tokens <= 4.
-constexpr int kDecodeMaxPairs = 64;
-constexpr int kDecodeMaxTokens = 4;
-constexpr int kMetaB = 520;  // bucket capacity of the meta block (>= kMaxExperts + 1)
-constexpr int kMetaInts = 2 + 3 * kMetaB;
+namespace moe {
 
 // Expert -> slot table of one stage, passed by value as a kernel argument so
 // that each launch carries its own table (no copy, no reuse hazard).
 struct SlotView {
   int16_t slot[kMaxExperts];
 };
-
-// 16-byte units of one token's decode block scales: nb floats padded to a
-// multiple of 4 (the row stride of xs is 4 * xs_units(nb) floats).
-inline constexpr int xs_units(int nb) { return (nb + 3) / 4; }
 
 // z[t][e] = x[t] . W[e] (+ b[e]) in the fixed fp32 order.  The waves also
 // prepare each token's x for the expert kernels, in one of two forms:
@@ -49,11 +40,6 @@ bool router_decode_fits(int T, int d, int E);
 hipError_t launch_topk(const float *z, int T, int E, int k, int norm_topk, int32_t *idx,
                        float *w, int32_t *h_idx, float *h_w, hipStream_t s);
 
-// Decode bucket list: buckets[0] = count; bucket b at buckets + 1 + b*kBucketInts
-// holds {slot, pair count, pairs[kDecodeMaxTokens]} (pairs ascending, the last
-// one repeated past the count).
-constexpr int kBucketInts = 6;  // 2 + kDecodeMaxTokens
-
 // Decode top-k (T <= kDecodeMaxTokens, T*k + shared pairs <= kDecodeMaxPairs,
 // h_flag set; else hipErrorInvalidValue): as launch_topk (idx, w on the device,
 // h_idx, h_w page-locked), and also maps each routed pair to its slot through
@@ -76,15 +62,6 @@ struct DecodeTopk {
   uint32_t seq;
 };
 hipError_t launch_topk_decode(const float *z, int T, int E, const DecodeTopk &a, hipStream_t s);
-
-// Tokens of one bucket that one matrix-core workgroup takes per pass.
-constexpr int kGemmTokens = 32;
-
-// Work items of the matrix-core GEMM for `pairs` pairs in at most `buckets`
-// buckets: one per started pass of kGemmTokens tokens of a bucket.
-inline int gemm_items_bound(int buckets, int pairs) {
-  return buckets + (pairs + kGemmTokens - 1) / kGemmTokens;
-}
 
 // Expert -> slot remap of the routed pairs (plus one shared pair per token when
 // shared_slot >= 0) and stable bucketing per slot, for batches beyond the
@@ -121,33 +98,14 @@ struct GemvArgs {
   float *out;                  // [pairs][rows]
 };
 
-static_assert(kBucketInts == 2 + kDecodeMaxTokens, "bucket list entry size");
-
 // Buckets built on the host (stream mode, decode path, after the slot fills):
 // bucket b reads the expert record at src[b] (a device slot).
-constexpr int kTabMax = 32;
 struct BucketTable {
   const uint8_t *src[kTabMax];
   int n;                                  // buckets, or -1 for "no table"
   uint8_t cnt[kTabMax];                   // pairs per bucket (<= kDecodeMaxTokens)
   uint8_t pairs[kTabMax][kDecodeMaxTokens];  // pair ids (< kDecodeMaxPairs)
 };
-
-struct GemvShape {
-  int G;        // lanes per row
-  int KS;       // waves of a workgroup that split a row's K blocks
-  int R;        // rows per lane
-  int TT;       // tokens per bucket pass (1, 2 or 4)
-  int NW;       // waves per workgroup
-  int rows_wg;  // rows per workgroup
-};
-
-// Decode GEMV shape for rows of nb blocks and buckets of up to `tokens` pairs:
-// glu = gate/up (+ SwiGLU), else down.
-GemvShape choose_gemv(bool glu, int nb, int tokens);
-
-// Dynamic LDS of one decode GEMV workgroup (the bucket's activation planes).
-size_t gemv_lds_bytes(bool glu, int nb, int tokens);
 
 // Decode GEMV over Q4 slot records with 4-bit integer dot products.  glu = 1:
 // out[pair][r] = silu(G x) * (U x) from the router's digit planes and block

@@ -6,8 +6,11 @@
 // host-miss partial sum against a plain scalar evaluation of the same bytes.
 // Also drives the thread pool (every worker runs each job once, a spin barrier
 // orders the workers' writes, idle gaps long enough for the workers to fall
-// asleep) and the caller's first task of a host partial (runs once; an
-// exception it throws surfaces after the run, whose results are complete).
+// asleep, an exception on any worker reaches the caller of run()), the
+// caller's first task of a host partial (runs once; an exception it throws
+// surfaces after the run, whose results are complete), and the per-call
+// device workspace layout (sizes, alignment, overlaps, the decode decision,
+// mixed call orders on one growing arena).
 // Built under ThreadSanitizer with the argument "threads": the pool and the
 // host partial only.  Exit status 0 and "ok" on success.
 #include <cmath>
@@ -23,10 +26,13 @@
 #include <random>
 #include <set>
 #include <vector>
+#include <new>
+#include <algorithm>
 
 #include "../../expert_cache_host_amd/csrc/host_expert.hpp"
 #include "../../expert_cache_host_amd/csrc/layout.hpp"
 #include "../../expert_cache_host_amd/csrc/planner.hpp"
+#include "../../expert_cache_host_amd/csrc/workspace.hpp"
 
 #define CHECK(c)                                                   \
   do {                                                             \
@@ -228,11 +234,108 @@ static void caller_first_runs(std::mt19937_64 &rng) {
   CHECK(std::memcmp(a.data(), b.data(), a.size() * 4) == 0);
 }
 
+// Workspace layouts of every call shape the cache admits along the sweep:
+// tokens 1..512, several top-k, expert counts, shared experts and model shapes;
+// both miss modes share the layout (the page-locked buffers are separate).
+// Every layout must pass ws_check; a layout with any region shrunk by 4 bytes
+// must fail it; the decode decision must match the limits it is made of; and a
+// mixed sequence of calls (small after large, decode after matrix-core) must
+// always find its regions inside an arena that only grows.
+static void workspace_runs(std::mt19937_64 &rng) {
+  const int ks[] = {1, 2, 4, 8, 15, 16, 64};
+  const int Es[] = {8, 64, 128, 256, 512};
+  const int shapes[][2] = {{64, 32}, {256, 512}, {2816, 704}, {2048, 768}, {6144, 2048}};
+  size_t arena = 0;
+  int checked = 0;
+  for (int T = 1; T <= 512; T += (T < 8 ? 1 : (T < 64 ? 7 : 61))) {
+    for (int k : ks)
+      for (int E : Es) {
+        if (k > E) continue;
+        for (int ns = 0; ns <= 1; ++ns)
+          for (const auto &sh : shapes) {
+            const moe::WsParams p{T, E, k, ns, sh[0], sh[1]};
+            const moe::WsLayout L = moe::ws_layout(p);
+            const char *bad = moe::ws_check(L, p);
+            if (bad) std::fprintf(stderr, "T=%d k=%d E=%d ns=%d d=%d: %s\n", T, k, E, ns, sh[0], bad);
+            CHECK(bad == nullptr);
+            const bool small = T <= moe::kDecodeMaxTokens && T * (k + ns) <= moe::kDecodeMaxPairs;
+            CHECK(L.decode == (small && moe::gemv_lds_bytes(true, sh[0] / 32, T) <= moe::kDecodeLdsBudget &&
+                               moe::gemv_lds_bytes(false, sh[1] / 32, T) <= moe::kDecodeLdsBudget));
+            CHECK(L.pairs == T * k + T * ns);
+            // planted mistakes: every region, shrunk, must be caught
+            moe::WsRegion moe::WsLayout::*regions[] = {
+                &moe::WsLayout::z,  &moe::WsLayout::idx, &moe::WsLayout::w,
+                &moe::WsLayout::h,  &moe::WsLayout::y,   &moe::WsLayout::xq,
+                &moe::WsLayout::xs, &moe::WsLayout::buckets, &moe::WsLayout::pair_slot,
+                &moe::WsLayout::meta, &moe::WsLayout::bucket_pair, &moe::WsLayout::items,
+                &moe::WsLayout::xp, &moe::WsLayout::xscale, &moe::WsLayout::hp,
+                &moe::WsLayout::hscale};
+            for (auto r : regions) {
+              if ((L.*r).bytes < 4) continue;
+              moe::WsLayout M = L;
+              (M.*r).bytes -= 4;
+              CHECK(moe::ws_check(M, p) != nullptr);
+            }
+            // an overlap is caught too
+            moe::WsLayout O = L;
+            O.y.off = O.h.off;
+            CHECK(moe::ws_check(O, p) != nullptr);
+            ++checked;
+          }
+      }
+  }
+  CHECK(checked > 1000);
+  // mixed call orders on one arena
+  for (int call = 0; call < 4000; ++call) {
+    const int E = Es[rng() % 5];
+    int k = ks[rng() % 7];
+    if (k > E) k = E;
+    const int T = rng() % 3 ? 1 + (int)(rng() % 4) : 1 + (int)(rng() % 512);
+    const auto &sh = shapes[rng() % 5];
+    const moe::WsParams p{T, E, k, (int)(rng() % 2), sh[0], sh[1]};
+    const moe::WsLayout L = moe::ws_layout(p);
+    CHECK(moe::ws_check(L, p) == nullptr);
+    arena = std::max(arena, L.total);  // the arena grows, never shrinks
+    // every region of this call lies inside the arena as it stands
+    for (const moe::WsRegion *r : {&L.z, &L.idx, &L.w, &L.h, &L.y, &L.xq, &L.xs, &L.buckets,
+                                   &L.pair_slot, &L.meta, &L.bucket_pair, &L.items, &L.xp,
+                                   &L.xscale, &L.hp, &L.hscale})
+      CHECK(r->off + r->bytes <= L.total && L.total <= arena);
+  }
+}
+
+// Exceptions inside the pool: a worker's (not only the caller's) reaches the
+// caller of run() once every worker has finished, and the pool keeps working.
+static void pool_exception_runs() {
+  for (int n : {2, 5}) {
+    moe::ThreadPool pool(n);
+    for (int thrower = 0; thrower < n; ++thrower) {
+      std::atomic<int> done{0};
+      bool caught = false;
+      try {
+        pool.run([&](int tid) {
+          done.fetch_add(1);
+          if (tid == thrower) throw std::bad_alloc();
+        });
+      } catch (const std::bad_alloc &) {
+        caught = true;
+      }
+      CHECK(caught);
+      CHECK(done.load() == n);
+      std::atomic<int> again{0};
+      pool.run([&](int) { again.fetch_add(1); });
+      CHECK(again.load() == n);
+    }
+  }
+}
+
 int main(int argc, char **argv) {
   std::mt19937_64 rng(12345);
   const bool threads_only = argc > 1 && std::string(argv[1]) == "threads";
   if (!threads_only) planner_runs(rng);
+  if (!threads_only) workspace_runs(rng);
   pool_runs(rng);
+  pool_exception_runs();
   caller_first_runs(rng);
   if (!threads_only) host_expert_runs(rng);
   std::printf("ok\n");
