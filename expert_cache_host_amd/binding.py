@@ -68,6 +68,7 @@ def load_library():
         "moe_cache_default_opts": (None, [ctypes.POINTER(Opts)]),
         "moe_cache_create": (I32, [I32, I32, I32, I32, I32, P, ctypes.POINTER(Opts), ctypes.POINTER(P)]),
         "moe_layer_forward": (I32, [P, I32, P, I32, P, P, P, P]),
+        "moe_layer_forward_noalloc": (I32, [P, I32, P, I32, P, P, P, P]),
         "moe_cache_stats": (I32, [P, I32, ctypes.POINTER(Stats)]),
         "moe_cache_reset_stats": (I32, [P]),
         "moe_cache_set_timing": (I32, [P, I32]),
@@ -179,9 +180,14 @@ class MoECache:
         self.adopt = adopt
 
     # -- compute ---------------------------------------------------------------
-    def forward(self, layer: int, x, router_w, router_bias=None, out=None, stream=None):
-        """out [T, d] = layer(x) for torch float32 CUDA tensors (contiguous)."""
+    def forward(self, layer: int, x, router_w, router_bias=None, out=None, stream=None,
+                noalloc: bool = False):
+        """out [T, d] = layer(x) for torch float32 CUDA tensors (contiguous).
+        noalloc: through moe_layer_forward_noalloc (the library's fixed scratch;
+        `out` must then be given, since creating it would allocate)."""
         import torch
+        if noalloc and out is None:
+            raise ValueError("noalloc calls need a preallocated out")
         if out is None:
             out = torch.empty_like(x)
         for t in (x, router_w, out) + ((router_bias,) if router_bias is not None else ()):
@@ -192,7 +198,8 @@ class MoECache:
         if tuple(router_w.shape) != (self.n_experts, self.d_model):
             raise ValueError("router_w must be [n_experts, d_model]")
         s = torch.cuda.current_stream() if stream is None else stream
-        rc = load_library().moe_layer_forward(
+        fn = load_library().moe_layer_forward_noalloc if noalloc else load_library().moe_layer_forward
+        rc = fn(
             self._h, layer, x.data_ptr(), x.shape[0], router_w.data_ptr(),
             router_bias.data_ptr() if router_bias is not None else None, out.data_ptr(),
             s.cuda_stream)

@@ -191,8 +191,10 @@ struct moe_cache {
   bool poisoned = false;
   bool timing = false;   // per-layer compute and fill events
   uint32_t kmask = 0;    // kernels timed one launch at a time (bit MOE_K_*)
-  // device workspace of moe_layer_forward (grown on demand)
+  // device workspace of moe_layer_forward (grown on demand) and the fixed
+  // scratch array of moe_layer_forward_noalloc on this device
   DevBuf arena;
+  void *scratch = nullptr;
   // stream of the last call: the workspace above is shared by every layer
   hipStream_t last_stream = nullptr;
   bool called = false;
@@ -495,10 +497,12 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
   }
 }
 
-// One layer call; the cache's arena and page-locked buffers grow as needed.
+// One layer call.  noalloc: the workspace is the fixed scratch array and
+// nothing is allocated (the caller checked that the call fits); else the
+// cache's arena and page-locked buffers grow as needed.
 moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
                         const float *router_w, const float *router_bias, float *out,
-                        hipStream_t st) {
+                        hipStream_t st, bool noalloc = false) {
   LayerState &ly = c->layers[layer];
   const int32_t k = c->o.top_k, E = c->E, d = c->d;
   const bool host_mode = c->o.miss_mode == MOE_MISS_HOST;
@@ -507,9 +511,17 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   const moe::WsLayout WL = moe::ws_layout(wp);
   if (const char *bad = moe::ws_check(WL, wp))
     throw HipError(std::string("workspace region ") + bad + " does not cover the call");
-  c->ensure_pinned(T);
-  c->ensure_arena(WL.total);
-  const Ws ws = carve(c->arena.p, WL);
+  void *base;
+  if (noalloc) {
+    if (WL.total > moe::kNoAllocScratchBytes || !c->pinned_fits(T) || !c->scratch)
+      throw HipError("call does not fit the fixed scratch");
+    base = c->scratch;
+  } else {
+    c->ensure_pinned(T);
+    c->ensure_arena(WL.total);
+    base = c->arena.p;
+  }
+  const Ws ws = carve(base, WL);
   // Stream rule: slot fills (the pull kernel on `st`, copies after an event on
   // `st`) rely on every earlier reader of the victims being before them on
   // `st`, and every layer's calls share the cache's workspace (logits, planes,
@@ -893,12 +905,14 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
       HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence));
     HIPCHK(hipHostMalloc((void **)&c->h_flag, 64, hipHostMallocCoherent));
     *c->h_flag = 0;
-    // page-locked buffers and host bookkeeping of a decode call
-    c->ensure_pinned(moe::kDecodeMaxTokens);
+    // the fixed scratch of moe_layer_forward_noalloc on this device, and the
+    // page-locked buffers and host bookkeeping of its largest call
+    HIPCHK(moe::noalloc_scratch(&c->scratch));
+    c->ensure_pinned(moe::kNoAllocMaxTokens);
     c->jobs.resize((size_t)n_experts);
-    for (auto &j : c->jobs) j.tokens.reserve(moe::kDecodeMaxTokens);
+    for (auto &j : c->jobs) j.tokens.reserve(moe::kNoAllocMaxTokens);
     c->job_of.reserve((size_t)n_experts);
-    c->rank_job.reserve((size_t)moe::kDecodeMaxTokens * o.top_k);
+    c->rank_job.reserve((size_t)moe::kNoAllocMaxTokens * o.top_k);
     c->layers.resize(layers);
     for (int32_t l = 0; l < layers; ++l) {
       LayerState &ly = c->layers[l];
@@ -942,6 +956,45 @@ moe_status moe_layer_forward(moe_cache *c, int32_t layer, const float *x, int32_
   return guarded(c, [&]() {
     TraceRange tr("moe.layer_forward");
     return forward_impl(c, layer, x, n_tokens, router_w, router_bias, out, (hipStream_t)stream);
+  });
+}
+
+moe_status moe_layer_forward_noalloc(moe_cache *c, int32_t layer, const float *x,
+                                     int32_t n_tokens, const float *router_w,
+                                     const float *router_bias, float *out, void *stream) {
+  g_err.clear();
+  if (!c) return fail(MOE_EINVAL, "cache is NULL");
+  if (layer < 0 || layer >= c->L) return fail(MOE_EINVAL, "layer out of range");
+  if (n_tokens < 1) return fail(MOE_EINVAL, "n_tokens must be >= 1");
+  if (n_tokens > moe::kNoAllocMaxTokens)
+    return fail(MOE_EINVAL, "n_tokens exceeds the allocation-free maximum (4)");
+  if (!x || !router_w || !out) return fail(MOE_EINVAL, "x, router_w and out must be non-NULL");
+  if (c->o.keep_debug)
+    return fail(MOE_EINVAL, "keep_debug copies allocate: use moe_layer_forward");
+  const moe::WsLayout WL = moe::ws_layout(c->ws_params(n_tokens));
+  if (WL.total > moe::kNoAllocScratchBytes)
+    return fail(MOE_EINVAL, "the call's workspace (" + std::to_string(WL.total) +
+                                " bytes) exceeds the fixed scratch (" +
+                                std::to_string(moe::kNoAllocScratchBytes) + " bytes)");
+  if (!c->pinned_fits(n_tokens)) return fail(MOE_EINVAL, "page-locked buffers too small");
+  return guarded(c, [&]() {
+    TraceRange tr("moe.layer_forward_noalloc");
+    // no timing events here: creating them would allocate
+    const bool timing = c->timing;
+    const uint32_t kmask = c->kmask;
+    c->timing = false;
+    c->kmask = 0;
+    struct Restore {
+      moe_cache *c;
+      bool t;
+      uint32_t m;
+      ~Restore() {
+        c->timing = t;
+        c->kmask = m;
+      }
+    } restore{c, timing, kmask};
+    return forward_impl(c, layer, x, n_tokens, router_w, router_bias, out, (hipStream_t)stream,
+                        true);
   });
 }
 

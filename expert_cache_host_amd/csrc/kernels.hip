@@ -8,8 +8,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kernels.hpp"
+#include "workspace.hpp"
 
 namespace moe {
 
@@ -1638,6 +1640,31 @@ hipError_t launch_combine(const float *y, const float *w, const int32_t *idx,
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, y, w, idx, view, all_gpu, pair_slot,
                      T, k, d, n_shared, host_part, out, dbg_gpu);
   return hipGetLastError();
+}
+
+// ============================================================== fixed scratch
+// The workspace of moe_layer_forward_noalloc, for callers that may not
+// allocate: one array per device, loaded with the code object and held until
+// the process ends.  Every call on a device shares it.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex m;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(m);
+  if (addr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace moe

@@ -156,4 +156,10 @@ hipError_t launch_combine(const float *y, const float *w, const int32_t *idx,
                           int k, int d, int n_shared, const float *host_part, float *out,
                           float *dbg_gpu, hipStream_t s);
 
+// Device address of the fixed scratch array (kNoAllocScratchBytes, one per
+// device, held until the process ends) on the current device.  The first call
+// on a device looks the address up with that device current and keeps it; the
+// array's host-side name is not a device address and is never used on the host.
+hipError_t noalloc_scratch(void **ptr);
+
 }  // namespace moe

@@ -6,7 +6,9 @@
 // metadata.  ws_layout() decides which path a call takes and carves every
 // region it needs from one base address at 256-byte boundaries; ws_check()
 // restates, launch by launch, what each kernel indexes and verifies that the
-// layout covers it.  moe_layer_forward carves a device arena grown on demand.
+// layout covers it.  moe_layer_forward carves a device arena grown on demand;
+// moe_layer_forward_noalloc carves the library's fixed scratch array and
+// rejects calls whose layout does not fit it.
 #pragma once
 #include <cstddef>
 #include <cstdint>
@@ -15,6 +17,11 @@
 
 namespace moe {
 
+// Bytes of the fixed per-device scratch array of moe_layer_forward_noalloc.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+// Tokens per call that moe_layer_forward_noalloc accepts (its page-locked
+// routing and host-partial buffers are sized for this at create).
+constexpr int kNoAllocMaxTokens = kDecodeMaxTokens;
 // Dynamic LDS a decode GEMV workgroup may use.
 constexpr size_t kDecodeLdsBudget = 60 * 1024;
 constexpr size_t kWsAlign = 256;

@@ -201,6 +201,36 @@ moe_status moe_layer_forward(moe_cache *c, int32_t layer, const float *x, int32_
                              const float *router_w, const float *router_bias, float *out,
                              void *stream);
 
+/*
+ * moe_layer_forward_noalloc -- moe_layer_forward for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, same kernels and the same results as
+ * moe_layer_forward (outputs, routing, slot tables, eviction log and stats).
+ *
+ * It calls no hipMalloc, hipFree, hipHostMalloc or other allocating routine:
+ * the call's device workspace is a fixed array of 16 MiB per device inside the
+ * library (looked up once per device at moe_cache_create and held until the
+ * process ends), and its page-locked routing and host-partial buffers were
+ * sized at create for its largest call.  It records no timing events.  Host
+ * bookkeeping (planner, host-miss jobs) reuses the cache's vectors, whose
+ * capacity create reserves.
+ *
+ * Limits (MOE_EINVAL, nothing changed): 1 <= n_tokens <= 4; the call's
+ * workspace (router logits, routing, prepared activations, the pairs' hidden
+ * rows and outputs, bucket lists) must fit the 16 MiB; the cache must not have
+ * keep_debug set.
+ *
+ * The array is shared by every call on the device and keeps the last call's
+ * contents (every region is written before it is read).  Calls that overlap on
+ * one device -- two caches, or streams that are not ordered -- race on it; a
+ * cache orders its own calls (a call on another stream than its last one waits
+ * for the device first).  It may be mixed with moe_layer_forward on the same
+ * cache.
+ */
+moe_status moe_layer_forward_noalloc(moe_cache *c, int32_t layer, const float *x,
+                                     int32_t n_tokens, const float *router_w,
+                                     const float *router_bias, float *out, void *stream);
+
 /* Counters of one layer (layer >= 0) or summed over layers (layer == -1).
  * Synchronises the library's own streams to read device timings. */
 moe_status moe_cache_stats(moe_cache *c, int32_t layer, moe_stats *out);
