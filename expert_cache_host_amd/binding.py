@@ -99,6 +99,7 @@ def load_library():
         "moe_planner_slots": (I32, [P, P, P]),
         "moe_planner_evictions": (I32, [P, P, SZ, ctypes.POINTER(SZ)]),
         "moe_planner_destroy": (None, [P]),
+        "moe_host_topk": (I32, [P, I32, I32, I32, I32, P, P]),
         "moe_host_expert_forward": (I32, [P, I32, I32, P, I32, P, I32]),
     }
     for name, (res, args) in sig.items():
@@ -386,3 +387,15 @@ def host_expert_forward(expert_q4: np.ndarray, d_model: int, d_ff: int, x: np.nd
     _check(load_library().moe_host_expert_forward(_ptr(e), d_model, d_ff, _ptr(xx), xx.shape[0],
                                                   _ptr(y), threads))
     return y
+
+
+def host_topk(z: np.ndarray, top_k: int, norm_topk: bool = True):
+    """(idx [T, k] int32, w [T, k] float32): the host's selection on logits z [T, E]."""
+    zz = np.ascontiguousarray(z, dtype=np.float32)
+    if zz.ndim != 2:
+        raise ValueError("z must be [T, E]")
+    idx = np.empty((zz.shape[0], top_k), np.int32)
+    w = np.empty((zz.shape[0], top_k), np.float32)
+    _check(load_library().moe_host_topk(_ptr(zz), zz.shape[0], zz.shape[1], top_k,
+                                        1 if norm_topk else 0, _ptr(idx), _ptr(w)))
+    return idx, w

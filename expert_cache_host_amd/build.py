@@ -35,6 +35,8 @@ def _jobs():
                                 os.path.join(BUILD, "host_expert.o")]),
         (["g++"] + CXX_FLAGS + ["-c", os.path.join(CSRC, "workspace.cpp"), "-o",
                                 os.path.join(BUILD, "workspace.o")]),
+        (["g++"] + CXX_FLAGS + ["-c", os.path.join(CSRC, "host_routing.cpp"), "-o",
+                                os.path.join(BUILD, "host_routing.o")]),
     ]
 
 
@@ -58,7 +60,7 @@ def build(verbose: bool = False) -> str:
         msg = "\n".join(" ".join(c) + "\n" + t for c, t in failed)
         raise RuntimeError("libmoecache build failed:\n" + msg)
     objs = [os.path.join(BUILD, n) for n in ("kernels.o", "api.o", "planner.o", "host_expert.o",
-                                             "workspace.o")]
+                                             "workspace.o", "host_routing.o")]
     tmp = OUT + f".tmp{os.getpid()}"
     link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs + [
         "-L" + os.path.join(ROCM, "lib"), "-lrocprofiler-sdk-roctx", "-pthread"]

@@ -27,6 +27,7 @@
 
 #include "../../include/moe_cache.h"
 #include "host_expert.hpp"
+#include "host_routing.hpp"
 #include "kernels.hpp"
 #include "layout.hpp"
 #include "planner.hpp"
@@ -184,10 +185,10 @@ struct moe_cache {
   hipStream_t side[kCopyStreams] = {};  // slot fills rotate over the copy streams
   int fill_rr = 0;                      // copy stream of the next fill
   hipEvent_t ev_idx = nullptr, ev_ready = nullptr;
-  // decode calls: the top-k kernel stores the call's sequence number here
-  // (page-locked, coherent) once the routing copy is visible to the host
-  uint32_t *h_flag = nullptr;
-  uint32_t flag_seq = 0;
+  // decode calls: the router publishes every logit here as (seq << 32) | bits
+  // (page-locked, coherent, [kDecodeMaxTokens][E]); the host selects from it
+  uint64_t *h_z = nullptr;
+  uint32_t z_seq = 0;
   bool poisoned = false;
   bool timing = false;   // per-layer compute and fill events
   uint32_t kmask = 0;    // kernels timed one launch at a time (bit MOE_K_*)
@@ -204,6 +205,7 @@ struct moe_cache {
   bool partial_used[2] = {false, false};
   int partial_cur = 0;
   std::vector<float> h_scratch;
+  std::vector<float> h_zf;  // the published logits as floats
   // host-mode bookkeeping, reused across calls
   std::vector<moe::HostExpertJob> jobs;
   std::vector<int32_t> job_of, rank_job;
@@ -230,7 +232,7 @@ struct moe_cache {
     }
     layers.clear();
     if (h_arena) (void)hipHostFree(h_arena);
-    if (h_flag) (void)hipHostFree(h_flag);
+    if (h_z) (void)hipHostFree(h_z);
     if (ev_idx) (void)hipEventDestroy(ev_idx);
     if (ev_ready) (void)hipEventDestroy(ev_ready);
     for (auto &e : partial_ev)
@@ -315,23 +317,40 @@ struct KTime {
   }
 };
 
-// Waits until the decode top-k kernel has published the call's routing copy
-// (flag == flag_seq, acquire).  A stream that went idle without the flag, or
-// 30 s without it, is an error rather than a hang.
-void wait_routing(moe_cache *c, hipStream_t st) {
-  const uint32_t want = c->flag_seq;
+// Waits until the router has published every logit of the call (each word of
+// h_z carries z_seq), then selects the call's experts and gating weights on the
+// host into h_idx / h_w.  A stream that went idle without them, or 30 s
+// without them, is an error rather than a hang.
+void wait_routing(moe_cache *c, hipStream_t st, int32_t T) {
+  const uint32_t want = c->z_seq;
+  const int64_t n = (int64_t)T * c->E;
   const double t0 = now_s();
+  int64_t ready = 0;  // words 0..ready-1 seen with the call's number
   for (uint64_t i = 0;; ++i) {
-    if (__atomic_load_n(c->h_flag, __ATOMIC_ACQUIRE) == want) return;
+    while (ready < n && (uint32_t)(__atomic_load_n(c->h_z + ready, __ATOMIC_ACQUIRE) >> 32) == want)
+      ++ready;
+    if (ready == n) break;
     if ((i & 4095) == 4095) {
       const hipError_t e = hipStreamQuery(st);
       if (e != hipSuccess && e != hipErrorNotReady) HIPCHK(e);
-      if (__atomic_load_n(c->h_flag, __ATOMIC_ACQUIRE) == want) return;
-      if (e == hipSuccess) throw HipError("routing flag missing after the top-k kernel completed");
-      if (now_s() - t0 > 30.0) throw HipError("routing flag not set within 30 s");
+      if (e == hipSuccess) {
+        while (ready < n &&
+               (uint32_t)(__atomic_load_n(c->h_z + ready, __ATOMIC_ACQUIRE) >> 32) == want)
+          ++ready;
+        if (ready == n) break;
+        throw HipError("router logits missing after the call's kernels completed");
+      }
+      if (now_s() - t0 > 30.0) throw HipError("router logits not published within 30 s");
     }
     __builtin_ia32_pause();
   }
+  float *z = c->h_zf.data();
+  for (int64_t i = 0; i < n; ++i) {
+    const uint32_t b = (uint32_t)c->h_z[i];
+    std::memcpy(&z[i], &b, 4);
+  }
+  moe::host_topk(z, T, c->E, c->o.top_k, c->o.norm_topk, (int32_t *)c->h_idx.p,
+                 (float *)c->h_w.p);
 }
 
 // Copies the fills of one stage on the side streams after every earlier reader
@@ -560,17 +579,16 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
     a.norm_topk = c->o.norm_topk;
     a.idx = (int32_t *)ws.idx;
     a.w = (float *)ws.w;
-    a.h_idx = (int32_t *)c->h_idx.p;
-    a.h_w = (float *)c->h_w.p;
     a.view = pre;
     a.shared_slot = ns > 0 ? c->S : -1;
     a.buckets = (int32_t *)ws.buckets;
     a.pair_slot = (int32_t *)ws.pair_slot;
-    a.h_flag = c->h_flag;
-    a.seq = ++c->flag_seq;
+    // a new number for every call: words left from earlier calls never match
+    if (++c->z_seq == 0) ++c->z_seq;
     HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)ws.z, nullptr,
                               nullptr, (uint4 *)ws.xq, (float *)ws.xs, st,
-                              router_x ? (float *)c->h_x.p : nullptr));
+                              router_x ? (float *)c->h_x.p : nullptr,
+                              (unsigned long long *)c->h_z, c->z_seq));
     kt.end(4.0 * ((double)E * d + (double)T * d * 2 + (double)T * E + (router_bias ? E : 0)));
     KTime kt2(c, MOE_K_TOPK, st);
     HIPCHK(moe::launch_topk_decode((const float *)ws.z, T, E, a, st));
@@ -609,7 +627,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   {
     TraceRange tr("moe.wait_routing");
     if (dec)
-      wait_routing(c, st);
+      wait_routing(c, st, T);
     else
       HIPCHK(hipEventSynchronize(c->ev_idx));
   }
@@ -903,8 +921,12 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
     // no system-scope fence
     for (auto &e : c->partial_ev)
       HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence));
-    HIPCHK(hipHostMalloc((void **)&c->h_flag, 64, hipHostMallocCoherent));
-    *c->h_flag = 0;
+    {
+      const size_t nz = (size_t)moe::kDecodeMaxTokens * n_experts;
+      HIPCHK(hipHostMalloc((void **)&c->h_z, nz * 8, hipHostMallocCoherent));
+      std::memset(c->h_z, 0, nz * 8);
+      c->h_zf.resize(nz);
+    }
     // the fixed scratch of moe_layer_forward_noalloc on this device, and the
     // page-locked buffers and host bookkeeping of its largest call
     HIPCHK(moe::noalloc_scratch(&c->scratch));
@@ -1339,6 +1361,18 @@ moe_status moe_planner_scores(moe_planner *p, double *scores) {
 }
 
 void moe_planner_destroy(moe_planner *p) { delete p; }
+
+moe_status moe_host_topk(const float *z, int32_t n_tokens, int32_t n_experts, int32_t top_k,
+                         int32_t norm_topk, int32_t *idx, float *w) {
+  g_err.clear();
+  if (!z || !idx || !w) return fail(MOE_EINVAL, "NULL argument");
+  if (n_tokens < 1) return fail(MOE_EINVAL, "n_tokens must be >= 1");
+  if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS) return fail(MOE_EINVAL, "n_experts out of range");
+  if (top_k < 1 || top_k > n_experts) return fail(MOE_EINVAL, "top_k must be in [1, n_experts]");
+  if (norm_topk != 0 && norm_topk != 1) return fail(MOE_EINVAL, "norm_topk must be 0 or 1");
+  moe::host_topk(z, n_tokens, n_experts, top_k, norm_topk, idx, w);
+  return MOE_OK;
+}
 
 moe_status moe_host_expert_forward(const void *expert_q4, int32_t d_model, int32_t d_ff,
                                    const float *x, int32_t n_tokens, float *y, int32_t threads) {

@@ -108,6 +108,17 @@ __device__ __forceinline__ uint4 digit_planes8(const float (&v)[8], float inv) {
   return make_uint4(p[0], p[1], p[2], p[3]);
 }
 
+// Publishes one router logit to the host: the value's bits with the call's
+// sequence number above them, in one 8-byte store at system scope.  The host
+// polls the words of a call until every one carries its sequence number; a
+// word is written whole, so no fence is needed for the logit itself.
+__device__ __forceinline__ void publish_logit(unsigned long long *h_z, long long i, float v,
+                                              uint32_t seq) {
+  const unsigned long long w =
+      ((unsigned long long)seq << 32) | (unsigned long long)__builtin_bit_cast(uint32_t, v);
+  __hip_atomic_store(h_z + i, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // Smallest block maximum the 16-bit encoding scales by: keeps 30000 / m finite
 // (a block whose values all lie below it is encoded on this coarser scale).
 constexpr float kMinBlockMax = 0x1p-100f;
@@ -154,7 +165,8 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
                                                      uint32_t *__restrict__ xp,
                                                      float *__restrict__ xscale,
                                                      uint4 *__restrict__ xq,
-                                                     float *__restrict__ xs) {
+                                                     float *__restrict__ xs,
+                                                     unsigned long long *h_z, uint32_t seq) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -204,7 +216,11 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
   if (lane == 0) {
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-      if (tt < nt) z[(long long)(t0 + tt) * E + e] = bias ? p[tt] + bias[e] : p[tt];
+      if (tt < nt) {
+        const float v = bias ? p[tt] + bias[e] : p[tt];
+        z[(long long)(t0 + tt) * E + e] = v;
+        if (h_z != nullptr) publish_logit(h_z, (long long)(t0 + tt) * E + e, v, seq);
+      }
     }
   }
   if (xp == nullptr && xq == nullptr) return;
@@ -282,7 +298,9 @@ __global__ __launch_bounds__(256) void router_decode_kernel(const float *__restr
                                                             const float *__restrict__ bias, int E,
                                                             float *__restrict__ z,
                                                             uint4 *__restrict__ xq,
-                                                            float *__restrict__ xs, float *h_x) {
+                                                            float *__restrict__ xs, float *h_x,
+                                                            unsigned long long *h_z,
+                                                            uint32_t seq) {
 #pragma clang fp contract(off)
   extern __shared__ float sprod[];  // [TT][d] products
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -341,6 +359,7 @@ __global__ __launch_bounds__(256) void router_decode_kernel(const float *__restr
     }
   }
   __syncthreads();
+  float zv = 0.0f;
   if (wave < T) {
     const float *pr = sprod + wave * d + lane;
     const int M = d >> 6;
@@ -351,7 +370,8 @@ __global__ __launch_bounds__(256) void router_decode_kernel(const float *__restr
       const float o = __shfl_down(p, off, 64);
       if (lane < off) p = p + o;
     }
-    if (lane == 0) z[(long long)wave * E + e] = bias ? p + bias[e] : p;
+    zv = bias ? p + bias[e] : p;
+    if (lane == 0) z[(long long)wave * E + e] = zv;
   }
   // decode GEMV input: digit planes with one scale per 32-element block (the
   // block's four units are four consecutive threads; words is a multiple of 8,
@@ -374,8 +394,13 @@ __global__ __launch_bounds__(256) void router_decode_kernel(const float *__restr
             make_float4(px[tt][4], px[tt][5], px[tt][6], px[tt][7]);
       }
     }
-    // the host reads h_x once a later kernel raises its flag
+    // every thread's copy of x reaches host memory before the workgroup
+    // publishes its logits (the host reads x once it has every logit)
     if (h_x != nullptr) __threadfence_system();
+  }
+  if (h_z != nullptr) {
+    __syncthreads();
+    if (wave < T && lane == 0) publish_logit(h_z, (long long)wave * E + e, zv, seq);
   }
 }
 
@@ -386,32 +411,32 @@ bool router_decode_fits(int T, int d, int E) {
 
 hipError_t launch_router(const float *x, int T, int d, const float *W, const float *bias, int E,
                          float *z, uint32_t *xp, float *xscale, uint4 *xq, float *xs,
-                         hipStream_t s, float *h_x) {
+                         hipStream_t s, float *h_x, unsigned long long *h_z, uint32_t seq) {
   const int tt = T <= 1 ? 1 : (T <= 2 ? 2 : 4);
   const size_t lds = (size_t)tt * d * 4;
   if (xq != nullptr && xp == nullptr && router_decode_fits(T, d, E)) {
     if (tt == 1)
       hipLaunchKernelGGL(router_decode_kernel<1>, dim3(E), dim3(256), lds, s, x, T, d, W, bias, E,
-                         z, xq, xs, h_x);
+                         z, xq, xs, h_x, h_z, seq);
     else if (tt == 2)
       hipLaunchKernelGGL(router_decode_kernel<2>, dim3(E), dim3(256), lds, s, x, T, d, W, bias, E,
-                         z, xq, xs, h_x);
+                         z, xq, xs, h_x, h_z, seq);
     else
       hipLaunchKernelGGL(router_decode_kernel<4>, dim3(E), dim3(256), lds, s, x, T, d, W, bias, E,
-                         z, xq, xs, h_x);
+                         z, xq, xs, h_x, h_z, seq);
     return hipGetLastError();
   }
   if (h_x != nullptr) return hipErrorInvalidValue;
   const int gx = (E + 3) / 4;
   if (T <= 1) {
     hipLaunchKernelGGL((router_kernel<1, 32>), dim3(gx, T), dim3(256), 0, s, x, T, d, W, bias, E,
-                       z, xp, xscale, xq, xs);
+                       z, xp, xscale, xq, xs, h_z, seq);
   } else if (T <= 4) {
     hipLaunchKernelGGL((router_kernel<4, 16>), dim3(gx, 1), dim3(256), 0, s, x, T, d, W, bias, E,
-                       z, xp, xscale, xq, xs);
+                       z, xp, xscale, xq, xs, h_z, seq);
   } else {
     hipLaunchKernelGGL((router_kernel<8, 8>), dim3(gx, (T + 7) / 8), dim3(256), 0, s, x, T, d, W,
-                       bias, E, z, xp, xscale, xq, xs);
+                       bias, E, z, xp, xscale, xq, xs, h_z, seq);
   }
   return hipGetLastError();
 }
@@ -495,13 +520,12 @@ __global__ __launch_bounds__(64) void topk_kernel(const float *__restrict__ z, i
 
 // Decode calls (T <= 4 tokens, T*k + shared pairs <= 64): one workgroup, wave t
 // selects token t's experts; then wave 0 maps every pair to its slot through
-// `view` (shared pairs to shared_slot), lists the buckets (pairs grouped by slot,
-// a bucket per slot in order of its first pair, pairs ascending), writes the
-// page-locked routing copy and raises the host flag.  Every thread of the
-// workgroup (at least 64 * T) calls it.
+// `view` (shared pairs to shared_slot) and lists the buckets (pairs grouped by
+// slot, a bucket per slot in order of its first pair, pairs ascending).  The
+// host makes the same selection from the published logits, so nothing here
+// goes to host memory.  Every thread of the workgroup (at least 64 * T) calls it.
 __device__ void topk_decode_block(const float *z, int T, int E, const DecodeTopk &a) {
   __shared__ int sidx[kDecodeMaxPairs];
-  __shared__ float sw[kDecodeMaxPairs];
   const int t = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int k = a.k;
   if (t < T) {
@@ -513,19 +537,12 @@ __device__ void topk_decode_block(const float *z, int T, int E, const DecodeTopk
       a.idx[o] = my_e;
       a.w[o] = my_w;
       sidx[o] = my_e;
-      sw[o] = my_w;
     }
   }
   __syncthreads();
   if (t != 0) return;
   const int Pr = T * k;
   const int P = Pr + (a.shared_slot >= 0 ? T : 0);
-  // wave 0 alone writes the page-locked routing copy, so that its own fence
-  // publishes all of it before the flag
-  if (lane < Pr) {
-    a.h_idx[lane] = sidx[lane];
-    a.h_w[lane] = sw[lane];
-  }
   int s = -1;
   if (lane < P) s = lane < Pr ? (int)a.view.slot[sidx[lane]] : a.shared_slot;
   if (lane < Pr) a.pair_slot[lane] = s;
@@ -554,9 +571,6 @@ __device__ void topk_decode_block(const float *z, int T, int E, const DecodeTopk
     nbk++;
   }
   if (lane == 0) a.buckets[0] = nbk;
-  // publish the routing copy to the host: system-scope release, then the flag
-  __threadfence_system();
-  if (lane == 0) __hip_atomic_store(a.h_flag, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 __global__ __launch_bounds__(256) void topk_decode_kernel(const float *z, int T, int E,
@@ -573,7 +587,7 @@ hipError_t launch_topk(const float *z, int T, int E, int k, int norm_topk, int32
 
 static bool decode_args_ok(int T, const DecodeTopk &a) {
   return T >= 1 && T <= kDecodeMaxTokens &&
-         T * a.k + (a.shared_slot >= 0 ? T : 0) <= kDecodeMaxPairs && a.h_flag != nullptr;
+         T * a.k + (a.shared_slot >= 0 ? T : 0) <= kDecodeMaxPairs;
 }
 
 hipError_t launch_topk_decode(const float *z, int T, int E, const DecodeTopk &a, hipStream_t s) {
@@ -728,6 +742,16 @@ __device__ __forceinline__ int pair_row(const GemvArgs &a, int p) {
   return p < a.T * a.k ? p / a.k : p - a.T * a.k;
 }
 
+// Expert weights are read once per launch and not again for many calls (other
+// layers' experts pass through the caches in between), so the GEMV loads them
+// with the nontemporal hint: they stream past the caches' retained lines (the
+// activations, scales and router rows) instead of replacing them.  About 5%
+// faster for both GEMV kernels at 6144 x 2048 experts.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldnt(const uint4 *p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 // ============================================================== bucket lookup
 // The expert record and pairs of bucket b on the decode path, from the list the
 // decode top-k kernel wrote (BK_LIST; workgroup-uniform, so scalar loads) or
@@ -881,8 +905,8 @@ __global__ __launch_bounds__(64 * NW) void q4_gateup_kernel(GemvArgs a, BucketTa
     const int j = blk_of(min(f, NI - 1));
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      wg[f][i] = q0[ro[i] + j];
-      wu[f][i] = q1[ro[i] + j];
+      wg[f][i] = ldnt(&q0[ro[i] + j]);
+      wu[f][i] = ldnt(&q1[ro[i] + j]);
     }
   }
 #pragma unroll
@@ -926,8 +950,8 @@ __global__ __launch_bounds__(64 * NW) void q4_gateup_kernel(GemvArgs a, BucketTa
           const int jn = blk_of(it + PF);
 #pragma unroll
           for (int i = 0; i < R; ++i) {
-            wg[f][i] = q0[ro[i] + jn];
-            wu[f][i] = q1[ro[i] + jn];
+            wg[f][i] = ldnt(&q0[ro[i] + jn]);
+            wu[f][i] = ldnt(&q1[ro[i] + jn]);
           }
         }
         float dg[R], du[R];
@@ -1028,6 +1052,7 @@ __global__ __launch_bounds__(64 * NW) void q4_down_kernel(GemvArgs a, BucketTabl
   auto load_units = [&](int u0, float4 (&v0)[kHUnits], float4 (&v1)[kHUnits]) {
 #pragma unroll
     for (int c = 0; c < kHUnits; ++c) {
+      if (u0 + NT * c >= n_units) break;  // uniform
       const int u = min(u0 + tid + NT * c, n_units - 1);
       const int tt = u / (nb * 4), rem = u - tt * nb * 4;
       const int b = rem >> 2, j = rem & 3;
@@ -1063,7 +1088,7 @@ __global__ __launch_bounds__(64 * NW) void q4_down_kernel(GemvArgs a, BucketTabl
   for (int f = 0; f < PF; ++f) {
     const int j = blk_of(min(f, NI - 1));
 #pragma unroll
-    for (int i = 0; i < R; ++i) wd[f][i] = q0[ro[i] + j];
+    for (int i = 0; i < R; ++i) wd[f][i] = ldnt(&q0[ro[i] + j]);
   }
   if (tid < n_s) srow[tid] = sv0;
   if (tid + NT < n_s) srow[tid + NT] = sv1;
@@ -1097,7 +1122,7 @@ __global__ __launch_bounds__(64 * NW) void q4_down_kernel(GemvArgs a, BucketTabl
         if (it + PF < NI) {
           const int jn = blk_of(it + PF);
 #pragma unroll
-          for (int i = 0; i < R; ++i) wd[f][i] = q0[ro[i] + jn];
+          for (int i = 0; i < R; ++i) wd[f][i] = ldnt(&q0[ro[i] + jn]);
         }
         float dd[R];
 #pragma unroll

@@ -27,11 +27,15 @@ struct SlotView {
 //   (for 32-bit word j of block b = j/4 and g = 4*(j%4): (x[g],x[g+2]),
 //   (x[g+16],x[g+18]), (x[g+1],x[g+3]), (x[g+17],x[g+19]) of the block, hi then
 //   lo).
+// h_z (page-locked, coherent; when given): logit t*E + e also goes to
+// h_z[t*E + e] as (seq << 32) | bits in one 8-byte store, the host's copy of the
+// routing input.
 // h_x (decode planes only, when router_decode_fits): page-locked host copy of
-// x [T][d], visible to the host once a later kernel raises its flag.
+// x [T][d]; a workgroup's part of it reaches host memory before its logits.
 hipError_t launch_router(const float *x, int T, int d, const float *W, const float *bias, int E,
                          float *z, uint32_t *xp, float *xscale, uint4 *xq, float *xs,
-                         hipStream_t s, float *h_x = nullptr);
+                         hipStream_t s, float *h_x = nullptr, unsigned long long *h_z = nullptr,
+                         uint32_t seq = 0);
 // The one-workgroup-per-expert decode router handles this call.
 bool router_decode_fits(int T, int d, int E);
 
@@ -40,26 +44,19 @@ bool router_decode_fits(int T, int d, int E);
 hipError_t launch_topk(const float *z, int T, int E, int k, int norm_topk, int32_t *idx,
                        float *w, int32_t *h_idx, float *h_w, hipStream_t s);
 
-// Decode top-k (T <= kDecodeMaxTokens, T*k + shared pairs <= kDecodeMaxPairs,
-// h_flag set; else hipErrorInvalidValue): as launch_topk (idx, w on the device,
-// h_idx, h_w page-locked), and also maps each routed pair to its slot through
-// `view` (pair_slot[T*k], -1 when not cached) and writes the bucket list of the
-// cached experts plus, when shared_slot >= 0, one bucket of the shared expert's
-// T pairs (pair T*k + t) at slot shared_slot.  When h_idx / h_w are complete and
-// visible to the host, seq is stored into *h_flag (page-locked, coherent) with
-// a system-scope release, so that the host can wait on the flag instead of an
-// event with a full-device fence.
+// Decode top-k (T <= kDecodeMaxTokens, T*k + shared pairs <= kDecodeMaxPairs;
+// else hipErrorInvalidValue): as launch_topk on the device (idx, w), and also
+// maps each routed pair to its slot through `view` (pair_slot[T*k], -1 when not
+// cached) and writes the bucket list of the cached experts plus, when
+// shared_slot >= 0, one bucket of the shared expert's T pairs (pair T*k + t) at
+// slot shared_slot.  Writes nothing to host memory.
 struct DecodeTopk {
   int k, norm_topk;
   int32_t *idx;
   float *w;
-  int32_t *h_idx;
-  float *h_w;
   SlotView view;
   int shared_slot;
   int32_t *buckets, *pair_slot;
-  uint32_t *h_flag;
-  uint32_t seq;
 };
 hipError_t launch_topk_decode(const float *z, int T, int E, const DecodeTopk &a, hipStream_t s);
 

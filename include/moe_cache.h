@@ -378,6 +378,17 @@ moe_status moe_planner_evictions(moe_planner *p, moe_evict_rec *buf, size_t cap,
 
 void moe_planner_destroy(moe_planner *p);
 
+/* The host's expert selection on decode calls: per token, the k largest of the
+ * E logits z[t][*], ordered by decreasing value, equal values (-0 == +0) to the
+ * lower expert id, and the gating weights (softmax over all E logits in
+ * binary64, renormalised over the k when norm_topk, rounded to float32).  The
+ * GPU's top-k kernel selects the same ids from the same float32 logits.
+ * z: host float32 [n_tokens][n_experts]; idx, w: host [n_tokens][top_k].
+ * Requirements: n_tokens >= 1; 1 <= top_k <= n_experts <= MOE_MAX_EXPERTS;
+ * norm_topk 0 or 1. */
+moe_status moe_host_topk(const float *z, int32_t n_tokens, int32_t n_experts, int32_t top_k,
+                         int32_t norm_topk, int32_t *idx, float *w);
+
 /* One expert on host cores, as host mode computes a miss: y[t] = D (silu(G x_t)
  * * (U x_t)) for t < n_tokens.  expert_q4: host pointer to ONE expert in the
  * interchange layout; x, y: host float32 [n_tokens][d_model]; threads <= 0
