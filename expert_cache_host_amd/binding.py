@@ -99,6 +99,8 @@ def load_library():
         "moe_planner_slots": (I32, [P, P, P]),
         "moe_planner_evictions": (I32, [P, P, SZ, ctypes.POINTER(SZ)]),
         "moe_planner_destroy": (None, [P]),
+        "moe_debug_fill_delay": (I32, [P, I32]),
+        "moe_debug_fail_alloc": (I32, [I32]),
         "moe_host_topk": (I32, [P, I32, I32, I32, I32, P, P]),
         "moe_host_expert_forward": (I32, [P, I32, I32, P, I32, P, I32]),
     }

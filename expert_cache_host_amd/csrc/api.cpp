@@ -56,6 +56,42 @@ struct HipError : std::runtime_error {
   using std::runtime_error::runtime_error;
 };
 
+// A device or page-locked allocation failed: MOE_ENOMEM, and the cache (if
+// any) stays usable, since every allocation precedes the work that needs it.
+struct AllocError : std::runtime_error {
+  using std::runtime_error::runtime_error;
+};
+
+// Failure injection for tests (moe_debug_fail_alloc): the allocation this many
+// allocations from now fails as if the device were out of memory (-1: none).
+thread_local int64_t g_fail_alloc_in = -1;
+
+bool injected_alloc_failure() {
+  if (g_fail_alloc_in < 0) return false;
+  if (g_fail_alloc_in-- > 0) return false;
+  g_fail_alloc_in = -1;
+  return true;
+}
+
+hipError_t dev_malloc(void **p, size_t n) {
+  if (injected_alloc_failure()) return hipErrorOutOfMemory;
+  return hipMalloc(p, n);
+}
+
+hipError_t host_malloc(void **p, size_t n, unsigned flags) {
+  if (injected_alloc_failure()) return hipErrorOutOfMemory;
+  return hipHostMalloc(p, n, flags);
+}
+
+#define ALLOCCHK(expr, what)                                                              \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess) {                                                               \
+      (void)hipGetLastError();                                                            \
+      throw AllocError(std::string(what) + ": " + hipGetErrorString(e_));                 \
+    }                                                                                     \
+  } while (0)
+
 #define HIPCHK(expr)                                                                      \
   do {                                                                                    \
     hipError_t e_ = (expr);                                                               \
@@ -81,7 +117,7 @@ struct PinnedBuf {
     if (p) (void)hipHostFree(p);
     p = nullptr;
     bytes = 0;
-    HIPCHK(hipHostMalloc(&p, n, hipHostMallocDefault));
+    ALLOCCHK(host_malloc(&p, n, hipHostMallocDefault), "page-locked buffer");
     bytes = n;
   }
   ~PinnedBuf() {
@@ -97,7 +133,7 @@ struct DevBuf {
     if (p) (void)hipFree(p);
     p = nullptr;
     bytes = 0;
-    HIPCHK(hipMalloc(&p, n));
+    ALLOCCHK(dev_malloc(&p, n), "device buffer");
     bytes = n;
   }
   ~DevBuf() {
@@ -185,6 +221,7 @@ struct moe_cache {
   hipStream_t side[kCopyStreams] = {};  // slot fills rotate over the copy streams
   int fill_rr = 0;                      // copy stream of the next fill
   hipEvent_t ev_idx = nullptr, ev_ready = nullptr;
+  int32_t fill_delay_us = 0;  // moe_debug_fill_delay: host wait before each fill batch
   // decode calls: the router publishes every logit here as (seq << 32) | bits
   // (page-locked, coherent, [kDecodeMaxTokens][E]); the host selects from it
   uint64_t *h_z = nullptr;
@@ -360,6 +397,11 @@ void wait_routing(moe_cache *c, hipStream_t st, int32_t T) {
 // slots).  Host-mode calls (after_prev_call) wait only for the layer's previous
 // call and fills: no slot a call reads is its own victim, so the copies need
 // not wait for the call's own kernels.
+// Host function on a copy stream (moe_debug_fill_delay): holds the stream.
+void hold_fills(void *us) {
+  std::this_thread::sleep_for(std::chrono::microseconds(*static_cast<const int32_t *>(us)));
+}
+
 void enqueue_fills(moe_cache *c, int32_t layer, const std::vector<moe::Fill> &fills,
                    hipStream_t st, bool after_prev_call = false) {
   LayerState &ly = c->layers[layer];
@@ -381,6 +423,12 @@ void enqueue_fills(moe_cache *c, int32_t layer, const std::vector<moe::Fill> &fi
     if (ly.read_done_set) HIPCHK(hipStreamWaitEvent(sd, ly.read_done, 0));
     for (int p = 0; p < kCopyStreams; ++p)
       if (ly.fill_used[p] && p != phys(i)) HIPCHK(hipStreamWaitEvent(sd, ly.fill_ev[p], 0));
+  }
+  if (c->fill_delay_us > 0) {
+    // a slow link, forced from the host: each copy stream holds its copies
+    // back this long; nothing that reads a slot may get ahead of its copy
+    for (int i = 0; i < n_sd; ++i)
+      HIPCHK(hipLaunchHostFunc(c->side[phys(i)], hold_fills, &c->fill_delay_us));
   }
   if (c->timing) {
     t0 = ly.t_h2d.get();
@@ -807,6 +855,8 @@ moe_status guarded(moe_cache *c, F &&f) {
   } catch (const HipError &e) {
     if (c) c->poisoned = true;
     return fail(MOE_EHIP, e.what());
+  } catch (const AllocError &e) {
+    return fail(MOE_ENOMEM, e.what());
   } catch (const std::bad_alloc &) {
     return fail(MOE_ENOMEM, "host allocation failed");
   } catch (const std::exception &e) {
@@ -890,8 +940,7 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
     HIPCHK(hipGetDevice(&c->device));
     const size_t ntot = (size_t)n_experts + o.n_shared;
     const size_t arena = (size_t)layers * ntot * c->rec();
-    hipError_t he = hipHostMalloc((void **)&c->h_arena, arena, hipHostMallocDefault);
-    if (he != hipSuccess) {
+    if (host_malloc((void **)&c->h_arena, arena, hipHostMallocDefault) != hipSuccess) {
       c->h_arena = nullptr;
       (void)hipGetLastError();
       return fail(MOE_ENOMEM, "page-locked host arena allocation failed");
@@ -923,7 +972,7 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
       HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence));
     {
       const size_t nz = (size_t)moe::kDecodeMaxTokens * n_experts;
-      HIPCHK(hipHostMalloc((void **)&c->h_z, nz * 8, hipHostMallocCoherent));
+      ALLOCCHK(host_malloc((void **)&c->h_z, nz * 8, hipHostMallocCoherent), "logit buffer");
       std::memset(c->h_z, 0, nz * 8);
       c->h_zf.resize(nz);
     }
@@ -941,8 +990,7 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
       ly.planner.reset(
           new moe::SlotPlanner(n_experts, slots, o.policy, o.preheat ? o.adopt : -1));
       const size_t nslots = (size_t)slots + o.n_shared;
-      he = hipMalloc((void **)&ly.d_slots, nslots * c->rec());
-      if (he != hipSuccess) {
+      if (dev_malloc((void **)&ly.d_slots, nslots * c->rec()) != hipSuccess) {
         ly.d_slots = nullptr;
         (void)hipGetLastError();
         return fail(MOE_ENOMEM, "device slot arena allocation failed");
@@ -1147,6 +1195,21 @@ moe_status moe_cache_preload(moe_cache *c, const uint32_t *counts) {
 }
 
 void moe_cache_destroy(moe_cache *c) { delete c; }
+
+moe_status moe_debug_fill_delay(moe_cache *c, int32_t usec) {
+  g_err.clear();
+  if (!c) return fail(MOE_EINVAL, "cache is NULL");
+  if (usec < 0 || usec > 1000000) return fail(MOE_EINVAL, "usec must be in [0, 1000000]");
+  c->fill_delay_us = usec;
+  return MOE_OK;
+}
+
+moe_status moe_debug_fail_alloc(int32_t nth) {
+  g_err.clear();
+  if (nth < -1) return fail(MOE_EINVAL, "nth must be >= -1");
+  g_fail_alloc_in = nth;
+  return MOE_OK;
+}
 
 moe_status moe_debug_last_call(moe_cache *c, int32_t layer, int32_t *n_stages, int32_t *n_tokens) {
   g_err.clear();

@@ -340,6 +340,23 @@ moe_status moe_debug_partials(moe_cache *c, int32_t layer, float *gpu_part, floa
  * bit-for-bit comparison.  Synchronises the device. */
 moe_status moe_debug_logits(moe_cache *c, int32_t layer, float *z);
 
+/* ---- failure forcing for tests (host-driven; every kernel still runs normally) ---- */
+
+/* Holds every batch of copy-engine slot fills of this cache (host mode, staged
+ * calls) for usec microseconds before it starts (a host function on the copy
+ * stream), as a slow link would.  Results, tables and logs must not change:
+ * no kernel reads a slot before its copy has landed ("Keeping the cache
+ * fresh", llama.cpp + MoE expert cache: a slot leaves the table before its copy
+ * and is published after it).  0 turns it off; usec in [0, 1e6]. */
+moe_status moe_debug_fill_delay(moe_cache *c, int32_t usec);
+
+/* Makes the nth device or page-locked allocation from now on, on this thread,
+ * fail as if memory were exhausted (0 = the next one; -1 = none).  The call
+ * that needed it returns MOE_ENOMEM: moe_cache_create frees everything it had
+ * allocated, moe_layer_forward leaves the cache usable (its allocations precede
+ * its work).  Fires once. */
+moe_status moe_debug_fail_alloc(int32_t nth);
+
 /* ---- host-only pieces, callable without a GPU ---- */
 
 typedef struct moe_planner moe_planner; /* the per-layer LRU slot planner alone */
