@@ -52,8 +52,7 @@ KERNEL_SRC = os.path.join(ROOT, "expert_cache_host_amd", "csrc", "kernels.hip")
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 # the library's kernel ids -> kernel names in rocprofv3 output
 KERNEL_SYMBOL = {"gateup": "q4_gateup_kernel", "down": "q4_down_kernel", "fill": "pull_kernel",
-                 "router": "router_decode_kernel", "topk": "topk_decode_kernel", "combine": "combine_kernel",
-                 "gemv": "q4_fused_kernel"}
+                 "router": "router_decode_kernel", "topk": "topk_decode_kernel", "combine": "combine_kernel"}
 # batches beyond the decode path (more than 4 tokens) take these instead
 KERNEL_SYMBOL_GEMM = {**KERNEL_SYMBOL, "gateup": "q4_mfma_kernel<true>", "down": "q4_mfma_kernel<false>",
                       "router": "router_kernel", "topk": "topk_kernel", "remap": "remap_kernel",
@@ -367,7 +366,7 @@ def run_leg(wl, weights, steps, warmup, policy="lru", max_fills=-1, breakdown=Tr
     cache.sync()
     st0 = cache.stats()  # the warm-up calls: slots start from the preload
     cache.reset_stats()
-    cache.set_kernel_timing(["gateup", "down", "gemv"])
+    cache.set_kernel_timing(["gateup", "down"])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run(warmup, steps)
@@ -435,12 +434,8 @@ def run_leg(wl, weights, steps, warmup, policy="lru", max_fills=-1, breakdown=Tr
                          "inside the timed region"}
 
     if decode:
-        if ks["gemv"][0]:
-            # one launch: gate/up + SwiGLU and down of every cached expert
-            leg["roofline"] = hbm_roof("gemv")
-        else:
-            leg["roofline"] = hbm_roof("gateup")
-            leg["roofline_down"] = hbm_roof("down")
+        leg["roofline"] = hbm_roof("gateup")
+        leg["roofline_down"] = hbm_roof("down")
     else:
         ng, sg, bg = ks["gateup"]
         nd, sd, bd = ks["down"]

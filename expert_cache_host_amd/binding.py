@@ -101,8 +101,6 @@ def load_library():
         "moe_planner_destroy": (None, [P]),
         "moe_debug_fill_delay": (I32, [P, I32]),
         "moe_debug_fail_alloc": (I32, [I32]),
-        "moe_cache_set_fused": (I32, [P, I32]),
-        "moe_debug_gemv_status": (I32, [P, P]),
         "moe_host_topk": (I32, [P, I32, I32, I32, I32, P, P]),
         "moe_host_expert_forward": (I32, [P, I32, I32, P, I32, P, I32]),
     }
@@ -217,20 +215,10 @@ class MoECache:
         _check(load_library().moe_cache_stats(self._h, layer, ctypes.byref(st)))
         return {n: getattr(st, n) for n, _ in Stats._fields_}
 
-    KERNELS = ("router", "topk", "remap", "gateup", "down", "combine", "fill", "prep", "gemv")
+    KERNELS = ("router", "topk", "remap", "gateup", "down", "combine", "fill", "prep")
 
     def set_timing(self, on: bool):
         _check(load_library().moe_cache_set_timing(self._h, 1 if on else 0))
-
-    def set_fused(self, on: bool):
-        """Decode GEMV in one launch over the XCDs (True, the default) or two."""
-        _check(load_library().moe_cache_set_fused(self._h, 1 if on else 0))
-
-    def gemv_status(self) -> int:
-        """The one-launch decode GEMV's sticky error word (0 = none)."""
-        v = ctypes.c_uint32()
-        _check(load_library().moe_debug_gemv_status(self._h, ctypes.byref(v)))
-        return v.value
 
     def set_kernel_timing(self, kernels):
         """Times only the named kernels (names from KERNELS) from now on."""

@@ -227,8 +227,6 @@ struct moe_cache {
   uint64_t *h_z = nullptr;
   uint32_t z_seq = 0;
   bool poisoned = false;
-  bool fused_on = false;      // decode GEMV as one launch split over the XCDs
-  uint32_t *d_err = nullptr;  // the fused GEMV's sticky error word (device)
   bool timing = false;   // per-layer compute and fill events
   uint32_t kmask = 0;    // kernels timed one launch at a time (bit MOE_K_*)
   // device workspace of moe_layer_forward (grown on demand) and the fixed
@@ -251,9 +249,7 @@ struct moe_cache {
   std::unique_ptr<moe::ThreadPool> pool;
 
   size_t rec() const { return (size_t)lay.bytes; }
-  moe::WsParams ws_params(int32_t T) const {
-    return {T, E, o.top_k, o.n_shared, d, f, fused_on ? 1 : 0};
-  }
+  moe::WsParams ws_params(int32_t T) const { return {T, E, o.top_k, o.n_shared, d, f}; }
   int32_t n_total() const { return E + o.n_shared; }
   const uint8_t *host_record(int32_t l, int32_t e) const {
     return h_arena + ((size_t)l * n_total() + e) * rec();
@@ -274,7 +270,6 @@ struct moe_cache {
     layers.clear();
     if (h_arena) (void)hipHostFree(h_arena);
     if (h_z) (void)hipHostFree(h_z);
-    if (d_err) (void)hipFree(d_err);
     if (ev_idx) (void)hipEventDestroy(ev_idx);
     if (ev_ready) (void)hipEventDestroy(ev_ready);
     for (auto &e : partial_ev)
@@ -316,7 +311,7 @@ namespace {
 // Device pointers of one call's workspace, carved from `base` by its layout.
 struct Ws {
   void *z, *idx, *w, *h, *y;
-  void *xq, *xs, *buckets, *pair_slot, *gsync;
+  void *xq, *xs, *buckets, *pair_slot;
   void *meta, *bucket_pair, *items, *xp, *xscale, *hp, *hscale;
 };
 
@@ -324,9 +319,9 @@ Ws carve(void *base, const moe::WsLayout &L) {
   auto at = [&](const moe::WsRegion &r) -> void * {
     return r.bytes ? (void *)((uint8_t *)base + r.off) : nullptr;
   };
-  return Ws{at(L.z),    at(L.idx),         at(L.w),       at(L.h),         at(L.y),
-            at(L.xq),   at(L.xs),          at(L.buckets), at(L.pair_slot), at(L.gsync),
-            at(L.meta), at(L.bucket_pair), at(L.items),   at(L.xp),        at(L.xscale),
+  return Ws{at(L.z),    at(L.idx),         at(L.w),     at(L.h),  at(L.y),
+            at(L.xq),   at(L.xs),          at(L.buckets), at(L.pair_slot),
+            at(L.meta), at(L.bucket_pair), at(L.items), at(L.xp), at(L.xscale),
             at(L.hp),   at(L.hscale)};
 }
 
@@ -547,35 +542,6 @@ void run_experts(moe_cache *c, int32_t layer, int32_t T, const moe::SlotView &vi
     return;
   }
   moe::GemvShape sh1 = moe::choose_gemv(true, a.nb, T);
-  if (WL.fused) {
-    // one launch for gate/up and down, split over the XCDs
-    moe::GemvArgs b = a;
-    b.off_q0 = L.off_dq;
-    b.off_s0 = L.off_ds;
-    b.rows = c->d;
-    b.nb = (int)L.nb_dn;
-    b.in = (const float *)ws.h;
-    b.in_by_pair = 1;
-    b.out = nullptr;
-    const moe::FusedShape fs = moe::fused_shape(b.nb);
-    moe::FusedArgs fa{};
-    int max_rows = 0;
-    for (int x = 0; x <= moe::kSlices; ++x) fa.kb[x] = moe::slice_begin(b.nb, x);
-    for (int x = 0; x < moe::kSlices; ++x) max_rows = std::max(max_rows, 32 * (fa.kb[x + 1] - fa.kb[x]));
-    fa.gu_tiles = (max_rows + sh1.rows_wg - 1) / sh1.rows_wg;
-    fa.dn_tiles = (c->d + moe::fused_down_rows(fs) - 1) / moe::fused_down_rows(fs);
-    fa.n_buckets = n_buckets;
-    fa.cnt = (int32_t *)ws.gsync;
-    fa.err = c->d_err;
-    fa.y_part = (float *)ws.y;
-    fa.part_stride = (long long)WL.pairs * c->d;
-    if ((int64_t)n_buckets * moe::kSlices > (int64_t)(WL.gsync.bytes / 4))
-      throw HipError("fused GEMV counters too small for the launch");
-    KTime kt(c, MOE_K_GEMV, st);
-    HIPCHK(moe::launch_fused(a, b, fa, tab, sh1, st));
-    kt.end(work_experts * 3.0 * (double)c->d * (double)L.nb_dn * 18.0);
-    return;
-  }
   {
     KTime kt(c, MOE_K_GATEUP, st);
     HIPCHK(moe::launch_gemv(a, tab, sh1, true, n_buckets, st));
@@ -665,8 +631,6 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
     a.shared_slot = ns > 0 ? c->S : -1;
     a.buckets = (int32_t *)ws.buckets;
     a.pair_slot = (int32_t *)ws.pair_slot;
-    a.gemv_cnt = WL.fused ? (int32_t *)ws.gsync : nullptr;
-    a.n_cnt = WL.fused ? (int)(WL.gsync.bytes / 4) : 0;
     // a new number for every call: words left from earlier calls never match
     if (++c->z_seq == 0) ++c->z_seq;
     HIPCHK(moe::launch_router(x, T, d, router_w, router_bias, E, (float *)ws.z, nullptr,
@@ -722,11 +686,9 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
                      host_mode ? c->o.max_fills_per_call : -1, ly.plan);
   }
   ly.st.plan_s += now_s() - tp;
-  if (c->kmask & ((1u << MOE_K_GATEUP) | (1u << MOE_K_DOWN) | (1u << MOE_K_GEMV))) {
+  if (c->kmask & ((1u << MOE_K_GATEUP) | (1u << MOE_K_DOWN))) {
     const double n_hit = (double)(ly.plan.stages[0].members.size() -
                                   (host_mode ? 0 : ly.plan.stages[0].fills.size())) + ns;
-    if (WL.fused && (c->kmask & (1u << MOE_K_GEMV)))
-      c->kt[MOE_K_GEMV].bytes += n_hit * 3.0 * (double)c->d * (double)c->lay.nb_dn * 18.0;
     if (c->kmask & (1u << MOE_K_GATEUP))
       c->kt[MOE_K_GATEUP].bytes += n_hit * 2.0 * (double)c->f * (double)c->lay.nb_gu * 18.0;
     if (c->kmask & (1u << MOE_K_DOWN))
@@ -758,8 +720,6 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
         }
         pl.n = tab.n;
         pl.per_expert = 32;
-        pl.gemv_cnt = WL.fused ? (int32_t *)ws.gsync : nullptr;
-        pl.n_cnt = WL.fused ? (int)(WL.gsync.bytes / 4) : 0;
         pl.bytes16 = (long long)c->rec() / 16;
         {
           TraceRange tr("moe.fill_pull");
@@ -839,8 +799,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
       {
         TraceRange tr("moe.combine");
         KTime kt(c, MOE_K_COMBINE, st);
-        HIPCHK(moe::launch_combine((const float *)ws.y, WL.y_parts,
-                                   (long long)WL.pairs * d, (const float *)ws.w,
+        HIPCHK(moe::launch_combine((const float *)ws.y, (const float *)ws.w,
                                    (const int32_t *)ws.idx, pre, 0,
                                    dec ? (const int32_t *)ws.pair_slot : nullptr, T, k, d, ns,
                                    host_part, out, dbg_gpu, st));
@@ -856,8 +815,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   if (!combined) {
     TraceRange tr("moe.combine");
     KTime kt(c, MOE_K_COMBINE, st);
-    HIPCHK(moe::launch_combine((const float *)ws.y, WL.y_parts, (long long)WL.pairs * d,
-                               (const float *)ws.w,
+    HIPCHK(moe::launch_combine((const float *)ws.y, (const float *)ws.w,
                                (const int32_t *)ws.idx, pre, host_mode ? 0 : 1,
                                dec ? (const int32_t *)ws.pair_slot : nullptr, T, k, d, ns,
                                nullptr, out, dbg_gpu, st));
@@ -1018,8 +976,6 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
       std::memset(c->h_z, 0, nz * 8);
       c->h_zf.resize(nz);
     }
-    ALLOCCHK(dev_malloc((void **)&c->d_err, 4), "error word");
-    HIPCHK(hipMemset(c->d_err, 0, 4));
     // the fixed scratch of moe_layer_forward_noalloc on this device, and the
     // page-locked buffers and host bookkeeping of its largest call
     HIPCHK(moe::noalloc_scratch(&c->scratch));
@@ -1204,31 +1160,6 @@ moe_status moe_cache_sync(moe_cache *c) {
   if (!c) return fail(MOE_EINVAL, "cache is NULL");
   return guarded(c, [&]() {
     for (auto sd : c->side) HIPCHK(hipStreamSynchronize(sd));
-    uint32_t err = 0;
-    HIPCHK(hipMemcpy(&err, c->d_err, 4, hipMemcpyDeviceToHost));
-    if (err) throw HipError("fused GEMV reported error " + std::to_string(err));
-    return MOE_OK;
-  });
-}
-
-moe_status moe_cache_set_fused(moe_cache *c, int32_t on) {
-  g_err.clear();
-  if (!c) return fail(MOE_EINVAL, "cache is NULL");
-  if (on != 0 && on != 1) return fail(MOE_EINVAL, "on must be 0 or 1");
-  return guarded(c, [&]() {
-    // the workspace layout changes with it: no call may be in flight
-    HIPCHK(hipDeviceSynchronize());
-    c->fused_on = on != 0;
-    return MOE_OK;
-  });
-}
-
-moe_status moe_debug_gemv_status(moe_cache *c, uint32_t *err) {
-  g_err.clear();
-  if (!c || !err) return fail(MOE_EINVAL, "NULL argument");
-  return guarded(c, [&]() {
-    HIPCHK(hipDeviceSynchronize());
-    HIPCHK(hipMemcpy(err, c->d_err, 4, hipMemcpyDeviceToHost));
     return MOE_OK;
   });
 }

@@ -539,7 +539,6 @@ __device__ void topk_decode_block(const float *z, int T, int E, const DecodeTopk
       sidx[o] = my_e;
     }
   }
-  for (int i = threadIdx.x; i < a.n_cnt; i += blockDim.x) a.gemv_cnt[i] = 0;
   __syncthreads();
   if (t != 0) return;
   const int Pr = T * k;
@@ -836,11 +835,8 @@ __device__ __forceinline__ int scale_chunks(int rows_here, int nb) {
 
 // gate/up + SwiGLU.  LDS: the bucket's x planes [TT][nb][4], its x block scales
 // [TT][4 * xs_units(nb)], then the gate and the up scales of the workgroup's rows.
-// One workgroup's rows [r0, min(r0 + RWG, r_end)) of bucket `bi` (r0 a multiple
-// of 8).  Returns false when the bucket does not exist (nothing written).
 template <int G, int KS, int R, int TT, int MODE, int NW, int PF>
-__device__ __forceinline__ bool gateup_rows(const GemvArgs &a, const BucketTable &tab, int bi,
-                                            int r0, int r_end) {
+__global__ __launch_bounds__(64 * NW) void q4_gateup_kernel(GemvArgs a, BucketTable tab) {
   constexpr int RW = 64 / G;
   constexpr int RWG = (NW / KS) * RW * R;
   constexpr int NT = 64 * NW;
@@ -849,11 +845,12 @@ __device__ __forceinline__ bool gateup_rows(const GemvArgs &a, const BucketTable
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int ks = wave % KS, rg = wave / KS;
   Bucket<TT> bk;
-  if (!find_bucket<TT, MODE>(a, tab, bi, bk)) return false;
+  if (!find_bucket<TT, MODE>(a, tab, blockIdx.y, bk)) return;
   const uint8_t *rec = bk.src;
   const int nb = a.nb;
   const int gl = lane % G;
-  const int rows_here = min(RWG, r_end - r0);
+  const int r0 = blockIdx.x * RWG;
+  const int rows_here = min(RWG, a.rows - r0);
   const int rbase = r0 + rg * RW * R + lane / G;
   const uint4 *q0 = reinterpret_cast<const uint4 *>(rec + a.off_q0);
   const uint4 *q1 = reinterpret_cast<const uint4 *>(rec + a.off_q1);
@@ -867,7 +864,7 @@ __device__ __forceinline__ bool gateup_rows(const GemvArgs &a, const BucketTable
   long long ro[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    const int r = min(rbase + RW * i, r_end - 1);
+    const int r = min(rbase + RW * i, a.rows - 1);
     rl[i] = (r - r0) * nb;
     ro[i] = (long long)r * nb;
   }
@@ -880,7 +877,7 @@ __device__ __forceinline__ bool gateup_rows(const GemvArgs &a, const BucketTable
   const int n_stage = n_x + n_xs + 2 * n_s;
   const uint4 *xs4 = reinterpret_cast<const uint4 *>(a.xs);
   auto row_of = [&](int tt) {
-    return TT <= 2 ? pick(tok, tt) : pair_row(a, pair_at<TT, MODE>(a, tab, bi, bk, tt));
+    return TT <= 2 ? pick(tok, tt) : pair_row(a, pair_at<TT, MODE>(a, tab, blockIdx.y, bk, tt));
   };
   auto stage_ld = [&](int u) -> uint4 {
     u = min(u, n_stage - 1);
@@ -1001,24 +998,17 @@ __device__ __forceinline__ bool gateup_rows(const GemvArgs &a, const BucketTable
   for (int o = tid; o < (NW / KS) * RW * R * TT; o += NT) {
     const int g = o / (RW * R * TT), rr = (o / TT) % (RW * R), tt = o % TT;
     const int r = r0 + g * RW * R + rr;
-    if (r < r_end && tt < bk.cnt) {
+    if (r < a.rows && tt < bk.cnt) {
       float gg = 0.0f, uu = 0.0f;
 #pragma unroll
       for (int q = 0; q < KS; ++q) {
         gg += red[g * KS + q][rr][tt][0];
         uu += red[g * KS + q][rr][tt][1];
       }
-      const int p = pair_at<TT, MODE>(a, tab, bi, bk, tt);
+      const int p = pair_at<TT, MODE>(a, tab, blockIdx.y, bk, tt);
       a.out[(long long)p * a.rows + r] = silu_f(gg) * uu;
     }
   }
-  return true;
-}
-
-template <int G, int KS, int R, int TT, int MODE, int NW, int PF>
-__global__ __launch_bounds__(64 * NW) void q4_gateup_kernel(GemvArgs a, BucketTable tab) {
-  constexpr int RWG = (NW / KS) * (64 / G) * R;
-  (void)gateup_rows<G, KS, R, TT, MODE, NW, PF>(a, tab, blockIdx.y, blockIdx.x * RWG, a.rows);
 }
 
 // down: y = D h.  The prologue turns the bucket's h rows (fp32, by pair) into
@@ -1235,224 +1225,6 @@ hipError_t launch_gemv(const GemvArgs &a, const BucketTable *tab, const GemvShap
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
-}
-
-// ============================================================== fused decode GEMV
-// Gate/up + SwiGLU and down of every bucket in one launch, split over the
-// XCDs.  Workgroup i of the 1-D grid runs on XCD i % kSlices (the round-robin
-// dispatch of the MI355X; each workgroup checks it).  Slice x owns whole 32-
-// element blocks [kb[x], kb[x+1]) of the hidden dimension f: the gate/up rows
-// that make those h elements, and the same K range of the down projection.
-// Each XCD therefore does 1/kSlices of every expert, and the h it needs never
-// leaves its own L2:
-//   - workgroups [0, n_gu) compute gate/up row tiles (bucket-major per slice),
-//     store their h rows, wait until those stores have reached the L2
-//     (s_waitcnt vmcnt(0)), then add one to the counter of (slice, bucket);
-//   - workgroups [n_gu, n_gu + n_dn) compute down row tiles over their slice's
-//     K range: one thread waits until the counter shows every gate/up tile of
-//     (slice, bucket) (a bounded wait; a wait that runs out sets err bit 1),
-//     then the workgroup reads its h slice with sc0 loads (past the CU's L1,
-//     from the XCD's L2), turns it into block-scaled digit planes and writes
-//     one partial output per slice, y_part[x][pair][row]; the combine adds the
-//     kSlices partials in slice order.
-// No L2 write-back or invalidate is needed, since producer and consumer share
-// the L2.  Workgroups are dispatched in order on each XCD, so every gate/up
-// workgroup of a slice is resident or done before its first down workgroup
-// starts waiting.  The counters are zeroed by the kernel that precedes the
-// launch on the stream (the decode top-k kernel, or the pull kernel).
-// Polls of a down workgroup's wait (each an agent-scope load and a short sleep,
-// about 1-2 us): a wait that could not end stops within ~0.1 s and sets err bit 1.
-constexpr int kSpinLimit = 1 << 16;
-
-template <int GD, int RD, int TT, int MODE, int NW, int RWG_GU>
-__device__ __forceinline__ void down_slice(const GemvArgs &b, const FusedArgs &f,
-                                           const BucketTable &tab, int bi, int x, int tile) {
-  constexpr int RW = 64 / GD;
-  constexpr int RWG = NW * RW * RD;  // rows per workgroup
-  __shared__ uint4 hpl[TT * kFusedMaxSliceBlocks * 4];  // digit planes [TT][blocks][4]
-  __shared__ float hsc[TT * kFusedMaxSliceBlocks];      // block scales [TT][blocks]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
-  Bucket<TT> bk;
-  if (!find_bucket<TT, MODE>(b, tab, bi, bk)) return;
-  const int r0 = tile * RWG;
-  if (r0 >= b.rows) return;
-  const int kb0 = f.kb[x], nbx = f.kb[x + 1] - kb0;
-  // every gate/up tile of this slice and bucket has published its h rows
-  const int need = (32 * nbx + RWG_GU - 1) / RWG_GU;
-  if (tid == 0) {
-    bool ok = false;
-    for (int i = 0; i < kSpinLimit; ++i) {
-      if (__hip_atomic_load(f.cnt + x * f.n_buckets + bi, __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_AGENT) >= need) {
-        ok = true;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-    if (!ok) __hip_atomic_fetch_or(f.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  // the h slice as digit planes with one scale per block: unit tid = (token,
-  // block, word), 8 elements, read from the L2 (sc0); a block's four units are
-  // four consecutive threads
-  const int n_units = TT * nbx * 4;
-  if (tid < n_units) {
-    const int tt = tid / (nbx * 4), rem = tid - tt * nbx * 4, blk = rem >> 2, j = rem & 3;
-    const int p = pair_at<TT, MODE>(b, tab, bi, bk, tt);
-    const float *hr = b.in + (long long)p * (b.nb * 32) + 32 * (kb0 + blk) + 4 * j;
-    float v[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[q] = __hip_atomic_load(hr + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      v[q + 4] = __hip_atomic_load(hr + 16 + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    float sb;
-    const uint4 pl = block_planes8(v, sb);
-    hpl[tid] = pl;
-    if (j == 0) hsc[tt * nbx + blk] = sb;
-  }
-  __syncthreads();
-  const uint8_t *rec = bk.src;
-  const uint4 *q0 = reinterpret_cast<const uint4 *>(rec + b.off_q0);
-  const _Float16 *s0 = reinterpret_cast<const _Float16 *>(rec + b.off_s0);
-  const int gl = lane % GD;
-  const int rbase = r0 + wave * RW * RD + lane / GD;
-  long long ro[RD];
-#pragma unroll
-  for (int i = 0; i < RD; ++i) ro[i] = (long long)min(rbase + RW * i, b.rows - 1) * b.nb;
-  float acc[RD][TT];
-#pragma unroll
-  for (int i = 0; i < RD; ++i)
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) acc[i][tt] = 0.0f;
-  for (int j0 = 0; j0 < nbx; j0 += GD) {
-    const int jb = j0 + gl;
-    const bool okb = jb < nbx;
-    const int jc = min(jb, nbx - 1);
-    uint4 w[RD];
-    _Float16 sc[RD];
-#pragma unroll
-    for (int i = 0; i < RD; ++i) {
-      w[i] = ldnt(&q0[ro[i] + kb0 + jc]);
-      sc[i] = s0[ro[i] + kb0 + jc];
-    }
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      uint4 P[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) P[q] = hpl[(tt * nbx + jc) * 4 + q];
-      const float se = hsc[tt * nbx + jc];
-#pragma unroll
-      for (int i = 0; i < RD; ++i)
-        acc[i][tt] = __builtin_fmaf((float)dot_block_i4(w[i], P) * se, okb ? (float)sc[i] : 0.0f,
-                                    acc[i][tt]);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < RD; ++i)
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-#pragma unroll
-      for (int o = GD / 2; o >= 1; o >>= 1) acc[i][tt] += __shfl_xor(acc[i][tt], o, 64);
-    }
-  if (gl == 0) {
-    float *yp = f.y_part + (long long)x * f.part_stride;
-#pragma unroll
-    for (int i = 0; i < RD; ++i) {
-      const int r = rbase + RW * i;
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        if (r < b.rows && tt < bk.cnt)
-          yp[(long long)pair_at<TT, MODE>(b, tab, bi, bk, tt) * b.rows + r] = acc[i][tt];
-      }
-    }
-  }
-}
-
-template <int G, int KS, int R, int GD, int RD, int TT, int MODE, int NW, int PF>
-__global__ __launch_bounds__(64 * NW) void q4_fused_kernel(GemvArgs a, GemvArgs b, FusedArgs f,
-                                                           BucketTable tab) {
-  constexpr int RWG_GU = (NW / KS) * (64 / G) * R;
-  const int lin = blockIdx.x, x = lin % kSlices;
-  if (threadIdx.x == 0 && (__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u) != (unsigned)x)
-    __hip_atomic_fetch_or(f.err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int n_gu = kSlices * f.n_buckets * f.gu_tiles;
-  if (lin < n_gu) {
-    const int item = lin / kSlices;
-    const int bi = item / f.gu_tiles, tile = item - bi * f.gu_tiles;
-    const int row1 = 32 * f.kb[x + 1];
-    const int r0 = 32 * f.kb[x] + tile * RWG_GU;
-    if (r0 >= row1) return;
-    if (!gateup_rows<G, KS, R, TT, MODE, NW, PF>(a, tab, bi, r0, row1)) return;
-    // this workgroup's h rows reach the L2 before the count
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(f.cnt + x * f.n_buckets + bi, 1, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-    return;
-  }
-  const int item = (lin - n_gu) / kSlices;
-  const int bi = item / f.dn_tiles, tile = item - bi * f.dn_tiles;
-  down_slice<GD, RD, TT, MODE, NW, RWG_GU>(b, f, tab, bi, x, tile);
-}
-
-template <int G, int KS, int R, int GD, int RD, int TT, int MODE, int PF>
-static void launch_fused_one(const GemvArgs &a, const GemvArgs &b, const FusedArgs &f,
-                             const BucketTable &tab, size_t lds, hipStream_t s) {
-  const int n = kSlices * f.n_buckets * (f.gu_tiles + f.dn_tiles);
-  hipLaunchKernelGGL((q4_fused_kernel<G, KS, R, GD, RD, TT, MODE, 4, PF>), dim3(n), dim3(256),
-                     lds, s, a, b, f, tab);
-}
-
-template <int G, int KS, int R, int GD, int RD, int PF = 1>
-static void launch_fused_tt(const GemvArgs &a, const GemvArgs &b, const FusedArgs &f,
-                            const BucketTable &tab, int TT, size_t lds, hipStream_t s) {
-  const bool t = tab.n >= 0;
-  switch (TT) {
-    case 1:
-      t ? launch_fused_one<G, KS, R, GD, RD, 1, BK_TABLE, PF>(a, b, f, tab, lds, s)
-        : launch_fused_one<G, KS, R, GD, RD, 1, BK_LIST, PF>(a, b, f, tab, lds, s);
-      break;
-    case 2:
-      t ? launch_fused_one<G, KS, R, GD, RD, 2, BK_TABLE, PF>(a, b, f, tab, lds, s)
-        : launch_fused_one<G, KS, R, GD, RD, 2, BK_LIST, PF>(a, b, f, tab, lds, s);
-      break;
-    default:
-      t ? launch_fused_one<G, KS, R, GD, RD, 4, BK_TABLE, PF>(a, b, f, tab, lds, s)
-        : launch_fused_one<G, KS, R, GD, RD, 4, BK_LIST, PF>(a, b, f, tab, lds, s);
-      break;
-  }
-}
-
-template <int GD, int RD>
-static hipError_t launch_fused_gd(const GemvArgs &a, const GemvArgs &b, const FusedArgs &f,
-                                  const BucketTable &t, const GemvShape &sh, size_t lds,
-                                  hipStream_t s) {
-  switch (sh.G * 100 + sh.KS * 10 + sh.R) {
-    case 1600 + 40 + 2: launch_fused_tt<16, 4, 2, GD, RD>(a, b, f, t, sh.TT, lds, s); break;
-    case 800 + 40 + 1: launch_fused_tt<8, 4, 1, GD, RD>(a, b, f, t, sh.TT, lds, s); break;
-    case 800 + 10 + 2: launch_fused_tt<8, 1, 2, GD, RD>(a, b, f, t, sh.TT, lds, s); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_fused(const GemvArgs &a, const GemvArgs &b, const FusedArgs &f,
-                        const BucketTable *tab, const GemvShape &sh, hipStream_t s) {
-  if (f.n_buckets <= 0) return hipSuccess;
-  if (!tab && !a.bt) return hipErrorInvalidValue;
-  const FusedShape fs = fused_shape(b.nb);
-  if (!fs.ok || sh.TT * fs.max_blocks > kFusedMaxTokenBlocks) return hipErrorInvalidValue;
-  BucketTable none;
-  none.n = -1;
-  const BucketTable &t = tab ? *tab : none;
-  const size_t lds = gemv_lds_bytes(true, a.nb, sh.TT);
-  switch (fs.GD) {
-    case 4: return launch_fused_gd<4, 4>(a, b, f, t, sh, lds, s);
-    case 8: return launch_fused_gd<8, 4>(a, b, f, t, sh, lds, s);
-    default: return launch_fused_gd<16, 8>(a, b, f, t, sh, lds, s);
-  }
 }
 
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
@@ -1797,8 +1569,6 @@ hipError_t launch_prep_pairs(const float *in, int rows, int K, uint32_t *xp, flo
 
 // ============================================================== slot fills
 __global__ __launch_bounds__(256) void pull_kernel(PullList l) {
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < l.n_cnt; i += blockDim.x) l.gemv_cnt[i] = 0;
   const int e = blockIdx.x / l.per_expert, part = blockIdx.x % l.per_expert;
   if (e >= l.n) return;
   const long long per = (l.bytes16 + l.per_expert - 1) / l.per_expert;
@@ -1832,8 +1602,7 @@ hipError_t launch_pull(const PullList &l, hipStream_t s) {
 // top-k kernel's table), else when view.slot[idx[p]] >= 0.  The loads of 8
 // pairs are issued together; pairs off the GPU are skipped by select, since
 // their y rows were never written.
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y, int n_parts,
-                                                      long long part_stride,
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y,
                                                       const float *__restrict__ w,
                                                       const int32_t *__restrict__ idx,
                                                       SlotView view, int all_gpu,
@@ -1859,13 +1628,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
       on[u] = g;
       wv[u] = w[p];
       yv[u] = *reinterpret_cast<const float4 *>(y + p * d + i);
-      for (int q = 1; q < n_parts; ++q) {
-        const float4 v = *reinterpret_cast<const float4 *>(y + q * part_stride + p * d + i);
-        yv[u].x += v.x;
-        yv[u].y += v.y;
-        yv[u].z += v.z;
-        yv[u].w += v.w;
-      }
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -1878,15 +1640,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     }
   }
   if (n_shared) {
-    float4 yv = *reinterpret_cast<const float4 *>(y + ((long long)T * k + t) * d + i);
-    for (int q = 1; q < n_parts; ++q) {
-      const float4 v =
-          *reinterpret_cast<const float4 *>(y + q * part_stride + ((long long)T * k + t) * d + i);
-      yv.x += v.x;
-      yv.y += v.y;
-      yv.z += v.z;
-      yv.w += v.w;
-    }
+    const float4 yv = *reinterpret_cast<const float4 *>(y + ((long long)T * k + t) * d + i);
     acc.x += yv.x;
     acc.y += yv.y;
     acc.z += yv.z;
@@ -1903,13 +1657,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   *reinterpret_cast<float4 *>(out + (long long)t * d + i) = acc;
 }
 
-hipError_t launch_combine(const float *y, int n_parts, long long part_stride, const float *w,
-                          const int32_t *idx, const SlotView &view, int all_gpu,
-                          const int32_t *pair_slot, int T, int k, int d, int n_shared,
-                          const float *host_part, float *out, float *dbg_gpu, hipStream_t s) {
+hipError_t launch_combine(const float *y, const float *w, const int32_t *idx,
+                          const SlotView &view, int all_gpu, const int32_t *pair_slot, int T,
+                          int k, int d, int n_shared, const float *host_part, float *out,
+                          float *dbg_gpu, hipStream_t s) {
   const dim3 grid((d / 4 + 255) / 256, T);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, y, n_parts, part_stride, w, idx, view,
-                     all_gpu, pair_slot, T, k, d, n_shared, host_part, out, dbg_gpu);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, y, w, idx, view, all_gpu, pair_slot,
+                     T, k, d, n_shared, host_part, out, dbg_gpu);
   return hipGetLastError();
 }
 

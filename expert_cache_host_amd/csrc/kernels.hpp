@@ -57,8 +57,6 @@ struct DecodeTopk {
   SlotView view;
   int shared_slot;
   int32_t *buckets, *pair_slot;
-  int32_t *gemv_cnt;  // fused GEMV counters to zero (n_cnt ints), or nullptr
-  int n_cnt;
 };
 hipError_t launch_topk_decode(const float *z, int T, int E, const DecodeTopk &a, hipStream_t s);
 
@@ -116,28 +114,6 @@ struct BucketTable {
 hipError_t launch_gemv(const GemvArgs &a, const BucketTable *tab, const GemvShape &sh, bool glu,
                        int n_buckets, hipStream_t s);
 
-// Fused decode GEMV: gate/up + SwiGLU and down of every bucket in one launch,
-// split over the kSlices XCDs (slice x owns down K blocks [kb[x], kb[x+1]) and
-// the gate/up rows that make them).  a: the gate/up arguments (rows d_ff,
-// out = h), b: the down arguments (rows d_model, in = h); the buckets come as
-// for launch_gemv.  Output: y_part[x][pair][row], one partial per slice.  The
-// counters (kSlices x n_buckets ints) must be zero at launch (the decode top-k
-// and the pull kernel zero them); *err gets bit 1 when a down workgroup's
-// bounded wait ran out and bit 2 when a workgroup ran on another XCD than its
-// slice (either means the outputs are not to be trusted).
-struct FusedArgs {
-  int kb[kSlices + 1];
-  int gu_tiles;          // gate/up workgroups per (slice, bucket) in the grid
-  int dn_tiles;          // down workgroups per (slice, bucket)
-  int n_buckets;         // bucket capacity of the grid
-  int32_t *cnt;
-  uint32_t *err;
-  float *y_part;
-  long long part_stride;  // pairs * d_model
-};
-hipError_t launch_fused(const GemvArgs &a, const GemvArgs &b, const FusedArgs &f,
-                        const BucketTable *tab, const GemvShape &sh, hipStream_t s);
-
 // Prefill grouped GEMM on the matrix cores (batches beyond the decode path).
 // Work items from launch_remap; per workgroup 64 weight rows of one bucket's
 // expert and one pass of up to kGemmTokens of its tokens.  Each wave streams its
@@ -166,19 +142,16 @@ struct PullList {
   int n;
   int per_expert;
   long long bytes16;
-  int32_t *gemv_cnt;  // fused GEMV counters to zero (n_cnt ints), or nullptr
-  int n_cnt;
 };
 hipError_t launch_pull(const PullList &l, hipStream_t s);
 
 // out[t] = sum_j [pair on GPU] w * y[t*k+j] (j ascending) + shared + host part,
 // where a pair is on the GPU when all_gpu, else when pair_slot[p] >= 0 (if
-// pair_slot != nullptr), else when view.slot[idx[p]] >= 0.  y holds n_parts
-// partials per pair (slice-major, part_stride floats apart), added in order.
-hipError_t launch_combine(const float *y, int n_parts, long long part_stride, const float *w,
-                          const int32_t *idx, const SlotView &view, int all_gpu,
-                          const int32_t *pair_slot, int T, int k, int d, int n_shared,
-                          const float *host_part, float *out, float *dbg_gpu, hipStream_t s);
+// pair_slot != nullptr), else when view.slot[idx[p]] >= 0.
+hipError_t launch_combine(const float *y, const float *w, const int32_t *idx,
+                          const SlotView &view, int all_gpu, const int32_t *pair_slot, int T,
+                          int k, int d, int n_shared, const float *host_part, float *out,
+                          float *dbg_gpu, hipStream_t s);
 
 // Device address of the fixed scratch array (kNoAllocScratchBytes, one per
 // device, held until the process ends) on the current device.  The first call

@@ -36,36 +36,6 @@ inline int gemm_items_bound(int buckets, int pairs) {
   return buckets + (pairs + kGemmTokens - 1) / kGemmTokens;
 }
 
-// Fused decode GEMV (one launch for gate/up and down, split over the XCDs):
-// slices of the hidden dimension, one per XCD, of whole 32-element blocks.
-constexpr int kSlices = 8;               // XCDs of the MI355X
-constexpr int kFusedMaxSliceBlocks = 16;  // blocks of one slice
-constexpr int kFusedMaxTokenBlocks = 64;  // tokens x blocks of one slice (<= 256 units / 4)
-
-struct FusedShape {
-  bool ok;         // the fused GEMV takes this d_ff
-  int max_blocks;  // most blocks of one slice
-  int GD;          // lanes per down row (4, 8 or 16)
-  int RD;          // down rows per lane
-};
-
-// Slice x of nb_dn blocks: [x * nb_dn / kSlices, (x + 1) * nb_dn / kSlices).
-inline int slice_begin(int nb_dn, int x) { return x * nb_dn / kSlices; }
-
-// The fused GEMV needs at least one block per slice and at most
-// kFusedMaxSliceBlocks; the down tile's lanes per row follow the slice width.
-inline FusedShape fused_shape(int nb_dn) {
-  FusedShape s{};
-  s.max_blocks = (nb_dn + kSlices - 1) / kSlices;
-  s.ok = nb_dn >= kSlices && s.max_blocks <= kFusedMaxSliceBlocks;
-  s.GD = s.max_blocks <= 4 ? 4 : (s.max_blocks <= 8 ? 8 : 16);
-  s.RD = s.GD == 16 ? 8 : 4;
-  return s;
-}
-
-// Rows of one fused down workgroup (4 waves of 64 / GD rows x RD).
-inline int fused_down_rows(const FusedShape &s) { return 4 * (64 / s.GD) * s.RD; }
-
 struct GemvShape {
   int G;        // lanes per row
   int KS;       // waves of a workgroup that split a row's K blocks

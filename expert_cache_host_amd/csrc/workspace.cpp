@@ -61,13 +61,6 @@ bool decode_path(const WsParams &p) {
          gemv_lds_bytes(false, p.f / 32, p.T) <= kDecodeLdsBudget;
 }
 
-bool fused_path(const WsParams &p) {
-  if (!p.allow_fused || !decode_path(p)) return false;
-  const FusedShape fs = fused_shape(p.f / 32);
-  const int tt = p.T <= 1 ? 1 : (p.T <= 2 ? 2 : 4);
-  return fs.ok && tt * fs.max_blocks <= kFusedMaxTokenBlocks;
-}
-
 namespace {
 
 size_t up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
@@ -88,8 +81,6 @@ WsLayout ws_layout(const WsParams &p) {
   const size_t T = (size_t)p.T, E = (size_t)p.E, k = (size_t)p.k, d = (size_t)p.d,
                f = (size_t)p.f;
   L.decode = decode_path(p);
-  L.fused = fused_path(p);
-  L.y_parts = L.fused ? kSlices : 1;
   L.pairs = p.T * p.k + p.T * p.n_shared;
   const size_t P = (size_t)L.pairs;
   size_t o = 0;
@@ -97,9 +88,7 @@ WsLayout ws_layout(const WsParams &p) {
   L.idx = take(o, T * k * 4);
   L.w = take(o, T * k * 4);
   L.h = take(o, P * f * 4);
-  L.y = take(o, (size_t)L.y_parts * P * d * 4);
-  // at most one bucket per pair; the decode path has at most kDecodeMaxPairs pairs
-  if (L.fused) L.gsync = take(o, (size_t)kSlices * P * 4);
+  L.y = take(o, P * d * 4);
   if (L.decode) {
     L.xq = take(o, T * d * 2);  // [T][d/32 blocks][4 words] x 16 bytes
     L.xs = take(o, T * (size_t)xs_units(p.d / 32) * 16);
@@ -130,18 +119,14 @@ const char *ws_check(const WsLayout &L, const WsParams &p) {
   const double T = p.T, E = p.E, k = p.k, d = p.d, f = p.f;
   const double P = T * k + T * p.n_shared;
   const bool dec = decode_path(p);
-  const bool fus = fused_path(p);
-  if (dec != L.decode || fus != L.fused || (int)P != L.pairs) return "path";
-  if (L.y_parts != (fus ? kSlices : 1)) return "y_parts";
+  if (dec != L.decode || (int)P != L.pairs) return "path";
   Need common[] = {
       {"z", &L.z, T * E * 4},     // router logits [T][E]
       {"idx", &L.idx, T * k * 4},  // top-k ids [T][k]
       {"w", &L.w, T * k * 4},      // gating weights [T][k]
       {"h", &L.h, P * f * 4},      // gate/up output by pair [P][f]
-      {"y", &L.y, L.y_parts * P * d * 4},  // down output by pair [parts][P][d]
+      {"y", &L.y, P * d * 4},      // down output by pair [P][d]
   };
-  // the fused GEMV's counters: one per slice and bucket (at most one bucket per pair)
-  Need fused[] = {{"gsync", &L.gsync, (double)kSlices * P * 4}};
   Need decode[] = {
       {"xq", &L.xq, T * (d / 32) * 4 * 16},  // digit planes: 4 words x 16 B per block
       {"xs", &L.xs, T * xs_units(p.d / 32) * 4 * 4},  // block scales, padded rows
@@ -161,7 +146,6 @@ const char *ws_check(const WsLayout &L, const WsParams &p) {
   };
   std::vector<const Need *> used;
   for (const Need &n : common) used.push_back(&n);
-  if (fus) used.push_back(&fused[0]);
   if (dec)
     for (const Need &n : decode) used.push_back(&n);
   else

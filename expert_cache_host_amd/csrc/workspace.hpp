@@ -32,7 +32,6 @@ struct WsParams {
   int k;         // top-k
   int n_shared;  // resident shared experts (0 or 1)
   int d, f;      // d_model, d_ff
-  int allow_fused = 1;  // 0: decode calls use the two-launch GEMV
 };
 
 struct WsRegion {
@@ -41,13 +40,11 @@ struct WsRegion {
 
 struct WsLayout {
   bool decode = false;  // decode GEMV path, else the matrix-core GEMM
-  bool fused = false;   // decode path through the fused GEMV (y holds kSlices partials)
   int pairs = 0;        // T*k routed pairs + T*n_shared shared pairs
-  int y_parts = 1;      // partial outputs per pair in y
   // every call
   WsRegion z, idx, w, h, y;
-  // decode path (gsync: the fused GEMV's counters, kSlices x pairs ints)
-  WsRegion xq, xs, buckets, pair_slot, gsync;
+  // decode path
+  WsRegion xq, xs, buckets, pair_slot;
   // matrix-core path
   WsRegion meta, bucket_pair, items, xp, xscale, hp, hscale;
   size_t total = 0;  // bytes from the base address
@@ -56,11 +53,6 @@ struct WsLayout {
 // True when the call takes the decode GEMV: at most kDecodeMaxTokens tokens,
 // at most kDecodeMaxPairs pairs, and both GEMV workgroups' LDS within budget.
 bool decode_path(const WsParams &p);
-
-// True when a decode call takes the fused GEMV: d_ff gives every slice one to
-// kFusedMaxSliceBlocks blocks, and tokens x slice blocks fit one down workgroup's
-// h staging.
-bool fused_path(const WsParams &p);
 
 // Regions of the call's path (the other path's regions stay empty).
 WsLayout ws_layout(const WsParams &p);

@@ -264,8 +264,7 @@ moe_status moe_cache_set_timing(moe_cache *c, int32_t on);
 #define MOE_K_COMBINE 5 /* weighted combine */
 #define MOE_K_FILL 6    /* slot fills pulled from the page-locked arena by a kernel */
 #define MOE_K_PREP 7    /* binary16 hi/lo preparation of h for the prefill down GEMM */
-#define MOE_K_GEMV 8    /* decode gate/up + SwiGLU + down in one launch over the XCDs */
-#define MOE_K_COUNT 9
+#define MOE_K_COUNT 8
 
 /* Times only the kernels whose bit (1 << MOE_K_*) is set in kernel_mask, one
  * launch at a time, from now on; the per-layer compute and fill timings of
@@ -286,23 +285,10 @@ moe_status moe_cache_set_kernel_timing(moe_cache *c, uint32_t kernel_mask);
 moe_status moe_cache_kernel_stats(moe_cache *c, int32_t kernel, int64_t *launches, double *seconds,
                                   double *bytes);
 
-/* Decode GEMV form (default 0).  0: two launches, gate/up then down; 1: one
- * launch computes gate/up + SwiGLU and down for every cached expert, each of
- * the MI355X's 8 XCDs taking 1/8 of the hidden dimension (its gate/up rows and
- * the matching K range of down), so that h passes from gate/up to down inside
- * one XCD's L2.  The one-launch form is the slower of the two at 6144 x 2048
- * experts (its down reads each weight row in 8 separate pieces), so it is an
- * option, not the default.  Shapes it does not take (fewer than 8 blocks of
- * d_ff, or more than 16 blocks per slice) use two launches either way.  Waits
- * for the device; results are the same within the layer's tolerance. */
-moe_status moe_cache_set_fused(moe_cache *c, int32_t on);
-
 /* Zeroes every counter and timing (slot contents and eviction logs stay). */
 moe_status moe_cache_reset_stats(moe_cache *c);
 
-/* Waits for the library's side-stream work (slot fills) to finish.  MOE_EHIP
- * (and the cache poisoned) when a one-launch decode GEMV reported a fault of
- * its own checks (see moe_debug_gemv_status). */
+/* Waits for the library's side-stream work (slot fills) to finish. */
 moe_status moe_cache_sync(moe_cache *c);
 
 /* Frees everything the cache owns; waits for its streams first.  NULL is a no-op. */
@@ -342,11 +328,6 @@ moe_status moe_debug_scores(moe_cache *c, int32_t layer, double *scores);
  * records into buf (may be NULL when cap == 0) and stores the total in *n. */
 moe_status moe_debug_evictions(moe_cache *c, int32_t layer, moe_evict_rec *buf, size_t cap,
                                size_t *n);
-
-/* The one-launch decode GEMV's sticky error word (0 = none): bit 1, a down
- * workgroup's bounded wait for its gate/up rows ran out; bit 2, a workgroup ran
- * on another XCD than the slice it was given.  Waits for the device. */
-moe_status moe_debug_gemv_status(moe_cache *c, uint32_t *err);
 
 /* Requires opts.keep_debug.  gpu_part [n_tokens*d_model]: the GPU's sum (routed
  * experts on slots + shared); host_part: the host cores' weighted sum (zeros in

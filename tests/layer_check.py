@@ -28,7 +28,7 @@ def log(msg):
 
 class Runner:
     def __init__(self, wl, layers, slots=None, mode="stream", max_fills=-1, keep_debug=False,
-                 host_threads=0, weights=None, policy="lru", adopt=-1, fused=False):
+                 host_threads=0, weights=None, policy="lru", adopt=-1):
         import torch
         import expert_cache_host_amd as m
         import synth
@@ -48,8 +48,6 @@ class Runner:
                                 top_k=wl.top_k, miss_mode=mode, n_shared=wl.n_shared,
                                 max_fills_per_call=max_fills, keep_debug=keep_debug,
                                 host_threads=host_threads, policy=policy, adopt=adopt)
-        if fused:
-            self.cache.set_fused(True)
         self.policy = policy
         self.sims = [LayerSlots(wl.n_experts, self.S, policy, adopt) for _ in self.layers]
         self.routers = []
@@ -70,8 +68,6 @@ class Runner:
         out = self.cache.forward(li, x_d, w_r_d, b_d)
         torch.cuda.synchronize()
         out_np = out.cpu().numpy()
-        # the one-launch decode GEMV's own checks (its waits, its XCD placement)
-        assert self.cache.gemv_status() == 0, "fused GEMV reported an error"
         # routing, bit for bit
         z = router_logits_fp32(x_np, w_r, b)
         idx_ref = topk(z, wl.top_k)

@@ -262,17 +262,11 @@ static void workspace_runs(std::mt19937_64 &rng) {
             CHECK(L.decode == (small && moe::gemv_lds_bytes(true, sh[0] / 32, T) <= moe::kDecodeLdsBudget &&
                                moe::gemv_lds_bytes(false, sh[1] / 32, T) <= moe::kDecodeLdsBudget));
             CHECK(L.pairs == T * k + T * ns);
-            CHECK(L.fused == (L.decode && sh[1] / 32 >= moe::kSlices &&
-                              (sh[1] / 32 + moe::kSlices - 1) / moe::kSlices <= moe::kFusedMaxSliceBlocks &&
-                              (T <= 1 ? 1 : (T <= 2 ? 2 : 4)) * ((sh[1] / 32 + moe::kSlices - 1) / moe::kSlices) <=
-                                  moe::kFusedMaxTokenBlocks));
-            CHECK(L.y_parts == (L.fused ? moe::kSlices : 1));
             // planted mistakes: every region, shrunk, must be caught
             moe::WsRegion moe::WsLayout::*regions[] = {
                 &moe::WsLayout::z,  &moe::WsLayout::idx, &moe::WsLayout::w,
                 &moe::WsLayout::h,  &moe::WsLayout::y,   &moe::WsLayout::xq,
                 &moe::WsLayout::xs, &moe::WsLayout::buckets, &moe::WsLayout::pair_slot,
-                &moe::WsLayout::gsync,
                 &moe::WsLayout::meta, &moe::WsLayout::bucket_pair, &moe::WsLayout::items,
                 &moe::WsLayout::xp, &moe::WsLayout::xscale, &moe::WsLayout::hp,
                 &moe::WsLayout::hscale};
@@ -304,7 +298,7 @@ static void workspace_runs(std::mt19937_64 &rng) {
     arena = std::max(arena, L.total);  // the arena grows, never shrinks
     // every region of this call lies inside the arena as it stands
     for (const moe::WsRegion *r : {&L.z, &L.idx, &L.w, &L.h, &L.y, &L.xq, &L.xs, &L.buckets,
-                                   &L.pair_slot, &L.gsync, &L.meta, &L.bucket_pair, &L.items, &L.xp,
+                                   &L.pair_slot, &L.meta, &L.bucket_pair, &L.items, &L.xp,
                                    &L.xscale, &L.hp, &L.hscale})
       CHECK(r->off + r->bytes <= L.total && L.total <= arena);
   }

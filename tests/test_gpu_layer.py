@@ -611,20 +611,3 @@ def test_large_host_lru_all_columns():
         r.call(0, x[t])
     r.check_log()
     r.close()
-
-
-@pytest.mark.parametrize("case", ["tiny_stream", "tiny_host", "gemma_host", "large_host"])
-def test_fused_gemv(case):
-    """The decode GEMV as one launch split over the XCDs (the opt-in form): the
-    same checks as the default two-launch form."""
-    name, mode = case.split("_")
-    wl = synth.WORKLOADS[name]
-    log(f"one-launch GEMV, {name}, {mode} misses")
-    ncalls = {"tiny": 24, "gemma": 8, "large": 4}[name]
-    r = Runner(wl, [0], mode=mode, fused=True)
-    x = synth.gen_hidden(wl, 0, ncalls)
-    cols = None if name != "large" else np.random.default_rng(9).choice(wl.d_model, 256, replace=False)
-    for t in range(ncalls):
-        r.call(0, x[t], col_sample=cols)
-    r.check_log()
-    r.close()
