@@ -158,6 +158,10 @@ struct TimingLog {
     HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
     return e;
   }
+  void put_back(hipEvent_t a, hipEvent_t b) {
+    free_list.push_back(a);
+    free_list.push_back(b);
+  }
   void collect() {
     for (auto &pr : pending) {
       HIPCHK(hipEventSynchronize(pr.second));
@@ -333,24 +337,36 @@ moe::SlotView make_view(const std::vector<int32_t> &table) {
 }
 
 // Event pair around one kernel launch (timing on only).
+// Times the one kernel launched between construction and end(): the launch
+// records the pair at its own dispatch start and end (set_launch_events).
 struct KTime {
   moe_cache *c;
   int kid;
-  hipStream_t st;
-  hipEvent_t a = nullptr;
-  KTime(moe_cache *c_, int kid_, hipStream_t st_) : c(c_), kid(kid_), st(st_) {
+  hipEvent_t a = nullptr, b = nullptr;
+  KTime(moe_cache *c_, int kid_, hipStream_t) : c(c_), kid(kid_) {
     if (c->kmask & (1u << kid)) {
       a = c->kt[kid].log.get();
-      HIPCHK(hipEventRecord(a, st));
+      b = c->kt[kid].log.get();
+      moe::set_launch_events(a, b);
     }
   }
   void end(double bytes) {
-    if (!(c->kmask & (1u << kid))) return;
-    hipEvent_t b = c->kt[kid].log.get();
-    HIPCHK(hipEventRecord(b, st));
+    if (!a) return;
+    if (moe::launch_events_pending()) {  // nothing was launched: the pair goes back
+      c->kt[kid].log.put_back(a, b);
+      a = nullptr;
+      return;
+    }
     c->kt[kid].log.pending.emplace_back(a, b);
     c->kt[kid].launches++;
     c->kt[kid].bytes += bytes;
+    a = nullptr;
+  }
+  ~KTime() {
+    if (a) {  // left by an exception: no later launch may take the pair
+      (void)moe::launch_events_pending();
+      c->kt[kid].log.put_back(a, b);
+    }
   }
 };
 

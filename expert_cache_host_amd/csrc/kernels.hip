@@ -6,6 +6,7 @@
 // high nibble; w = d * (q - 8).
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <mutex>
@@ -14,6 +15,35 @@
 #include "workspace.hpp"
 
 namespace moe {
+
+// ============================================================== launches
+// Every kernel goes out through launch_k.  A start / stop event pair set by
+// set_launch_events is handed to the next launch of the same host thread,
+// which records them at that kernel's own dispatch start and end
+// (hipExtLaunchKernel): the pair then times the kernel alone, without the
+// host's launch latency that events recorded around the call would include
+// whenever the stream is idle.
+static thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+void set_launch_events(hipEvent_t start, hipEvent_t stop) {
+  t_ev_start = start;
+  t_ev_stop = stop;
+}
+
+bool launch_events_pending() {
+  const bool p = t_ev_start != nullptr;
+  t_ev_start = t_ev_stop = nullptr;
+  return p;
+}
+
+template <typename... KArgs, typename... Args>
+static void launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 blk, size_t lds, hipStream_t s,
+                     Args... args) {
+  hipEvent_t a = t_ev_start, b = t_ev_stop;
+  t_ev_start = t_ev_stop = nullptr;
+  hipExtLaunchKernelGGL(kernel, grid, blk, (uint32_t)lds, s, a, b, 0u, static_cast<KArgs>(args)...);
+}
+
 
 // ============================================================== small helpers
 
@@ -416,26 +446,26 @@ hipError_t launch_router(const float *x, int T, int d, const float *W, const flo
   const size_t lds = (size_t)tt * d * 4;
   if (xq != nullptr && xp == nullptr && router_decode_fits(T, d, E)) {
     if (tt == 1)
-      hipLaunchKernelGGL(router_decode_kernel<1>, dim3(E), dim3(256), lds, s, x, T, d, W, bias, E,
+      launch_k(router_decode_kernel<1>, dim3(E), dim3(256), lds, s, x, T, d, W, bias, E,
                          z, xq, xs, h_x, h_z, seq);
     else if (tt == 2)
-      hipLaunchKernelGGL(router_decode_kernel<2>, dim3(E), dim3(256), lds, s, x, T, d, W, bias, E,
+      launch_k(router_decode_kernel<2>, dim3(E), dim3(256), lds, s, x, T, d, W, bias, E,
                          z, xq, xs, h_x, h_z, seq);
     else
-      hipLaunchKernelGGL(router_decode_kernel<4>, dim3(E), dim3(256), lds, s, x, T, d, W, bias, E,
+      launch_k(router_decode_kernel<4>, dim3(E), dim3(256), lds, s, x, T, d, W, bias, E,
                          z, xq, xs, h_x, h_z, seq);
     return hipGetLastError();
   }
   if (h_x != nullptr) return hipErrorInvalidValue;
   const int gx = (E + 3) / 4;
   if (T <= 1) {
-    hipLaunchKernelGGL((router_kernel<1, 32>), dim3(gx, T), dim3(256), 0, s, x, T, d, W, bias, E,
+    launch_k((router_kernel<1, 32>), dim3(gx, T), dim3(256), 0, s, x, T, d, W, bias, E,
                        z, xp, xscale, xq, xs, h_z, seq);
   } else if (T <= 4) {
-    hipLaunchKernelGGL((router_kernel<4, 16>), dim3(gx, 1), dim3(256), 0, s, x, T, d, W, bias, E,
+    launch_k((router_kernel<4, 16>), dim3(gx, 1), dim3(256), 0, s, x, T, d, W, bias, E,
                        z, xp, xscale, xq, xs, h_z, seq);
   } else {
-    hipLaunchKernelGGL((router_kernel<8, 8>), dim3(gx, (T + 7) / 8), dim3(256), 0, s, x, T, d, W,
+    launch_k((router_kernel<8, 8>), dim3(gx, (T + 7) / 8), dim3(256), 0, s, x, T, d, W,
                        bias, E, z, xp, xscale, xq, xs, h_z, seq);
   }
   return hipGetLastError();
@@ -580,7 +610,7 @@ __global__ __launch_bounds__(256) void topk_decode_kernel(const float *z, int T,
 
 hipError_t launch_topk(const float *z, int T, int E, int k, int norm_topk, int32_t *idx, float *w,
                        int32_t *h_idx, float *h_w, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(64), 0, s, z, T, E, k, norm_topk, idx, w, h_idx,
+  launch_k(topk_kernel, dim3(T), dim3(64), 0, s, z, T, E, k, norm_topk, idx, w, h_idx,
                      h_w);
   return hipGetLastError();
 }
@@ -592,7 +622,7 @@ static bool decode_args_ok(int T, const DecodeTopk &a) {
 
 hipError_t launch_topk_decode(const float *z, int T, int E, const DecodeTopk &a, hipStream_t s) {
   if (!decode_args_ok(T, a)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(topk_decode_kernel, dim3(1), dim3(64 * T), 0, s, z, T, E, a);
+  launch_k(topk_decode_kernel, dim3(1), dim3(64 * T), 0, s, z, T, E, a);
   return hipGetLastError();
 }
 
@@ -691,7 +721,7 @@ hipError_t launch_remap(const int32_t *idx, int T, int k, const SlotView &view, 
                         int n_slot_ids, int32_t *meta, int32_t *bucket_pair, int32_t *items,
                         hipStream_t s) {
   if (n_slot_ids < 1 || n_slot_ids > kMetaB) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(remap_kernel, dim3(1), dim3(64 * kRemapWaves), 0, s, idx, T, k, view,
+  launch_k(remap_kernel, dim3(1), dim3(64 * kRemapWaves), 0, s, idx, T, k, view,
                      shared_slot, n_slot_ids, meta, bucket_pair, items);
   return hipGetLastError();
 }
@@ -1173,10 +1203,10 @@ static void launch_one(const GemvArgs &a, const BucketTable &tab, int nbk, size_
   constexpr int RWG = (NW / KS) * (64 / G) * R;
   const dim3 grid((a.rows + RWG - 1) / RWG, nbk);
   if constexpr (GLU)
-    hipLaunchKernelGGL((q4_gateup_kernel<G, KS, R, TT, MODE, NW, PF>), grid, dim3(64 * NW), lds, s,
+    launch_k((q4_gateup_kernel<G, KS, R, TT, MODE, NW, PF>), grid, dim3(64 * NW), lds, s,
                        a, tab);
   else
-    hipLaunchKernelGGL((q4_down_kernel<G, KS, R, TT, MODE, NW, PF>), grid, dim3(64 * NW), lds, s,
+    launch_k((q4_down_kernel<G, KS, R, TT, MODE, NW, PF>), grid, dim3(64 * NW), lds, s,
                        a, tab);
 }
 
@@ -1514,9 +1544,9 @@ hipError_t launch_mfma(const GemvArgs &a, bool glu, int n_items, hipStream_t s) 
   if (n_items > 65535) return hipErrorInvalidValue;
   const dim3 grid((a.rows + K6_ROWS - 1) / K6_ROWS, n_items);
   if (glu)
-    hipLaunchKernelGGL(q4_mfma_kernel<true>, grid, dim3(256), 0, s, a);
+    launch_k(q4_mfma_kernel<true>, grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(q4_mfma_kernel<false>, grid, dim3(256), 0, s, a);
+    launch_k(q4_mfma_kernel<false>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1563,7 +1593,7 @@ __global__ __launch_bounds__(64) void prep_pairs_kernel(const float *__restrict_
 hipError_t launch_prep_pairs(const float *in, int rows, int K, uint32_t *xp, float *xscale,
                              hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(prep_pairs_kernel, dim3(rows), dim3(64), 0, s, in, rows, K, xp, xscale);
+  launch_k(prep_pairs_kernel, dim3(rows), dim3(64), 0, s, in, rows, K, xp, xscale);
   return hipGetLastError();
 }
 
@@ -1592,7 +1622,7 @@ __global__ __launch_bounds__(256) void pull_kernel(PullList l) {
 
 hipError_t launch_pull(const PullList &l, hipStream_t s) {
   if (l.n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(pull_kernel, dim3(l.n * l.per_expert), dim3(256), 0, s, l);
+  launch_k(pull_kernel, dim3(l.n * l.per_expert), dim3(256), 0, s, l);
   return hipGetLastError();
 }
 
@@ -1662,7 +1692,7 @@ hipError_t launch_combine(const float *y, const float *w, const int32_t *idx,
                           int k, int d, int n_shared, const float *host_part, float *out,
                           float *dbg_gpu, hipStream_t s) {
   const dim3 grid((d / 4 + 255) / 256, T);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, y, w, idx, view, all_gpu, pair_slot,
+  launch_k(combine_kernel, grid, dim3(256), 0, s, y, w, idx, view, all_gpu, pair_slot,
                      T, k, d, n_shared, host_part, out, dbg_gpu);
   return hipGetLastError();
 }

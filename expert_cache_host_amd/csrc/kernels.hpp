@@ -8,6 +8,14 @@
 
 namespace moe {
 
+// The next kernel launch of the calling host thread records `start` at its
+// dispatch start and `stop` at its end (both may be null: no timing).
+void set_launch_events(hipEvent_t start, hipEvent_t stop);
+// True when events set by set_launch_events were not taken by a launch (the
+// launch function returned without launching); clears them either way.
+bool launch_events_pending();
+
+
 // Expert -> slot table of one stage, passed by value as a kernel argument so
 // that each launch carries its own table (no copy, no reuse hazard).
 struct SlotView {

@@ -269,13 +269,14 @@ moe_status moe_cache_set_timing(moe_cache *c, int32_t on);
 /* Times only the kernels whose bit (1 << MOE_K_*) is set in kernel_mask, one
  * launch at a time, from now on; the per-layer compute and fill timings of
  * moe_cache_set_timing stay as they are.  moe_cache_set_timing(c, 1) sets every
- * bit, (c, 0) clears them.  Each timed launch costs two event records on its
- * stream (host time on the calling thread), so a narrow mask perturbs the
- * calls least.  MOE_EINVAL for bits at or past MOE_K_COUNT. */
+ * bit, (c, 0) clears them.  A timed launch carries a start and a stop event
+ * that the GPU records at that kernel's own dispatch start and end
+ * (hipExtLaunchKernel), so the time is the kernel's alone, without the host's
+ * launch latency.  MOE_EINVAL for bits at or past MOE_K_COUNT. */
 moe_status moe_cache_set_kernel_timing(moe_cache *c, uint32_t kernel_mask);
 
-/* Launches, summed device seconds (HIP events on the launching stream, read
- * when this is called) and summed algorithmic bytes of kernel `kernel` since the
+/* Launches, summed device seconds (the launches' own start / stop events on
+ * the launching stream, read when this is called) and summed algorithmic bytes of kernel `kernel` since the
  * last reset.  Algorithmic bytes: router = W_r + x + logits; Q4 kernels = the
  * 18/32-byte-per-weight bytes of every expert matrix the launch reads; fill =
  * the slot records copied host -> device; prep = h read + pairs written;
