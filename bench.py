@@ -14,9 +14,10 @@ Prints one JSON line.  `value` = MoE-layer tokens/s (tokens x layers / wall
 time) over exactly K timed steps, with inputs resident in HBM and the expert
 weights in the library's page-locked host arena before the timed region
 starts.  Inside the timed region the two expert GEMV launches of every call
-carry HIP start / stop events that the GPU records at each kernel's own
-dispatch start and end (hipExtLaunchKernel, on the stream the kernel runs on),
-and nothing else is timed: `roofline` is the gate/up + SwiGLU
+are timed with HIP events on the stream they run on, and nothing else is: a
+start / stop pair the launch itself carries (hipExtLaunchKernel) and one event
+recorded just before it, each launch's time running from the later start to
+the stop: `roofline` is the gate/up + SwiGLU
 kernel (the one with the most device time) on the bytes it reads, against HBM;
 `roofline_down` the down projection.  A further pass of the same length times
 every kernel (`extra.kernels_breakdown_pass`, `dominant_kernel_by_device_time`).
@@ -431,8 +432,9 @@ def run_leg(wl, weights, steps, warmup, policy="lru", max_fills=-1, breakdown=Tr
                 "traffic": pmc_traffic(f"{wl.name}/{wl.miss_mode}", k, 0, 0),
                 "avg_launch_us": e["avg_us"], "launches": e["launches"],
                 "algorithmic_bytes_per_launch": e["algorithmic_bytes_per_launch"],
-                "timed": "HIP start / stop events recorded by each launch itself "
-                         "(hipExtLaunchKernel) on its stream, inside the timed region"}
+                "timed": "HIP events on the launch's stream, inside the timed region: the "
+                         "launch's own start / stop (hipExtLaunchKernel) and one recorded "
+                         "before it, from the later start to the stop"}
 
     if decode:
         leg["roofline"] = hbm_roof("gateup")
@@ -456,8 +458,9 @@ def run_leg(wl, weights, steps, warmup, policy="lru", max_fills=-1, breakdown=Tr
                 "algorithmic_flops_per_ubatch_layer": flops / (steps * wl.layers),
                 "gemm_ms_per_ubatch_layer": 1e3 * t_mm / (steps * wl.layers),
                 "per_kernel": {"gateup": entry("gateup", ks), "down": entry("down", ks)},
-                "timed": "HIP start / stop events recorded by each launch itself "
-                         "(hipExtLaunchKernel) on its stream, inside the timed region"}
+                "timed": "HIP events on the launch's stream, inside the timed region: the "
+                         "launch's own start / stop (hipExtLaunchKernel) and one recorded "
+                         "before it, from the later start to the stop"}
     if ks_all is not None:
         kernels = {k: entry(k, ks_all) for k in ks_all if entry(k, ks_all)}
         leg["kernels_breakdown_pass"] = kernels

@@ -142,8 +142,14 @@ struct DevBuf {
 };
 
 // Pairs of timing events, summed on demand.
+// One timed span: from `start` to `stop`, or, when `before` is set too, from
+// the later of the two starts (see KTime).
+struct TimedSpan {
+  hipEvent_t start, stop, before;
+};
+
 struct TimingLog {
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+  std::vector<TimedSpan> pending;
   std::vector<hipEvent_t> free_list;
   double total = 0.0;
   hipEvent_t get() {
@@ -158,26 +164,33 @@ struct TimingLog {
     HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
     return e;
   }
-  void put_back(hipEvent_t a, hipEvent_t b) {
-    free_list.push_back(a);
-    free_list.push_back(b);
+  void put_back(hipEvent_t e) {
+    if (e) free_list.push_back(e);
+  }
+  void add(hipEvent_t start, hipEvent_t stop, hipEvent_t before = nullptr) {
+    pending.push_back({start, stop, before});
   }
   void collect() {
-    for (auto &pr : pending) {
-      HIPCHK(hipEventSynchronize(pr.second));
+    for (const TimedSpan &sp : pending) {
+      HIPCHK(hipEventSynchronize(sp.stop));
       float ms = 0.f;
-      HIPCHK(hipEventElapsedTime(&ms, pr.first, pr.second));
+      HIPCHK(hipEventElapsedTime(&ms, sp.start, sp.stop));
+      if (sp.before) {
+        float mb = 0.f;
+        HIPCHK(hipEventElapsedTime(&mb, sp.before, sp.stop));
+        ms = std::min(ms, mb);
+      }
       total += ms * 1e-3;
-      free_list.push_back(pr.first);
-      free_list.push_back(pr.second);
+      put_back(sp.start);
+      put_back(sp.stop);
+      put_back(sp.before);
     }
     pending.clear();
   }
   ~TimingLog() {
-    for (auto &pr : pending) {
-      (void)hipEventDestroy(pr.first);
-      (void)hipEventDestroy(pr.second);
-    }
+    for (const TimedSpan &sp : pending)
+      for (hipEvent_t e : {sp.start, sp.stop, sp.before})
+        if (e) (void)hipEventDestroy(e);
     for (auto e : free_list) (void)hipEventDestroy(e);
   }
 };
@@ -337,35 +350,51 @@ moe::SlotView make_view(const std::vector<int32_t> &table) {
 }
 
 // Event pair around one kernel launch (timing on only).
-// Times the one kernel launched between construction and end(): the launch
-// records the pair at its own dispatch start and end (set_launch_events).
+// Times the one kernel launched between construction and end().  The launch
+// records `a` at its dispatch start and `b` at its end (set_launch_events);
+// the GPU stamps `a` when it takes up the launch, which is before the launch
+// has waited for earlier work on the stream when there is any.  `w`, recorded
+// on the stream just before the launch, completes when that earlier work
+// does, but on an idle stream it is stamped before the host has finished
+// submitting the launch.  Both are lower bounds of the kernel's start, each
+// tight in the case where the other is not, so the span runs from the later
+// of the two to `b`.
 struct KTime {
   moe_cache *c;
   int kid;
-  hipEvent_t a = nullptr, b = nullptr;
-  KTime(moe_cache *c_, int kid_, hipStream_t) : c(c_), kid(kid_) {
+  hipEvent_t w = nullptr, a = nullptr, b = nullptr;
+  KTime(moe_cache *c_, int kid_, hipStream_t st) : c(c_), kid(kid_) {
     if (c->kmask & (1u << kid)) {
-      a = c->kt[kid].log.get();
-      b = c->kt[kid].log.get();
+      TimingLog &lg = c->kt[kid].log;
+      w = lg.get();
+      a = lg.get();
+      b = lg.get();
+      HIPCHK(hipEventRecord(w, st));
       moe::set_launch_events(a, b);
     }
   }
+  void release() {
+    TimingLog &lg = c->kt[kid].log;
+    lg.put_back(w);
+    lg.put_back(a);
+    lg.put_back(b);
+    w = a = b = nullptr;
+  }
   void end(double bytes) {
     if (!a) return;
-    if (moe::launch_events_pending()) {  // nothing was launched: the pair goes back
-      c->kt[kid].log.put_back(a, b);
-      a = nullptr;
+    if (moe::launch_events_pending()) {  // nothing was launched: the events go back
+      release();
       return;
     }
-    c->kt[kid].log.pending.emplace_back(a, b);
+    c->kt[kid].log.add(a, b, w);
     c->kt[kid].launches++;
     c->kt[kid].bytes += bytes;
-    a = nullptr;
+    w = a = b = nullptr;
   }
   ~KTime() {
     if (a) {  // left by an exception: no later launch may take the pair
       (void)moe::launch_events_pending();
-      c->kt[kid].log.put_back(a, b);
+      release();
     }
   }
 };
@@ -466,7 +495,7 @@ void enqueue_fills(moe_cache *c, int32_t layer, const std::vector<moe::Fill> &fi
     for (int i = 1; i < n_sd; ++i)
       HIPCHK(hipStreamWaitEvent(c->side[phys(0)], ly.fill_ev[phys(i)], 0));
     HIPCHK(hipEventRecord(t1, c->side[phys(0)]));
-    ly.t_h2d.pending.emplace_back(t0, t1);
+    ly.t_h2d.add(t0, t1);
   }
   ly.st.fills += fills.size();
   ly.st.fill_bytes += fills.size() * (uint64_t)c->rec();
@@ -844,7 +873,7 @@ moe_status forward_impl(moe_cache *c, int32_t layer, const float *x, int32_t T,
   }
   if (c->timing) {
     HIPCHK(hipEventRecord(g1, st));
-    ly.t_gpu.pending.emplace_back(g0, g1);
+    ly.t_gpu.add(g0, g1);
   }
   // record of the call
   ly.last_T = T;

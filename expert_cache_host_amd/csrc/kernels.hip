@@ -1250,7 +1250,6 @@ hipError_t launch_gemv(const GemvArgs &a, const BucketTable *tab, const GemvShap
         launch_tt<true, 8, 4, 1>(a, t, n_buckets, sh.TT, lds, s);
       break;
     case 1000 + 800 + 10 + 2: launch_tt<true, 8, 1, 2>(a, t, n_buckets, sh.TT, lds, s); break;
-    case 1600 + 10 + 4: launch_tt<false, 16, 1, 4>(a, t, n_buckets, sh.TT, lds, s); break;
     case 800 + 40 + 4: launch_tt<false, 8, 4, 4>(a, t, n_buckets, sh.TT, lds, s); break;
     default: return hipErrorInvalidValue;
   }

@@ -11,10 +11,10 @@ namespace moe {
 // Shapes measured on MI355X for one token per bucket over the decode shapes
 // d x f = 6144 x 2048 and 2816 x 704: gate/up rows of >= 128 blocks run best
 // with 16 lanes per row and 2 rows per lane, rows of 32-127 blocks with 8 lanes
-// and 1 row per lane, K split over the 4 waves; down rows of >= 64 blocks with
-// 16 lanes per row, whole K per wave and 4 rows per lane, shorter ones with 8
-// lanes and K over 4 waves.  Rows of fewer than 32 gate/up blocks keep K in one
-// wave.
+// and 1 row per lane, K split over the 4 waves; down rows with 8 lanes per row,
+// 4 rows per lane and K split over the 4 waves (at 64 blocks per row 4% faster
+// than 16 lanes with whole K per wave: the four waves read a row's K range
+// together).  Rows of fewer than 32 gate/up blocks keep K in one wave.
 GemvShape choose_gemv(bool glu, int nb, int tokens) {
   GemvShape sh{};
   sh.TT = tokens <= 1 ? 1 : (tokens <= 2 ? 2 : 4);
@@ -33,13 +33,8 @@ GemvShape choose_gemv(bool glu, int nb, int tokens) {
     }
   } else {
     sh.R = 4;
-    if (nb >= 64) {
-      sh.G = 16;
-      sh.KS = 1;
-    } else {
-      sh.G = 8;
-      sh.KS = 4;
-    }
+    sh.G = 8;
+    sh.KS = 4;
   }
   sh.NW = 4;
   sh.rows_wg = (sh.NW / sh.KS) * (64 / sh.G) * sh.R;

@@ -49,7 +49,33 @@ def stats_md(d: str, title: str, command: str) -> str:
     for r in rows:
         out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.2f} |")
+    hits = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if hits:
+        out += ["", by_shape_md(d)]
     return "\n".join(out) + "\n"
+
+
+def by_shape(d: str, marker: str = "moe::q4_"):
+    """Dispatches of the expert kernels grouped by kernel and row tiles per
+    launch (grid x in workgroups): one kernel serves several layer shapes, and
+    the row tiles tell them apart.  {(kernel, tiles): (dispatches, mean us)}."""
+    acc = defaultdict(lambda: [0, 0])
+    for r in csv.DictReader(open(_find(d, "kernel_trace.csv"))):
+        if marker not in r["Kernel_Name"]:
+            continue
+        tiles = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        k = (r["Kernel_Name"].split("(")[0].replace("void ", ""), tiles)
+        acc[k][0] += 1
+        acc[k][1] += int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return {k: (n, t / n / 1e3) for k, (n, t) in acc.items()}
+
+
+def by_shape_md(d: str) -> str:
+    out = ["Expert kernels by launch shape (row tiles = workgroups along x; from the kernel trace):",
+           "", "| kernel | row tiles | dispatches | avg us |", "|---|---|---|---|"]
+    for (k, tiles), (n, us) in sorted(by_shape(d).items(), key=lambda kv: (kv[0][0], -kv[0][1])):
+        out.append(f"| `{k}` | {tiles} | {n} | {us:.2f} |")
+    return "\n".join(out)
 
 
 def pmc_table(d: str, counter: str):

@@ -270,13 +270,15 @@ moe_status moe_cache_set_timing(moe_cache *c, int32_t on);
  * launch at a time, from now on; the per-layer compute and fill timings of
  * moe_cache_set_timing stay as they are.  moe_cache_set_timing(c, 1) sets every
  * bit, (c, 0) clears them.  A timed launch carries a start and a stop event
- * that the GPU records at that kernel's own dispatch start and end
- * (hipExtLaunchKernel), so the time is the kernel's alone, without the host's
- * launch latency.  MOE_EINVAL for bits at or past MOE_K_COUNT. */
+ * that the GPU records at that kernel's own dispatch (hipExtLaunchKernel),
+ * and a third event is recorded on the stream just before it; the time runs
+ * from the later of the two starts to the stop, which leaves out both the
+ * host's launch latency (idle stream) and the wait for earlier work on the
+ * stream (busy stream).  MOE_EINVAL for bits at or past MOE_K_COUNT. */
 moe_status moe_cache_set_kernel_timing(moe_cache *c, uint32_t kernel_mask);
 
-/* Launches, summed device seconds (the launches' own start / stop events on
- * the launching stream, read when this is called) and summed algorithmic bytes of kernel `kernel` since the
+/* Launches, summed device seconds (the launches' own events on the launching
+ * stream, as set out for moe_cache_set_kernel_timing, read when this is called) and summed algorithmic bytes of kernel `kernel` since the
  * last reset.  Algorithmic bytes: router = W_r + x + logits; Q4 kernels = the
  * 18/32-byte-per-weight bytes of every expert matrix the launch reads; fill =
  * the slot records copied host -> device; prep = h read + pairs written;

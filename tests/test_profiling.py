@@ -1,7 +1,8 @@
 """The rocprofv3 summary tool (expert_cache_host_amd/profiling.py) on small
 hand-made traces with known answers: pull launches grouped by records carried,
-one call's timeline with workgroup counts, ROCTx range statistics, and the
-calibrated traffic file the benchmark reads."""
+one call's timeline with workgroup counts, expert kernels split by launch
+shape, ROCTx range statistics, and the calibrated traffic file the benchmark
+reads."""
 import csv
 import json
 import os
@@ -90,3 +91,20 @@ def test_traffic_json_scales_by_the_copy(tmp_path):
     assert abs(d["fetch_scale"] - 2.0) < 1e-12 and abs(d["write_scale"] - 1.0) < 1e-12
     g = json.load(open(out))["workloads"]["w/host"]["gateup"]
     assert g["fetch_KiB"] == 200.0 and g["write_KiB"] == 20.0 and g["dispatches"] == 2
+
+
+def test_expert_kernels_split_by_launch_shape(tmp_path):
+    """One down kernel serving two layer shapes: 192 row tiles (d_model 6144)
+    and 88 (2816) are reported apart, each with its own mean."""
+    k = "void moe::q4_down_kernel<8, 4, 4, 1, 1, 4, 1>(moe::GemvArgs, moe::BucketTable)"
+    rows = [_kernel(k, 0, 13_000, 192), _kernel(k, 50_000, 64_000, 192),
+            _kernel(k, 100_000, 107_000, 88), _kernel(k, 200_000, 208_000, 88),
+            _kernel(k, 300_000, 309_000, 88),
+            _kernel("moe::combine_kernel(float)", 400_000, 407_000, 6)]
+    _write(str(tmp_path / "t" / "run_kernel_trace.csv"), KT_FIELDS, rows)
+    t = P.by_shape(str(tmp_path))
+    name = "moe::q4_down_kernel<8, 4, 4, 1, 1, 4, 1>"
+    assert t == {(name, 192): (2, 13.5), (name, 88): (3, 8.0)}
+    md = P.by_shape_md(str(tmp_path))
+    assert f"| `{name}` | 192 | 2 | 13.50 |" in md
+    assert f"| `{name}` | 88 | 3 | 8.00 |" in md
