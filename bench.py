@@ -450,7 +450,8 @@ def run_leg(wl, weights, steps, warmup, policy="lru", max_fills=-1, breakdown=Tr
             leg["roofline"] = {
                 "bound": "hbm", "kernel": "q4_mfma_kernel (gate/up + down, every stage)",
                 "achieved": hbm, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": hbm / HBM_PEAK_GBS,
-                "traffic": None, "launches": ng + nd,
+                "traffic": pmc_traffic(f"{wl.name}/{wl.miss_mode}", "mfma", 0, 0),
+                "algorithmic_bytes_per_launch": (bg + bd) / max(1, ng + nd), "launches": ng + nd,
                 "avg_launch_us": 1e6 * t_mm / max(1, ng + nd),
                 "mfma_achieved_TFLOP_per_s": flops / t_mm / 1e12,
                 "mfma_peak_TFLOP_per_s": MFMA_F16_PEAK_TFLOPS,
