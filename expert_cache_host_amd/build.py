@@ -1,4 +1,5 @@
-"""Builds libmoecache.so in-tree: host C++ with g++, gfx950 kernels with hipcc.
+"""Builds libmoecache.so in-tree: host C++ with g++, gfx950 kernels with hipcc;
+also the streaming-read probe (expert_cache_host_amd/_build/readbw).
 
     python -m expert_cache_host_amd.build
 """
@@ -37,6 +38,9 @@ def _jobs():
                                 os.path.join(BUILD, "workspace.o")]),
         (["g++"] + CXX_FLAGS + ["-c", os.path.join(CSRC, "host_routing.cpp"), "-o",
                                 os.path.join(BUILD, "host_routing.o")]),
+        # the streaming-read probe (a measurement aid, not part of the library)
+        ([HIPCC] + HIP_FLAGS + [os.path.join(HERE, "probes", "readbw.hip"), "-o",
+                                os.path.join(BUILD, "readbw")]),
     ]
 
 
