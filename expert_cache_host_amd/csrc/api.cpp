@@ -23,6 +23,7 @@
 #include <stdexcept>
 #include <string>
 #include <thread>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/moe_cache.h"
@@ -32,6 +33,9 @@
 #include "layout.hpp"
 #include "planner.hpp"
 #include "workspace.hpp"
+
+// The header's stream type is HIP's own (no HIP header needed there).
+static_assert(std::is_same<moe_stream_t, hipStream_t>::value, "moe_stream_t must be hipStream_t");
 
 namespace {
 
@@ -1061,7 +1065,7 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
 
 moe_status moe_layer_forward(moe_cache *c, int32_t layer, const float *x, int32_t n_tokens,
                              const float *router_w, const float *router_bias, float *out,
-                             void *stream) {
+                             moe_stream_t stream) {
   g_err.clear();
   if (!c) return fail(MOE_EINVAL, "cache is NULL");
   if (layer < 0 || layer >= c->L) return fail(MOE_EINVAL, "layer out of range");
@@ -1070,13 +1074,13 @@ moe_status moe_layer_forward(moe_cache *c, int32_t layer, const float *x, int32_
   if (!x || !router_w || !out) return fail(MOE_EINVAL, "x, router_w and out must be non-NULL");
   return guarded(c, [&]() {
     TraceRange tr("moe.layer_forward");
-    return forward_impl(c, layer, x, n_tokens, router_w, router_bias, out, (hipStream_t)stream);
+    return forward_impl(c, layer, x, n_tokens, router_w, router_bias, out, stream);
   });
 }
 
 moe_status moe_layer_forward_noalloc(moe_cache *c, int32_t layer, const float *x,
                                      int32_t n_tokens, const float *router_w,
-                                     const float *router_bias, float *out, void *stream) {
+                                     const float *router_bias, float *out, moe_stream_t stream) {
   g_err.clear();
   if (!c) return fail(MOE_EINVAL, "cache is NULL");
   if (layer < 0 || layer >= c->L) return fail(MOE_EINVAL, "layer out of range");
@@ -1108,7 +1112,7 @@ moe_status moe_layer_forward_noalloc(moe_cache *c, int32_t layer, const float *x
         c->kmask = m;
       }
     } restore{c, timing, kmask};
-    return forward_impl(c, layer, x, n_tokens, router_w, router_bias, out, (hipStream_t)stream,
+    return forward_impl(c, layer, x, n_tokens, router_w, router_bias, out, stream,
                         true);
   });
 }

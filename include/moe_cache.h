@@ -43,6 +43,12 @@
 extern "C" {
 #endif
 
+/* The caller's HIP stream.  hip/hip_runtime.h declares hipStream_t as a pointer
+ * to struct ihipStream_t; this is the same type, declared here so that the
+ * header needs no HIP header.  NULL is the default stream. */
+struct ihipStream_t;
+typedef struct ihipStream_t *moe_stream_t;
+
 typedef int32_t moe_status;
 #define MOE_OK 0
 #define MOE_EINVAL (-1)
@@ -101,8 +107,9 @@ typedef struct moe_cache_opts {
 } moe_cache_opts;
 
 /* Counters since create or the last moe_cache_reset_stats.  A "selection" is one
- * (token, rank) pick of the router; hits and misses count selections, as the
- * pages' hit rates do ("of the picks"). */
+ * (token, rank) pick of the router; hits and misses count selections, which is
+ * how the hit rates of "llama.cpp + MoE expert cache" (The idea: cache the hot
+ * experts on the GPU) are counted. */
 typedef struct moe_stats {
   uint64_t calls;           /* moe_layer_forward calls */
   uint64_t tokens;          /* tokens over all calls */
@@ -199,7 +206,7 @@ moe_status moe_cache_create(int32_t layers, int32_t n_experts, int32_t slots, in
  */
 moe_status moe_layer_forward(moe_cache *c, int32_t layer, const float *x, int32_t n_tokens,
                              const float *router_w, const float *router_bias, float *out,
-                             void *stream);
+                             moe_stream_t stream);
 
 /*
  * moe_layer_forward_noalloc -- moe_layer_forward for callers that cannot
@@ -229,7 +236,7 @@ moe_status moe_layer_forward(moe_cache *c, int32_t layer, const float *x, int32_
  */
 moe_status moe_layer_forward_noalloc(moe_cache *c, int32_t layer, const float *x,
                                      int32_t n_tokens, const float *router_w,
-                                     const float *router_bias, float *out, void *stream);
+                                     const float *router_bias, float *out, moe_stream_t stream);
 
 /* Counters of one layer (layer >= 0) or summed over layers (layer == -1).
  * Synchronises the library's own streams to read device timings. */
