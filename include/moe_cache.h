@@ -409,7 +409,10 @@ void moe_planner_destroy(moe_planner *p);
  * E logits z[t][*], ordered by decreasing value, equal values (-0 == +0) to the
  * lower expert id, and the gating weights (softmax over all E logits in
  * binary64, renormalised over the k when norm_topk, rounded to float32).  The
- * GPU's top-k kernel selects the same ids from the same float32 logits.
+ * GPU's top-k kernel selects the same ids from the same float32 logits: both
+ * order by the float's bits mapped to an order-preserving key, so even
+ * non-finite logits (outside the method) get one order, a NaN with the sign
+ * bit clear above +inf and one with it set below -inf.
  * z: host float32 [n_tokens][n_experts]; idx, w: host [n_tokens][top_k].
  * Requirements: n_tokens >= 1; 1 <= top_k <= n_experts <= MOE_MAX_EXPERTS;
  * norm_topk 0 or 1. */

@@ -10,7 +10,8 @@
 // caller's first task of a host partial (runs once; an exception it throws
 // surfaces after the run, whose results are complete), and the per-call
 // device workspace layout (sizes, alignment, overlaps, the decode decision,
-// mixed call orders on one growing arena).
+// mixed call orders on one growing arena), and the host's expert selection
+// over logits with infinities, NaNs and signed zeros.
 // Built under ThreadSanitizer with the argument "threads": the pool and the
 // host partial only.  Exit status 0 and "ok" on success.
 #include <cmath>
@@ -30,6 +31,7 @@
 #include <algorithm>
 
 #include "../../expert_cache_host_amd/csrc/host_expert.hpp"
+#include "../../expert_cache_host_amd/csrc/host_routing.hpp"
 #include "../../expert_cache_host_amd/csrc/layout.hpp"
 #include "../../expert_cache_host_amd/csrc/planner.hpp"
 #include "../../expert_cache_host_amd/csrc/workspace.hpp"
@@ -329,11 +331,44 @@ static void pool_exception_runs() {
   }
 }
 
+// The host's selection: any float32 logits, non-finite ones included, give k
+// distinct ids in range and gating weights that are finite and sum to 1 when
+// every logit is finite.
+static void host_topk_runs(std::mt19937_64 &rng) {
+  const float specials[] = {INFINITY, -INFINITY, NAN, -NAN, 0.0f, -0.0f, 1e38f, -1e-38f};
+  for (int call = 0; call < 3000; ++call) {
+    const int E = 1 + (int)(rng() % 512), k = 1 + (int)(rng() % E), T = 1 + (int)(rng() % 4);
+    const bool finite = rng() % 2;
+    std::vector<float> z((size_t)T * E);
+    std::normal_distribution<float> nd(0.0f, 3.0f);
+    for (float &v : z) v = (!finite && rng() % 8 == 0) ? specials[rng() % 8] : nd(rng);
+    if (finite)
+      for (float &v : z)
+        if (rng() % 16 == 0) v = (rng() % 2) ? 0.0f : -0.0f;
+    std::vector<int32_t> idx((size_t)T * k, -1);
+    std::vector<float> w((size_t)T * k, -1.0f);
+    moe::host_topk(z.data(), T, E, k, (int)(rng() % 2), idx.data(), w.data());
+    for (int t = 0; t < T; ++t) {
+      std::set<int32_t> seen;
+      double sum = 0.0;
+      for (int j = 0; j < k; ++j) {
+        const int32_t e = idx[(size_t)t * k + j];
+        CHECK(e >= 0 && e < E);
+        seen.insert(e);
+        sum += w[(size_t)t * k + j];
+      }
+      CHECK((int)seen.size() == k);
+      if (finite) CHECK(std::isfinite(sum) && sum <= 1.0 + 1e-5);
+    }
+  }
+}
+
 int main(int argc, char **argv) {
   std::mt19937_64 rng(12345);
   const bool threads_only = argc > 1 && std::string(argv[1]) == "threads";
   if (!threads_only) planner_runs(rng);
   if (!threads_only) workspace_runs(rng);
+  if (!threads_only) host_topk_runs(rng);
   pool_runs(rng);
   pool_exception_runs();
   caller_first_runs(rng);

@@ -1,5 +1,5 @@
 """The host-only runtime (slot planner, host-miss experts, thread pool, the
-per-call device workspace layout) built
+per-call device workspace layout, the host's expert selection) built
 with g++ under AddressSanitizer and UndefinedBehaviorSanitizer and driven
 through random calls (tests/sanitize/host_runtime_driver.cpp): no out-of-bounds
 access, no use after free, no undefined behaviour, and the driver's own
@@ -24,7 +24,8 @@ def test_host_runtime_under_sanitizers(tmp_path):
            "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
            os.path.join(HERE, "sanitize", "host_runtime_driver.cpp"),
            os.path.join(CSRC, "planner.cpp"), os.path.join(CSRC, "host_expert.cpp"),
-           os.path.join(CSRC, "workspace.cpp"), "-pthread", "-o", exe]
+           os.path.join(CSRC, "workspace.cpp"), os.path.join(CSRC, "host_routing.cpp"),
+           "-pthread", "-o", exe]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-4000:]
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0",
@@ -40,7 +41,8 @@ def test_thread_pool_under_thread_sanitizer(tmp_path):
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=thread",
            os.path.join(HERE, "sanitize", "host_runtime_driver.cpp"),
            os.path.join(CSRC, "planner.cpp"), os.path.join(CSRC, "host_expert.cpp"),
-           os.path.join(CSRC, "workspace.cpp"), "-pthread", "-o", exe]
+           os.path.join(CSRC, "workspace.cpp"), os.path.join(CSRC, "host_routing.cpp"),
+           "-pthread", "-o", exe]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-4000:]
     env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1:second_deadlock_stack=1")
