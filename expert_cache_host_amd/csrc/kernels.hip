@@ -1643,6 +1643,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   const int t = blockIdx.y;
   const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= d) return;
+  // the host partial sits in page-locked host memory: its read crosses PCIe,
+  // so it goes out first and its latency overlaps the expert outputs' reads
+  float4 hv = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (host_part) hv = *reinterpret_cast<const float4 *>(host_part + (long long)t * d + i);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j0 = 0; j0 < k; j0 += 8) {
     float4 yv[8];
@@ -1677,7 +1681,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   }
   if (dbg_gpu) *reinterpret_cast<float4 *>(dbg_gpu + (long long)t * d + i) = acc;
   if (host_part) {
-    const float4 hv = *reinterpret_cast<const float4 *>(host_part + (long long)t * d + i);
     acc.x += hv.x;
     acc.y += hv.y;
     acc.z += hv.z;
