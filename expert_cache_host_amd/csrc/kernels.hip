@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "kernels.hpp"
 #include "workspace.hpp"
@@ -1263,48 +1264,61 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
 }
 
 // ============================================================== prefill MFMA GEMM
-// Per workgroup: 4 waves x 16 weight rows of one bucket's expert, and one pass of
-// up to 32 of the bucket's tokens (two 16-token tiles).  Each wave streams its
-// own rows through registers: lane l loads the whole 16-byte nibble block
-// 4c + l/16 of row l%16 for K chunk c (4 blocks), two chunks ahead of the one it
-// multiplies.  A 4 x 4 word transpose across the four 16-lane rows of the wave
-// (two rounds of gfx950 lane swaps, no LDS) turns "block per lane row" into the
-// MFMA A layout (lane l: row l%16, word l/16 of each of the 4 blocks); the 16
-// rows' block scales go to the C layout (lane l: rows 4*(l/16)+i) through a
-// small wave-private LDS table of fp32 values.  The activation tiles (binary16
-// hi/lo pairs for the chunk's 4 blocks and the pass's tokens) are staged per
-// chunk for the whole workgroup in two LDS buffers, loaded two chunks ahead,
-// with one barrier per chunk.
-// A lane turns its nibble word into binary16 q - 8 (exact: 1024 + q from the
-// exponent trick, minus 1032); each 32-weight block is one pair of
-// v_mfma_f32_16x16x32_f16 (x hi, x lo) per token tile, and the block scale d
-// multiplies the pair's result into the fp32 accumulators.  Operand lanes: A
-// lane l = row l%16 and the 8 K values of word l/16 of the block (elements g,
-// g+2, g+16, g+18, g+1, g+3, g+17, g+19 with g = 4*(l/16)); B lane l = token
-// l%16 and the same 8 K values; C lane l = rows 4*(l/16)+i, token l%16.
+// Per workgroup: 8 waves over one pass of up to 32 of a bucket's tokens (one or
+// two 16-token tiles, a compile-time count) and a tile of weight rows of the
+// bucket's expert.  Each wave owns 32 rows (two groups of 16) of one matrix:
+// for the fused GLU, waves 0-3 take 128 rows of the gate projection and waves
+// 4-7 the same rows of the up projection (the gate sums reach the up waves
+// through LDS at the end); the down GEMM gives its 8 waves 256 rows.
+// The MFMA takes the tokens as its A operand and the weight rows as its B
+// operand, so that a lane's accumulators (C: lane l = tokens 4*(l/16)+i, weight
+// row l%16) all belong to one weight row and each block scale is one register
+// value; both row groups of a wave share every activation fragment read.
+// A wave streams its rows through registers: for each group, lane l loads the
+// whole 16-byte nibble block 4c + l/16 of row l%16 for K chunk c (4 blocks),
+// and its 16-bit scale, PD chunks ahead of the one it multiplies.  A 4 x 4 word
+// transpose across the four 16-lane rows of the wave (two rounds of gfx950 lane
+// swaps) turns "block per lane row" into the operand layout (lane l: row l%16,
+// word l/16 of each of the 4 blocks); the same swaps gather the four scales of
+// a row into every lane of that row.  The activation tiles (binary16 hi/lo
+// pairs for the chunk's 4 blocks and the pass's tokens) are staged per chunk
+// for the whole workgroup in two LDS buffers, with one barrier per chunk.
+// A lane turns its nibble word into binary16 q - 8 exactly: the exponent trick
+// puts q (or 16 q, for the nibbles at bits 4-7 of each half) in the mantissa of
+// 1024, and one packed subtract (or multiply-add by 1/16) leaves q - 8.  Each
+// 32-weight block is one pair of v_mfma_f32_16x16x32_f16 (x hi, x lo) per token
+// tile and row group, and the block scale d multiplies the pair's result into
+// the fp32 accumulators.  Operand lanes: weights lane l = row l%16 and the 8 K
+// values of word l/16 of the block (elements g, g+2, g+16, g+18, g+1, g+3,
+// g+17, g+19 with g = 4*(l/16)); tokens lane l = token l%16 and the same 8 K
+// values.
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int K6_WAVES = 4;
-constexpr int K6_ROWS = K6_WAVES * 16;  // rows per workgroup
+constexpr int K6_WAVES = 8;
 constexpr int K6_KC = 4;                // blocks per K chunk
 constexpr int K6_TOK = kGemmTokens;     // tokens per pass (two tiles of 16)
 constexpr int K6_PD = 2;                // K chunks in flight per wave
 
-__device__ __forceinline__ float pick4(const float4 &v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
+// weight rows per workgroup
+constexpr int k6_rows(bool glu) { return glu ? 32 * K6_WAVES / 2 : 32 * K6_WAVES; }
 
 // binary16 pairs of (q - 8) for the 8 nibbles of word w, in the operand order
 __device__ __forceinline__ half8_t decode_word_h(uint32_t w) {
-  const uint32_t m = 0x000F000Fu, mag = 0x64006400u;
+  const uint32_t m = 0x000F000Fu, m16 = 0x00F000F0u, mag = 0x64006400u;
   const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-  half8_t r;
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const half2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const uint32_t w8 = w >> 8;
+  // 1024 + q - 1032, and (1024 + 16 q) / 16 - 72: both exact in binary16
   const half2_t p0 = __builtin_bit_cast(half2_t, and_or(w, m, mag)) - off;
-  const half2_t p1 = __builtin_bit_cast(half2_t, and_or(w >> 4, m, mag)) - off;
-  const half2_t p2 = __builtin_bit_cast(half2_t, and_or(w >> 8, m, mag)) - off;
-  const half2_t p3 = __builtin_bit_cast(half2_t, and_or(w >> 12, m, mag)) - off;
+  const half2_t p1 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, and_or(w, m16, mag)),
+                                               sixteenth, off16);
+  const half2_t p2 = __builtin_bit_cast(half2_t, and_or(w8, m, mag)) - off;
+  const half2_t p3 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, and_or(w8, m16, mag)),
+                                               sixteenth, off16);
+  half8_t r;
   r[0] = p0[0];
   r[1] = p0[1];
   r[2] = p1[0];
@@ -1328,26 +1342,38 @@ __device__ __forceinline__ uint4 transpose_rows(uint4 v) {
   return make_uint4(c[0], c[1], d[0], d[1]);
 }
 
-template <int NM>
+// All-gather over the wave's four 16-lane rows: on entry row g holds s_g, on
+// exit every row holds (s_0, s_1, s_2, s_3).  permlane32_swap exchanges the
+// upper half of its first operand with the lower half of its second, so after
+// it each lane holds (s_{g mod 2}, s_{g mod 2 + 2}); permlane16_swap then does
+// the same between rows 2j + 1 and 2j.
+__device__ __forceinline__ uint4 gather_rows(uint32_t s) {
+  const auto a = __builtin_amdgcn_permlane32_swap(s, s, false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(a[0], a[0], false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[1], a[1], false, false);
+  return make_uint4(b[0], b[1], c[0], c[1]);
+}
+
 struct K6Lds {
   // [buf][token][word * 2 + hi/lo]; one spare entry per token row staggers the
-  // rows over the banks (row stride 528 B = 16 B mod 128 B)
+  // rows over the banks (row stride 528 B = 16 B mod 128 B).  After the last
+  // chunk the buffers hold the gate sums for the up waves.
   uint4 B[2][K6_TOK][K6_KC * 8 + 1];
-  float S[K6_WAVES][NM][K6_KC][16];  // block scales [block][row], wave-private
+  // block scales of one window of 16 blocks, wave-private: [wave][row group]
+  // [row][8 binary16 pairs + 2 spare] (row stride 40 B: the 16 rows' 8-byte
+  // reads fall on distinct banks)
+  uint32_t SC[K6_WAVES][2][16][10];
   int tok[K6_TOK];
 };
 
-// The pass body for NT token tiles of 16: a pass of up to 16 tokens stages and
-// multiplies half the activation rows.  NT = 1 and 2 are straight code; NT = 0
-// takes the tile count at run time (and stages all 32 rows).
-template <bool GLU, int NT>
-__device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds<GLU ? 2 : 1> &L, int item,
-                                          int tile);
+// The pass body for NT token tiles of 16 (a pass of up to 16 tokens stages and
+// multiplies half the activation rows).
+template <bool GLU, int NT, bool SW>
+__device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds &L, int item, int tile);
 
 template <bool GLU>
-__global__ __launch_bounds__(256, 2) void q4_mfma_kernel(GemvArgs a) {
-  constexpr int NM = GLU ? 2 : 1;
-  __shared__ K6Lds<NM> L;
+__global__ __launch_bounds__(64 * K6_WAVES, 4) void q4_mfma_kernel(GemvArgs a) {
+  __shared__ K6Lds L;
   // XCD-aware order: workgroup l of the grid runs on XCD l % 8; each XCD takes a
   // contiguous run of the (item, row tile) work, so that the row tiles of one
   // item, which read the same activations, share that XCD's L2.  Workgroups past
@@ -1362,22 +1388,28 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(GemvArgs a) {
   const int item = a.items[1 + work / gx];
   const int tile = work % gx;
   const int ntok = min(K6_TOK, a.meta[2 + 2 * kMetaB + (item & 0xFFFF)] - (item >> 16) * K6_TOK);
-  // gate/up: one body for both tile counts (the two-tile form alone needs
-  // every register and spills; so would two forms in one kernel); down: a
-  // straight body per tile count, both within 90 registers
-  if constexpr (GLU)
-    mfma_pass<GLU, 0>(a, L, item, tile);
-  else if (ntok > 16)
-    mfma_pass<GLU, 2>(a, L, item, tile);
-  else
-    mfma_pass<GLU, 1>(a, L, item, tile);
+  // rows of a multiple of 16 blocks take their scales in windows of 16 blocks
+  // (one 16-byte load per lane and window); other rows per chunk
+  const bool sw = (a.nb & 15) == 0;
+  if (ntok > 16) {
+    if (sw)
+      mfma_pass<GLU, 2, true>(a, L, item, tile);
+    else
+      mfma_pass<GLU, 2, false>(a, L, item, tile);
+  } else {
+    if (sw)
+      mfma_pass<GLU, 1, true>(a, L, item, tile);
+    else
+      mfma_pass<GLU, 1, false>(a, L, item, tile);
+  }
 }
 
-template <bool GLU, int NT>
-__device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds<GLU ? 2 : 1> &L, int item,
-                                          int tile) {
-  constexpr int NM = GLU ? 2 : 1;
+template <bool GLU, int NT, bool SW>
+__device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds &L, int item, int tile) {
+  constexpr int NTH = 64 * K6_WAVES;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = GLU ? wave / (K6_WAVES / 2) : 0;             // matrix of this wave
+  const int rw = GLU ? wave % (K6_WAVES / 2) : wave;        // its 32-row slice
   const int bucket = item & 0xFFFF;
   const int g0 = (item >> 16) * K6_TOK;
   const int slot = a.meta[2 + bucket];
@@ -1386,151 +1418,214 @@ __device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds<GLU ? 2 : 1> 
   const uint8_t *rec = a.slots + (long long)slot * a.rec_bytes;
   const int nb = a.nb, words = nb * 4;
   const int lr = lane & 15, lg = lane >> 4;
-  const int row0 = tile * K6_ROWS + wave * 16;
-  const long long my_row = min(row0 + lr, a.rows - 1);
-  const uint4 *q0row = reinterpret_cast<const uint4 *>(rec + a.off_q0) + my_row * nb;
-  const _Float16 *s0row = reinterpret_cast<const _Float16 *>(rec + a.off_s0) + my_row * nb;
-  const uint4 *q1row = reinterpret_cast<const uint4 *>(rec + a.off_q1) + my_row * nb;
-  const _Float16 *s1row = reinterpret_cast<const _Float16 *>(rec + a.off_s1) + my_row * nb;
+  const int row0 = tile * k6_rows(GLU) + rw * 32;
+  const long long rowA = min(row0 + lr, a.rows - 1), rowB = min(row0 + 16 + lr, a.rows - 1);
+  const uint4 *q = reinterpret_cast<const uint4 *>(rec + (m ? a.off_q1 : a.off_q0));
+  const uint16_t *sc = reinterpret_cast<const uint16_t *>(rec + (m ? a.off_s1 : a.off_s0));
+  const uint4 *qA = q + rowA * nb, *qB = q + rowB * nb;
+  const uint16_t *sA = sc + rowA * nb, *sB = sc + rowB * nb;
   const int nch = (nb + K6_KC - 1) / K6_KC;
   const int ntok = min(K6_TOK, cnt - g0);
-  const int n_tiles = NT ? NT : (ntok + 15) >> 4;
-  if (tid < K6_TOK) {
+  if (tid < NT * 16) {
     const int p = a.bucket_pair[off + g0 + min(tid, ntok - 1)];
     L.tok[tid] = a.in_by_pair ? p : pair_row(a, p);
   }
   __syncthreads();
 
   // activation staging of chunk c: per token 16 words x (hi, lo) = 512
-  // contiguous bytes, 32 lanes per token, four 16-B loads per thread.  Two
-  // register sets: the loads of chunk c + 2 are issued in step c and stored to
-  // LDS at the end of step c + 1.
-  auto load_b = [&](int c, uint4 &o0, uint4 &o1, uint4 &o2, uint4 &o3)
-      __attribute__((always_inline)) {
-    const int v = tid & 31;
-    const int wd = min(c * 16 + (v >> 1), words - 1);
-    auto src = [&](int j) -> const uint4 * {
-      return reinterpret_cast<const uint4 *>(
-                 a.xp + ((long long)L.tok[(tid >> 5) + 8 * j] * words + wd) * 8) +
-             (v & 1);
-    };
-    o0 = *src(0);
-    o1 = *src(1);
-    if constexpr (NT != 1) {
-      o2 = *src(2);
-      o3 = *src(3);
+  // contiguous bytes in 32 units of 16 B; thread tid stages unit tid % 32 of
+  // tokens tid / 32 (and + 16 for two tiles).  Two register sets: the loads of
+  // chunk c + 2 are issued in step c and stored to LDS at the end of step c + 1.
+  static_assert(NTH == 16 * 32, "one staging unit per thread and tile");
+  const int sv = tid & 31, st = tid >> 5;
+  const uint4 *bsrc0 = reinterpret_cast<const uint4 *>(a.xp + (long long)L.tok[st] * words * 8) +
+                       (sv & 1);
+  const uint4 *bsrc1 = NT == 2 ? reinterpret_cast<const uint4 *>(
+                                     a.xp + (long long)L.tok[st + 16] * words * 8) +
+                                     (sv & 1)
+                               : bsrc0;
+  auto load_b = [&](int c, uint4 &o0, uint4 &o1) __attribute__((always_inline)) {
+    const int wd = min(c * 16 + (sv >> 1), words - 1);
+    o0 = bsrc0[2 * wd];
+    if constexpr (NT == 2) o1 = bsrc1[2 * wd];
+  };
+  auto store_b = [&](int buf, const uint4 &o0, const uint4 &o1) __attribute__((always_inline)) {
+    L.B[buf][st][sv] = o0;
+    if constexpr (NT == 2) L.B[buf][st + 16][sv] = o1;
+  };
+  // this lane's weight blocks of chunk c (one per row group) and their scales,
+  // packed group A low / group B high, zero for blocks past the row end (also
+  // for every block of a chunk c >= nch).  Unconditional loads (clamped block)
+  // keep the code straight.
+  auto load_a = [&](int c, uint4 &wA, uint4 &wB, uint32_t &s) __attribute__((always_inline)) {
+    const int blk = c * K6_KC + lg;
+    const int bc = min(blk, nb - 1);
+    wA = qA[bc];
+    wB = qB[bc];
+    if constexpr (!SW) {
+      const uint32_t lo = sA[bc], hi = sB[bc];
+      s = blk < nb ? (lo | (hi << 16)) : 0u;
     }
   };
-  auto store_b = [&](int buf, const uint4 &o0, const uint4 &o1, const uint4 &o2,
-                     const uint4 &o3) __attribute__((always_inline)) {
-    const int v = tid & 31, t = tid >> 5;
-    L.B[buf][t][v] = o0;
-    L.B[buf][t + 8][v] = o1;
-    if constexpr (NT != 1) {
-      L.B[buf][t + 16][v] = o2;
-      L.B[buf][t + 24][v] = o3;
-    }
+  // Scale windows (SW: nb is a multiple of 16, so every window is whole and the
+  // chunk count a multiple of 4): lane (lr, lg) loads 8 scales of row lr of
+  // group lg / 2, blocks 16k + 8 (lg % 2) ..., one window ahead, and writes
+  // them to the wave's table at the window's first chunk; each chunk then
+  // reads its 4 blocks' scales of row lr for both groups (8 bytes each).
+  const uint16_t *swp = (lg >> 1) ? sB : sA;
+  const int sj = (lg & 1) * 8, nwin = nb >> 4;
+  uint4 swin = make_uint4(0u, 0u, 0u, 0u);
+  auto load_w = [&](int k) __attribute__((always_inline)) {
+    swin = *reinterpret_cast<const uint4 *>(swp + min(k, nwin - 1) * 16 + sj);
   };
-  // this lane's weight block of chunk c, per matrix (the second one only for
-  // the GLU), held in named registers.  Unconditional loads (clamped block):
-  // blocks past the row end get a zero scale when the chunk is used.
-  auto load_a = [&](int c, uint4 &w0, uint4 &w1, _Float16 &s0, _Float16 &s1)
-      __attribute__((always_inline)) {
-    const int bc = min(c * K6_KC + lg, nb - 1);
-    w0 = q0row[bc];
-    s0 = s0row[bc];
-    if constexpr (GLU) {
-      w1 = q1row[bc];
-      s1 = s1row[bc];
-    }
+  auto store_w = [&]() __attribute__((always_inline)) {
+    uint32_t *dst = &L.SC[wave][lg >> 1][lr][sj >> 1];
+    *reinterpret_cast<uint2 *>(dst) = make_uint2(swin.x, swin.y);
+    *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(swin.z, swin.w);
   };
   static_assert(K6_PD == 2, "the chunk ring is written out for two chunks");
   uint4 wa0, wa1, wb0, wb1;
-  _Float16 sa0, sa1, sb0, sb1;
-  uint4 ba0, ba1, ba2, ba3, bb0, bb1, bb2, bb3;
+  uint32_t sa, sb;
+  uint4 xa0, xa1, xb0, xb1;
   // issue order as in the steady state (activations, then weights, per chunk)
-  load_b(0, ba0, ba1, ba2, ba3);
-  load_a(0, wa0, wa1, sa0, sa1);
-  load_b(min(1, nch - 1), bb0, bb1, bb2, bb3);
-  load_a(min(1, nch - 1), wb0, wb1, sb0, sb1);
-  store_b(0, ba0, ba1, ba2, ba3);
+  if constexpr (SW) load_w(0);
+  load_b(0, xa0, xa1);
+  load_a(0, wa0, wa1, sa);
+  load_b(min(1, nch - 1), xb0, xb1);
+  load_a(1, wb0, wb1, sb);
+  store_b(0, xa0, xa1);
   __syncthreads();
 
+  // accumulators [row group][token tile]
   floatx4 acc00 = {0.f, 0.f, 0.f, 0.f}, acc01 = acc00, acc10 = acc00, acc11 = acc00;
 
-  // one matrix of one chunk: transposed words t, scales from the LDS table
-  auto mma = [&](int cur, int q, const uint4 &t, floatx4 &c0, floatx4 &c1)
-      __attribute__((always_inline)) {
+  // one K chunk: transpose, gather scales, refill the ring slot with chunk
+  // c + 2, multiply, stage chunk c + 1, barrier.  (wA, wB, s, l*): this
+  // chunk's ring slot; (n*): the activations of chunk c + 1.
+  auto step = [&](auto first, int c, uint4 &wA, uint4 &wB, uint32_t &s, uint4 &l0, uint4 &l1,
+                  const uint4 &n0, const uint4 &n1) __attribute__((always_inline)) {
+    // keep the scheduler from pulling the next step's transposes (and so the
+    // wait for its weights) into this one: that would shorten the prefetch
+    __builtin_amdgcn_sched_barrier(0);
+    const int cur = c & 1;
+    const uint4 tA = transpose_rows(wA);
+    const uint4 tB = transpose_rows(wB);
+    // the chunk's scales: (sAl, sAh) = row lr of group A, blocks 0-1 / 2-3 as
+    // binary16 pairs, (sBl, sBh) the same for group B
+    uint32_t sAl, sAh, sBl, sBh;
+    if constexpr (SW) {
+      if constexpr (decltype(first)::value) {
+        store_w();
+        load_w(c / 4 + 1);
+      }
+      const uint2 pA = *reinterpret_cast<const uint2 *>(&L.SC[wave][0][lr][2 * (c & 3)]);
+      const uint2 pB = *reinterpret_cast<const uint2 *>(&L.SC[wave][1][lr][2 * (c & 3)]);
+      sAl = pA.x;
+      sAh = pA.y;
+      sBl = pB.x;
+      sBh = pB.y;
+    } else {
+      // lane row g holds (group A, group B) of block g: gather all four, then
+      // regroup per row group
+      const uint4 sg = gather_rows(s);
+      sAl = __builtin_amdgcn_perm(sg.y, sg.x, 0x05040100u);
+      sAh = __builtin_amdgcn_perm(sg.w, sg.z, 0x05040100u);
+      sBl = __builtin_amdgcn_perm(sg.y, sg.x, 0x07060302u);
+      sBh = __builtin_amdgcn_perm(sg.w, sg.z, 0x07060302u);
+    }
+    // Loads past the last chunk re-read it (clamped) so that the code stays
+    // straight and the waits exact; load_a takes the chunk unclamped, so that
+    // such a chunk's scales are zero.
+    load_b(min(c + K6_PD, nch - 1), l0, l1);
+    load_a(c + K6_PD, wA, wB, s);
 #pragma unroll
     for (int b = 0; b < K6_KC; ++b) {
-      const uint32_t aw = b == 0 ? t.x : b == 1 ? t.y : b == 2 ? t.z : t.w;
-      const half8_t A = decode_word_h(aw);
-      const float4 d = *reinterpret_cast<const float4 *>(&L.S[wave][q][b][lg * 4]);
-      const half8_t Bh0 = __builtin_bit_cast(half8_t, L.B[cur][lr][(b * 4 + lg) * 2]);
-      const half8_t Bl0 = __builtin_bit_cast(half8_t, L.B[cur][lr][(b * 4 + lg) * 2 + 1]);
-      floatx4 cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh0, floatx4{0.f, 0.f, 0.f, 0.f},
-                                                          0, 0, 0);
-      cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl0, cc, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) c0[i] = __builtin_fmaf(pick4(d, i), cc[i], c0[i]);
-      if (NT == 2 || (NT == 0 && n_tiles > 1)) {
-        const half8_t Bh1 = __builtin_bit_cast(half8_t, L.B[cur][16 + lr][(b * 4 + lg) * 2]);
-        const half8_t Bl1 =
+      const uint32_t awA = b == 0 ? tA.x : b == 1 ? tA.y : b == 2 ? tA.z : tA.w;
+      const uint32_t awB = b == 0 ? tB.x : b == 1 ? tB.y : b == 2 ? tB.z : tB.w;
+      const half2_t hA = __builtin_bit_cast(half2_t, b < 2 ? sAl : sAh);
+      const half2_t hB = __builtin_bit_cast(half2_t, b < 2 ? sBl : sBh);
+      const float dA = (float)hA[b & 1], dB = (float)hB[b & 1];
+      const half8_t WA = decode_word_h(awA);
+      const half8_t WB = decode_word_h(awB);
+      const half8_t Xh0 = __builtin_bit_cast(half8_t, L.B[cur][lr][(b * 4 + lg) * 2]);
+      const half8_t Xl0 = __builtin_bit_cast(half8_t, L.B[cur][lr][(b * 4 + lg) * 2 + 1]);
+      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+      floatx4 cA0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xh0, WA, z, 0, 0, 0);
+      floatx4 cB0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xh0, WB, z, 0, 0, 0);
+      cA0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xl0, WA, cA0, 0, 0, 0);
+      cB0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xl0, WB, cB0, 0, 0, 0);
+      if constexpr (NT == 2) {
+        const half8_t Xh1 = __builtin_bit_cast(half8_t, L.B[cur][16 + lr][(b * 4 + lg) * 2]);
+        const half8_t Xl1 =
             __builtin_bit_cast(half8_t, L.B[cur][16 + lr][(b * 4 + lg) * 2 + 1]);
-        floatx4 c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            A, Bh1, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl1, c2, 0, 0, 0);
+        floatx4 cA1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xh1, WA, z, 0, 0, 0);
+        floatx4 cB1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xh1, WB, z, 0, 0, 0);
+        cA1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xl1, WA, cA1, 0, 0, 0);
+        cB1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xl1, WB, cB1, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) c1[i] = __builtin_fmaf(pick4(d, i), c2[i], c1[i]);
+        for (int i = 0; i < 4; ++i) {
+          acc01[i] = __builtin_fmaf(dA, cA1[i], acc01[i]);
+          acc11[i] = __builtin_fmaf(dB, cB1[i], acc11[i]);
+        }
       }
-    }
-  };
-
-  // one K chunk: scales to the table, transpose, refill the ring slots,
-  // multiply, stage the next activations, barrier.  (w*, s*): this chunk's
-  // weights, refilled with chunk c + 2; (l*): the activation set that receives
-  // chunk c + 2; (m*): the set holding chunk c + 1.
-  auto step = [&](int c, uint4 &w0, uint4 &w1, _Float16 &s0, _Float16 &s1, uint4 &l0,
-                  uint4 &l1, uint4 &l2, uint4 &l3, const uint4 &m0, const uint4 &m1,
-                  const uint4 &m2, const uint4 &m3) __attribute__((always_inline)) {
-    const int cur = c & 1;
-    const bool live = c * K6_KC + lg < nb;
-    L.S[wave][0][lg][lr] = live ? (float)s0 : 0.0f;
-    if constexpr (GLU) L.S[wave][NM - 1][lg][lr] = live ? (float)s1 : 0.0f;
-    const uint4 t0 = transpose_rows(w0);
-    uint4 t1 = t0;
-    if constexpr (GLU) t1 = transpose_rows(w1);
-    // Loads past the last chunk re-read it (clamped) so that the code stays
-    // straight and the waits exact.
-    load_b(min(c + 2, nch - 1), l0, l1, l2, l3);
-    load_a(min(c + K6_PD, nch - 1), w0, w1, s0, s1);
-    __builtin_amdgcn_wave_barrier();
-    mma(cur, 0, t0, acc00, acc01);
-    if constexpr (GLU) mma(cur, NM - 1, t1, acc10, acc11);
-    store_b(cur ^ 1, m0, m1, m2, m3);  // buffer cur ^ 1 is idle until the barrier
-    __syncthreads();
-  };
-  // steps in pairs, unconditionally (straight code keeps the load waits exact);
-  // for an odd chunk count the last step is a chunk past the row end, whose
-  // blocks all have a zero scale
-  for (int c0 = 0; c0 < nch; c0 += K6_PD) {
-    step(c0, wa0, wa1, sa0, sa1, ba0, ba1, ba2, ba3, bb0, bb1, bb2, bb3);
-    step(c0 + 1, wb0, wb1, sb0, sb1, bb0, bb1, bb2, bb3, ba0, ba1, ba2, ba3);
-  }
-  // C lane layout: rows row0 + 4*lg + i, token column t*16 + lr
-#pragma unroll
-  for (int t = 0; t < (NT ? NT : 2); ++t) {
-    const int col = t * 16 + lr;
-    if (t < n_tiles && col < ntok) {
-      const int p = a.bucket_pair[off + g0 + col];
-      const float sc = a.xscale[L.tok[col]];
-      const floatx4 g = t == 0 ? acc00 : acc01;
-      const floatx4 u = t == 0 ? acc10 : acc11;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = row0 + lg * 4 + i;
-        if (r < a.rows) {
-          const float v = GLU ? silu_f(g[i] * sc) * (u[i] * sc) : g[i] * sc;
+        acc00[i] = __builtin_fmaf(dA, cA0[i], acc00[i]);
+        acc10[i] = __builtin_fmaf(dB, cB0[i], acc10[i]);
+      }
+    }
+    store_b(cur ^ 1, n0, n1);  // buffer cur ^ 1 is idle until the barrier
+    __syncthreads();
+  };
+  // steps in pairs (in fours with scale windows), unconditionally (straight
+  // code keeps the load waits exact); for an odd chunk count the last step is a
+  // chunk past the row end, whose blocks all have a zero scale
+  const std::integral_constant<bool, true> win;
+  const std::integral_constant<bool, false> nowin;
+  if constexpr (SW) {
+    for (int c0 = 0; c0 < nch; c0 += 4) {
+      step(win, c0, wa0, wa1, sa, xa0, xa1, xb0, xb1);
+      step(nowin, c0 + 1, wb0, wb1, sb, xb0, xb1, xa0, xa1);
+      step(nowin, c0 + 2, wa0, wa1, sa, xa0, xa1, xb0, xb1);
+      step(nowin, c0 + 3, wb0, wb1, sb, xb0, xb1, xa0, xa1);
+    }
+  } else {
+    for (int c0 = 0; c0 < nch; c0 += K6_PD) {
+      step(nowin, c0, wa0, wa1, sa, xa0, xa1, xb0, xb1);
+      step(nowin, c0 + 1, wb0, wb1, sb, xb0, xb1, xa0, xa1);
+    }
+  }
+  // C lane layout: token column t*16 + 4*lg + i, weight row row0 + 16*g + lr.
+  // The GLU's gate waves hand their sums to the up waves of the same rows
+  // through the (now idle) activation buffers.
+  floatx4 *xg = reinterpret_cast<floatx4 *>(&L.B[0][0][0]) + rw * 4 * 64 + lane;
+  if constexpr (GLU) {
+    if (m == 0) {
+      xg[0] = acc00;
+      xg[64] = acc10;
+      if constexpr (NT == 2) {
+        xg[128] = acc01;
+        xg[192] = acc11;
+      }
+    }
+    __syncthreads();
+    if (m == 0) return;
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int r = row0 + 16 * g + lr;
+      const floatx4 u = g == 0 ? (t == 0 ? acc00 : acc01) : (t == 0 ? acc10 : acc11);
+      floatx4 gt = u;
+      if constexpr (GLU) gt = xg[(t * 2 + g) * 64];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = t * 16 + 4 * lg + i;
+        if (col < ntok && r < a.rows) {
+          const int p = a.bucket_pair[off + g0 + col];
+          const float s = a.xscale[L.tok[col]];
+          const float v = GLU ? silu_f(gt[i] * s) * (u[i] * s) : u[i] * s;
           a.out[(long long)p * a.rows + r] = v;
         }
       }
@@ -1541,11 +1636,12 @@ __device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds<GLU ? 2 : 1> 
 hipError_t launch_mfma(const GemvArgs &a, bool glu, int n_items, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
   if (n_items > 65535) return hipErrorInvalidValue;
-  const dim3 grid((a.rows + K6_ROWS - 1) / K6_ROWS, n_items);
+  const int rows_wg = k6_rows(glu);
+  const dim3 grid((a.rows + rows_wg - 1) / rows_wg, n_items);
   if (glu)
-    launch_k(q4_mfma_kernel<true>, grid, dim3(256), 0, s, a);
+    launch_k(q4_mfma_kernel<true>, grid, dim3(64 * K6_WAVES), 0, s, a);
   else
-    launch_k(q4_mfma_kernel<false>, grid, dim3(256), 0, s, a);
+    launch_k(q4_mfma_kernel<false>, grid, dim3(64 * K6_WAVES), 0, s, a);
   return hipGetLastError();
 }
 

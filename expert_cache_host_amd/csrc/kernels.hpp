@@ -123,16 +123,17 @@ hipError_t launch_gemv(const GemvArgs &a, const BucketTable *tab, const GemvShap
                        int n_buckets, hipStream_t s);
 
 // Prefill grouped GEMM on the matrix cores (batches beyond the decode path).
-// Work items from launch_remap; per workgroup 64 weight rows of one bucket's
-// expert and one pass of up to kGemmTokens of its tokens.  Each wave streams its
-// 16 rows' nibbles through registers (two K chunks in flight) and decodes them
-// to exact binary16 (q - 8) A operands; activations come as binary16 hi/lo pairs
-// in the same K order (xp / xscale as prepared for the gate/up GEMM, indexed
-// by token for gate/up and by pair for down), staged per chunk in LDS.  Each
-// 32-weight block is one pair of v_mfma_f32_16x16x32_f16 (hi, lo) per 16-token
-// tile, and its scale is applied per block in fp32.  glu: out[p][r] =
-// silu(g) * u; else out = M in.  A grid of n_items columns covers at most that
-// many work items (more than 65535: hipErrorInvalidValue).
+// Work items from launch_remap; per workgroup of 8 waves one pass of up to
+// kGemmTokens of a bucket's tokens and 128 weight rows of both GLU matrices
+// (256 rows of the down matrix).  Each wave streams 32 rows' nibbles through
+// registers (two K chunks in flight) and decodes them to exact binary16 (q - 8)
+// operands; activations come as binary16 hi/lo pairs in the same K order (xp /
+// xscale as prepared for the gate/up GEMM, indexed by token for gate/up and by
+// pair for down), staged per chunk in LDS.  Each 32-weight block is one pair of
+// v_mfma_f32_16x16x32_f16 (hi, lo) per 16-token tile and 16 rows, and its scale
+// is applied per block in fp32.  glu: out[p][r] = silu(g) * u; else out = M in.
+// A grid of n_items columns covers at most that many work items (more than
+// 65535: hipErrorInvalidValue).
 hipError_t launch_mfma(const GemvArgs &a, bool glu, int n_items, hipStream_t s);
 
 // Binary16 hi/lo pairs and power-of-two scale of `rows` float rows of length K

@@ -33,16 +33,18 @@ def _lib():
     return load_library()
 
 
-@pytest.mark.parametrize("mode,T", [("host", 1), ("host", 3), ("stream", 64)])
-def test_delayed_fills_change_nothing(mode, T):
+@pytest.mark.parametrize("mode,T,policy", [("host", 1, "lru"), ("host", 3, "lru"),
+                                           ("stream", 64, "lru"), ("host", 1, "score")])
+def test_delayed_fills_change_nothing(mode, T, policy):
     """Host mode publishes a call's fills at the layer's next call; staged
     stream calls wait for each stage's fills.  With every fill batch held 4 ms
-    on its copy stream, both caches give the same bits."""
+    on its copy stream, both caches give the same bits (the score policy's
+    admitted fills too)."""
     wl = synth.Workload("delay", 80, 2, 256, 512, 16, 4, 4, n_shared=1, router_sigma=0.12,
                         zipf_s=0.6, rho=0.6 if T < 64 else None, tokens=8 * T, batch=T)
-    log(f"delayed fills mode={mode} T={T}")
-    ref = Runner(wl, [0, 1], mode=mode)
-    slow = Runner(wl, [0, 1], mode=mode, weights=ref.weights)
+    log(f"delayed fills mode={mode} T={T} policy={policy}")
+    ref = Runner(wl, [0, 1], mode=mode, policy=policy)
+    slow = Runner(wl, [0, 1], mode=mode, weights=ref.weights, policy=policy)
     assert _lib().moe_debug_fill_delay(slow.cache._h, 4000) == 0
     xs = [synth.gen_hidden(wl, l, 8) for l in (0, 1)]
     fills = 0
