@@ -1359,10 +1359,10 @@ struct K6Lds {
   // rows over the banks (row stride 528 B = 16 B mod 128 B).  After the last
   // chunk the buffers hold the gate sums for the up waves.
   uint4 B[2][K6_TOK][K6_KC * 8 + 1];
-  // block scales of one window of 16 blocks, wave-private: [wave][row group]
-  // [row][8 binary16 pairs + 2 spare] (row stride 40 B: the 16 rows' 8-byte
-  // reads fall on distinct banks)
-  uint32_t SC[K6_WAVES][2][16][10];
+  // block scales of windows of 32 blocks, two buffers, wave-private: [buffer]
+  // [wave][row group][row][16 binary16 pairs + 2 spare] (row stride 72 B: the
+  // 16 rows' 8-byte reads fall on distinct banks)
+  uint32_t SC[2][K6_WAVES][2][16][18];
   int tok[K6_TOK];
 };
 
@@ -1388,9 +1388,9 @@ __global__ __launch_bounds__(64 * K6_WAVES, 4) void q4_mfma_kernel(GemvArgs a) {
   const int item = a.items[1 + work / gx];
   const int tile = work % gx;
   const int ntok = min(K6_TOK, a.meta[2 + 2 * kMetaB + (item & 0xFFFF)] - (item >> 16) * K6_TOK);
-  // rows of a multiple of 16 blocks take their scales in windows of 16 blocks
-  // (one 16-byte load per lane and window); other rows per chunk
-  const bool sw = (a.nb & 15) == 0;
+  // rows of a multiple of 32 blocks take their scales in windows of 32 blocks
+  // (two 16-byte loads per lane and window); other rows per chunk
+  const bool sw = (a.nb & 31) == 0;
   if (ntok > 16) {
     if (sw)
       mfma_pass<GLU, 2, true>(a, L, item, tile);
@@ -1434,8 +1434,10 @@ __device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds &L, int item,
 
   // activation staging of chunk c: per token 16 words x (hi, lo) = 512
   // contiguous bytes in 32 units of 16 B; thread tid stages unit tid % 32 of
-  // tokens tid / 32 (and + 16 for two tiles).  Two register sets: the loads of
-  // chunk c + 2 are issued in step c and stored to LDS at the end of step c + 1.
+  // tokens tid / 32 (and + 16 for two tiles).  The loads of chunk c + 1 are
+  // issued at the start of step c and stored to LDS at its end (they mostly hit
+  // the L2: every row tile of the pass reads the same activations); one
+  // register set instead of two leaves room for the scale windows.
   static_assert(NTH == 16 * 32, "one staging unit per thread and tile");
   const int sv = tid & 31, st = tid >> 5;
   const uint4 *bsrc0 = reinterpret_cast<const uint4 *>(a.xp + (long long)L.tok[st] * words * 8) +
@@ -1467,31 +1469,36 @@ __device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds &L, int item,
       s = blk < nb ? (lo | (hi << 16)) : 0u;
     }
   };
-  // Scale windows (SW: nb is a multiple of 16, so every window is whole and the
-  // chunk count a multiple of 4): lane (lr, lg) loads 8 scales of row lr of
-  // group lg / 2, blocks 16k + 8 (lg % 2) ..., one window ahead, and writes
-  // them to the wave's table at the window's first chunk; each chunk then
-  // reads its 4 blocks' scales of row lr for both groups (8 bytes each).
-  const uint16_t *swp = (lg >> 1) ? sB : sA;
-  const int sj = (lg & 1) * 8, nwin = nb >> 4;
+  // Scale windows (SW: nb is a multiple of 32, so every window is whole and the
+  // chunk count a multiple of 8).  Half h of window k holds row group h's
+  // scales of blocks 32k ... 32k + 31: lane (lr, lg) loads the 8 of row lr
+  // from block 32k + 8 lg (each load reads 64 contiguous bytes of 16 rows).
+  // Window k's half 1 is loaded at chunk 8k - 4 and written to table buffer
+  // k % 2 at chunk 8k; half 0 of window k + 1 is loaded at chunk 8k and
+  // written at chunk 8k + 4, to the other buffer, which window k - 1 has left.
+  // Each chunk reads its 4 blocks' scales of row lr for both groups (8 bytes
+  // each) from buffer (c / 8) % 2.
+  const int nwin = nb >> 5;
   uint4 swin = make_uint4(0u, 0u, 0u, 0u);
-  auto load_w = [&](int k) __attribute__((always_inline)) {
-    swin = *reinterpret_cast<const uint4 *>(swp + min(k, nwin - 1) * 16 + sj);
+  auto load_w = [&](int k, int h) __attribute__((always_inline)) {
+    swin = *reinterpret_cast<const uint4 *>((h ? sB : sA) + min(k, nwin - 1) * 32 + 8 * lg);
   };
-  auto store_w = [&]() __attribute__((always_inline)) {
-    uint32_t *dst = &L.SC[wave][lg >> 1][lr][sj >> 1];
+  auto store_w = [&](int buf, int h) __attribute__((always_inline)) {
+    uint32_t *dst = &L.SC[buf][wave][h][lr][4 * lg];
     *reinterpret_cast<uint2 *>(dst) = make_uint2(swin.x, swin.y);
     *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(swin.z, swin.w);
   };
   static_assert(K6_PD == 2, "the chunk ring is written out for two chunks");
   uint4 wa0, wa1, wb0, wb1;
   uint32_t sa, sb;
-  uint4 xa0, xa1, xb0, xb1;
-  // issue order as in the steady state (activations, then weights, per chunk)
-  if constexpr (SW) load_w(0);
+  uint4 xa0, xa1;
+  if constexpr (SW) {
+    load_w(0, 0);
+    store_w(0, 0);
+    load_w(0, 1);
+  }
   load_b(0, xa0, xa1);
   load_a(0, wa0, wa1, sa);
-  load_b(min(1, nch - 1), xb0, xb1);
   load_a(1, wb0, wb1, sb);
   store_b(0, xa0, xa1);
   __syncthreads();
@@ -1499,27 +1506,32 @@ __device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds &L, int item,
   // accumulators [row group][token tile]
   floatx4 acc00 = {0.f, 0.f, 0.f, 0.f}, acc01 = acc00, acc10 = acc00, acc11 = acc00;
 
-  // one K chunk: transpose, gather scales, refill the ring slot with chunk
-  // c + 2, multiply, stage chunk c + 1, barrier.  (wA, wB, s, l*): this
-  // chunk's ring slot; (n*): the activations of chunk c + 1.
+  // one K chunk: stage-load chunk c + 1, transpose, gather scales, refill the
+  // ring slot with chunk c + 2, multiply, store chunk c + 1's activations,
+  // barrier.  (wA, wB, s): this chunk's ring slot; l*, n*: the staging set.
   auto step = [&](auto first, int c, uint4 &wA, uint4 &wB, uint32_t &s, uint4 &l0, uint4 &l1,
                   const uint4 &n0, const uint4 &n1) __attribute__((always_inline)) {
     // keep the scheduler from pulling the next step's transposes (and so the
     // wait for its weights) into this one: that would shorten the prefetch
     __builtin_amdgcn_sched_barrier(0);
     const int cur = c & 1;
+    load_b(min(c + 1, nch - 1), xa0, xa1);
     const uint4 tA = transpose_rows(wA);
     const uint4 tB = transpose_rows(wB);
     // the chunk's scales: (sAl, sAh) = row lr of group A, blocks 0-1 / 2-3 as
     // binary16 pairs, (sBl, sBh) the same for group B
     uint32_t sAl, sAh, sBl, sBh;
     if constexpr (SW) {
-      if constexpr (decltype(first)::value) {
-        store_w();
-        load_w(c / 4 + 1);
+      const int k = c >> 3;
+      if constexpr (decltype(first)::value == 1) {  // chunk 8k
+        store_w(k & 1, 1);
+        load_w(k + 1, 0);
+      } else if constexpr (decltype(first)::value == 2) {  // chunk 8k + 4
+        store_w((k + 1) & 1, 0);
+        load_w(k + 1, 1);
       }
-      const uint2 pA = *reinterpret_cast<const uint2 *>(&L.SC[wave][0][lr][2 * (c & 3)]);
-      const uint2 pB = *reinterpret_cast<const uint2 *>(&L.SC[wave][1][lr][2 * (c & 3)]);
+      const uint2 pA = *reinterpret_cast<const uint2 *>(&L.SC[k & 1][wave][0][lr][2 * (c & 7)]);
+      const uint2 pB = *reinterpret_cast<const uint2 *>(&L.SC[k & 1][wave][1][lr][2 * (c & 7)]);
       sAl = pA.x;
       sAh = pA.y;
       sBl = pB.x;
@@ -1536,7 +1548,6 @@ __device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds &L, int item,
     // Loads past the last chunk re-read it (clamped) so that the code stays
     // straight and the waits exact; load_a takes the chunk unclamped, so that
     // such a chunk's scales are zero.
-    load_b(min(c + K6_PD, nch - 1), l0, l1);
     load_a(c + K6_PD, wA, wB, s);
 #pragma unroll
     for (int b = 0; b < K6_KC; ++b) {
@@ -1574,25 +1585,30 @@ __device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds &L, int item,
         acc10[i] = __builtin_fmaf(dB, cB0[i], acc10[i]);
       }
     }
-    store_b(cur ^ 1, n0, n1);  // buffer cur ^ 1 is idle until the barrier
+    store_b(cur ^ 1, xa0, xa1);  // buffer cur ^ 1 is idle until the barrier
     __syncthreads();
   };
   // steps in pairs (in fours with scale windows), unconditionally (straight
   // code keeps the load waits exact); for an odd chunk count the last step is a
   // chunk past the row end, whose blocks all have a zero scale
-  const std::integral_constant<bool, true> win;
-  const std::integral_constant<bool, false> nowin;
+  const std::integral_constant<int, 0> nowin;
+  const std::integral_constant<int, 1> win0;
+  const std::integral_constant<int, 2> win4;
   if constexpr (SW) {
-    for (int c0 = 0; c0 < nch; c0 += 4) {
-      step(win, c0, wa0, wa1, sa, xa0, xa1, xb0, xb1);
-      step(nowin, c0 + 1, wb0, wb1, sb, xb0, xb1, xa0, xa1);
-      step(nowin, c0 + 2, wa0, wa1, sa, xa0, xa1, xb0, xb1);
-      step(nowin, c0 + 3, wb0, wb1, sb, xb0, xb1, xa0, xa1);
+    for (int c0 = 0; c0 < nch; c0 += 8) {
+      step(win0, c0, wa0, wa1, sa, xa0, xa1, xa0, xa1);
+      step(nowin, c0 + 1, wb0, wb1, sb, xa0, xa1, xa0, xa1);
+      step(nowin, c0 + 2, wa0, wa1, sa, xa0, xa1, xa0, xa1);
+      step(nowin, c0 + 3, wb0, wb1, sb, xa0, xa1, xa0, xa1);
+      step(win4, c0 + 4, wa0, wa1, sa, xa0, xa1, xa0, xa1);
+      step(nowin, c0 + 5, wb0, wb1, sb, xa0, xa1, xa0, xa1);
+      step(nowin, c0 + 6, wa0, wa1, sa, xa0, xa1, xa0, xa1);
+      step(nowin, c0 + 7, wb0, wb1, sb, xa0, xa1, xa0, xa1);
     }
   } else {
     for (int c0 = 0; c0 < nch; c0 += K6_PD) {
-      step(nowin, c0, wa0, wa1, sa, xa0, xa1, xb0, xb1);
-      step(nowin, c0 + 1, wb0, wb1, sb, xb0, xb1, xa0, xa1);
+      step(nowin, c0, wa0, wa1, sa, xa0, xa1, xa0, xa1);
+      step(nowin, c0 + 1, wb0, wb1, sb, xa0, xa1, xa0, xa1);
     }
   }
   // C lane layout: token column t*16 + 4*lg + i, weight row row0 + 16*g + lr.
