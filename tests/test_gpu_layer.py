@@ -514,6 +514,24 @@ def test_matrix_core_extreme_scales(scale, mode):
     r.close()
 
 
+@pytest.mark.parametrize("d,f", [(1024, 3072), (3072, 1024)])
+def test_matrix_core_scale_windows(d, f):
+    """Matrix-core calls on rows of 32 and 96 blocks: the scale windows of 32
+    blocks then number one and three (the large shape has six and two), and a
+    40-token call has a pass of 8 tokens after one of 32."""
+    wl = synth.Workload(f"win_{d}_{f}", 70 + d // 1024, 1, d, f, 16, 4, 6, n_shared=1,
+                        router_sigma=0.4 / np.sqrt(d), zipf_s=0.5, rho=None, tokens=40 * 3,
+                        batch=40)
+    log(f"matrix-core scale windows d={d} f={f}, T=40")
+    r = Runner(wl, [0], mode="stream")
+    x = synth.gen_hidden(wl, 0)
+    for c in range(x.shape[0]):
+        _, res = r.call(0, x[c])
+        assert len(res.stage_views) > 1
+    r.check_log()
+    r.close()
+
+
 @pytest.mark.parametrize("scale", [2.0 ** -20, 1.0 / 3000.0])
 def test_decode_extreme_scales(scale):
     """Decode calls on inputs far below unit scale (the block scales follow)."""
