@@ -1276,13 +1276,15 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
 // value; both row groups of a wave share every activation fragment read.
 // A wave streams its rows through registers: for each group, lane l loads the
 // whole 16-byte nibble block 4c + l/16 of row l%16 for K chunk c (4 blocks),
-// and its 16-bit scale, PD chunks ahead of the one it multiplies.  A 4 x 4 word
-// transpose across the four 16-lane rows of the wave (two rounds of gfx950 lane
-// swaps) turns "block per lane row" into the operand layout (lane l: row l%16,
-// word l/16 of each of the 4 blocks); the same swaps gather the four scales of
-// a row into every lane of that row.  The activation tiles (binary16 hi/lo
-// pairs for the chunk's 4 blocks and the pass's tokens) are staged per chunk
-// for the whole workgroup in two LDS buffers, with one barrier per chunk.
+// two chunks ahead of the one it multiplies.  A 4 x 4 word transpose across the
+// four 16-lane rows of the wave (two rounds of gfx950 lane swaps) turns "block
+// per lane row" into the operand layout (lane l: row l%16, word l/16 of each of
+// the 4 blocks).  Block scales: rows of a multiple of 32 blocks take them in
+// windows of 32 blocks through a wave-private LDS table; other rows load each
+// chunk's scales beside its weights, and the same lane swaps gather the four
+// scales of a row into every lane of that row.  The activation tiles (binary16
+// hi/lo pairs for the chunk's 4 blocks and the pass's tokens) are staged per
+// chunk for the whole workgroup in two LDS buffers, with one barrier per chunk.
 // A lane turns its nibble word into binary16 q - 8 exactly: the exponent trick
 // puts q (or 16 q, for the nibbles at bits 4-7 of each half) in the mantissa of
 // 1024, and one packed subtract (or multiply-add by 1/16) leaves q - 8.  Each
@@ -1455,10 +1457,10 @@ __device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds &L, int item,
     L.B[buf][st][sv] = o0;
     if constexpr (NT == 2) L.B[buf][st + 16][sv] = o1;
   };
-  // this lane's weight blocks of chunk c (one per row group) and their scales,
-  // packed group A low / group B high, zero for blocks past the row end (also
-  // for every block of a chunk c >= nch).  Unconditional loads (clamped block)
-  // keep the code straight.
+  // this lane's weight blocks of chunk c (one per row group) and, without scale
+  // windows, their scales, packed group A low / group B high, zero for blocks
+  // past the row end (also for every block of a chunk c >= nch).  Unconditional
+  // loads (clamped block) keep the code straight.
   auto load_a = [&](int c, uint4 &wA, uint4 &wB, uint32_t &s) __attribute__((always_inline)) {
     const int blk = c * K6_KC + lg;
     const int bc = min(blk, nb - 1);
