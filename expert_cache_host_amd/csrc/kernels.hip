@@ -1458,28 +1458,27 @@ __device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds &L, int item,
     if constexpr (NT == 2) L.B[buf][st + 16][sv] = o1;
   };
   // this lane's weight blocks of chunk c (one per row group) and, without scale
-  // windows, their scales, packed group A low / group B high, zero for blocks
-  // past the row end (also for every block of a chunk c >= nch).  Unconditional
-  // loads (clamped block) keep the code straight.
-  auto load_a = [&](int c, uint4 &wA, uint4 &wB, uint32_t &s) __attribute__((always_inline)) {
-    const int blk = c * K6_KC + lg;
-    const int bc = min(blk, nb - 1);
+  // windows, their scales (group A, group B) as loaded: packing them here would
+  // make the loads' wait immediate.  Unconditional loads (clamped block) keep
+  // the code straight.
+  auto load_a = [&](int c, uint4 &wA, uint4 &wB, uint2 &s) __attribute__((always_inline)) {
+    const int bc = min(c * K6_KC + lg, nb - 1);
     wA = qA[bc];
     wB = qB[bc];
-    if constexpr (!SW) {
-      const uint32_t lo = sA[bc], hi = sB[bc];
-      s = blk < nb ? (lo | (hi << 16)) : 0u;
-    }
+    if constexpr (!SW) s = make_uint2(sA[bc], sB[bc]);
   };
   // Scale windows (SW: nb is a multiple of 32, so every window is whole and the
   // chunk count a multiple of 8).  Half h of window k holds row group h's
   // scales of blocks 32k ... 32k + 31: lane (lr, lg) loads the 8 of row lr
   // from block 32k + 8 lg (each load reads 64 contiguous bytes of 16 rows).
-  // Window k's half 1 is loaded at chunk 8k - 4 and written to table buffer
-  // k % 2 at chunk 8k; half 0 of window k + 1 is loaded at chunk 8k and
-  // written at chunk 8k + 4, to the other buffer, which window k - 1 has left.
-  // Each chunk reads its 4 blocks' scales of row lr for both groups (8 bytes
-  // each) from buffer (c / 8) % 2.
+  // Window k + 1 arrives during window k, both halves inside the same loop
+  // trip: half 0 is loaded at chunk 8k and written at chunk 8k + 3, half 1
+  // loaded at 8k + 3 and written at 8k + 6, to table buffer (k + 1) % 2, which
+  // window k - 1 has left.  (A load in one trip consumed in the next made the
+  // compiler's wait at the trip's start cover every load in flight, the next
+  // chunk's weights too.)  Each chunk reads its 4 blocks' scales of row lr for
+  // both groups (8 bytes each) from buffer (c / 8) % 2; window 0 is written
+  // before the loop.
   const int nwin = nb >> 5;
   uint4 swin = make_uint4(0u, 0u, 0u, 0u);
   auto load_w = [&](int k, int h) __attribute__((always_inline)) {
@@ -1492,12 +1491,13 @@ __device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds &L, int item,
   };
   static_assert(K6_PD == 2, "the chunk ring is written out for two chunks");
   uint4 wa0, wa1, wb0, wb1;
-  uint32_t sa, sb;
+  uint2 sa = make_uint2(0u, 0u), sb = sa;
   uint4 xa0, xa1;
   if constexpr (SW) {
     load_w(0, 0);
     store_w(0, 0);
     load_w(0, 1);
+    store_w(0, 1);
   }
   load_b(0, xa0, xa1);
   load_a(0, wa0, wa1, sa);
@@ -1511,7 +1511,7 @@ __device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds &L, int item,
   // one K chunk: stage-load chunk c + 1, transpose, gather scales, refill the
   // ring slot with chunk c + 2, multiply, store chunk c + 1's activations,
   // barrier.  (wA, wB, s): this chunk's ring slot; l*, n*: the staging set.
-  auto step = [&](auto first, int c, uint4 &wA, uint4 &wB, uint32_t &s, uint4 &l0, uint4 &l1,
+  auto step = [&](auto first, int c, uint4 &wA, uint4 &wB, uint2 &s, uint4 &l0, uint4 &l1,
                   const uint4 &n0, const uint4 &n1) __attribute__((always_inline)) {
     // keep the scheduler from pulling the next step's transposes (and so the
     // wait for its weights) into this one: that would shorten the prefetch
@@ -1526,11 +1526,12 @@ __device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds &L, int item,
     if constexpr (SW) {
       const int k = c >> 3;
       if constexpr (decltype(first)::value == 1) {  // chunk 8k
-        store_w(k & 1, 1);
         load_w(k + 1, 0);
-      } else if constexpr (decltype(first)::value == 2) {  // chunk 8k + 4
+      } else if constexpr (decltype(first)::value == 2) {  // chunk 8k + 3
         store_w((k + 1) & 1, 0);
         load_w(k + 1, 1);
+      } else if constexpr (decltype(first)::value == 3) {  // chunk 8k + 6
+        store_w((k + 1) & 1, 1);
       }
       const uint2 pA = *reinterpret_cast<const uint2 *>(&L.SC[k & 1][wave][0][lr][2 * (c & 7)]);
       const uint2 pB = *reinterpret_cast<const uint2 *>(&L.SC[k & 1][wave][1][lr][2 * (c & 7)]);
@@ -1539,17 +1540,18 @@ __device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds &L, int item,
       sBl = pB.x;
       sBh = pB.y;
     } else {
-      // lane row g holds (group A, group B) of block g: gather all four, then
+      // lane row g holds (group A, group B) of block g (zero past the row end,
+      // also for every block of a chunk c >= nch): gather all four, then
       // regroup per row group
-      const uint4 sg = gather_rows(s);
+      const bool live = c * K6_KC + lg < nb;
+      const uint4 sg = gather_rows(live ? (s.x | (s.y << 16)) : 0u);
       sAl = __builtin_amdgcn_perm(sg.y, sg.x, 0x05040100u);
       sAh = __builtin_amdgcn_perm(sg.w, sg.z, 0x05040100u);
       sBl = __builtin_amdgcn_perm(sg.y, sg.x, 0x07060302u);
       sBh = __builtin_amdgcn_perm(sg.w, sg.z, 0x07060302u);
     }
     // Loads past the last chunk re-read it (clamped) so that the code stays
-    // straight and the waits exact; load_a takes the chunk unclamped, so that
-    // such a chunk's scales are zero.
+    // straight and the waits exact.
     load_a(c + K6_PD, wA, wB, s);
 #pragma unroll
     for (int b = 0; b < K6_KC; ++b) {
@@ -1595,16 +1597,17 @@ __device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds &L, int item,
   // chunk past the row end, whose blocks all have a zero scale
   const std::integral_constant<int, 0> nowin;
   const std::integral_constant<int, 1> win0;
-  const std::integral_constant<int, 2> win4;
+  const std::integral_constant<int, 2> win3;
+  const std::integral_constant<int, 3> win6;
   if constexpr (SW) {
     for (int c0 = 0; c0 < nch; c0 += 8) {
       step(win0, c0, wa0, wa1, sa, xa0, xa1, xa0, xa1);
       step(nowin, c0 + 1, wb0, wb1, sb, xa0, xa1, xa0, xa1);
       step(nowin, c0 + 2, wa0, wa1, sa, xa0, xa1, xa0, xa1);
-      step(nowin, c0 + 3, wb0, wb1, sb, xa0, xa1, xa0, xa1);
-      step(win4, c0 + 4, wa0, wa1, sa, xa0, xa1, xa0, xa1);
+      step(win3, c0 + 3, wb0, wb1, sb, xa0, xa1, xa0, xa1);
+      step(nowin, c0 + 4, wa0, wa1, sa, xa0, xa1, xa0, xa1);
       step(nowin, c0 + 5, wb0, wb1, sb, xa0, xa1, xa0, xa1);
-      step(nowin, c0 + 6, wa0, wa1, sa, xa0, xa1, xa0, xa1);
+      step(win6, c0 + 6, wa0, wa1, sa, xa0, xa1, xa0, xa1);
       step(nowin, c0 + 7, wb0, wb1, sb, xa0, xa1, xa0, xa1);
     }
   } else {
