@@ -1510,9 +1510,9 @@ __device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds &L, int item,
 
   // one K chunk: stage-load chunk c + 1, transpose, gather scales, refill the
   // ring slot with chunk c + 2, multiply, store chunk c + 1's activations,
-  // barrier.  (wA, wB, s): this chunk's ring slot; l*, n*: the staging set.
-  auto step = [&](auto first, int c, uint4 &wA, uint4 &wB, uint2 &s, uint4 &l0, uint4 &l1,
-                  const uint4 &n0, const uint4 &n1) __attribute__((always_inline)) {
+  // barrier.  (wA, wB, s): this chunk's ring slot.
+  auto step = [&](auto first, int c, uint4 &wA, uint4 &wB, uint2 &s)
+      __attribute__((always_inline)) {
     // keep the scheduler from pulling the next step's transposes (and so the
     // wait for its weights) into this one: that would shorten the prefetch
     __builtin_amdgcn_sched_barrier(0);
@@ -1601,19 +1601,19 @@ __device__ __forceinline__ void mfma_pass(const GemvArgs &a, K6Lds &L, int item,
   const std::integral_constant<int, 3> win6;
   if constexpr (SW) {
     for (int c0 = 0; c0 < nch; c0 += 8) {
-      step(win0, c0, wa0, wa1, sa, xa0, xa1, xa0, xa1);
-      step(nowin, c0 + 1, wb0, wb1, sb, xa0, xa1, xa0, xa1);
-      step(nowin, c0 + 2, wa0, wa1, sa, xa0, xa1, xa0, xa1);
-      step(win3, c0 + 3, wb0, wb1, sb, xa0, xa1, xa0, xa1);
-      step(nowin, c0 + 4, wa0, wa1, sa, xa0, xa1, xa0, xa1);
-      step(nowin, c0 + 5, wb0, wb1, sb, xa0, xa1, xa0, xa1);
-      step(win6, c0 + 6, wa0, wa1, sa, xa0, xa1, xa0, xa1);
-      step(nowin, c0 + 7, wb0, wb1, sb, xa0, xa1, xa0, xa1);
+      step(win0, c0, wa0, wa1, sa);
+      step(nowin, c0 + 1, wb0, wb1, sb);
+      step(nowin, c0 + 2, wa0, wa1, sa);
+      step(win3, c0 + 3, wb0, wb1, sb);
+      step(nowin, c0 + 4, wa0, wa1, sa);
+      step(nowin, c0 + 5, wb0, wb1, sb);
+      step(win6, c0 + 6, wa0, wa1, sa);
+      step(nowin, c0 + 7, wb0, wb1, sb);
     }
   } else {
     for (int c0 = 0; c0 < nch; c0 += K6_PD) {
-      step(nowin, c0, wa0, wa1, sa, xa0, xa1, xa0, xa1);
-      step(nowin, c0 + 1, wb0, wb1, sb, xa0, xa1, xa0, xa1);
+      step(nowin, c0, wa0, wa1, sa);
+      step(nowin, c0 + 1, wb0, wb1, sb);
     }
   }
   // C lane layout: token column t*16 + 4*lg + i, weight row row0 + 16*g + lr.
