@@ -514,11 +514,12 @@ def test_matrix_core_extreme_scales(scale, mode):
     r.close()
 
 
-@pytest.mark.parametrize("d,f", [(1024, 3072), (3072, 1024)])
+@pytest.mark.parametrize("d,f", [(1024, 3072), (3072, 1024), (1280, 2816)])
 def test_matrix_core_scale_windows(d, f):
-    """Matrix-core calls on rows of 32 and 96 blocks: the scale windows of 32
-    blocks then number one and three (the large shape has six and two), and a
-    40-token call has a pass of 8 tokens after one of 32."""
+    """Matrix-core calls on rows of 32 and 96 blocks, where the scale windows of
+    32 blocks number one and three (the large shape has six and two), and on
+    rows of 40 and 88 blocks, which take per-chunk scales; a 40-token call has
+    a pass of 8 tokens after one of 32."""
     wl = synth.Workload(f"win_{d}_{f}", 70 + d // 1024, 1, d, f, 16, 4, 6, n_shared=1,
                         router_sigma=0.4 / np.sqrt(d), zipf_s=0.5, rho=None, tokens=40 * 3,
                         batch=40)
