@@ -370,18 +370,22 @@ struct KTime {
   KTime(moe_cache *c_, int kid_, hipStream_t st) : c(c_), kid(kid_) {
     if (c->kmask & (1u << kid)) {
       TimingLog &lg = c->kt[kid].log;
-      w = lg.get();
-      a = lg.get();
-      b = lg.get();
-      HIPCHK(hipEventRecord(w, st));
+      try {
+        w = lg.get();
+        a = lg.get();
+        b = lg.get();
+        HIPCHK(hipEventRecord(w, st));
+      } catch (...) {  // the destructor does not run for a throwing constructor
+        release();
+        throw;
+      }
       moe::set_launch_events(a, b);
     }
   }
   void release() {
     TimingLog &lg = c->kt[kid].log;
-    lg.put_back(w);
-    lg.put_back(a);
-    lg.put_back(b);
+    for (hipEvent_t e : {w, a, b})
+      if (e) lg.put_back(e);
     w = a = b = nullptr;
   }
   void end(double bytes) {
